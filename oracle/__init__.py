@@ -1,0 +1,228 @@
+"""ctypes wrapper around the CPU oracle ``libnf4ref.so``.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package. It shares no code
+with the GPU library ``nf4_quantize_amd`` and never imports it.
+
+Every function takes and returns numpy arrays on the host. The arithmetic lives
+in ``nf4ref.c``; this module only marshals arguments.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnf4ref.so")
+_lib = None
+
+BLOCK = 64
+DQ_BLOCK = 256
+F32, BF16 = 0, 1
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            _build.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.nf4ref_codebook.argtypes = [_p]
+        L.nf4ref_normal_quantile.argtypes = [ctypes.c_double]
+        L.nf4ref_normal_quantile.restype = ctypes.c_double
+        L.nf4ref_construct_codebook.argtypes = [ctypes.c_double, _p]
+        L.nf4ref_solve_delta.argtypes = [ctypes.c_double]
+        L.nf4ref_solve_delta.restype = ctypes.c_double
+        L.nf4ref_nearest_code.argtypes = [ctypes.c_float]
+        L.nf4ref_nearest_code_array.argtypes = [_p, _i64, _p]
+        L.nf4ref_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.nf4ref_bf16_to_f32.restype = ctypes.c_float
+        L.nf4ref_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.nf4ref_f32_to_bf16.restype = ctypes.c_uint16
+        L.nf4ref_f32_to_bf16_array.argtypes = [_p, _i64, _p]
+        L.nf4ref_quantize.argtypes = [_p, ctypes.c_int, _i64, _p, _p]
+        L.nf4ref_e4m3_encode.argtypes = [ctypes.c_float]
+        L.nf4ref_e4m3_encode.restype = ctypes.c_uint8
+        L.nf4ref_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.nf4ref_e4m3_decode.restype = ctypes.c_float
+        L.nf4ref_e4m3_encode_array.argtypes = [_p, _i64, _p]
+        L.nf4ref_double_quantize.argtypes = [_p, _i64, _p, _p]
+        L.nf4ref_block_scale.argtypes = [_i64, _p, _p, _p]
+        L.nf4ref_block_scale.restype = ctypes.c_float
+        L.nf4ref_dequantize.argtypes = [_p, _i64, _p, _p, _p, _p, ctypes.c_int]
+        L.nf4ref_storage_bytes.argtypes = [_i64, ctypes.c_int]
+        L.nf4ref_storage_bytes.restype = _i64
+        for name in ("nf4ref_linear_forward", "nf4ref_linear_backward_input"):
+            getattr(L, name).argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i32,
+                                         ctypes.c_double, _p, _i64, _p, _i64, _p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its input (status {rc})")
+
+
+def _as_bits(w):
+    """Returns (array, dtype code) for fp32 arrays or bf16 given as uint16 bits."""
+    w = np.ascontiguousarray(w)
+    if w.dtype == np.float32:
+        return w, F32
+    if w.dtype == np.uint16:
+        return w, BF16
+    raise TypeError("oracle inputs are float32 or bf16 bit patterns (uint16)")
+
+
+def codebook():
+    q = np.zeros(16, np.float32)
+    lib().nf4ref_codebook(_ptr(q))
+    return q
+
+
+def construct_codebook(delta):
+    out = np.zeros(16, np.float64)
+    _check(lib().nf4ref_construct_codebook(float(delta), _ptr(out)), "construct_codebook")
+    return out
+
+
+def normal_quantile(p):
+    return lib().nf4ref_normal_quantile(float(p))
+
+
+def solve_delta(level14):
+    return lib().nf4ref_solve_delta(float(level14))
+
+
+def nearest_code(n):
+    return int(lib().nf4ref_nearest_code(float(np.float32(n))))
+
+
+def nearest_code_array(n):
+    n = np.ascontiguousarray(n, dtype=np.float32)
+    out = np.zeros(n.shape, np.uint8)
+    _check(lib().nf4ref_nearest_code_array(_ptr(n), n.size, _ptr(out)), "nearest_code_array")
+    return out
+
+
+def f32_to_bf16(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    _check(lib().nf4ref_f32_to_bf16_array(_ptr(x), x.size, _ptr(out)), "f32_to_bf16")
+    return out
+
+
+def bf16_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def nblocks(n):
+    return (n + BLOCK - 1) // BLOCK
+
+
+def ngroups(n):
+    return (nblocks(n) + DQ_BLOCK - 1) // DQ_BLOCK
+
+
+def quantize(w):
+    """Blockwise NF4: returns (packed codes uint8[ceil(n/2)], absmax float32[ceil(n/64)])."""
+    w, dt = _as_bits(w)
+    n = w.size
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    absmax = np.zeros(nblocks(n), np.float32)
+    _check(lib().nf4ref_quantize(_ptr(w), dt, n, _ptr(codes), _ptr(absmax)), "quantize")
+    return codes, absmax
+
+
+def double_quantize(absmax):
+    absmax = np.ascontiguousarray(absmax, dtype=np.float32)
+    nb = absmax.size
+    q = np.zeros(nb, np.uint8)
+    scale = np.zeros((nb + DQ_BLOCK - 1) // DQ_BLOCK, np.float32)
+    _check(lib().nf4ref_double_quantize(_ptr(absmax), nb, _ptr(q), _ptr(scale)),
+           "double_quantize")
+    return q, scale
+
+
+def e4m3_encode(r):
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    out = np.zeros(r.shape, np.uint8)
+    _check(lib().nf4ref_e4m3_encode_array(_ptr(r), r.size, _ptr(out)), "e4m3_encode")
+    return out
+
+
+def e4m3_decode(c):
+    f = lib().nf4ref_e4m3_decode
+    return np.array([f(int(v)) for v in np.asarray(c).ravel()], np.float32)
+
+
+def dequantize(codes, n, absmax=None, q=None, scale=None, out_dtype=F32):
+    """Returns float32[n] (out_dtype F32) or bf16 bit patterns uint16[n] (BF16)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    out = np.zeros(n, np.float32 if out_dtype == F32 else np.uint16)
+    _check(lib().nf4ref_dequantize(_ptr(codes), n, _ptr(absmax), _ptr(q), _ptr(scale),
+                                   _ptr(out), out_dtype), "dequantize")
+    return out
+
+
+def storage_bytes(n, dq):
+    return int(lib().nf4ref_storage_bytes(int(n), 1 if dq else 0))
+
+
+def _index(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int64)
+
+
+def linear_forward(x, wdeq, A=None, B=None, s=1.0, rows=None, cols=None):
+    """x: bf16 bits uint16 [m,K]; wdeq: float32 [N,K]; A: uint16 [K,r]; B: uint16 [r,N].
+    Returns float64 [len(rows), len(cols)]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    wdeq = np.ascontiguousarray(wdeq, dtype=np.float32)
+    m, K = x.shape
+    N = wdeq.shape[0]
+    assert wdeq.shape[1] == K
+    r = 0 if A is None else A.shape[1]
+    A = None if A is None else np.ascontiguousarray(A, dtype=np.uint16)
+    B = None if B is None else np.ascontiguousarray(B, dtype=np.uint16)
+    rows, cols = _index(rows), _index(cols)
+    nr = m if rows is None else rows.size
+    nc = N if cols is None else cols.size
+    out = np.zeros((nr, nc), np.float64)
+    _check(lib().nf4ref_linear_forward(_ptr(x), m, K, N, _ptr(wdeq), _ptr(A), _ptr(B), r,
+                                       float(s), _ptr(rows), nr, _ptr(cols), nc, _ptr(out)),
+           "linear_forward")
+    return out
+
+
+def linear_backward_input(dy, wdeq, A=None, B=None, s=1.0, rows=None, cols=None):
+    """dy: bf16 bits uint16 [m,N]; wdeq: float32 [N,K]. Returns float64 [len(rows), len(cols)]."""
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    wdeq = np.ascontiguousarray(wdeq, dtype=np.float32)
+    m, N = dy.shape
+    K = wdeq.shape[1]
+    assert wdeq.shape[0] == N
+    r = 0 if A is None else A.shape[1]
+    A = None if A is None else np.ascontiguousarray(A, dtype=np.uint16)
+    B = None if B is None else np.ascontiguousarray(B, dtype=np.uint16)
+    rows, cols = _index(rows), _index(cols)
+    nr = m if rows is None else rows.size
+    nc = K if cols is None else cols.size
+    out = np.zeros((nr, nc), np.float64)
+    _check(lib().nf4ref_linear_backward_input(_ptr(dy), m, K, N, _ptr(wdeq), _ptr(A), _ptr(B),
+                                              r, float(s), _ptr(rows), nr, _ptr(cols), nc,
+                                              _ptr(out)), "linear_backward_input")
+    return out

@@ -1,0 +1,416 @@
+/*
+ * nf4ref.c - CPU oracle for blockwise NF4 quantization, double quantization,
+ * dequantization and the QLoRA linear (forward and input gradient).
+ *
+ * TEST INFRASTRUCTURE ONLY: plain, slow, single-threaded C11, written step by
+ * step from the defining equations. It is built with -O2 -ffp-contract=off and
+ * no fast-math, so every float operation below is one IEEE-754 binary32
+ * operation rounded to nearest even (x86-64 SSE, FLT_EVAL_METHOD == 0).
+ * It shares no code with the GPU library. Source keys are listed in nf4ref.h.
+ *
+ * Readings where the pages are silent (each is also listed with its reason in
+ * the design notes of the repository):
+ *   - division w/c1 and c1/c2 are correctly rounded fp32 divisions;
+ *   - the argmin is taken over fp32 distances |fl32(n - q_i)|, lowest index on ties;
+ *   - a block with c1 == 0 gets code 7 (the exact zero level) everywhere;
+ *   - the double-quantization 8-bit format is OCP FP8 E4M3FN, round to nearest
+ *     even; c2 == 0 gives code 0 for every block of the group;
+ *   - the reconstructed scale is fl32(decode(code8) * c2), then the weight is
+ *     fl32(q[code] * scale); bf16 output rounds that fp32 value to nearest even;
+ *   - non-finite inputs are outside the contract and rejected (-2).
+ */
+#include "nf4ref.h"
+
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+_Static_assert(FLT_EVAL_METHOD == 0, "float expressions must evaluate in binary32");
+
+/* [MF] "4-Bit NormalFloat (NF4)": the printed list q_0 .. q_15. Each printed
+ * decimal is an exact binary32 value. */
+static const float NF4_Q[16] = {
+    -1.0f,
+    -0.6961928009986877f,
+    -0.5250730514526367f,
+    -0.39491748809814453f,
+    -0.28444138169288635f,
+    -0.18477343022823334f,
+    -0.09105003625154495f,
+    0.0f,
+    0.07958029955625534f,
+    0.16093020141124725f,
+    0.24611230194568634f,
+    0.33791524171829224f,
+    0.44070982933044434f,
+    0.5626170039176941f,
+    0.7229568362236023f,
+    1.0f,
+};
+
+void nf4ref_codebook(float q[16]) {
+    for (int i = 0; i < 16; ++i) q[i] = NF4_Q[i];
+}
+
+/* ---- codebook construction check ([MF] "4-Bit NormalFloat (NF4)") ---- */
+
+/* Lower-tail probability P(Z <= x) of the standard normal. */
+static double std_normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+double nf4ref_normal_quantile(double p) {
+    if (!(p > 0.0 && p < 1.0)) return NAN;
+    /* Bisect on the smaller tail (1 - p is exact for p >= 1/2), then use the
+     * symmetry quantile(p) = -quantile(1 - p). */
+    double tail = p < 0.5 ? p : 1.0 - p;
+    double lo = -40.0, hi = 0.0;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (std_normal_cdf(mid) < tail)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double x = 0.5 * (lo + hi);
+    return p < 0.5 ? x : -x;
+}
+
+int nf4ref_construct_codebook(double delta, double out[16]) {
+    if (!out || !(delta > 0.5 && delta < 1.0)) return -1;
+    /* Positive half: 8 levels at probabilities delta - i*(delta-1/2)/8, i=0..7
+     * (the 9th point of that grid is 1/2, whose quantile is the zero level).
+     * Negative half: 7 levels at delta - j*(delta-1/2)/7, j=0..6, mirrored. */
+    double top = nf4ref_normal_quantile(delta);
+    for (int i = 0; i < 8; ++i) {
+        double p = delta - (double)i * (delta - 0.5) / 8.0;
+        out[15 - i] = nf4ref_normal_quantile(p) / top;
+    }
+    out[7] = 0.0;
+    for (int j = 0; j < 7; ++j) {
+        double p = delta - (double)j * (delta - 0.5) / 7.0;
+        out[j] = -nf4ref_normal_quantile(p) / top;
+    }
+    return 0;
+}
+
+double nf4ref_solve_delta(double level14) {
+    double lo = 0.9, hi = 0.9999, v[16];
+    /* Level 14 of the construction decreases as delta grows on this interval:
+     * the normaliser quantile(delta) grows faster than quantile of the next
+     * probability down. */
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        nf4ref_construct_codebook(mid, v);
+        if (v[14] > level14)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+/* ---- nearest level ([MF] "Block-Wise Quantization Mechanics", argmin) ---- */
+
+int nf4ref_nearest_code(float n) {
+    int best = 0;
+    float best_d = fabsf(n - NF4_Q[0]);
+    for (int i = 1; i < 16; ++i) {
+        float d = fabsf(n - NF4_Q[i]);
+        if (d < best_d) { /* strict: on equal distance the lower index stays */
+            best_d = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+int nf4ref_nearest_code_array(const float *n, int64_t count, uint8_t *out) {
+    if (count < 0 || (count > 0 && (!n || !out))) return -1;
+    for (int64_t i = 0; i < count; ++i) out[i] = (uint8_t)nf4ref_nearest_code(n[i]);
+    return 0;
+}
+
+/* ---- bf16 ---- */
+
+static uint32_t f32_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+static float bits_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+float nf4ref_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+uint16_t nf4ref_f32_to_bf16(float f) {
+    /* bf16 keeps the upper 16 bits of binary32. The two candidates are the
+     * truncation and the next value up in magnitude; pick the nearer, and on
+     * an exact halfway point the one whose last kept bit is 0. */
+    uint32_t u = f32_bits(f);
+    uint32_t down = u & 0xFFFF0000u;
+    uint32_t rest = u & 0x0000FFFFu;
+    uint32_t up = down + 0x00010000u;
+    uint32_t pick;
+    if (rest > 0x8000u)
+        pick = up;
+    else if (rest < 0x8000u)
+        pick = down;
+    else
+        pick = ((down >> 16) & 1u) ? up : down;
+    return (uint16_t)(pick >> 16);
+}
+
+int nf4ref_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out) {
+    if (n < 0 || (n > 0 && (!x || !out))) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = nf4ref_f32_to_bf16(x[i]);
+    return 0;
+}
+
+/* ---- blockwise quantization ([MF] "Block-Wise Quantization Mechanics") ---- */
+
+static float load_elem(const void *w, int dtype, int64_t i) {
+    if (dtype == NF4REF_F32) return ((const float *)w)[i];
+    return nf4ref_bf16_to_f32(((const uint16_t *)w)[i]);
+}
+
+int nf4ref_quantize(const void *w, int dtype, int64_t n, uint8_t *codes, float *absmax) {
+    if (n < 0) return -1;
+    if (n == 0) return 0;
+    if (!w || !codes || !absmax) return -1;
+    if (dtype != NF4REF_F32 && dtype != NF4REF_BF16) return -1;
+    int64_t nblocks = (n + NF4REF_BLOCK - 1) / NF4REF_BLOCK;
+    memset(codes, 0, (size_t)((n + 1) / 2));
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int64_t lo = b * NF4REF_BLOCK;
+        int64_t hi = lo + NF4REF_BLOCK < n ? lo + NF4REF_BLOCK : n;
+        /* c1 = max |w| over the block. */
+        float c1 = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            float v = load_elem(w, dtype, i);
+            if (!isfinite(v)) return -2;
+            if (fabsf(v) > c1) c1 = fabsf(v);
+        }
+        absmax[b] = c1;
+        for (int64_t i = lo; i < hi; ++i) {
+            int code;
+            if (c1 == 0.0f) {
+                code = 7; /* the exact zero level */
+            } else {
+                float nrm = load_elem(w, dtype, i) / c1;
+                code = nf4ref_nearest_code(nrm);
+            }
+            codes[i / 2] |= (uint8_t)(code << (4 * (int)(i & 1)));
+        }
+    }
+    return 0;
+}
+
+/* ---- OCP FP8 E4M3FN ---- */
+
+uint8_t nf4ref_e4m3_encode(float r) {
+    /* E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinity,
+     * largest finite 448. Round to nearest, ties to even mantissa. Codes of
+     * non-negative values are monotone in value, so a mantissa that rounds up
+     * to 8 carries into the exponent by plain addition. */
+    uint8_t sign = 0;
+    double v = (double)r;
+    if (isnan(r)) return 0x7F;
+    if (v < 0) {
+        sign = 0x80;
+        v = -v;
+    }
+    if (v == 0.0) return sign;
+    if (v >= 464.0) return (uint8_t)(sign | 0x7E); /* beyond max + half step: saturate */
+    uint8_t code;
+    if (v < ldexp(1.0, -6)) {
+        /* subnormal range: value = m * 2^-9, m = 0..7; m == 8 is code 0x08 = 2^-6 */
+        code = (uint8_t)rint(v * 512.0);
+    } else {
+        int e2;
+        double f = frexp(v, &e2); /* v = f * 2^e2, f in [0.5, 1) */
+        int e = e2 - 1;           /* v = s * 2^e, s in [1, 2) */
+        double s = 2.0 * f;
+        int mant = (int)rint((s - 1.0) * 8.0);
+        int c = ((e + 7) << 3) + mant;
+        if (c > 0x7E) c = 0x7E;
+        code = (uint8_t)c;
+    }
+    return (uint8_t)(sign | code);
+}
+
+float nf4ref_e4m3_decode(uint8_t c) {
+    int s = (c >> 7) & 1;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return (float)(s ? -v : v);
+}
+
+int nf4ref_e4m3_encode_array(const float *r, int64_t n, uint8_t *out) {
+    if (n < 0 || (n > 0 && (!r || !out))) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = nf4ref_e4m3_encode(r[i]);
+    return 0;
+}
+
+/* ---- double quantization ([MF] "Double Quantization (DQ)") ---- */
+
+int nf4ref_double_quantize(const float *absmax, int64_t nblocks, uint8_t *q, float *scale) {
+    if (nblocks < 0) return -1;
+    if (nblocks == 0) return 0;
+    if (!absmax || !q || !scale) return -1;
+    int64_t ngroups = (nblocks + NF4REF_DQ_BLOCK - 1) / NF4REF_DQ_BLOCK;
+    for (int64_t g = 0; g < ngroups; ++g) {
+        int64_t lo = g * NF4REF_DQ_BLOCK;
+        int64_t hi = lo + NF4REF_DQ_BLOCK < nblocks ? lo + NF4REF_DQ_BLOCK : nblocks;
+        float c2 = 0.0f;
+        for (int64_t b = lo; b < hi; ++b) {
+            if (!isfinite(absmax[b])) return -2;
+            if (fabsf(absmax[b]) > c2) c2 = fabsf(absmax[b]);
+        }
+        scale[g] = c2;
+        for (int64_t b = lo; b < hi; ++b) {
+            float ratio = (c2 == 0.0f) ? 0.0f : absmax[b] / c2;
+            q[b] = nf4ref_e4m3_encode(ratio);
+        }
+    }
+    return 0;
+}
+
+/* ---- dequantization ([MF] "Block-Wise Quantization Mechanics", the
+ *      reconstruction equation, and the dequantize(c1, c2, W) of
+ *      "Forward Pass Computation") ---- */
+
+float nf4ref_block_scale(int64_t b, const float *absmax, const uint8_t *q, const float *scale) {
+    if (!q) return absmax[b];
+    return nf4ref_e4m3_decode(q[b]) * scale[b / NF4REF_DQ_BLOCK];
+}
+
+int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
+                      const float *scale, void *out, int out_dtype) {
+    if (n < 0) return -1;
+    if (n == 0) return 0;
+    if (!codes || !out) return -1;
+    if (!q && !absmax) return -1;
+    if (q && !scale) return -1;
+    if (out_dtype != NF4REF_F32 && out_dtype != NF4REF_BF16) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        int code = (codes[i / 2] >> (4 * (int)(i & 1))) & 15;
+        float c1 = nf4ref_block_scale(i / NF4REF_BLOCK, absmax, q, scale);
+        float v = NF4_Q[code] * c1;
+        if (out_dtype == NF4REF_F32)
+            ((float *)out)[i] = v;
+        else
+            ((uint16_t *)out)[i] = nf4ref_f32_to_bf16(v);
+    }
+    return 0;
+}
+
+/* ---- storage footprint ([L15] "Double quantisation" per-parameter tables) ---- */
+
+int64_t nf4ref_storage_bytes(int64_t n, int dq) {
+    if (n < 0) return -1;
+    int64_t nblocks = (n + NF4REF_BLOCK - 1) / NF4REF_BLOCK;
+    int64_t ngroups = (nblocks + NF4REF_DQ_BLOCK - 1) / NF4REF_DQ_BLOCK;
+    int64_t code_bytes = (n + 1) / 2;
+    if (!dq) return code_bytes + 4 * nblocks;
+    return code_bytes + nblocks + 4 * ngroups;
+}
+
+/* ---- QLoRA linear ([MF] "Forward Pass Computation", "Gradient Computation") ---- */
+
+int nf4ref_linear_forward(const uint16_t *x, int64_t m, int64_t K, int64_t N, const float *wdeq,
+                          const uint16_t *A, const uint16_t *B, int32_t r, double s,
+                          const int64_t *rows, int64_t nrows, const int64_t *cols, int64_t ncols,
+                          double *out) {
+    if (!x || !wdeq || !out || m < 0 || K < 0 || N < 0 || r < 0) return -1;
+    int lora = (A != NULL && r > 0);
+    if (lora && !B) return -1;
+    if (!rows) nrows = m;
+    if (!cols) ncols = N;
+    double t[4096];
+    if (r > 4096) return -1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t row = rows ? rows[i] : i;
+        if (row < 0 || row >= m) return -1;
+        const uint16_t *xr = x + row * K;
+        /* adapter down-projection of this row: t = x_row . A (r values) */
+        if (lora) {
+            for (int32_t c = 0; c < r; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += (double)nf4ref_bf16_to_f32(xr[k]) *
+                           (double)nf4ref_bf16_to_f32(A[k * r + c]);
+                t[c] = acc;
+            }
+        }
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t col = cols ? cols[j] : j;
+            if (col < 0 || col >= N) return -1;
+            const float *wr = wdeq + col * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)nf4ref_bf16_to_f32(xr[k]) * (double)wr[k];
+            if (lora) {
+                double side = 0.0;
+                for (int32_t c = 0; c < r; ++c)
+                    side += t[c] * (double)nf4ref_bf16_to_f32(B[(int64_t)c * N + col]);
+                acc += s * side;
+            }
+            out[i * ncols + j] = acc;
+        }
+    }
+    return 0;
+}
+
+int nf4ref_linear_backward_input(const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                                 const float *wdeq, const uint16_t *A, const uint16_t *B,
+                                 int32_t r, double s, const int64_t *rows, int64_t nrows,
+                                 const int64_t *cols, int64_t ncols, double *out) {
+    if (!dy || !wdeq || !out || m < 0 || K < 0 || N < 0 || r < 0) return -1;
+    int lora = (A != NULL && r > 0);
+    if (lora && !B) return -1;
+    if (!rows) nrows = m;
+    if (!cols) ncols = K;
+    double u[4096];
+    if (r > 4096) return -1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t row = rows ? rows[i] : i;
+        if (row < 0 || row >= m) return -1;
+        const uint16_t *gr = dy + row * N;
+        /* u = dy_row . B^T (r values) */
+        if (lora) {
+            for (int32_t c = 0; c < r; ++c) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += (double)nf4ref_bf16_to_f32(gr[n]) *
+                           (double)nf4ref_bf16_to_f32(B[(int64_t)c * N + n]);
+                u[c] = acc;
+            }
+        }
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t col = cols ? cols[j] : j;
+            if (col < 0 || col >= K) return -1;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                acc += (double)nf4ref_bf16_to_f32(gr[n]) * (double)wdeq[n * K + col];
+            if (lora) {
+                double side = 0.0;
+                for (int32_t c = 0; c < r; ++c)
+                    side += u[c] * (double)nf4ref_bf16_to_f32(A[col * r + c]);
+                acc += s * side;
+            }
+            out[i * ncols + j] = acc;
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,120 @@
+/*
+ * nf4ref.h - CPU oracle for blockwise NF4 quantization with double quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY. This library is the slow, plain reference that the
+ * GPU library is checked against. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it. It shares no code, header, table or
+ * constant generator with the GPU library, and it includes nothing from it.
+ *
+ * Sources (web pages), cited by title and section:
+ *   [MF]  "QLoRA: Mathematical Foundations of 4-Bit NormalFloat Quantization,
+ *          Double Quantization, and Paged Optimizers" (llms.blog)
+ *   [L15] "Lesson 15. NF4 and Double Quantisation" (tokencemetery)
+ *   [QP]  "QLoRA in Production: 4-bit NormalFloat & Double Quantization Deep
+ *          Dive" (devtechtools.org)
+ *
+ * Fixed parameters: block size B1 = 64 ([MF] "Block-Wise Quantization
+ * Mechanics"), double-quantization block B2 = 256 ([MF] "Double Quantization").
+ *
+ * Layout conventions (the pages leave them open; they are readings, not pins):
+ *   - codes: two 4-bit codes per byte, element 2j in the low nibble, element
+ *     2j+1 in the high nibble; for odd n the last high nibble is 0.
+ *     PARITY UNPINNED (a storage convention the pages do not fix).
+ *   - blocks are consecutive runs of 64 elements of the flattened tensor; the
+ *     last block may be partial and takes the max over its valid elements.
+ *
+ * All functions return 0 on success and a negative value on invalid input
+ * (NULL pointer, negative size, non-finite input).
+ */
+#ifndef NF4REF_H
+#define NF4REF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4REF_BLOCK 64
+#define NF4REF_DQ_BLOCK 256
+
+enum { NF4REF_F32 = 0, NF4REF_BF16 = 1 };
+
+/* The 16 NF4 levels exactly as printed in [MF] "4-Bit NormalFloat (NF4)". */
+void nf4ref_codebook(float q[16]);
+
+/* Standard normal quantile (inverse CDF) by bisection on 0.5*erfc(-x/sqrt 2). */
+double nf4ref_normal_quantile(double p);
+
+/* The asymmetric quantile construction of [MF] "4-Bit NormalFloat (NF4)":
+ * 8 positive levels from probabilities evenly spaced from delta down to 1/2,
+ * 7 negative levels likewise, an exact zero, all divided by the largest.
+ * Writes 16 ascending levels. */
+int nf4ref_construct_codebook(double delta, double out[16]);
+
+/* Solves the tail probability delta for which the construction's level 14
+ * equals `level14` (bisection on [0.9, 0.9999]). */
+double nf4ref_solve_delta(double level14);
+
+/* Nearest-level code of one normalised value n: the first index i that
+ * minimises |fl32(n - q_i)| ([MF] "Block-Wise Quantization Mechanics", argmin). */
+int nf4ref_nearest_code(float n);
+int nf4ref_nearest_code_array(const float *n, int64_t count, uint8_t *out);
+
+/* bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even. */
+float nf4ref_bf16_to_f32(uint16_t h);
+uint16_t nf4ref_f32_to_bf16(float f);
+int nf4ref_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);
+
+/* Blockwise NF4 quantization of n elements (dtype NF4REF_F32 or NF4REF_BF16).
+ * codes: ceil(n/2) bytes. absmax: ceil(n/64) floats. */
+int nf4ref_quantize(const void *w, int dtype, int64_t n, uint8_t *codes, float *absmax);
+
+/* OCP FP8 E4M3FN encode / decode (double-quantization code format). */
+uint8_t nf4ref_e4m3_encode(float r);
+float nf4ref_e4m3_decode(uint8_t c);
+int nf4ref_e4m3_encode_array(const float *r, int64_t n, uint8_t *out);
+
+/* Double quantization of nblocks fp32 absmax values. q: nblocks bytes.
+ * scale: ceil(nblocks/256) floats. */
+int nf4ref_double_quantize(const float *absmax, int64_t nblocks, uint8_t *q, float *scale);
+
+/* Reconstructed first-level scale of block b: absmax[b] when q == NULL, else
+ * fl32(decode(q[b]) * scale[b/256]). */
+float nf4ref_block_scale(int64_t b, const float *absmax, const uint8_t *q, const float *scale);
+
+/* Dequantization to fp32 (out_dtype NF4REF_F32) or bf16 (NF4REF_BF16).
+ * Uses absmax when q == NULL, else (q, scale). */
+int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
+                      const float *scale, void *out, int out_dtype);
+
+/* Storage bytes of an n-element NF4 tensor: codes + scales (dq != 0: 8-bit
+ * codes plus fp32 second-level scales; dq == 0: fp32 absmax). */
+int64_t nf4ref_storage_bytes(int64_t n, int dq);
+
+/* Forward of the QLoRA linear ([MF] "Forward Pass Computation") on selected
+ * rows and columns, in double with no intermediate rounding:
+ *   out[i][j] = sum_k x[rows[i],k] * wdeq[cols[j],k]
+ *             + s * sum_t (sum_k x[rows[i],k] * A[k,t]) * B[t,cols[j]]
+ * x: bf16 [m x K]; wdeq: fp32 [N x K] (the dequantized weight, stored
+ * [d_out x d_in]); A: bf16 [K x r]; B: bf16 [r x N]; A == NULL or r == 0
+ * skips the adapter. rows/cols may be NULL (all). out: double [nrows x ncols]. */
+int nf4ref_linear_forward(const uint16_t *x, int64_t m, int64_t K, int64_t N, const float *wdeq,
+                          const uint16_t *A, const uint16_t *B, int32_t r, double s,
+                          const int64_t *rows, int64_t nrows, const int64_t *cols, int64_t ncols,
+                          double *out);
+
+/* Input gradient ([MF] "Gradient Computation", the activation-gradient
+ * equation) on selected rows and columns, in double:
+ *   out[i][j] = sum_n dy[rows[i],n] * wdeq[n,cols[j]]
+ *             + s * sum_t (sum_n dy[rows[i],n] * B[t,n]) * A[cols[j],t]
+ * dy: bf16 [m x N]. out: double [nrows x ncols]. */
+int nf4ref_linear_backward_input(const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                                 const float *wdeq, const uint16_t *A, const uint16_t *B,
+                                 int32_t r, double s, const int64_t *rows, int64_t nrows,
+                                 const int64_t *cols, int64_t ncols, double *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
