@@ -1,0 +1,381 @@
+"""Benchmark of the NF4 storage hot path on one MI355X.
+
+A step is one pass of the whole storage path over the 11008 x 4096 bf16 MLP
+weight (N(0, 0.02^2), 0.1% outliers x10): blockwise NF4 quantization with the
+double quantization fused in, then dequantization back to bf16. The step's
+value is algorithmic HBM bytes per second (inputs read once, outputs written
+once). Inputs are resident in HBM; four input/output sets rotate so that the
+256 MB last-level cache never holds a step's input from the previous use.
+
+Printed: one JSON line with the contract fields, plus
+  roofline      the dominant kernel (quantize), bytes / HIP-event duration
+  cpu_baseline  the CPU oracle on the same workload (single thread)
+  kernels       every kernel of the path measured alone: quantize and
+                dequantize on the 1024x1024 fp32 and 11008x4096 bf16 weights,
+                the decode GEMV (M = 1, 4, 16 on 28672 x 8192) and the QLoRA
+                linear forward / input gradient (4096 x 8192 x 8192, r = 64).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-kernels]
+                       [--no-cpu-baseline] [--stack]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bytes_quantize(n, in_bytes):
+    """Algorithmic bytes of quantize + fused DQ: input once, packed output once."""
+    import nf4_quantize_amd as nq
+
+    return n * in_bytes + nq.nf4_storage_bytes(n)
+
+
+def bytes_dequantize(n, out_bytes):
+    import nf4_quantize_amd as nq
+
+    return nq.nf4_storage_bytes(n) + n * out_bytes
+
+
+class Events:
+    """HIP events recorded on torch's current stream (the stream the library
+    launches on)."""
+
+    def __init__(self, count):
+        import torch
+
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+
+    def __getitem__(self, i):
+        return self.ev[i]
+
+
+def time_op(fn, iters, warmup):
+    """Median / mean milliseconds of fn() by HIP events around each call."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = Events(2 * iters)
+    for i in range(iters):
+        ev[2 * i].record()
+        fn(i)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters))
+    return ms[len(ms) // 2], sum(ms) / len(ms)
+
+
+def make_sets(dev, w_host_bits, nsets):
+    import torch
+    import nf4_quantize_amd as nq
+
+    base = torch.from_numpy(w_host_bits.reshape(-1).view("int16")).view(torch.bfloat16).to(dev)
+    sets = []
+    for _ in range(nsets):
+        w = base.clone()
+        packed = nq.empty_nf4(tuple(w.shape), dev, double_quant=True)
+        out = torch.empty_like(w)
+        sets.append((w, packed, out))
+    del base
+    return sets
+
+
+def main_step_bench(args, dev):
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    shape = workloads.MLP_SHAPE
+    n = shape[0] * shape[1]
+    log(f"workload: {shape[0]}x{shape[1]} bf16, quantize+DQ then dequantize to bf16")
+    w_bits = workloads.weight_mlp_outliers_bf16()
+    sets = make_sets(dev, w_bits, 4)
+
+    def step(i):
+        w, p, o = sets[i % len(sets)]
+        nq.nf4_quantize(w, p.codes, None, p.absmax_q, p.absmax_scale)
+        nq.nf4_dequantize(p.codes, n, o, absmax_q=p.absmax_q, absmax_scale=p.absmax_scale)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = Events(3 * args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w, p, o = sets[i % len(sets)]
+        ev[3 * i].record()
+        nq.nf4_quantize(w, p.codes, None, p.absmax_q, p.absmax_scale)
+        ev[3 * i + 1].record()
+        nq.nf4_dequantize(p.codes, n, o, absmax_q=p.absmax_q, absmax_scale=p.absmax_scale)
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)]
+    d_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)]
+    qb = bytes_quantize(n, 2)
+    db = bytes_dequantize(n, 2)
+    step_bytes = qb + db
+    ms_per_step = wall * 1e3 / args.steps
+    q_avg = sum(q_ms) / len(q_ms)
+    d_avg = sum(d_ms) / len(d_ms)
+    res = {
+        "n": n,
+        "step_bytes": step_bytes,
+        "ms_per_step": ms_per_step,
+        "gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "quantize_ms": q_avg,
+        "dequantize_ms": d_avg,
+        "quantize_gbs": qb / (q_avg * 1e-3) / 1e9,
+        "dequantize_gbs": db / (d_avg * 1e-3) / 1e9,
+        "quantize_bytes": qb,
+        "dequantize_bytes": db,
+    }
+    # parity guard on the timed buffers: the last step's codes against a fresh run
+    del sets
+    torch.cuda.empty_cache()
+    return res, w_bits
+
+
+def cpu_baseline(w_bits, target_s=10.0):
+    """The CPU oracle (single thread) on the same weight: quantize, double
+    quantize, dequantize to bf16; repeated until about target_s seconds."""
+    import oracle
+
+    n = w_bits.size
+    flat = w_bits.reshape(-1)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        codes, absmax = oracle.quantize(flat)
+        q8, scale = oracle.double_quantize(absmax)
+        oracle.dequantize(codes, n, q=q8, scale=scale, out_dtype=oracle.BF16)
+        reps += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    step_bytes = (n * 2 + oracle.storage_bytes(n, True)) * 2
+    return {
+        "value": round(step_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole 11008x4096 bf16 weight, quantize+DQ+dequantize, {reps} passes "
+                  f"({dt:.2f} s each) on one host thread",
+    }
+
+
+def kernel_benches(dev, iters, warmup, with_stack):
+    import torch
+    import numpy as np
+    import nf4_quantize_amd as nq
+    import workloads
+
+    out = {}
+
+    # workload 1: 1024 x 1024 fp32 (launch-bound size)
+    w1 = torch.from_numpy(workloads.weight_1024_f32()).to(dev)
+    n1 = w1.numel()
+    p1 = nq.empty_nf4(tuple(w1.shape), dev)
+    o1 = torch.empty_like(w1)
+    ms, _ = time_op(lambda i: nq.nf4_quantize(w1, p1.codes, None, p1.absmax_q, p1.absmax_scale),
+                    iters, warmup)
+    out["quantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_quantize(n1, 4) / ms / 1e6}
+    ms, _ = time_op(lambda i: nq.nf4_dequantize(p1.codes, n1, o1, absmax_q=p1.absmax_q,
+                                                absmax_scale=p1.absmax_scale), iters, warmup)
+    out["dequantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_dequantize(n1, 4) / ms / 1e6}
+    log(f"1024x1024: {out['quantize_1024x1024_f32']} {out['dequantize_1024x1024_f32']}")
+
+    # workload 4: decode GEMV on a 28672 x 8192 NF4 weight, 4 rotating copies
+    N, K = workloads.GEMV_N, workloads.GEMV_K
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    wts = []
+    for c in range(4):
+        w = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        wts.append(nq.quantize(w))
+        del w
+    x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
+    wbytes = nq.nf4_storage_bytes(N * K)
+    for m in workloads.GEMV_MS:
+        xm = x[:m].contiguous()
+        ym = [torch.empty((m, N), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        ms, _ = time_op(lambda i: nq.linear_forward(xm, wts[i % 4], out=ym[i % 4]), iters, warmup)
+        byts = wbytes + m * K * 2 + m * N * 2
+        out[f"gemv_M{m}_28672x8192"] = {"ms": ms, "GB/s": byts / ms / 1e6,
+                                         "TFLOP/s": 2 * m * N * K / ms / 1e9,
+                                         "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS}
+        log(f"gemv M={m}: {out[f'gemv_M{m}_28672x8192']}")
+    del wts, x
+    torch.cuda.empty_cache()
+
+    # workload 5: QLoRA linear 4096 x 8192 x 8192, r = 64
+    M, N, K, r, s = (workloads.LIN_M, workloads.LIN_N, workloads.LIN_K, workloads.LIN_R,
+                     workloads.LIN_SCALE)
+    g.manual_seed(5)
+    w = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    wt = nq.quantize(w)
+    del w
+    X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    dY = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+    A = (torch.randn((K, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    B = (torch.randn((r, N), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nq.nf4_linear_workspace_size(M, r), dtype=torch.uint8, device=dev)
+    flops = 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+    lin_iters = max(3, iters // 2)
+    ms, _ = time_op(lambda i: nq.linear_forward(X, wt, A, B, s, out=Y, workspace=ws), lin_iters,
+                    max(1, warmup // 2))
+    out["linear_fwd_4096x8192x8192_r64"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                            "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
+    log(f"linear fwd: {out['linear_fwd_4096x8192x8192_r64']}")
+    ms, _ = time_op(lambda i: nq.linear_backward_input(dY, wt, A, B, s, out=dX, workspace=ws),
+                    lin_iters, max(1, warmup // 2))
+    out["linear_dgrad_4096x8192x8192_r64"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                              "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
+    log(f"linear dgrad: {out['linear_dgrad_4096x8192x8192_r64']}")
+    # practical ceiling: the vendor bf16 GEMM on a pre-dequantized weight
+    Wd = nq.dequantize(wt, torch.bfloat16)
+    ms, _ = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))
+    out["hipblaslt_bf16_4096x8192x8192_reference"] = {"ms": ms,
+                                                      "TFLOP/s": 2 * M * N * K / ms / 1e9}
+    del X, dY, A, B, Y, dX, ws, Wd, wt
+    torch.cuda.empty_cache()
+
+    if with_stack:
+        out.update(stack_bench(dev))
+    return out
+
+
+def stack_bench(dev):
+    """Workload 3: quantize all 224 matrices of a 32-layer 8B-shaped stack,
+    then stream-dequantize every matrix to bf16."""
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    mats = []
+    for layer in range(workloads.STACK_LAYERS):
+        for mi in range(len(workloads.STACK_MATRICES)):
+            mats.append(workloads.stack_matrix_bf16(layer, mi, dev).view(-1))
+    packed = [nq.empty_nf4(tuple(m.shape), dev) for m in mats]
+    outbuf = torch.empty(max(m.numel() for m in mats), dtype=torch.bfloat16, device=dev)
+    total = sum(m.numel() for m in mats)
+
+    def qall():
+        for m, p in zip(mats, packed):
+            nq.nf4_quantize(m, p.codes, None, p.absmax_q, p.absmax_scale)
+
+    def dall():
+        for m, p in zip(mats, packed):
+            nq.nf4_dequantize(p.codes, m.numel(), outbuf[:m.numel()], absmax_q=p.absmax_q,
+                              absmax_scale=p.absmax_scale)
+
+    qall(); dall()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, byts in (("quantize", qall, bytes_quantize(total, 2)),
+                           ("dequantize", dall, bytes_dequantize(total, 2))):
+        ev = Events(2)
+        ev[0].record()
+        fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1])
+        res[f"stack_{name}_224_matrices"] = {"ms": ms, "GB/s": byts / ms / 1e6, "params": total}
+        log(f"stack {name}: {res[f'stack_{name}_224_matrices']}")
+    del mats, packed, outbuf
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-kernels", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stack", action="store_true", help="also time the 224-matrix 8B stack")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path needs no exchange between GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nf4_quantize_amd as nq
+
+    nq.lib()
+    dev = torch.device("cuda:0")
+    main_res, w_bits = main_step_bench(args, dev)
+    log(f"main step: {main_res}")
+
+    kernels = {}
+    if not args.no_kernels:
+        kernels = kernel_benches(dev, iters=20, warmup=5, with_stack=args.stack)
+
+    q_bytes = main_res["quantize_bytes"]
+    q_ms = main_res["quantize_ms"]
+    achieved = q_bytes / (q_ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": "quantize_groups_kernel<bf16, DQ>",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "bytes_per_launch": q_bytes,
+        "avg_launch_ms": round(q_ms, 5),
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w_bits)
+
+    line = {
+        "metric": "NF4 quant/dequant HBM GB/s + fused NF4-GEMM TFLOP/s, % of roofline",
+        "value": round(main_res["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "11008x4096 bf16 MLP weight, N(0,0.02^2) with 0.1% outliers x10: "
+                        "NF4 blocksize 64 + double quantization 256, quantize then dequantize to bf16",
+            "elements": main_res["n"],
+            "step_bytes": main_res["step_bytes"],
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_kernels": {
+            "quantize": {"ms": round(main_res["quantize_ms"], 5),
+                         "GB/s": round(main_res["quantize_gbs"], 1)},
+            "dequantize": {"ms": round(main_res["dequantize_ms"], 5),
+                           "GB/s": round(main_res["dequantize_gbs"], 1)},
+        },
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

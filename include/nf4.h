@@ -1,0 +1,158 @@
+/*
+ * nf4.h - C ABI of the MI355X (gfx950) NF4 library: blockwise 4-bit
+ * NormalFloat quantization with double quantization of the block scales,
+ * dequantization, and the fused NF4-dequant linear (forward and input
+ * gradient) with the low-rank adapter side path.
+ *
+ * Sources (web pages), cited by title and section:
+ *   [MF]  "QLoRA: Mathematical Foundations of 4-Bit NormalFloat Quantization,
+ *          Double Quantization, and Paged Optimizers" (llms.blog)
+ *   [L15] "Lesson 15. NF4 and Double Quantisation" (tokencemetery)
+ *   [QP]  "QLoRA in Production: 4-bit NormalFloat & Double Quantization Deep
+ *          Dive" (devtechtools.org)
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is allocated and owned by the caller. Buffers marked
+ *     "device" must be device memory of the current HIP device; the library
+ *     keeps no pointer after a call returns and allocates nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; the host is never synchronised.
+ *     Results are valid in stream order after the call.
+ *   - Arguments are validated on the host before any HIP call. On an error the
+ *     call returns a non-zero nf4_status and launches nothing. NF4_ERR_LAUNCH
+ *     is returned when the HIP runtime reports a launch failure.
+ *   - A size of zero elements (n == 0, m == 0) returns NF4_OK and launches nothing.
+ *   - Alignment: element buffers (weights, codes, activations, outputs, the
+ *     workspace) must be 16-byte aligned; scale buffers (absmax, absmax_q,
+ *     absmax_scale) must be 4-byte aligned. Otherwise NF4_ERR_ALIGN.
+ *   - Only block size 64 ([MF] "Block-Wise Quantization Mechanics", B1 = 64)
+ *     and double-quantization block 256 ([MF] "Double Quantization (DQ)",
+ *     B2 = 256) are supported; anything else is NF4_ERR_UNSUPPORTED.
+ *   - Non-finite inputs are outside the contract (their output is unspecified).
+ *
+ * Packed storage layout of an n-element tensor (row-major flattening):
+ *   codes          uint8[ceil(n/2)]    element 2j in the low nibble of byte j,
+ *                                      element 2j+1 in the high nibble; for odd
+ *                                      n the final high nibble is 0
+ *   absmax         float[ceil(n/64)]   c1 of each 64-element block
+ *   absmax_q       uint8[ceil(n/64)]   E4M3FN code of c1/c2 (double quantization)
+ *   absmax_scale   float[ceil(ceil(n/64)/256)]  c2 of each group of 256 blocks
+ * The last block / group may be partial; it covers the remaining elements.
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NF4_OK = 0,
+    NF4_ERR_NULL = 1,        /* a required pointer is NULL */
+    NF4_ERR_SIZE = 2,        /* negative size, K % 64 != 0, r out of range, too large */
+    NF4_ERR_UNSUPPORTED = 3, /* block size, DQ block size, dtype or format not supported */
+    NF4_ERR_ALIGN = 4,       /* a buffer is not aligned as required */
+    NF4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than nf4_linear_workspace_size */
+    NF4_ERR_LAUNCH = 6       /* the HIP runtime reported an error at launch */
+} nf4_status;
+
+typedef enum { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char *nf4_status_string(int status);
+
+/* The 16 NF4 levels q_0..q_15 used by every kernel: the values printed in [MF]
+ * "4-Bit NormalFloat (NF4)". Returns a pointer to a static host array. */
+const float *nf4_codebook(void);
+
+/* Bytes of the packed storage of an n-element tensor: codes plus either fp32
+ * absmax (double_quant == 0) or 8-bit codes plus fp32 second-level scales.
+ * ([L15] "Double quantisation": 0.5625 and ~0.5159 bytes per parameter.)
+ * Returns -1 for n < 0 or unsupported block sizes. */
+int64_t nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t dq_blocksize, int32_t double_quant);
+
+/* Blockwise NF4 quantization ([MF] "Block-Wise Quantization Mechanics"), with
+ * the double quantization of the block scales fused in
+ * ([MF] "Double Quantization (DQ)").
+ *   w             device, n elements, fp32 or bf16 (w_dtype), 16-byte aligned
+ *   codes         device out, ceil(n/2) bytes
+ *   absmax        device out or NULL, ceil(n/64) floats: c1 = max |w| per block
+ *   absmax_q      device out or NULL, ceil(n/64) bytes: E4M3FN(c1 / c2)
+ *   absmax_scale  device out or NULL, one float per 256 blocks: c2 = max c1
+ * absmax_q and absmax_scale are both given (double quantization) or both NULL
+ * (then absmax is required). For each element the code is the index of the
+ * nearest level to fl32(w / c1), lower index on an exact tie; a block with
+ * c1 == 0 gets code 7 (the zero level); a group with c2 == 0 gets code8 0. */
+nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int32_t blocksize,
+                        uint8_t *codes, float *absmax, int32_t dq_blocksize, uint8_t *absmax_q,
+                        float *absmax_scale, void *stream);
+
+/* Double quantization of existing fp32 block scales ([MF] "Double
+ * Quantization (DQ)"): c2 = max over each group of 256 absmax values, and
+ * absmax_q[b] = E4M3FN(fl32(absmax[b] / c2)) with round to nearest even.
+ *   absmax        device, nblocks floats;  absmax_q device out, nblocks bytes;
+ *   absmax_scale  device out, ceil(nblocks/256) floats. */
+nf4_status nf4_double_quantize(const float *absmax, int64_t nblocks, int32_t dq_blocksize,
+                               uint8_t *absmax_q, float *absmax_scale, void *stream);
+
+/* Dequantization ([MF] "Block-Wise Quantization Mechanics", reconstruction;
+ * the dequantize(c1^FP8, c2, W^NF4) of "Forward Pass Computation"):
+ *   scale(b) = absmax[b]                                  if absmax_q == NULL
+ *            = fl32(decodeE4M3(absmax_q[b]) * absmax_scale[b/256])  otherwise
+ *   out[i]   = fl32(q[code_i] * scale(i/64)), rounded to nearest-even bf16
+ *              when out_dtype == NF4_BF16.
+ *   codes device ceil(n/2) bytes; out device n elements (16-byte aligned). */
+nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t blocksize, const float *absmax,
+                          const uint8_t *absmax_q, const float *absmax_scale,
+                          int32_t dq_blocksize, void *out, nf4_dtype out_dtype, void *stream);
+
+/* A frozen NF4 weight W stored [n_out x k_in] row-major (d_out x d_in, the
+ * transpose of [MF]'s W in R^{d_in x d_out}), quantized with nf4_quantize over
+ * its flattening. Either absmax_q + absmax_scale (double quantization) or
+ * absmax must be set. k_in must be a multiple of 64 so that no block crosses
+ * a row; groups of 256 blocks may cross rows. */
+typedef struct {
+    const uint8_t *codes;
+    const uint8_t *absmax_q;
+    const float *absmax_scale;
+    const float *absmax;
+    int64_t n_out; /* N = d_out */
+    int64_t k_in;  /* K = d_in  */
+    int32_t blocksize;
+    int32_t dq_blocksize;
+} nf4_weight;
+
+/* Bytes of device workspace that nf4_linear_forward / nf4_linear_backward_input
+ * need for m rows and adapter rank r (0 when r == 0). */
+size_t nf4_linear_workspace_size(int64_t m, int32_t r);
+
+/* Fused QLoRA linear forward ([MF] "Forward Pass Computation"):
+ *   Y = X . dequantize(W)^T + lora_scale * (X . A) . B
+ *   x        device bf16 [m x K] row-major
+ *   lora_a   device bf16 [K x r] row-major, or NULL (no adapter; then r must be 0)
+ *   lora_b   device bf16 [r x N] row-major
+ *   y        device bf16 [m x N] out
+ * bf16 operands, fp32 accumulation, bf16 output. lora_scale is alpha/r.
+ * 0 <= r <= 256. workspace: device, >= nf4_linear_workspace_size(m, r) bytes
+ * (holds the bf16 product X.A); may be NULL when r == 0. */
+nf4_status nf4_linear_forward(const void *x, int64_t m, const nf4_weight *w, const void *lora_a,
+                              const void *lora_b, int32_t r, float lora_scale, void *y,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Input gradient of the same linear ([MF] "Gradient Computation", the
+ * activation-gradient equation):
+ *   dX = dY . dequantize(W) + lora_scale * (dY . B^T) . A^T
+ *   dy  device bf16 [m x N];  dx device bf16 [m x K] out.
+ * Same operand, precision and workspace rules as nf4_linear_forward. */
+nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf4_weight *w,
+                                     const void *lora_a, const void *lora_b, int32_t r,
+                                     float lora_scale, void *dx, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NF4_H */

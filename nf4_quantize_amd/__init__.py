@@ -1,0 +1,335 @@
+"""Python binding of ``libnf4.so``, the gfx950 NF4 / double-quantization /
+fused NF4-linear library (C ABI in ``include/nf4.h``).
+
+The functions named like the C entry points (``nf4_quantize`` ...) marshal
+torch device tensors into pointers and call the library; every step of the
+computation runs in the library's HIP kernels. torch supplies device memory
+and the current HIP stream only. The convenience layer (``quantize``,
+``dequantize``, ``linear_forward`` ...) allocates outputs with ``torch.empty``
+and calls those functions.
+
+The library must be built first (``python -m nf4_quantize_amd.build``); when
+it is missing every call raises ``NF4LibraryMissing`` - there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4.so")
+
+BLOCK = 64
+DQ_BLOCK = 256
+NF4_F32, NF4_BF16 = 0, 1
+
+STATUS = {
+    0: "NF4_OK",
+    1: "NF4_ERR_NULL",
+    2: "NF4_ERR_SIZE",
+    3: "NF4_ERR_UNSUPPORTED",
+    4: "NF4_ERR_ALIGN",
+    5: "NF4_ERR_WORKSPACE",
+    6: "NF4_ERR_LAUNCH",
+}
+
+# Every extern "C" function declared in include/nf4.h.
+EXPORTS = (
+    "nf4_status_string",
+    "nf4_codebook",
+    "nf4_storage_bytes",
+    "nf4_quantize",
+    "nf4_double_quantize",
+    "nf4_dequantize",
+    "nf4_linear_workspace_size",
+    "nf4_linear_forward",
+    "nf4_linear_backward_input",
+)
+
+
+class NF4LibraryMissing(RuntimeError):
+    pass
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS.get(status, status)}")
+
+
+class nf4_weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("absmax_scale", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+        ("n_out", ctypes.c_int64),
+        ("k_in", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32),
+        ("dq_blocksize", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Loads libnf4.so (once). Raises NF4LibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NF4LibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m nf4_quantize_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.nf4_status_string.argtypes = [ctypes.c_int]
+    L.nf4_status_string.restype = ctypes.c_char_p
+    L.nf4_codebook.argtypes = []
+    L.nf4_codebook.restype = ctypes.POINTER(ctypes.c_float)
+    L.nf4_storage_bytes.argtypes = [i64, i32, i32, i32]
+    L.nf4_storage_bytes.restype = i64
+    L.nf4_quantize.argtypes = [p, ctypes.c_int, i64, i32, p, p, i32, p, p, p]
+    L.nf4_quantize.restype = ctypes.c_int
+    L.nf4_double_quantize.argtypes = [p, i64, i32, p, p, p]
+    L.nf4_double_quantize.restype = ctypes.c_int
+    L.nf4_dequantize.argtypes = [p, i64, i32, p, p, p, i32, p, ctypes.c_int, p]
+    L.nf4_dequantize.restype = ctypes.c_int
+    L.nf4_linear_workspace_size.argtypes = [i64, i32]
+    L.nf4_linear_workspace_size.restype = ctypes.c_size_t
+    for name in ("nf4_linear_forward", "nf4_linear_backward_input"):
+        fn = getattr(L, name)
+        fn.argtypes = [p, i64, ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p,
+                       ctypes.c_size_t, p]
+        fn.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != 0:
+        raise NF4Error(status, what)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt):
+    import torch
+
+    if dt == torch.float32:
+        return NF4_F32
+    if dt == torch.bfloat16:
+        return NF4_BF16
+    raise TypeError(f"unsupported dtype {dt}: float32 or bfloat16")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+# ------------------------------------------------------------- C-named calls
+
+def nf4_codebook():
+    cb = lib().nf4_codebook()
+    return [cb[i] for i in range(16)]
+
+
+def nf4_storage_bytes(n, double_quant=True, blocksize=BLOCK, dq_blocksize=DQ_BLOCK):
+    return int(lib().nf4_storage_bytes(n, blocksize, dq_blocksize, 1 if double_quant else 0))
+
+
+def nf4_quantize(w, codes, absmax=None, absmax_q=None, absmax_scale=None,
+                 blocksize=BLOCK, dq_blocksize=DQ_BLOCK):
+    """w: float32/bfloat16 device tensor (any shape, flattened). Outputs as in nf4.h."""
+    _need_cuda(w, codes, absmax, absmax_q, absmax_scale)
+    st = lib().nf4_quantize(_ptr(w), _dtype_code(w.dtype), w.numel(), blocksize, _ptr(codes),
+                            _ptr(absmax), dq_blocksize, _ptr(absmax_q), _ptr(absmax_scale),
+                            _stream(w.device))
+    _check(st, "nf4_quantize")
+
+
+def nf4_double_quantize(absmax, absmax_q, absmax_scale, dq_blocksize=DQ_BLOCK):
+    _need_cuda(absmax, absmax_q, absmax_scale)
+    st = lib().nf4_double_quantize(_ptr(absmax), absmax.numel(), dq_blocksize, _ptr(absmax_q),
+                                   _ptr(absmax_scale), _stream(absmax.device))
+    _check(st, "nf4_double_quantize")
+
+
+def nf4_dequantize(codes, n, out, absmax=None, absmax_q=None, absmax_scale=None,
+                   blocksize=BLOCK, dq_blocksize=DQ_BLOCK):
+    _need_cuda(codes, out, absmax, absmax_q, absmax_scale)
+    st = lib().nf4_dequantize(_ptr(codes), n, blocksize, _ptr(absmax), _ptr(absmax_q),
+                              _ptr(absmax_scale), dq_blocksize, _ptr(out), _dtype_code(out.dtype),
+                              _stream(codes.device))
+    _check(st, "nf4_dequantize")
+
+
+def nf4_linear_workspace_size(m, r):
+    return int(lib().nf4_linear_workspace_size(m, r))
+
+
+# ------------------------------------------------------------- convenience
+
+@dataclass
+class NF4Config:
+    """The four quantization knobs of the pages' configuration ("Lesson 15. NF4
+    and Double Quantisation", "The configuration"), plus the block sizes.
+    Only NF4 storage with bf16 compute is supported."""
+    load_in_4bit: bool = True
+    quant_type: str = "nf4"
+    use_double_quant: bool = True
+    compute_dtype: str = "bfloat16"
+    blocksize: int = BLOCK
+    dq_blocksize: int = DQ_BLOCK
+
+    def validate(self):
+        if not self.load_in_4bit:
+            raise ValueError("only 4-bit storage is implemented")
+        if self.quant_type != "nf4":
+            raise ValueError("only quant_type='nf4' is implemented")
+        if str(self.compute_dtype).replace("torch.", "") != "bfloat16":
+            raise ValueError("only bfloat16 compute is implemented")
+        if self.blocksize != BLOCK or self.dq_blocksize != DQ_BLOCK:
+            raise ValueError("block sizes 64 / 256 only")
+        return self
+
+
+@dataclass
+class NF4Tensor:
+    """Packed NF4 storage of a tensor of `shape` (row-major flattening)."""
+    codes: "object"
+    absmax: Optional["object"]
+    absmax_q: Optional["object"]
+    absmax_scale: Optional["object"]
+    shape: Tuple[int, ...]
+
+    @property
+    def numel(self):
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+    @property
+    def double_quant(self):
+        return self.absmax_q is not None
+
+    def storage_bytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.codes, self.absmax, self.absmax_q, self.absmax_scale) if t is not None)
+
+    def weight_struct(self):
+        """nf4_weight view of a 2-D [N x K] weight (keep self alive while used)."""
+        if len(self.shape) != 2:
+            raise ValueError("a linear weight is 2-D [n_out x k_in]")
+        return nf4_weight(
+            codes=self.codes.data_ptr(),
+            absmax_q=self.absmax_q.data_ptr() if self.absmax_q is not None else None,
+            absmax_scale=self.absmax_scale.data_ptr() if self.absmax_scale is not None else None,
+            absmax=self.absmax.data_ptr() if self.absmax is not None else None,
+            n_out=self.shape[0], k_in=self.shape[1], blocksize=BLOCK, dq_blocksize=DQ_BLOCK)
+
+
+def nblocks(n):
+    return (n + BLOCK - 1) // BLOCK
+
+
+def ngroups(n):
+    return (nblocks(n) + DQ_BLOCK - 1) // DQ_BLOCK
+
+
+def empty_nf4(shape, device, double_quant=True, keep_absmax=False):
+    import torch
+
+    n = 1
+    for d in shape:
+        n *= d
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
+    absmax = (torch.empty(nblocks(n), dtype=torch.float32, device=device)
+              if (keep_absmax or not double_quant) else None)
+    q = torch.empty(nblocks(n), dtype=torch.uint8, device=device) if double_quant else None
+    sc = torch.empty(ngroups(n), dtype=torch.float32, device=device) if double_quant else None
+    return NF4Tensor(codes, absmax, q, sc, tuple(shape))
+
+
+def quantize(w, double_quant=True, keep_absmax=False, out: Optional[NF4Tensor] = None):
+    """Blockwise NF4 (+ double quantization) of a float32/bfloat16 device tensor."""
+    t = out if out is not None else empty_nf4(tuple(w.shape), w.device, double_quant, keep_absmax)
+    nf4_quantize(w.contiguous(), t.codes, t.absmax, t.absmax_q, t.absmax_scale)
+    return t
+
+
+def double_quantize(absmax):
+    import torch
+
+    q = torch.empty(absmax.numel(), dtype=torch.uint8, device=absmax.device)
+    sc = torch.empty((absmax.numel() + DQ_BLOCK - 1) // DQ_BLOCK, dtype=torch.float32,
+                     device=absmax.device)
+    nf4_double_quantize(absmax, q, sc)
+    return q, sc
+
+
+def dequantize(t: NF4Tensor, out_dtype=None, out=None):
+    import torch
+
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty(t.shape, dtype=out_dtype, device=t.codes.device)
+    if t.double_quant:
+        nf4_dequantize(t.codes, t.numel, out, absmax_q=t.absmax_q, absmax_scale=t.absmax_scale)
+    else:
+        nf4_dequantize(t.codes, t.numel, out, absmax=t.absmax)
+    return out
+
+
+def _linear(name, act, w: NF4Tensor, lora_a, lora_b, lora_scale, out_cols, out=None,
+            workspace=None):
+    import torch
+
+    _need_cuda(act, lora_a, lora_b, out, workspace)
+    if act.dtype != torch.bfloat16:
+        raise TypeError("activations are bfloat16")
+    m = act.shape[0]
+    r = 0 if lora_a is None else lora_a.shape[1]
+    if out is None:
+        out = torch.empty((m, out_cols), dtype=torch.bfloat16, device=act.device)
+    ws_bytes = nf4_linear_workspace_size(m, r)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=act.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws = w.weight_struct()
+    st = getattr(lib(), name)(_ptr(act), m, ctypes.byref(ws), _ptr(lora_a), _ptr(lora_b), r,
+                              float(lora_scale), _ptr(out), _ptr(workspace), ws_len,
+                              _stream(act.device))
+    _check(st, name)
+    return out
+
+
+def nf4_linear_forward(x, w: NF4Tensor, lora_a=None, lora_b=None, lora_scale=1.0, out=None,
+                       workspace=None):
+    """Y = X . dequantize(W)^T + lora_scale * (X . A) . B; x bf16 [m x K], W [N x K]."""
+    return _linear("nf4_linear_forward", x, w, lora_a, lora_b, lora_scale, w.shape[0], out,
+                   workspace)
+
+
+def nf4_linear_backward_input(dy, w: NF4Tensor, lora_a=None, lora_b=None, lora_scale=1.0,
+                              out=None, workspace=None):
+    """dX = dY . dequantize(W) + lora_scale * (dY . B^T) . A^T; dy bf16 [m x N]."""
+    return _linear("nf4_linear_backward_input", dy, w, lora_a, lora_b, lora_scale, w.shape[1],
+                   out, workspace)
+
+
+linear_forward = nf4_linear_forward
+linear_backward_input = nf4_linear_backward_input

@@ -1,0 +1,275 @@
+// api.hip - the extern "C" entry points of libnf4.so: host-side validation,
+// the NF4 code table, and dispatch to the gfx950 kernels. Declarations and
+// the contract of each entry point are in include/nf4.h.
+//
+// Every argument is checked before any HIP call; a rejected call launches
+// nothing and returns its status. The library allocates nothing.
+#pragma clang fp contract(off)
+
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "nf4_internal.h"
+
+#define NF4_API extern "C" __attribute__((visibility("default")))
+
+namespace nf4 {
+
+// [MF] "4-Bit NormalFloat (NF4)": the printed list q_0 .. q_15 (each printed
+// decimal is an exact binary32 value).
+const float kLevels[16] = {
+    -1.0f,
+    -0.6961928009986877f,
+    -0.5250730514526367f,
+    -0.39491748809814453f,
+    -0.28444138169288635f,
+    -0.18477343022823334f,
+    -0.09105003625154495f,
+    0.0f,
+    0.07958029955625534f,
+    0.16093020141124725f,
+    0.24611230194568634f,
+    0.33791524171829224f,
+    0.44070982933044434f,
+    0.5626170039176941f,
+    0.7229568362236023f,
+    1.0f,
+};
+
+namespace {
+
+// Nearest level of a normalised value by direct search: the first index with
+// the smallest |fl32(n - q_i)| ([MF] "Block-Wise Quantization Mechanics").
+// Host-side only, used to build the bucket table.
+int nearest_by_search(float n) {
+    int best = 0;
+    float bd = fabsf(n - kLevels[0]);
+    for (int i = 1; i < 16; ++i) {
+        const float d = fabsf(n - kLevels[i]);
+        if (d < bd) {
+            bd = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+// Total order of binary32 values as integers (for bisection over floats).
+int64_t f2ord(float x) {
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    return (b & 0x80000000u) ? -(int64_t)(b & 0x7FFFFFFFu) : (int64_t)b;
+}
+float ord2f(int64_t o) {
+    uint32_t b = o >= 0 ? (uint32_t)o : (0x80000000u | (uint32_t)(-o));
+    float x;
+    memcpy(&x, &b, 4);
+    return x;
+}
+
+bool build_lut(CodeLut *lut) {
+    // Bucket k covers n in [-1 + k/16, -1 + (k+1)/16); bucket 32 holds n >= 1.
+    for (int k = 0; k < 32; ++k) {
+        const float lo = -1.0f + (float)k / 16.0f;
+        const float hi = -1.0f + (float)(k + 1) / 16.0f;
+        const float last = ord2f(f2ord(hi) - 1);
+        const int c_lo = nearest_by_search(lo);
+        const int c_last = nearest_by_search(last);
+        lut->e[k].base = c_lo;
+        lut->e[k].thr = 2.0f;
+        if (c_last == c_lo) continue;
+        if (c_last != c_lo + 1) return false;  // more than one switch in a bucket
+        int64_t a = f2ord(lo), b = f2ord(last);  // code(a) == c_lo, code(b) == c_lo + 1
+        while (b - a > 1) {
+            const int64_t mid = a + (b - a) / 2;
+            if (nearest_by_search(ord2f(mid)) > c_lo)
+                b = mid;
+            else
+                a = mid;
+        }
+        const float thr = ord2f(b);
+        // Switch points must sit well inside their bucket, so that a q
+        // within kNearTol of n never crosses a switch point of a neighbour.
+        if (!(thr - lo >= 0x1p-10f && hi - thr >= 0x1p-10f)) return false;
+        lut->e[k].thr = thr;
+    }
+    lut->e[32].base = nearest_by_search(1.0f);
+    lut->e[32].thr = 2.0f;
+    return lut->e[32].base == 15 && lut->e[16].base == 7;
+}
+
+}  // namespace
+
+const CodeLut *code_lut() {
+    static CodeLut lut;
+    static bool ok = false;
+    static std::once_flag once;
+    std::call_once(once, [] { ok = build_lut(&lut); });
+    return ok ? &lut : nullptr;
+}
+
+}  // namespace nf4
+
+using namespace nf4;
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 37;  // keeps every grid below 2^32 threads
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nf4_status launch_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_LAUNCH; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+NF4_API const char *nf4_status_string(int status) {
+    switch (status) {
+        case NF4_OK: return "NF4_OK";
+        case NF4_ERR_NULL: return "NF4_ERR_NULL: a required pointer is NULL";
+        case NF4_ERR_SIZE: return "NF4_ERR_SIZE: size out of range";
+        case NF4_ERR_UNSUPPORTED: return "NF4_ERR_UNSUPPORTED: block size, dtype or format not supported";
+        case NF4_ERR_ALIGN: return "NF4_ERR_ALIGN: buffer not aligned as required";
+        case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace missing or too small";
+        case NF4_ERR_LAUNCH: return "NF4_ERR_LAUNCH: the HIP runtime reported a launch error";
+        default: return "unknown nf4_status";
+    }
+}
+
+NF4_API const float *nf4_codebook(void) { return kLevels; }
+
+NF4_API int64_t nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t dq_blocksize,
+                                  int32_t double_quant) {
+    if (n < 0 || blocksize != kBlock || (double_quant && dq_blocksize != kDqBlock)) return -1;
+    const int64_t nb = cdiv(n, kBlock);
+    const int64_t codes = cdiv(n, 2);
+    if (!double_quant) return codes + 4 * nb;
+    return codes + nb + 4 * cdiv(nb, kDqBlock);
+}
+
+NF4_API nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int32_t blocksize,
+                                uint8_t *codes, float *absmax, int32_t dq_blocksize,
+                                uint8_t *absmax_q, float *absmax_scale, void *stream) {
+    if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
+    if (blocksize != kBlock) return NF4_ERR_UNSUPPORTED;
+    if (w_dtype != NF4_F32 && w_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    const bool dq = absmax_q != nullptr || absmax_scale != nullptr;
+    if (dq && dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (n == 0) return NF4_OK;
+    if (!w || !codes) return NF4_ERR_NULL;
+    if (dq && (!absmax_q || !absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !absmax) return NF4_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codes, 16)) return NF4_ERR_ALIGN;
+    if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
+        (absmax_scale && !aligned(absmax_scale, 4)))
+        return NF4_ERR_ALIGN;
+    if (!code_lut()) return NF4_ERR_UNSUPPORTED;
+    return launch_status(launch_quantize(w, w_dtype, n, codes, absmax, absmax_q, absmax_scale,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_double_quantize(const float *absmax, int64_t nblocks, int32_t dq_blocksize,
+                                       uint8_t *absmax_q, float *absmax_scale, void *stream) {
+    if (nblocks < 0 || nblocks > kMaxElems / kBlock) return NF4_ERR_SIZE;
+    if (dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (nblocks == 0) return NF4_OK;
+    if (!absmax || !absmax_q || !absmax_scale) return NF4_ERR_NULL;
+    if (!aligned(absmax, 4) || !aligned(absmax_q, 4) || !aligned(absmax_scale, 4))
+        return NF4_ERR_ALIGN;
+    return launch_status(launch_double_quantize(absmax, nblocks, absmax_q, absmax_scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t blocksize,
+                                  const float *absmax, const uint8_t *absmax_q,
+                                  const float *absmax_scale, int32_t dq_blocksize, void *out,
+                                  nf4_dtype out_dtype, void *stream) {
+    if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
+    if (blocksize != kBlock) return NF4_ERR_UNSUPPORTED;
+    if (out_dtype != NF4_F32 && out_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    const bool dq = absmax_q != nullptr || absmax_scale != nullptr;
+    if (dq && dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (n == 0) return NF4_OK;
+    if (!codes || !out) return NF4_ERR_NULL;
+    if (dq && (!absmax_q || !absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !absmax) return NF4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(out, 16)) return NF4_ERR_ALIGN;
+    if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
+        (absmax_scale && !aligned(absmax_scale, 4)))
+        return NF4_ERR_ALIGN;
+    return launch_status(launch_dequantize(codes, n, dq ? nullptr : absmax, dq ? absmax_q : nullptr,
+                                           dq ? absmax_scale : nullptr, out, out_dtype,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+NF4_API size_t nf4_linear_workspace_size(int64_t m, int32_t r) {
+    if (m <= 0 || r <= 0) return 0;
+    // bf16 [m x r] adapter product, rounded up to 256 bytes.
+    const size_t bytes = (size_t)m * (size_t)r * 2u;
+    return (bytes + 255u) & ~(size_t)255u;
+}
+
+namespace {
+
+nf4_status check_linear(const void *act, int64_t m, const nf4_weight *w, const void *a,
+                        const void *b, int32_t r, const void *out, const void *ws,
+                        size_t ws_bytes) {
+    if (!w) return NF4_ERR_NULL;
+    if (m < 0 || w->n_out <= 0 || w->k_in <= 0 || (w->k_in % kBlock) != 0) return NF4_ERR_SIZE;
+    if (w->n_out * w->k_in > kMaxElems || m > (int64_t(1) << 31)) return NF4_ERR_SIZE;
+    if (m * w->k_in > kMaxElems || m * w->n_out > kMaxElems) return NF4_ERR_SIZE;
+    if (r < 0 || r > 256) return NF4_ERR_SIZE;
+    if (w->blocksize != kBlock) return NF4_ERR_UNSUPPORTED;
+    const bool dq = w->absmax_q != nullptr || w->absmax_scale != nullptr;
+    if (dq && w->dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (m == 0) return NF4_OK;
+    if (!act || !out || !w->codes) return NF4_ERR_NULL;
+    if (dq && (!w->absmax_q || !w->absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !w->absmax) return NF4_ERR_NULL;
+    if ((r > 0) != (a != nullptr) || (r > 0 && !b)) return NF4_ERR_NULL;
+    if (!aligned(act, 16) || !aligned(out, 16) || !aligned(w->codes, 16)) return NF4_ERR_ALIGN;
+    if ((w->absmax && !aligned(w->absmax, 4)) || (w->absmax_q && !aligned(w->absmax_q, 4)) ||
+        (w->absmax_scale && !aligned(w->absmax_scale, 4)))
+        return NF4_ERR_ALIGN;
+    if (r > 0) {
+        if (!aligned(a, 16) || !aligned(b, 16)) return NF4_ERR_ALIGN;
+        if (!ws || ws_bytes < nf4_linear_workspace_size(m, r)) return NF4_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return NF4_ERR_ALIGN;
+    }
+    return NF4_OK;
+}
+
+nf4_weight normalised(const nf4_weight *w) {
+    nf4_weight v = *w;
+    if (v.absmax_q) v.absmax = nullptr;
+    return v;
+}
+
+}  // namespace
+
+NF4_API nf4_status nf4_linear_forward(const void *x, int64_t m, const nf4_weight *w,
+                                      const void *lora_a, const void *lora_b, int32_t r,
+                                      float lora_scale, void *y, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    const nf4_status st = check_linear(x, m, w, lora_a, lora_b, r, y, workspace, workspace_bytes);
+    if (st != NF4_OK || m == 0) return st;
+    return launch_status(launch_linear_forward(
+        static_cast<const uint16_t *>(x), m, normalised(w), static_cast<const uint16_t *>(lora_a),
+        static_cast<const uint16_t *>(lora_b), r, lora_scale, static_cast<uint16_t *>(y),
+        workspace, static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf4_weight *w,
+                                             const void *lora_a, const void *lora_b, int32_t r,
+                                             float lora_scale, void *dx, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+    const nf4_status st = check_linear(dy, m, w, lora_a, lora_b, r, dx, workspace, workspace_bytes);
+    if (st != NF4_OK || m == 0) return st;
+    return launch_status(launch_linear_backward_input(
+        static_cast<const uint16_t *>(dy), m, normalised(w), static_cast<const uint16_t *>(lora_a),
+        static_cast<const uint16_t *>(lora_b), r, lora_scale, static_cast<uint16_t *>(dx),
+        workspace, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,155 @@
+// dequantize.hip - NF4 dequantization for gfx950 ([MF] "Block-Wise
+// Quantization Mechanics", reconstruction; the dequantize(c1^FP8, c2, W^NF4)
+// of "Forward Pass Computation"; source key in nf4_internal.h).
+//
+//   c1'(b) = fl32(decode8(absmax_q[b]) * c2[b / 256])   (or absmax[b] without DQ)
+//   w'     = fl32(q[code] * c1'(b)), then nearest-even bf16 for bf16 output.
+//
+// Work split: a wave owns chunks of 2048 weights (1 KiB of codes, 32 blocks).
+// Lane l reads code dwords j*256 + 4l (j = 0..3), so each wave load is 256
+// contiguous bytes and each lane's 8 weights per dword are contiguous in the
+// output: a bf16 store is one 16-byte vector per lane and 1 KiB per wave.
+// A byte of codes is turned into its two levels by one 8-byte LDS read from a
+// 256-entry (low, high) level table; the scale multiply and the bf16 rounding
+// (v_cvt_pk_bf16_f32) follow.
+#pragma clang fp contract(off)
+
+#include "nf4_internal.h"
+
+namespace nf4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 2048;             // weights per wave chunk
+constexpr int kChunkBytes = kChunk / 2;  // code bytes per chunk
+
+struct Levels {
+    float q[16];
+};
+
+__device__ __forceinline__ void build_pair_table(const Levels &lv, float2 *s_pair) {
+    const int t = threadIdx.x;  // 256 threads: one entry each
+    s_pair[t] = make_float2(lv.q[t & 15], lv.q[t >> 4]);
+}
+
+template <typename O> struct Out;
+template <> struct Out<uint16_t> {  // bf16
+    __device__ static void store8(uint16_t *dst, const float (&v)[8]) {
+        u32x4 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        o.z = pack_bf16x2(v[4], v[5]);
+        o.w = pack_bf16x2(v[6], v[7]);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
+    }
+    __device__ static void store1(uint16_t *dst, float v) {
+        *dst = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    }
+};
+template <> struct Out<float> {
+    __device__ static void store8(float *dst, const float (&v)[8]) {
+        const f32x4 a = {v[0], v[1], v[2], v[3]};
+        const f32x4 b = {v[4], v[5], v[6], v[7]};
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(dst));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4 *>(dst + 4));
+    }
+    __device__ static void store1(float *dst, float v) { *dst = v; }
+};
+
+template <typename O, bool kDQ, int kCPW>
+__global__ __launch_bounds__(kThreads) void dequantize_chunks_kernel(
+    const uint8_t *__restrict__ codes, int64_t nchunks, const float *__restrict__ absmax,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
+    O *__restrict__ out, Levels lv) {
+    __shared__ float2 s_pair[256];
+    build_pair_table(lv, s_pair);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+#pragma unroll
+    for (int c = 0; c < kCPW; ++c) {
+        const int64_t chunk = wave * kCPW + c;
+        if (chunk >= nchunks) return;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(codes + chunk * kChunkBytes);
+        uint32_t d[4];
+        float s[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = __builtin_nontemporal_load(&src[j * 64 + lane]);
+        const int64_t blk0 = chunk * (kChunk / kBlock);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t b = blk0 + j * 8 + (lane >> 3);
+            if (kDQ)
+                s[j] = e4m3_decode(absmax_q[b]) * absmax_scale[b / kDqBlock];
+            else
+                s[j] = absmax[b];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float2 qq = s_pair[(d[j] >> (8 * k)) & 0xFFu];
+                v[2 * k] = qq.x * s[j];
+                v[2 * k + 1] = qq.y * s[j];
+            }
+            Out<O>::store8(out + chunk * kChunk + j * 512 + lane * 8, v);
+        }
+    }
+}
+
+// Remaining weights after the last full chunk: one weight per thread.
+template <typename O>
+__global__ __launch_bounds__(kThreads) void dequantize_tail_kernel(
+    const uint8_t *__restrict__ codes, int64_t start, int64_t n, const float *__restrict__ absmax,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
+    O *__restrict__ out, Levels lv) {
+    __shared__ float2 s_pair[256];
+    build_pair_table(lv, s_pair);
+    __syncthreads();
+    const int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t code = (codes[i >> 1] >> (4 * (i & 1))) & 15u;
+    const float c1 = block_scale(i / kBlock, absmax, absmax_q, absmax_scale);
+    Out<O>::store1(out + i, s_pair[code].x * c1);
+}
+
+template <typename O>
+hipError_t launch_t(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *absmax_q,
+                    const float *absmax_scale, O *out, hipStream_t s) {
+    Levels lv;
+    for (int i = 0; i < 16; ++i) lv.q[i] = kLevels[i];
+    constexpr int kCPW = 2;
+    const int64_t nchunks = n / kChunk;
+    if (nchunks > 0) {
+        const int64_t waves = (nchunks + kCPW - 1) / kCPW;
+        const int64_t wgs = (waves + (kThreads / 64) - 1) / (kThreads / 64);
+        if (absmax_q)
+            dequantize_chunks_kernel<O, true, kCPW><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
+                codes, nchunks, absmax, absmax_q, absmax_scale, out, lv);
+        else
+            dequantize_chunks_kernel<O, false, kCPW><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
+                codes, nchunks, absmax, absmax_q, absmax_scale, out, lv);
+    }
+    const int64_t start = nchunks * kChunk;
+    if (start < n) {
+        const int64_t rem = n - start;
+        dequantize_tail_kernel<O><<<dim3((unsigned)((rem + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
+            codes, start, n, absmax, absmax_q, absmax_scale, out, lv);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absmax,
+                             const uint8_t *absmax_q, const float *absmax_scale, void *out,
+                             nf4_dtype dt, hipStream_t s) {
+    if (dt == NF4_BF16)
+        return launch_t<uint16_t>(codes, n, absmax, absmax_q, absmax_scale,
+                                  static_cast<uint16_t *>(out), s);
+    return launch_t<float>(codes, n, absmax, absmax_q, absmax_scale, static_cast<float *>(out), s);
+}
+
+}  // namespace nf4

@@ -1,0 +1,109 @@
+// nf4_internal.h - internal declarations of the gfx950 NF4 library (not part
+// of the C ABI). Shared by the library's own sources only.
+//
+// Sources (web pages), cited by title and section:
+//   [MF] "QLoRA: Mathematical Foundations of 4-Bit NormalFloat Quantization,
+//        Double Quantization, and Paged Optimizers" (llms.blog)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4.h"
+
+namespace nf4 {
+
+constexpr int kBlock = 64;                  // B1, [MF] "Block-Wise Quantization Mechanics"
+constexpr int kDqBlock = 256;               // B2, [MF] "Double Quantization (DQ)"
+constexpr int kGroup = kBlock * kDqBlock;   // 16384 weights share one c2
+
+// The 16 NF4 levels, [MF] "4-Bit NormalFloat (NF4)" (the printed list).
+extern const float kLevels[16];
+
+// Nearest-level lookup: the normalised value n in [-1, 1] is split into 32
+// buckets of width 1/16 (plus bucket 32 for n >= 1). No bucket holds more
+// than one switch point of the code function, so
+//   code(n) = base[k] + (n >= thr[k]),   k = floor(16 n + 16).
+// thr is 2.0 in a bucket without a switch point. Built on the host from the
+// codebook by nf4::code_lut() and passed to kernels by value.
+constexpr int kLutEntries = 33;
+struct LutEntry {
+    float thr;
+    int32_t base;
+};
+struct CodeLut {
+    LutEntry e[kLutEntries];
+};
+// Returns the table (built once, thread-safe), or nullptr if the codebook
+// failed the construction checks.
+const CodeLut *code_lut();
+
+// |q - n| bound used by the quantize kernels: with r within 1 ulp of 1/c1,
+// q = fl(w * r) and n = fl(w / c1) differ by less than 2.4e-7 for |w| <= c1;
+// a q closer than kNearTol (9.5e-7) to a switch point is re-done with the
+// correctly rounded division.
+constexpr float kNearTol = 0x1p-20f;
+
+// ---- internal launchers (host side; each validates nothing) ----
+hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *codes, float *absmax,
+                           uint8_t *absmax_q, float *absmax_scale, hipStream_t s);
+hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t *absmax_q,
+                                  float *absmax_scale, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absmax,
+                             const uint8_t *absmax_q, const float *absmax_scale, void *out,
+                             nf4_dtype dt, hipStream_t s);
+hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
+                                 const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
+                                 uint16_t *y, void *workspace, hipStream_t s);
+hipError_t launch_linear_backward_input(const uint16_t *dy, int64_t m, const nf4_weight &w,
+                                        const uint16_t *a, const uint16_t *b, int32_t r,
+                                        float s_lora, uint16_t *dx, void *workspace,
+                                        hipStream_t s);
+
+// ---- device helpers ----
+
+// Native 16-byte vectors (usable with the nontemporal load/store builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bits -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// OCP FP8 E4M3FN decode of a non-negative code (bias 7, 3 mantissa bits;
+// exponent field 0 is subnormal m * 2^-9).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (c & 0x80u) ? -v : v;
+}
+
+// OCP FP8 E4M3FN encode of r in [0, 1], round to nearest, ties to even.
+// Below 2^-6 the format is uniform with step 2^-9, so the code is the
+// rounded multiple of the step; above, the 23-bit mantissa is cut to 3 bits
+// and a round-up carries into the exponent because codes are monotone.
+__device__ __forceinline__ uint32_t e4m3_encode_unit(float r) {
+    uint32_t u = __float_as_uint(r);
+    if (u < 0x3C800000u) return (uint32_t)__builtin_rintf(r * 512.0f);
+    int e = (int)(u >> 23) - 127;
+    uint32_t mant = u & 0x7FFFFFu;
+    uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+    uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & (keep & 1u));
+    return (uint32_t)((e + 7) << 3) + keep + up;
+}
+
+// Reconstructed first-level scale c1' of one block.
+__device__ __forceinline__ float block_scale(int64_t b, const float *absmax, const uint8_t *q,
+                                             const float *scale) {
+    if (q == nullptr) return absmax[b];
+    return e4m3_decode(q[b]) * scale[b / kDqBlock];
+}
+
+}  // namespace nf4

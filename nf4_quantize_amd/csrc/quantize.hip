@@ -1,0 +1,292 @@
+// quantize.hip - blockwise NF4 quantization with fused double quantization
+// for gfx950 ([MF] "Block-Wise Quantization Mechanics" and "Double
+// Quantization (DQ)", see nf4_internal.h for the source key).
+//
+// Work split: one workgroup of 256 threads per group of 256 blocks (16384
+// weights), so c2 = max c1 of the group is a workgroup reduction and never
+// leaves the chip. Each lane owns one 16-byte slice of a block (8 bf16 or 4
+// fp32 weights); consecutive lanes own consecutive slices, so every wave
+// load is one contiguous 1 KiB run. A block's absmax is a DPP max across the
+// 8 (bf16) or 16 (fp32) lanes that hold it.
+//
+// The nearest level is found without a 16-way search: n is approximated by
+// q = fl(w * fl(1/c1)) (one multiply), bucketed (one fma + convert), and the
+// code is base + (q >= thr) from a 33-entry LDS table. q differs from the
+// exact fl(w / c1) by < 1.8e-7; lanes with q within 2^-20 of a switch point
+// redo their slice with the correctly rounded division, so codes are exactly
+// those of the definition.
+#pragma clang fp contract(off)
+
+#include "nf4_internal.h"
+
+namespace nf4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float dpp_max_quad_xor1(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float dpp_max_quad_xor2(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float dpp_max_half_mirror(float v) {  // lane i <-> 7-i in each 8
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float dpp_max_mirror(float v) {  // lane i <-> 15-i in each 16
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+}
+
+// Max over the whole workgroup (256 threads); every thread gets the result.
+__device__ __forceinline__ float wg_max(float v, float *s_red) {
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) s_red[wave] = v;
+    __syncthreads();
+    float r = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    return r;
+}
+
+// Code of an exactly normalised value n in [-1, 1] (or of q near it).
+__device__ __forceinline__ uint32_t lut_index(float v) {
+    int k = (int)fmaf(v, 16.0f, 16.0f);
+    return min((uint32_t)k, (uint32_t)(kLutEntries - 1));
+}
+
+// Input traits: one 16-byte slice per lane.
+template <typename T> struct Slice;
+template <> struct Slice<uint16_t> {  // bf16
+    static constexpr int kElems = 8;
+    using Vec = u32x4;
+    __device__ static void widen(const Vec &v, float (&f)[8]) {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+        f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+        f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+};
+template <> struct Slice<float> {
+    static constexpr int kElems = 4;
+    using Vec = f32x4;
+    __device__ static void widen(const Vec &v, float (&f)[4]) {
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    }
+};
+
+// Codes of one lane's slice. c1 is the block absmax (all lanes of the block
+// hold the same value). Returns the packed nibbles, element e at bits 4e.
+template <int E>
+__device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, const float2 *s_lut) {
+    // rcp ~ 1/c1 from v_rcp_f32 (within 1 ulp for a normal result): then
+    // |q - fl(w/c1)| stays below 2.4e-7 for |w| <= c1, well inside kNearTol.
+    // Blocks with c1 == 0 (all zero) take rcp = 0 (q = 0 -> code 7). A c1
+    // outside [2^-125, 2^125] - whose reciprocal would overflow or fall into
+    // the subnormal range, where v_rcp_f32 is not that accurate - takes the
+    // exact path for the whole slice.
+    const bool in_range = (c1 >= 0x1p-125f) & (c1 <= 0x1p125f);
+    const bool outside = (c1 > 0.0f) & !in_range;
+    const float rcp = in_range ? __builtin_amdgcn_rcpf(c1) : 0.0f;
+    uint32_t packed = 0;
+    bool near = outside;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float q = f[e] * rcp;
+        const float2 ent = s_lut[lut_index(q)];
+        const float d = q - ent.x;
+        const uint32_t code = (uint32_t)__float_as_int(ent.y) + (d >= 0.0f ? 1u : 0u);
+        near |= fabsf(d) < kNearTol;
+        packed |= code << (4 * e);
+    }
+    if (near) {  // rare: redo the slice with the correctly rounded division
+        packed = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float nrm = f[e] / c1;
+            const float2 ent = s_lut[lut_index(nrm)];
+            const uint32_t code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
+            packed |= code << (4 * e);
+        }
+    }
+    return packed;
+}
+
+__device__ __forceinline__ void load_lut(const CodeLut &lut, float2 *s_lut) {
+    if (threadIdx.x < kLutEntries)
+        s_lut[threadIdx.x] = make_float2(lut.e[threadIdx.x].thr, __int_as_float(lut.e[threadIdx.x].base));
+}
+
+// Double quantization of the group's 256 c1 values held in s_c1.
+__device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32_t *s_q8,
+                                         uint8_t *absmax_q, float *absmax_scale, int64_t g) {
+    const int t = threadIdx.x;
+    const float c1 = s_c1[t];
+    const float c2 = wg_max(c1, s_red);
+    const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
+    reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)e4m3_encode_unit(ratio);
+    __syncthreads();
+    if (t < kDqBlock / 4) reinterpret_cast<uint32_t *>(absmax_q + g * kDqBlock)[t] = s_q8[t];
+    if (t == 0) absmax_scale[g] = c2;
+}
+
+// One workgroup per full group of 16384 weights.
+template <typename T, bool kDQ>
+__global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
+    const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
+    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, CodeLut lut) {
+    using S = Slice<T>;
+    constexpr int E = S::kElems;               // weights per lane slice
+    constexpr int LPB = kBlock / E;            // lanes per block
+    constexpr int SLICES = kGroup / E;         // slices per group
+    constexpr int ITERS = SLICES / kThreads;   // slices per thread
+    constexpr int BPI = kThreads / LPB;        // blocks per iteration
+
+    __shared__ float2 s_lut[kLutEntries];
+    __shared__ float s_c1[kDqBlock];
+    __shared__ float s_red[4];
+    __shared__ uint32_t s_q8[kDqBlock / 4];
+
+    const int t = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    const typename S::Vec *src = reinterpret_cast<const typename S::Vec *>(w + g * kGroup);
+
+    typename S::Vec v[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * kThreads + t]);
+
+    load_lut(lut, s_lut);
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        float f[E];
+        S::widen(v[i], f);
+        float m = fabsf(f[0]);
+#pragma unroll
+        for (int e = 1; e < E; ++e) m = fmaxf(m, fabsf(f[e]));
+        m = dpp_max_quad_xor1(m);
+        m = dpp_max_quad_xor2(m);
+        m = dpp_max_half_mirror(m);
+        if (LPB == 16) m = dpp_max_mirror(m);
+        const int blk = i * BPI + t / LPB;  // block within the group
+        if ((t % LPB) == 0) {
+            if (kDQ) s_c1[blk] = m;
+            if (absmax) absmax[g * kDqBlock + blk] = m;
+        }
+        const uint32_t packed = slice_codes<E>(f, m, s_lut);
+        const int64_t slice = (int64_t)g * SLICES + i * kThreads + t;
+        if (E == 8)
+            reinterpret_cast<uint32_t *>(codes)[slice] = packed;
+        else
+            reinterpret_cast<uint16_t *>(codes)[slice] = (uint16_t)packed;
+    }
+    if (kDQ) {
+        __syncthreads();
+        group_dq(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
+    }
+}
+
+// The final partial group: thread t owns block t of the group and works
+// element by element with guarded accesses.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
+    const T *__restrict__ w, int64_t n, int64_t g, uint8_t *__restrict__ codes,
+    float *__restrict__ absmax, uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale,
+    CodeLut lut) {
+    __shared__ float2 s_lut[kLutEntries];
+    __shared__ float s_c1[kDqBlock];
+    __shared__ float s_red[4];
+    const int t = threadIdx.x;
+    load_lut(lut, s_lut);
+    __syncthreads();
+    const int64_t b = g * kDqBlock + t;
+    const int64_t lo = b * kBlock;
+    const int64_t hi = min(lo + kBlock, n);
+    auto elem = [&](int64_t i) -> float {
+        if constexpr (sizeof(T) == 2) return __uint_as_float((uint32_t)w[i] << 16);
+        else return w[i];
+    };
+    float c1 = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) c1 = fmaxf(c1, fabsf(elem(i)));
+    s_c1[t] = c1;
+    if (lo < n && absmax) absmax[b] = c1;
+    for (int64_t i = lo; i < hi; i += 2) {
+        uint32_t byte = 0;
+        for (int j = 0; j < 2 && i + j < hi; ++j) {
+            uint32_t code = 7;
+            if (c1 > 0.0f) {
+                const float nrm = elem(i + j) / c1;
+                const float2 ent = s_lut[lut_index(nrm)];
+                code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
+            }
+            byte |= code << (4 * j);
+        }
+        codes[i / 2] = (uint8_t)byte;
+    }
+    if (absmax_q) {
+        __syncthreads();
+        const float c2 = wg_max(s_c1[t], s_red);
+        const int64_t nblocks = (n + kBlock - 1) / kBlock;
+        if (b < nblocks) {
+            const float ratio = (c2 > 0.0f) ? s_c1[t] / c2 : 0.0f;
+            absmax_q[b] = (uint8_t)e4m3_encode_unit(ratio);
+        }
+        if (t == 0) absmax_scale[g] = c2;
+    }
+}
+
+// Standalone double quantization: one workgroup per group of 256 c1 values.
+__global__ __launch_bounds__(kThreads) void double_quantize_kernel(
+    const float *__restrict__ absmax, int64_t nblocks, uint8_t *__restrict__ absmax_q,
+    float *__restrict__ absmax_scale) {
+    __shared__ float s_red[4];
+    const int t = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    const int64_t b = g * kDqBlock + t;
+    const float c1 = (b < nblocks) ? absmax[b] : 0.0f;
+    const float c2 = wg_max(fabsf(c1), s_red);
+    if (b < nblocks) {
+        const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
+        absmax_q[b] = (uint8_t)e4m3_encode_unit(ratio);
+    }
+    if (t == 0) absmax_scale[g] = c2;
+}
+
+template <typename T>
+hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
+                             uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
+    const CodeLut &lut = *code_lut();
+    const int64_t full = n / kGroup;
+    if (full > 0) {
+        if (absmax_q)
+            quantize_groups_kernel<T, true><<<dim3((unsigned)full), dim3(kThreads), 0, s>>>(
+                w, codes, absmax, absmax_q, absmax_scale, lut);
+        else
+            quantize_groups_kernel<T, false><<<dim3((unsigned)full), dim3(kThreads), 0, s>>>(
+                w, codes, absmax, nullptr, nullptr, lut);
+    }
+    if (n % kGroup)
+        quantize_tail_kernel<T><<<1, kThreads, 0, s>>>(w, n, full, codes, absmax, absmax_q,
+                                                       absmax_scale, lut);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *codes, float *absmax,
+                           uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
+    if (dt == NF4_BF16)
+        return launch_quantize_t<uint16_t>(static_cast<const uint16_t *>(w), n, codes, absmax,
+                                           absmax_q, absmax_scale, s);
+    return launch_quantize_t<float>(static_cast<const float *>(w), n, codes, absmax, absmax_q,
+                                    absmax_scale, s);
+}
+
+hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t *absmax_q,
+                                  float *absmax_scale, hipStream_t s) {
+    const int64_t groups = (nblocks + kDqBlock - 1) / kDqBlock;
+    double_quantize_kernel<<<dim3((unsigned)groups), dim3(kThreads), 0, s>>>(absmax, nblocks,
+                                                                             absmax_q, absmax_scale);
+    return hipGetLastError();
+}
+
+}  // namespace nf4

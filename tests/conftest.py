@@ -53,3 +53,16 @@ def code_thresholds():
     bits = np.array([int(r[1], 16) for r in rows], dtype=np.uint32)
     assert bits.size == 15
     return bits.view(np.float32)
+
+
+@pytest.fixture(scope="session")
+def dev():
+    """The GPU (cuda:0) with the HIP library loaded; skips only without a GPU."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import nf4_quantize_amd as nq
+
+    nq.lib()  # raises NF4LibraryMissing when the library is not built
+    return torch.device("cuda:0")

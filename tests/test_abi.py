@@ -1,0 +1,160 @@
+"""The C-ABI library loads and exports every function include/nf4.h declares,
+and its host-side validation rejects bad arguments before any HIP call
+(CPU only: no call here reaches a kernel launch).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+import nf4_quantize_amd as nq
+
+FAKE = 0x10000  # a 16-byte-aligned, never dereferenced address
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nq.LIB_PATH):
+        from nf4_quantize_amd import build
+
+        build.build()
+    return nq.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "nf4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(nf4_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_match_header(L):
+    declared = header_functions()
+    assert declared == sorted(nq.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {nq.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\b(nf4_[a-z_0-9]+)\b", out)))
+    assert exported == declared
+
+
+def test_codebook_is_printed_table(L, printed_codebook):
+    assert np.array_equal(np.array(nq.nf4_codebook(), np.float64), printed_codebook)
+
+
+def test_storage_bytes(L):
+    assert nq.nf4_storage_bytes(1 << 20) == 540_928
+    assert nq.nf4_storage_bytes(1 << 20, double_quant=False) == (1 << 19) + 4 * (1 << 14)
+    assert nq.nf4_storage_bytes(11008 * 4096) / (11008 * 4096) == 0.515869140625
+    assert L.nf4_storage_bytes(-1, 64, 256, 1) == -1
+    assert L.nf4_storage_bytes(64, 32, 256, 1) == -1
+    assert L.nf4_storage_bytes(64, 64, 128, 1) == -1
+
+
+def test_status_strings(L):
+    for code, name in nq.STATUS.items():
+        assert L.nf4_status_string(code).decode().startswith(name)
+
+
+def q(L, w=FAKE, dt=1, n=128, bs=64, codes=FAKE, absmax=None, dq=256, aq=FAKE, asc=FAKE):
+    return L.nf4_quantize(w, dt, n, bs, codes, absmax, dq, aq, asc, None)
+
+
+def test_quantize_validation(L):
+    assert q(L, n=0) == 0  # empty: OK, nothing launched
+    assert q(L, n=-1) == 2
+    assert q(L, n=(1 << 37) + 1) == 2
+    assert q(L, bs=32) == 3
+    assert q(L, dq=128) == 3
+    assert q(L, dt=7) == 3
+    assert q(L, w=None) == 1
+    assert q(L, codes=None) == 1
+    assert q(L, aq=None) == 1  # only one of the DQ outputs
+    assert q(L, aq=None, asc=None) == 1  # no scale output at all
+    assert q(L, w=FAKE + 8) == 4
+    assert q(L, codes=FAKE + 4) == 4
+    assert q(L, asc=FAKE + 2) == 4
+    assert q(L, aq=None, asc=None, absmax=FAKE + 1) == 4
+
+
+def test_double_quantize_validation(L):
+    f = L.nf4_double_quantize
+    assert f(FAKE, 0, 256, FAKE, FAKE, None) == 0
+    assert f(FAKE, -3, 256, FAKE, FAKE, None) == 2
+    assert f(FAKE, 10, 64, FAKE, FAKE, None) == 3
+    assert f(None, 10, 256, FAKE, FAKE, None) == 1
+    assert f(FAKE, 10, 256, None, FAKE, None) == 1
+    assert f(FAKE + 2, 10, 256, FAKE, FAKE, None) == 4
+
+
+def test_dequantize_validation(L):
+    f = L.nf4_dequantize
+    assert f(FAKE, 0, 64, None, FAKE, FAKE, 256, FAKE, 1, None) == 0
+    assert f(FAKE, -1, 64, None, FAKE, FAKE, 256, FAKE, 1, None) == 2
+    assert f(FAKE, 100, 16, None, FAKE, FAKE, 256, FAKE, 1, None) == 3
+    assert f(FAKE, 100, 64, None, FAKE, FAKE, 256, FAKE, 5, None) == 3
+    assert f(None, 100, 64, None, FAKE, FAKE, 256, FAKE, 1, None) == 1
+    assert f(FAKE, 100, 64, None, None, None, 256, FAKE, 1, None) == 1  # no scales at all
+    assert f(FAKE, 100, 64, None, FAKE, None, 256, FAKE, 1, None) == 1
+    assert f(FAKE, 100, 64, None, FAKE, FAKE, 256, FAKE + 8, 1, None) == 4
+
+
+def _w(n=256, k=512, codes=FAKE, aq=FAKE, asc=FAKE, am=None, bs=64, dq=256):
+    return nq.nf4_weight(codes=codes, absmax_q=aq, absmax_scale=asc, absmax=am, n_out=n, k_in=k,
+                         blocksize=bs, dq_blocksize=dq)
+
+
+@pytest.mark.parametrize("fn", ["nf4_linear_forward", "nf4_linear_backward_input"])
+def test_linear_validation(L, fn):
+    f = getattr(L, fn)
+    ws = nq.nf4_linear_workspace_size(64, 16)
+    assert ws == 64 * 16 * 2
+
+    def call(act=FAKE, m=64, w=None, a=FAKE, b=FAKE, r=16, out=FAKE, wsp=FAKE, wsb=ws):
+        w = w if w is not None else _w()
+        return f(act, m, ctypes.byref(w), a, b, r, 2.0, out, wsp, wsb, None)
+
+    assert f(FAKE, 64, None, FAKE, FAKE, 16, 2.0, FAKE, FAKE, ws, None) == 1
+    assert call(m=0) == 0
+    assert call(m=-1) == 2
+    assert call(w=_w(k=100)) == 2  # K % 64 != 0
+    assert call(r=300) == 2
+    assert call(w=_w(bs=32)) == 3
+    assert call(w=_w(dq=64)) == 3
+    assert call(act=None) == 1
+    assert call(out=None) == 1
+    assert call(w=_w(codes=None)) == 1
+    assert call(w=_w(aq=None, asc=None)) == 1
+    assert call(a=None) == 1  # r > 0 without A
+    assert call(b=None) == 1
+    # r == 0 needs no adapter and no workspace: validation goes on to the alignment check
+    assert call(a=None, b=None, r=0, wsp=None, wsb=0, act=FAKE + 2) == 4
+    assert call(act=FAKE + 2) == 4
+    assert call(w=_w(codes=FAKE + 4)) == 4
+    assert call(wsp=None) == 5
+    assert call(wsb=ws - 1) == 5
+
+
+def test_workspace_size(L):
+    assert nq.nf4_linear_workspace_size(4096, 64) == 4096 * 64 * 2
+    assert nq.nf4_linear_workspace_size(3, 5) == 256
+    assert nq.nf4_linear_workspace_size(100, 0) == 0
+
+
+def test_config_surface():
+    nq.NF4Config().validate()
+    for bad in (dict(quant_type="fp4"), dict(compute_dtype="float32"), dict(blocksize=128),
+                dict(load_in_4bit=False)):
+        with pytest.raises(ValueError):
+            nq.NF4Config(**bad).validate()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(nq, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(nq, "_lib", None)
+    with pytest.raises(nq.NF4LibraryMissing):
+        nq.lib()

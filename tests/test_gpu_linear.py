@@ -1,0 +1,179 @@
+"""GPU parity of the fused NF4 linear (forward and input gradient, with and
+without the adapter) against the oracle's double-precision reference.
+
+Tolerance: max_i |y_i - r_i| / max(|r_i|, rms(r)) <= 2e-2 (bf16 operands,
+fp32 accumulation, bf16 output; the reference uses the oracle's fp32
+dequantized weight and no intermediate rounding). The weight is quantized by
+the oracle and uploaded, so no input of the reference comes from the GPU.
+"""
+import numpy as np
+import pytest
+
+import nf4_quantize_amd as nq
+import oracle
+import workloads
+from gpu_util import log, rel_err_metric, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def upload_weight(w32, dev, dq=True):
+    """Quantize on the CPU oracle and upload the packed weight."""
+    N, K = w32.shape
+    codes, absmax = oracle.quantize(w32.ravel())
+    q8, scale = oracle.double_quantize(absmax)
+    t = nq.NF4Tensor(to_dev(codes, dev), None if dq else to_dev(absmax, dev),
+                     to_dev(q8, dev) if dq else None, to_dev(scale, dev) if dq else None, (N, K))
+    host = dict(codes=codes, absmax=None if dq else absmax, q=q8 if dq else None,
+                scale=scale if dq else None)
+    return t, host
+
+
+def oracle_wdeq(host, shape, rows=None):
+    N, K = shape
+    if rows is None:
+        return oracle.dequantize(host["codes"], N * K, absmax=host["absmax"], q=host["q"],
+                                 scale=host["scale"]).reshape(N, K)
+    return oracle.dequantize_rows(host["codes"], shape, rows, absmax=host["absmax"], q=host["q"],
+                                  scale=host["scale"])
+
+
+def small_case(seed, m, n, k, r, dq=True, sigma_lora=0.05):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    x = workloads.to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    dy = workloads.to_bf16_bits(rng.standard_normal((m, n), dtype=np.float32))
+    a = b = None
+    if r:
+        a = workloads.to_bf16_bits(rng.standard_normal((k, r), dtype=np.float32) * np.float32(sigma_lora))
+        b = workloads.to_bf16_bits(rng.standard_normal((r, n), dtype=np.float32) * np.float32(sigma_lora))
+    return w, x, dy, a, b
+
+
+CASES = [
+    # (m, N, K, r)
+    (64, 512, 256, 16),
+    (1, 128, 64, 0),
+    (4, 1024, 2048, 8),
+    (16, 768, 1024, 0),
+    (37, 100, 192, 5),     # ragged rows and columns
+    (130, 96, 320, 64),
+    (256, 256, 512, 64),
+    (2, 4096, 128, 3),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", CASES)
+@pytest.mark.parametrize("dq", [True, False])
+def test_linear_small_full(dev, m, n, k, r, dq):
+    import torch
+
+    log(f"linear full check m={m} N={n} K={k} r={r} dq={dq}")
+    w, x, dy, a, b = small_case(m * 7 + n + k + r, m, n, k, r, dq)
+    wt, host = upload_weight(w, dev, dq)
+    wd = oracle_wdeq(host, (n, k))
+    s = 2.0
+    xa, dya = to_dev(x, dev), to_dev(dy, dev)
+    aa = to_dev(a, dev) if r else None
+    ba = to_dev(b, dev) if r else None
+    y = nq.linear_forward(xa, wt, aa, ba, s)
+    dx = nq.linear_backward_input(dya, wt, aa, ba, s)
+    torch.cuda.synchronize()
+    y_ref = oracle.linear_forward(x, wd, a, b, s)
+    dx_ref = oracle.linear_backward_input(dy, wd, a, b, s)
+    e_y, n_y = rel_err_metric(_bf16_to_f32(to_host(y)), y_ref)
+    e_dx, n_dx = rel_err_metric(_bf16_to_f32(to_host(dx)), dx_ref)
+    log(f"  fwd err {e_y:.3e} (normwise {n_y:.3e}); dx err {e_dx:.3e} (normwise {n_dx:.3e})")
+    assert e_y <= TOL and e_dx <= TOL
+
+
+def test_lora_path_is_present(dev):
+    """With the adapter's contribution comparable to the base path, dropping it
+    (or applying it with the wrong scale) would exceed the tolerance."""
+    import torch
+
+    m, n, k, r = 32, 256, 512, 16
+    w, x, dy, a, b = small_case(5, m, n, k, r, sigma_lora=0.2)
+    wt, host = upload_weight(w, dev)
+    wd = oracle_wdeq(host, (n, k))
+    y = nq.linear_forward(to_dev(x, dev), wt, to_dev(a, dev), to_dev(b, dev), 2.0)
+    torch.cuda.synchronize()
+    got = (to_host(y).astype(np.uint32) << 16).view(np.float32)
+    ref = oracle.linear_forward(x, wd, a, b, 2.0)
+    ref_half = oracle.linear_forward(x, wd, a, b, 1.0)
+    assert rel_err_metric(got, ref)[0] <= TOL
+    assert rel_err_metric(got, ref_half)[0] > 5 * TOL
+
+
+def _bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("m", workloads.GEMV_MS)
+def test_decode_gemv_sampled(dev, m, gemv_case):
+    """Decode shape: x [M x 8192] times the 28672 x 8192 NF4 weight; all M rows
+    on 384 sampled output columns."""
+    import torch
+
+    wt, host, x = gemv_case
+    N, K = wt.shape
+    y = nq.linear_forward(to_dev(x[:m], dev), wt)
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.Generator(np.random.PCG64(40 + m)).choice(N, 384, replace=False))
+    wd_rows = oracle_wdeq(host, (N, K), rows=cols)
+    ref = oracle.linear_forward(x[:m], wd_rows)  # columns of Y = rows of W
+    got = _bf16_to_f32(to_host(y))[:, cols]
+    e, nw = rel_err_metric(got, ref)
+    log(f"gemv M={m}: err {e:.3e} normwise {nw:.3e}")
+    assert e <= TOL
+
+
+@pytest.fixture(scope="module")
+def gemv_case(dev):
+    log("preparing 28672x8192 NF4 weight on the oracle")
+    w, x = workloads.gemv_inputs()
+    wt, host = upload_weight(w, dev)
+    return wt, host, x
+
+
+@pytest.fixture(scope="module")
+def linear_case(dev):
+    log("preparing 4096x8192x8192 r=64 case on the oracle")
+    d = workloads.linear_inputs()
+    wt, host = upload_weight(d["w"], dev)
+    wd = oracle_wdeq(host, d["w"].shape)
+    return d, wt, wd
+
+
+def test_qlora_linear_forward_sampled(dev, linear_case):
+    import torch
+
+    d, wt, wd = linear_case
+    s = workloads.LIN_SCALE
+    y = nq.linear_forward(to_dev(d["x"], dev), wt, to_dev(d["a"], dev), to_dev(d["b"], dev), s)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 777, 2048, 4095, 3001, 123, 4000])
+    ref = oracle.linear_forward(d["x"], wd, d["a"], d["b"], s, rows=rows)
+    got = _bf16_to_f32(to_host(y))[rows]
+    e, nw = rel_err_metric(got, ref)
+    log(f"qlora forward sampled rows: err {e:.3e} normwise {nw:.3e}")
+    assert e <= TOL
+
+
+def test_qlora_linear_backward_input_sampled(dev, linear_case):
+    import torch
+
+    d, wt, wd = linear_case
+    s = workloads.LIN_SCALE
+    dx = nq.linear_backward_input(to_dev(d["dy"], dev), wt, to_dev(d["a"], dev),
+                                  to_dev(d["b"], dev), s)
+    torch.cuda.synchronize()
+    rows = np.array([0, 4095, 1500, 2222])
+    cols = np.sort(np.random.Generator(np.random.PCG64(77)).choice(8192, 768, replace=False))
+    ref = oracle.linear_backward_input(d["dy"], wd, d["a"], d["b"], s, rows=rows, cols=cols)
+    got = _bf16_to_f32(to_host(dx))[np.ix_(rows, cols)]
+    e, nw = rel_err_metric(got, ref)
+    log(f"qlora input-grad sampled: err {e:.3e} normwise {nw:.3e}")
+    assert e <= TOL

@@ -259,3 +259,16 @@ def test_nf4_mse_below_uniform_4bit(oracle_mod):
     mse_nf4 = np.mean((w - nf4) ** 2)
     mse_uni = np.mean((w - uni) ** 2)
     assert mse_nf4 < mse_uni
+
+
+def test_dequantize_range_equals_slice(oracle_mod):
+    w = gaussian_f32(45, 64 * 256 * 3 + 50, 0.02)
+    n = w.size
+    codes, absmax = oracle_mod.quantize(w)
+    q8, scale = oracle_mod.double_quantize(absmax)
+    full = oracle_mod.dequantize(codes, n, q=q8, scale=scale)
+    for start, count in [(0, 7), (16383, 3), (20000, 16384), (n - 9, 9)]:
+        part = oracle_mod.dequantize_range(codes, n, start, count, q=q8, scale=scale)
+        assert np.array_equal(part, full[start:start + count])
+    rows = oracle_mod.dequantize_rows(codes, (n // 50, 50), [0, 3, 100], q=q8, scale=scale)
+    assert np.array_equal(rows[1], full[150:200])
