@@ -56,6 +56,7 @@ def lib():
         L.nf4ref_block_scale.argtypes = [_i64, _p, _p, _p]
         L.nf4ref_block_scale.restype = ctypes.c_float
         L.nf4ref_dequantize.argtypes = [_p, _i64, _p, _p, _p, _p, ctypes.c_int]
+        L.nf4ref_dequantize_range.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _p, ctypes.c_int]
         L.nf4ref_storage_bytes.argtypes = [_i64, ctypes.c_int]
         L.nf4ref_storage_bytes.restype = _i64
         for name in ("nf4ref_linear_forward", "nf4ref_linear_backward_input"):
@@ -176,6 +177,27 @@ def dequantize(codes, n, absmax=None, q=None, scale=None, out_dtype=F32):
     out = np.zeros(n, np.float32 if out_dtype == F32 else np.uint16)
     _check(lib().nf4ref_dequantize(_ptr(codes), n, _ptr(absmax), _ptr(q), _ptr(scale),
                                    _ptr(out), out_dtype), "dequantize")
+    return out
+
+
+def dequantize_range(codes, n, start, count, absmax=None, q=None, scale=None, out_dtype=F32):
+    """Elements [start, start+count) of the n-element tensor (global block indices)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    out = np.zeros(count, np.float32 if out_dtype == F32 else np.uint16)
+    _check(lib().nf4ref_dequantize_range(_ptr(codes), n, start, count, _ptr(absmax), _ptr(q),
+                                         _ptr(scale), _ptr(out), out_dtype), "dequantize_range")
+    return out
+
+
+def dequantize_rows(codes, shape, rows, absmax=None, q=None, scale=None):
+    """fp32 rows of a dequantized [N x K] weight."""
+    N, K = shape
+    out = np.zeros((len(rows), K), np.float32)
+    for i, r in enumerate(rows):
+        out[i] = dequantize_range(codes, N * K, int(r) * K, K, absmax, q, scale)
     return out
 
 

@@ -295,24 +295,31 @@ float nf4ref_block_scale(int64_t b, const float *absmax, const uint8_t *q, const
     return nf4ref_e4m3_decode(q[b]) * scale[b / NF4REF_DQ_BLOCK];
 }
 
-int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
-                      const float *scale, void *out, int out_dtype) {
-    if (n < 0) return -1;
-    if (n == 0) return 0;
+int nf4ref_dequantize_range(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                            const float *absmax, const uint8_t *q, const float *scale, void *out,
+                            int out_dtype) {
+    if (n < 0 || start < 0 || count < 0 || start + count > n) return -1;
+    if (count == 0) return 0;
     if (!codes || !out) return -1;
     if (!q && !absmax) return -1;
     if (q && !scale) return -1;
     if (out_dtype != NF4REF_F32 && out_dtype != NF4REF_BF16) return -1;
-    for (int64_t i = 0; i < n; ++i) {
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t i = start + j;
         int code = (codes[i / 2] >> (4 * (int)(i & 1))) & 15;
         float c1 = nf4ref_block_scale(i / NF4REF_BLOCK, absmax, q, scale);
         float v = NF4_Q[code] * c1;
         if (out_dtype == NF4REF_F32)
-            ((float *)out)[i] = v;
+            ((float *)out)[j] = v;
         else
-            ((uint16_t *)out)[i] = nf4ref_f32_to_bf16(v);
+            ((uint16_t *)out)[j] = nf4ref_f32_to_bf16(v);
     }
     return 0;
+}
+
+int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
+                      const float *scale, void *out, int out_dtype) {
+    return nf4ref_dequantize_range(codes, n, 0, n, absmax, q, scale, out, out_dtype);
 }
 
 /* ---- storage footprint ([L15] "Double quantisation" per-parameter tables) ---- */

@@ -88,6 +88,12 @@ float nf4ref_block_scale(int64_t b, const float *absmax, const uint8_t *q, const
 int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
                       const float *scale, void *out, int out_dtype);
 
+/* Dequantization of elements [start, start + count) of an n-element tensor,
+ * with the block and group indices of the whole tensor. out: count values. */
+int nf4ref_dequantize_range(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                            const float *absmax, const uint8_t *q, const float *scale, void *out,
+                            int out_dtype);
+
 /* Storage bytes of an n-element NF4 tensor: codes + scales (dq != 0: 8-bit
  * codes plus fp32 second-level scales; dq == 0: fp32 absmax). */
 int64_t nf4ref_storage_bytes(int64_t n, int dq);
