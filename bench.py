@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+COPY_BYTES = 256 << 20       # calibration copy: reads and writes this many bytes
 
 
 def log(msg):
@@ -310,6 +311,9 @@ def main():
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stack", action="store_true", help="also time the 224-matrix 8B stack")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy 3 times (reference for "
+                         "HBM byte counters under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -321,6 +325,14 @@ def main():
 
     nq.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {COPY_BYTES} bytes")
+        del src, dst
     main_res, w_bits = main_step_bench(args, dev)
     log(f"main step: {main_res}")
 

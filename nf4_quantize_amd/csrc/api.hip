@@ -69,35 +69,51 @@ float ord2f(int64_t o) {
     return x;
 }
 
+// Bucket of v, with the same fp32 formula as the kernels (see CodeLut).
+uint32_t bucket_of(float v) { return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f)) >> 3; }
+
 bool build_lut(CodeLut *lut) {
-    // Bucket k covers n in [-1 + k/16, -1 + (k+1)/16); bucket 32 holds n >= 1.
-    for (int k = 0; k < 32; ++k) {
-        const float lo = -1.0f + (float)k / 16.0f;
-        const float hi = -1.0f + (float)(k + 1) / 16.0f;
-        const float last = ord2f(f2ord(hi) - 1);
+    const float vmin = -1.0f - 0x1p-20f, vmax = 1.0f + 0x1p-20f;
+    // bucket_of is non-decreasing in v, so each bucket is an interval of floats.
+    int64_t start = f2ord(vmin);
+    const int64_t end = f2ord(vmax);
+    if (bucket_of(vmin) != 0 || bucket_of(vmax) != kLutUsed - 1) return false;
+    for (int k = 0; k < kLutUsed; ++k) {
+        // last float of bucket k: bisection for the largest ordinal with bucket <= k
+        int64_t a = start, b = end;
+        if (bucket_of(ord2f(b)) <= (uint32_t)k) {
+            a = b;
+        } else {
+            while (b - a > 1) {
+                const int64_t mid = a + (b - a) / 2;
+                if (bucket_of(ord2f(mid)) <= (uint32_t)k) a = mid; else b = mid;
+            }
+        }
+        const float lo = ord2f(start), hi = ord2f(a);
+        if (bucket_of(lo) != (uint32_t)k || bucket_of(hi) != (uint32_t)k) return false;
         const int c_lo = nearest_by_search(lo);
-        const int c_last = nearest_by_search(last);
+        const int c_hi = nearest_by_search(hi);
         lut->e[k].base = c_lo;
         lut->e[k].thr = 2.0f;
-        if (c_last == c_lo) continue;
-        if (c_last != c_lo + 1) return false;  // more than one switch in a bucket
-        int64_t a = f2ord(lo), b = f2ord(last);  // code(a) == c_lo, code(b) == c_lo + 1
-        while (b - a > 1) {
-            const int64_t mid = a + (b - a) / 2;
-            if (nearest_by_search(ord2f(mid)) > c_lo)
-                b = mid;
-            else
-                a = mid;
+        if (c_hi != c_lo) {
+            if (c_hi != c_lo + 1) return false;  // more than one switch in a bucket
+            int64_t u = f2ord(lo), v = f2ord(hi);  // code(u) == c_lo, code(v) == c_lo + 1
+            while (v - u > 1) {
+                const int64_t mid = u + (v - u) / 2;
+                if (nearest_by_search(ord2f(mid)) > c_lo) v = mid; else u = mid;
+            }
+            const float thr = ord2f(v);
+            // A switch point must sit inside its bucket by more than the
+            // |q - n| bound (2.4e-7), so that q and n can only straddle the
+            // switch point of the bucket q falls in (which the kernels test).
+            if (!(thr - lo >= 0x1p-16f && hi - thr >= 0x1p-16f)) return false;
+            lut->e[k].thr = thr;
         }
-        const float thr = ord2f(b);
-        // Switch points must sit well inside their bucket, so that a q
-        // within kNearTol of n never crosses a switch point of a neighbour.
-        if (!(thr - lo >= 0x1p-10f && hi - thr >= 0x1p-10f)) return false;
-        lut->e[k].thr = thr;
+        start = a + 1;
     }
-    lut->e[32].base = nearest_by_search(1.0f);
-    lut->e[32].thr = 2.0f;
-    return lut->e[32].base == 15 && lut->e[16].base == 7;
+    for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{2.0f, 15};
+    return lut->e[kLutUsed - 1].base == 15 && nearest_by_search(0.0f) == 7 &&
+           lut->e[bucket_of(0.0f)].base == 7;
 }
 
 }  // namespace
@@ -158,6 +174,7 @@ NF4_API nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int
     if (w_dtype != NF4_F32 && w_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
     const bool dq = absmax_q != nullptr || absmax_scale != nullptr;
     if (dq && dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (!code_lut()) return NF4_ERR_UNSUPPORTED;  // codebook table failed its checks
     if (n == 0) return NF4_OK;
     if (!w || !codes) return NF4_ERR_NULL;
     if (dq && (!absmax_q || !absmax_scale)) return NF4_ERR_NULL;
@@ -166,7 +183,6 @@ NF4_API nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int
     if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
         (absmax_scale && !aligned(absmax_scale, 4)))
         return NF4_ERR_ALIGN;
-    if (!code_lut()) return NF4_ERR_UNSUPPORTED;
     return launch_status(launch_quantize(w, w_dtype, n, codes, absmax, absmax_q, absmax_scale,
                                          static_cast<hipStream_t>(stream)));
 }

@@ -20,13 +20,20 @@ constexpr int kGroup = kBlock * kDqBlock;   // 16384 weights share one c2
 // The 16 NF4 levels, [MF] "4-Bit NormalFloat (NF4)" (the printed list).
 extern const float kLevels[16];
 
-// Nearest-level lookup: the normalised value n in [-1, 1] is split into 32
-// buckets of width 1/16 (plus bucket 32 for n >= 1). No bucket holds more
-// than one switch point of the code function, so
-//   code(n) = base[k] + (n >= thr[k]),   k = floor(16 n + 16).
-// thr is 2.0 in a bucket without a switch point. Built on the host from the
-// codebook by nf4::code_lut() and passed to kernels by value.
-constexpr int kLutEntries = 33;
+// Nearest-level lookup. A normalised value v in [-1, 1] is bucketed by
+//   offset(v) = bits(fl(v * 128 + (128 + 2^23))) & 0x1F8:
+// the fma result lies in [2^23, 2^24), where the float's ulp is 1, so its
+// low mantissa bits hold i = round(128 v + 128) and the mask keeps 8 * (i / 8),
+// the byte offset of an 8-byte table entry (bucket k = i / 8, about 1/16 wide).
+// No bucket holds more than one switch point of the code function, so
+//   code(v) = base[k] + (v >= thr[k]),
+// with thr = 2.0 in a bucket without a switch point. For |v| <= 1 + 2^-20
+// the bucket is 0..32; any input, NaN included, gives an offset below 512,
+// so the table has 64 entries. Built on the host from the codebook by
+// nf4::code_lut() (which buckets with this same fp32 formula) and passed to
+// kernels by value.
+constexpr int kLutEntries = 64;
+constexpr int kLutUsed = 33;
 struct LutEntry {
     float thr;
     int32_t base;
@@ -34,6 +41,9 @@ struct LutEntry {
 struct CodeLut {
     LutEntry e[kLutEntries];
 };
+__host__ __device__ __forceinline__ uint32_t lut_offset_bits(float fma_result) {
+    return __builtin_bit_cast(uint32_t, fma_result) & 0x1F8u;
+}
 // Returns the table (built once, thread-safe), or nullptr if the codebook
 // failed the construction checks.
 const CodeLut *code_lut();

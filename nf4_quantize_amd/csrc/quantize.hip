@@ -24,33 +24,32 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float dpp_max_quad_xor1(float v) {
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float dpp_max_quad_xor2(float v) {
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float dpp_max_half_mirror(float v) {  // lane i <-> 7-i in each 8
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float dpp_max_mirror(float v) {  // lane i <-> 15-i in each 16
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-}
-
-// Max over the whole workgroup (256 threads); every thread gets the result.
+// Max over the whole workgroup of T threads; every thread gets the result.
+template <int T = kThreads>
 __device__ __forceinline__ float wg_max(float v, float *s_red) {
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) s_red[wave] = v;
     __syncthreads();
-    float r = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float r = s_red[0];
+#pragma unroll
+    for (int i = 1; i < T / 64; ++i) r = fmaxf(r, s_red[i]);
     return r;
 }
 
-// Code of an exactly normalised value n in [-1, 1] (or of q near it).
-__device__ __forceinline__ uint32_t lut_index(float v) {
-    int k = (int)fmaf(v, 16.0f, 16.0f);
-    return min((uint32_t)k, (uint32_t)(kLutEntries - 1));
+// Byte offset of the table entry of a normalised value (see CodeLut).
+__device__ __forceinline__ uint32_t lut_offset(float v) {
+    return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f));
+}
+__device__ __forceinline__ float2 lut_entry(const float2 *s_lut, float v) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(s_lut) + lut_offset(v));
+}
+
+// Max of non-negative floats via their bit patterns (monotone as unsigned),
+// with the neighbour lane brought in by DPP.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, false));
 }
 
 // Input traits: one 16-byte slice per lane.
@@ -87,22 +86,22 @@ __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, c
     const bool outside = (c1 > 0.0f) & !in_range;
     const float rcp = in_range ? __builtin_amdgcn_rcpf(c1) : 0.0f;
     uint32_t packed = 0;
-    bool near = outside;
+    float dmin = __builtin_inff();
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const float q = f[e] * rcp;
-        const float2 ent = s_lut[lut_index(q)];
+        const float2 ent = lut_entry(s_lut, q);
         const float d = q - ent.x;
         const uint32_t code = (uint32_t)__float_as_int(ent.y) + (d >= 0.0f ? 1u : 0u);
-        near |= fabsf(d) < kNearTol;
+        dmin = fminf(dmin, fabsf(d));
         packed |= code << (4 * e);
     }
-    if (near) {  // rare: redo the slice with the correctly rounded division
+    if (outside | !(dmin >= kNearTol)) {  // rare: redo with the correctly rounded division
         packed = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float nrm = f[e] / c1;
-            const float2 ent = s_lut[lut_index(nrm)];
+            const float2 ent = lut_entry(s_lut, nrm);
             const uint32_t code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
             packed |= code << (4 * e);
         }
@@ -115,34 +114,39 @@ __device__ __forceinline__ void load_lut(const CodeLut &lut, float2 *s_lut) {
         s_lut[threadIdx.x] = make_float2(lut.e[threadIdx.x].thr, __int_as_float(lut.e[threadIdx.x].base));
 }
 
-// Double quantization of the group's 256 c1 values held in s_c1.
+// Double quantization of the group's 256 c1 values held in s_c1 (threads
+// 0..255 each own one block; a larger workgroup's other threads only join
+// the barriers).
+template <int T>
 __device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32_t *s_q8,
                                          uint8_t *absmax_q, float *absmax_scale, int64_t g) {
     const int t = threadIdx.x;
-    const float c1 = s_c1[t];
-    const float c2 = wg_max(c1, s_red);
-    const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
-    reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)e4m3_encode_unit(ratio);
+    const float c1 = (t < kDqBlock) ? s_c1[t] : 0.0f;
+    const float c2 = wg_max<T>(c1, s_red);
+    if (t < kDqBlock) {
+        const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
+        reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)e4m3_encode_unit(ratio);
+    }
     __syncthreads();
     if (t < kDqBlock / 4) reinterpret_cast<uint32_t *>(absmax_q + g * kDqBlock)[t] = s_q8[t];
     if (t == 0) absmax_scale[g] = c2;
 }
 
-// One workgroup per full group of 16384 weights.
-template <typename T, bool kDQ>
-__global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
+// One workgroup of TH threads per full group of 16384 weights.
+template <typename T, bool kDQ, int TH>
+__global__ __launch_bounds__(TH) void quantize_groups_kernel(
     const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
     uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, CodeLut lut) {
     using S = Slice<T>;
     constexpr int E = S::kElems;               // weights per lane slice
     constexpr int LPB = kBlock / E;            // lanes per block
     constexpr int SLICES = kGroup / E;         // slices per group
-    constexpr int ITERS = SLICES / kThreads;   // slices per thread
-    constexpr int BPI = kThreads / LPB;        // blocks per iteration
+    constexpr int ITERS = SLICES / TH;         // slices per thread
+    constexpr int BPI = TH / LPB;              // blocks per iteration
 
     __shared__ float2 s_lut[kLutEntries];
     __shared__ float s_c1[kDqBlock];
-    __shared__ float s_red[4];
+    __shared__ float s_red[TH / 64];
     __shared__ uint32_t s_q8[kDqBlock / 4];
 
     const int t = threadIdx.x;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
 
     typename S::Vec v[ITERS];
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * kThreads + t]);
+    for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * TH + t]);
 
     load_lut(lut, s_lut);
     __syncthreads();
@@ -160,20 +164,22 @@ __global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
     for (int i = 0; i < ITERS; ++i) {
         float f[E];
         S::widen(v[i], f);
-        float m = fabsf(f[0]);
+        float mf = fabsf(f[0]);
 #pragma unroll
-        for (int e = 1; e < E; ++e) m = fmaxf(m, fabsf(f[e]));
-        m = dpp_max_quad_xor1(m);
-        m = dpp_max_quad_xor2(m);
-        m = dpp_max_half_mirror(m);
-        if (LPB == 16) m = dpp_max_mirror(m);
+        for (int e = 1; e < E; ++e) mf = fmaxf(mf, fabsf(f[e]));
+        uint32_t mb = __float_as_uint(mf);
+        mb = dpp_umax<0xB1>(mb);   // quad_perm [1,0,3,2]
+        mb = dpp_umax<0x4E>(mb);   // quad_perm [2,3,0,1]
+        mb = dpp_umax<0x141>(mb);  // row_half_mirror: lanes i <-> 7-i
+        if (LPB == 16) mb = dpp_umax<0x140>(mb);  // row_mirror: lanes i <-> 15-i
+        const float m = __uint_as_float(mb);
         const int blk = i * BPI + t / LPB;  // block within the group
         if ((t % LPB) == 0) {
             if (kDQ) s_c1[blk] = m;
             if (absmax) absmax[g * kDqBlock + blk] = m;
         }
         const uint32_t packed = slice_codes<E>(f, m, s_lut);
-        const int64_t slice = (int64_t)g * SLICES + i * kThreads + t;
+        const int64_t slice = (int64_t)g * SLICES + i * TH + t;
         if (E == 8)
             reinterpret_cast<uint32_t *>(codes)[slice] = packed;
         else
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
     }
     if (kDQ) {
         __syncthreads();
-        group_dq(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
+        group_dq<TH>(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
     }
 }
 
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
             uint32_t code = 7;
             if (c1 > 0.0f) {
                 const float nrm = elem(i + j) / c1;
-                const float2 ent = s_lut[lut_index(nrm)];
+                const float2 ent = lut_entry(s_lut, nrm);
                 code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
             }
             byte |= code << (4 * j);
@@ -251,17 +257,21 @@ __global__ __launch_bounds__(kThreads) void double_quantize_kernel(
     if (t == 0) absmax_scale[g] = c2;
 }
 
+// Threads per group workgroup.
+constexpr int kGroupThreads = 256;
+
 template <typename T>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
                              uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
     const CodeLut &lut = *code_lut();
     const int64_t full = n / kGroup;
+    constexpr int TH = kGroupThreads;
     if (full > 0) {
         if (absmax_q)
-            quantize_groups_kernel<T, true><<<dim3((unsigned)full), dim3(kThreads), 0, s>>>(
+            quantize_groups_kernel<T, true, TH><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
                 w, codes, absmax, absmax_q, absmax_scale, lut);
         else
-            quantize_groups_kernel<T, false><<<dim3((unsigned)full), dim3(kThreads), 0, s>>>(
+            quantize_groups_kernel<T, false, TH><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
                 w, codes, absmax, nullptr, nullptr, lut);
     }
     if (n % kGroup)
