@@ -9,37 +9,13 @@
 // tile dequantized once into LDS and reused by all 64 rows of the tile, fp32
 // FMA. It serves any shape; the MFMA paths in linear_mfma.hip take the shapes
 // they tile exactly.
-#include "nf4_internal.h"
+#include "linear_common.h"
 
 namespace nf4 {
-
-// Weight view passed to kernels.
-struct WView {
-    const uint8_t *codes;
-    const uint8_t *q;      // E4M3 codes of c1/c2, or nullptr
-    const float *scale;    // c2 per group (with q)
-    const float *absmax;   // c1 per block (without q)
-    int64_t n, k;
-};
-
-__device__ __forceinline__ float wscale(const WView &w, int64_t b) {
-    return block_scale(b, w.absmax, w.q, w.scale);
-}
-
 namespace {
 
 constexpr int kT = 64;         // output tile edge and K step
 constexpr int kThreads = 256;  // 16 x 16 threads, 4 x 4 outputs each
-
-struct Levels {
-    float q[16];
-};
-
-Levels levels() {
-    Levels l;
-    for (int i = 0; i < 16; ++i) l.q[i] = kLevels[i];
-    return l;
-}
 
 // out[m, j] = sum_i act[m, i] * mat[i * ms_i + j * ms_j]  (bf16 in, fp32 acc,
 // bf16 out): the adapter's down-projection X.A (ms_i = r, ms_j = 1) or
@@ -137,21 +113,18 @@ __global__ __launch_bounds__(kThreads) void linear_tiled_kernel(
     }
 }
 
-WView view(const nf4_weight &w) {
-    return WView{w.codes, w.absmax_q, w.absmax_scale, w.absmax, w.n_out, w.k_in};
-}
-
 }  // namespace
 
 hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s) {
+    if (r == 0 && gemv_supported(m, w.k_in)) return launch_gemv(x, m, w, y, s);
     uint16_t *t = static_cast<uint16_t *>(workspace);
     if (r > 0)
         lora_down_simple_kernel<<<dim3((unsigned)((m * r + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
             x, m, w.k_in, a, r, 1, r, t);
     dim3 grid((unsigned)((w.n_out + kT - 1) / kT), (unsigned)((m + kT - 1) / kT));
-    linear_tiled_kernel<false><<<grid, kThreads, 0, s>>>(x, m, view(w), t, b, r, s_lora, y, levels());
+    linear_tiled_kernel<false><<<grid, kThreads, 0, s>>>(x, m, make_view(w), t, b, r, s_lora, y, levels());
     return hipGetLastError();
 }
 
@@ -164,7 +137,7 @@ hipError_t launch_linear_backward_input(const uint16_t *dy, int64_t m, const nf4
         lora_down_simple_kernel<<<dim3((unsigned)((m * r + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
             dy, m, w.n_out, b, 1, w.n_out, r, u);
     dim3 grid((unsigned)((w.k_in + kT - 1) / kT), (unsigned)((m + kT - 1) / kT));
-    linear_tiled_kernel<true><<<grid, kThreads, 0, s>>>(dy, m, view(w), u, a, r, s_lora, dx, levels());
+    linear_tiled_kernel<true><<<grid, kThreads, 0, s>>>(dy, m, make_view(w), u, a, r, s_lora, dx, levels());
     return hipGetLastError();
 }
 

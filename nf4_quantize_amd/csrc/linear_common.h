@@ -1,0 +1,42 @@
+// linear_common.h - weight view and level table shared by the fused NF4
+// linear kernels (internal).
+#pragma once
+
+#include "nf4_internal.h"
+
+namespace nf4 {
+
+// An NF4 weight [n x k] (row-major, 64-blocks along k) as passed to kernels.
+struct WView {
+    const uint8_t *codes;
+    const uint8_t *q;      // E4M3 codes of c1/c2, or nullptr
+    const float *scale;    // c2 per group (with q)
+    const float *absmax;   // c1 per block (without q)
+    int64_t n, k;
+};
+
+inline WView make_view(const nf4_weight &w) {
+    return WView{w.codes, w.absmax_q, w.absmax_scale, w.absmax, w.n_out, w.k_in};
+}
+
+// Reconstructed scale c1' of flat block index b.
+__device__ __forceinline__ float wscale(const WView &w, int64_t b) {
+    return block_scale(b, w.absmax, w.q, w.scale);
+}
+
+// The 16 levels by value (kernel argument).
+struct Levels {
+    float q[16];
+};
+inline Levels levels() {
+    Levels l;
+    for (int i = 0; i < 16; ++i) l.q[i] = kLevels[i];
+    return l;
+}
+
+// Decode-shaped path (1 <= m <= 16, K % 256 == 0, no adapter): linear_gemv.hip.
+bool gemv_supported(int64_t m, int64_t k);
+hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &w, uint16_t *y,
+                       hipStream_t s);
+
+}  // namespace nf4

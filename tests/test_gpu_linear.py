@@ -62,6 +62,15 @@ CASES = [
     (130, 96, 320, 64),
     (256, 256, 512, 64),
     (2, 4096, 128, 3),
+    # decode-shaped (no adapter): ragged column counts and odd row counts
+    (3, 100, 192, 0),
+    (16, 200, 320, 0),
+    (9, 48, 128, 0),
+    (5, 16 * 37, 64 * 11, 0),
+    (3, 100, 768, 0),       # decode path (K % 256 == 0), ragged N
+    (9, 48, 512, 0),
+    (1, 16 * 600 + 5, 256, 0),
+    (16, 1000, 1280, 0),
 ]
 
 
