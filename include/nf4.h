@@ -126,7 +126,8 @@ typedef struct {
 } nf4_weight;
 
 /* Bytes of device workspace that nf4_linear_forward / nf4_linear_backward_input
- * need for m rows and adapter rank r (0 when r == 0). */
+ * need for m rows and adapter rank r: the bf16 adapter product
+ * [m x (r rounded up to 64)], rounded up to 256 bytes (0 when r == 0). */
 size_t nf4_linear_workspace_size(int64_t m, int32_t r);
 
 /* Fused QLoRA linear forward ([MF] "Forward Pass Computation"):

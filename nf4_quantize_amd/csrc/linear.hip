@@ -5,10 +5,11 @@
 // ([MF] "Forward Pass Computation" and "Gradient Computation"; source key in
 // nf4_internal.h). W is stored [N x K] row-major with 64-blocks along K.
 //
-// This file holds the portable tiled path: 64x64 output tiles, the weight
-// tile dequantized once into LDS and reused by all 64 rows of the tile, fp32
-// FMA. It serves any shape; the MFMA paths in linear_mfma.hip take the shapes
-// they tile exactly.
+// This file holds the dispatch and the portable tiled path (64x64 output
+// tiles, the weight tile dequantized once into LDS and reused by all 64 rows
+// of the tile, fp32 FMA), which serves shapes the MFMA paths do not take:
+// linear_gemv.hip (m <= 16, no adapter) and linear_gemm.hip (N % 64 == 0,
+// r % 8 == 0).
 #include "linear_common.h"
 
 namespace nf4 {
@@ -119,6 +120,8 @@ hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight 
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s) {
     if (r == 0 && gemv_supported(m, w.k_in)) return launch_gemv(x, m, w, y, s);
+    if (gemm_supported(w.n_out, r))
+        return launch_gemm_forward(x, m, w, a, b, r, s_lora, y, static_cast<uint16_t *>(workspace), s);
     uint16_t *t = static_cast<uint16_t *>(workspace);
     if (r > 0)
         lora_down_simple_kernel<<<dim3((unsigned)((m * r + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
@@ -132,6 +135,8 @@ hipError_t launch_linear_backward_input(const uint16_t *dy, int64_t m, const nf4
                                         const uint16_t *a, const uint16_t *b, int32_t r,
                                         float s_lora, uint16_t *dx, void *workspace,
                                         hipStream_t s) {
+    if (gemm_supported(w.n_out, r))
+        return launch_gemm_dgrad(dy, m, w, a, b, r, s_lora, dx, static_cast<uint16_t *>(workspace), s);
     uint16_t *u = static_cast<uint16_t *>(workspace);
     if (r > 0)
         lora_down_simple_kernel<<<dim3((unsigned)((m * r + kThreads - 1) / kThreads)), kThreads, 0, s>>>(

@@ -39,4 +39,14 @@ bool gemv_supported(int64_t m, int64_t k);
 hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &w, uint16_t *y,
                        hipStream_t s);
 
+// Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
+// The workspace holds the bf16 adapter product [m x round64(r)].
+bool gemm_supported(int64_t n, int32_t r);
+hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *a,
+                               const uint16_t *b, int32_t r, float s_lora, uint16_t *y,
+                               uint16_t *t_ws, hipStream_t s);
+hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w, const uint16_t *a,
+                             const uint16_t *b, int32_t r, float s_lora, uint16_t *dx,
+                             uint16_t *u_ws, hipStream_t s);
+
 }  // namespace nf4

@@ -1,0 +1,509 @@
+// linear_gemm.hip - large-M fused NF4 linear for gfx950 on bf16 MFMA
+// ([MF] "Forward Pass Computation" and "Gradient Computation"; source key in
+// nf4_internal.h):
+//   forward   Y  = X . W'^T + s (X . A) . B
+//   dgrad     dX = dY . W'  + s (dY . B^T) . A^T
+// with W' = dequantize(W), W stored [N x K] NF4, A [K x r], B [r x N] bf16.
+//
+// One kernel template computes C[M x Nc] = sum over K-segments of
+// Aop[M x Kseg] . Bop[Nc x Kseg]^T, where Aop is a row-major bf16 matrix and
+// Bop is read from one of four sources:
+//   NF4_NT  Bop[n][k] = W'[n][k]   (forward: rows of W)
+//   NF4_NN  Bop[c][j] = W'[j][c]   (dgrad: columns of W)
+//   BF16_NT Bop[n][k] = Mat[n][k]
+//   BF16_NN Bop[n][k] = Mat[k][n]
+// A second K-segment carries the adapter: forward appends T' = s X.A with
+// Bop = B (BF16_NN), dgrad appends U' = s dY.B^T with Bop = A (BF16_NT);
+// T' and U' come from the same kernel (BF16_NN with Mat = A, and BF16_NT
+// with Mat = B) and are stored bf16 in the caller's workspace.
+//
+// Tiling: a workgroup of 4 waves owns a BM x BN tile of C; each wave a
+// (BM/2) x (BN/2) quarter, as 16x16 tiles of v_mfma_f32_16x16x32_bf16.
+// K advances 64 at a time (one NF4 block per weight row). Both operand tiles
+// are staged in LDS as bf16 [row][64] with 16-byte chunks XOR-swizzled by row
+// so that the MFMA operand reads (16 rows, one chunk) hit distinct banks.
+// The NF4 tile is dequantized on the way in, exactly as the dequantize path
+// does it: bf16(q[code] * c1'). The next K-step's global loads are issued
+// before the current step's MFMAs; LDS is double buffered.
+#include <algorithm>
+
+#include "linear_common.h"
+
+namespace nf4 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;           // K step (one NF4 block per weight row)
+constexpr int kRowBytes = kBK * 2;
+
+enum BMode { NF4_NT = 0, NF4_NN = 1, BF16_NT = 2, BF16_NN = 3 };
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of LDS tile row `row`.
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+    return (uint32_t)row * kRowBytes + 16u * (uint32_t)(chunk ^ ((row >> 1) & 7));
+}
+
+// One K-segment: C += Aop . Bop^T over ksteps of 64.
+struct Segment {
+    const uint16_t *a;   // Aop, row-major [M x lda]
+    int64_t lda;
+    int64_t klen;        // contraction length of the segment (multiple of 64)
+    // B source
+    WView w;             // NF4 modes
+    const uint16_t *mat; // bf16 modes
+    int64_t ldm;         // row stride of mat
+    int64_t mat_rows, mat_cols;  // bounds of mat
+};
+
+struct Params {
+    Segment seg[2];
+    int nseg;
+    int64_t M, Nc;       // C is [M x Nc]
+    uint16_t *c;         // bf16 output
+    int64_t ldc;
+    float out_scale;     // multiplies the fp32 accumulator before rounding
+    Levels lv;
+};
+
+// ---------------------------------------------------------------- staging
+
+// A tile: BM rows x 64 bf16 = BM * 8 chunks; each thread moves BM/32 chunks.
+template <int BM>
+struct AStage {
+    static constexpr int kChunks = BM * 8 / kThreads;
+    u32x4 v[kChunks];
+    __device__ void load(const Segment &sg, int64_t m0, int64_t M, int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = q * kThreads + threadIdx.x;
+            const int row = idx >> 3, ch = idx & 7;
+            const int64_t gr = m0 + row;
+            v[q] = u32x4{0, 0, 0, 0};
+            if (gr < M) v[q] = *reinterpret_cast<const u32x4 *>(sg.a + gr * sg.lda + k0 + ch * 8);
+        }
+    }
+    __device__ void store(char *lds) const {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = q * kThreads + threadIdx.x;
+            *reinterpret_cast<u32x4 *>(lds + swz(idx >> 3, idx & 7)) = v[q];
+        }
+    }
+};
+
+// 8x8 bf16 transpose within a thread: in[i] holds row i (8 values as 4
+// dwords), out[j] holds column j.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+    // element (i, j) is the 16-bit half (j & 1) of dword j >> 1 of in[i]
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = in[2 * p][j >> 1], hi = in[2 * p + 1][j >> 1];
+            // pick half (j & 1) of lo and of hi into one dword (lo half first)
+            d[p] = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        out[j] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+}
+
+// B tile, NF4 read along K (forward): BN weight rows x one 64-block.
+// Thread t owns row t % BN's block part: BN/64 ... for BN = 256 one full
+// block (64 weights); for BN = 64 a quarter block (16 weights).
+template <int BN>
+struct BStageNF4NT {
+    static constexpr int kW = BN * kBK / kThreads;  // weights per thread (64 or 16)
+    static constexpr int kParts = kBK / kW;         // threads per row
+    u32x4 c[kW / 32 > 0 ? kW / 32 : 1];             // packed codes (16 B = 32 weights)
+    uint32_t cw;                                    // 8 B case: codes of 16 weights
+    float sc;
+    __device__ void load(const Segment &sg, int64_t n0, int64_t Nc, int64_t k0) {
+        const int t = threadIdx.x;
+        const int row = t / kParts, part = t % kParts;
+        const int64_t n = n0 + row;
+        sc = 0.0f;
+        if (kW == 64) {
+            c[0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+            c[1] = c[0];
+        } else {
+            cw = 0x77777777u;
+        }
+        uint64_t cw2 = 0x7777777777777777ull;
+        if (n < Nc) {
+            const uint8_t *p = sg.w.codes + (uint64_t)n * ((uint64_t)sg.w.k / 2) + (uint64_t)k0 / 2 + part * (kW / 2);
+            if (kW == 64) {
+                c[0] = reinterpret_cast<const u32x4 *>(p)[0];
+                c[1] = reinterpret_cast<const u32x4 *>(p)[1];
+            } else {
+                cw2 = *reinterpret_cast<const uint64_t *>(p);
+            }
+            sc = wscale(sg.w, n * (sg.w.k / kBlock) + k0 / kBlock);
+        }
+        if (kW != 64) {
+            c[0] = u32x4{(uint32_t)cw2, (uint32_t)(cw2 >> 32), 0, 0};
+        }
+    }
+    __device__ void store(char *lds, const float *s_q) const {
+        const int t = threadIdx.x;
+        const int row = t / kParts, part = t % kParts;
+        constexpr int kDw = kW / 8;  // code dwords (8 weights each)
+#pragma unroll
+        for (int d = 0; d < kDw; ++d) {
+            const uint32_t cd = c[d / 4][d % 4];
+            u32x4 o;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t b = (cd >> (8 * h)) & 0xFFu;
+                o[h] = pack_bf16x2(s_q[b & 15] * sc, s_q[b >> 4] * sc);
+            }
+            *reinterpret_cast<u32x4 *>(lds + swz(row, part * kDw + d)) = o;
+        }
+    }
+};
+
+// B tile, NF4 read across rows (dgrad): Bop[c][j] = W'[j][c] for 64 rows j
+// and BN columns c. Thread t owns an 8 (j) x 8 (c) patch.
+template <int BN>
+struct BStageNF4NN {
+    static constexpr int kPatches = BN * kBK / 64;  // threads beyond this idle
+    static_assert(kPatches <= kThreads, "at most one 8x8 patch per thread");
+    uint32_t cd[8];  // codes of 8 rows j, 8 columns c (one dword each)
+    float sc[8];
+    __device__ void load(const Segment &sg, int64_t c0, int64_t Nc, int64_t j0) {
+        const int t = threadIdx.x;
+        if (t >= kPatches) return;
+        const int jp = t & 7, cp = t >> 3;  // j patch 0..7, c patch 0..BN/8-1
+        const int64_t cc = c0 + cp * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t j = j0 + jp * 8 + i;  // weight row
+            cd[i] = 0x77777777u;
+            sc[i] = 0.0f;
+            if (cc < Nc) {  // Nc = K of W, a multiple of 64, so cc + 7 < Nc
+                cd[i] = *reinterpret_cast<const uint32_t *>(sg.w.codes + (uint64_t)j * ((uint64_t)sg.w.k / 2) + (uint64_t)cc / 2);
+                sc[i] = wscale(sg.w, j * (sg.w.k / kBlock) + cc / kBlock);
+            }
+        }
+    }
+    __device__ void store(char *lds, const float *s_q) const {
+        const int t = threadIdx.x;
+        if (t >= kPatches) return;
+        const int jp = t & 7, cp = t >> 3;
+        u32x4 rows[8], cols[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t b = (cd[i] >> (8 * h)) & 0xFFu;
+                rows[i][h] = pack_bf16x2(s_q[b & 15] * sc[i], s_q[b >> 4] * sc[i]);
+            }
+        }
+        transpose8x8(rows, cols);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(lds + swz(cp * 8 + j, jp)) = cols[j];
+    }
+};
+
+// B tile, bf16 Bop[n][k] = Mat[n][k] (rows of Mat): like the A tile.
+template <int BN>
+struct BStageBF16NT {
+    static constexpr int kChunks = BN * 8 / kThreads;
+    u32x4 v[kChunks];
+    __device__ void load(const Segment &sg, int64_t n0, int64_t Nc, int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = q * kThreads + threadIdx.x;
+            const int row = idx >> 3, ch = idx & 7;
+            const int64_t n = n0 + row, k = k0 + ch * 8;
+            v[q] = u32x4{0, 0, 0, 0};
+            if (n < sg.mat_rows && k < sg.mat_cols)  // mat_cols is a multiple of 8
+                v[q] = *reinterpret_cast<const u32x4 *>(sg.mat + n * sg.ldm + k);
+        }
+    }
+    __device__ void store(char *lds, const float *) const {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = q * kThreads + threadIdx.x;
+            *reinterpret_cast<u32x4 *>(lds + swz(idx >> 3, idx & 7)) = v[q];
+        }
+    }
+};
+
+// B tile, bf16 Bop[n][k] = Mat[k][n] (columns of Mat): 8x8 patches.
+template <int BN>
+struct BStageBF16NN {
+    static constexpr int kPatches = BN * kBK / 64;  // threads beyond this idle
+    static_assert(kPatches <= kThreads, "at most one 8x8 patch per thread");
+    u32x4 r[8];
+    __device__ void load(const Segment &sg, int64_t n0, int64_t Nc, int64_t k0) {
+        const int t = threadIdx.x;
+        if (t >= kPatches) return;
+        const int kp = t & 7, np = t >> 3;
+        const int64_t n = n0 + np * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t k = k0 + kp * 8 + i;
+            r[i] = u32x4{0, 0, 0, 0};
+            if (k < sg.mat_rows && n < sg.mat_cols)  // mat_cols is a multiple of 8
+                r[i] = *reinterpret_cast<const u32x4 *>(sg.mat + k * sg.ldm + n);
+        }
+    }
+    __device__ void store(char *lds, const float *) const {
+        const int t = threadIdx.x;
+        if (t >= kPatches) return;
+        const int kp = t & 7, np = t >> 3;
+        u32x4 cols[8];
+        transpose8x8(r, cols);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(lds + swz(np * 8 + j, kp)) = cols[j];
+    }
+};
+
+template <int Mode, int BN> struct BStageOf;
+template <int BN> struct BStageOf<NF4_NT, BN> { using T = BStageNF4NT<BN>; };
+template <int BN> struct BStageOf<NF4_NN, BN> { using T = BStageNF4NN<BN>; };
+template <int BN> struct BStageOf<BF16_NT, BN> { using T = BStageBF16NT<BN>; };
+template <int BN> struct BStageOf<BF16_NN, BN> { using T = BStageBF16NN<BN>; };
+
+// ---------------------------------------------------------------- kernel
+
+// Tile index -> (m tile, n tile): consecutive workgroups go to different XCDs
+// (round robin over 8), so each XCD is given a contiguous run of tiles, taken
+// n-group-major (4 n tiles x all m tiles) so that its concurrent workgroups
+// share operand rows in its L2.
+__device__ __forceinline__ void tile_coords(int64_t wg, int64_t tm, int64_t tn, int64_t &mt, int64_t &nt) {
+    const int64_t total = tm * tn;
+    // a bijection only when total is a multiple of 8; otherwise keep the order
+    const int64_t L = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    const int64_t gn = 4;
+    const int64_t group = L / (gn * tm);
+    const int64_t within = L % (gn * tm);
+    const int64_t ncols = min(gn, tn - group * gn);
+    mt = within / ncols;
+    nt = group * gn + within % ncols;
+}
+
+template <int BM, int BN, int Mode0, int Mode1>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
+    constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
+    constexpr int TM = WM / 16, TN = WN / 16; // 16x16 MFMA tiles per wave
+    constexpr int kABytes = BM * kRowBytes, kBBytes = BN * kRowBytes;
+    extern __shared__ __align__(16) char smem[];
+    // LDS: A buffers 0/1, then B buffers 0/1, then the 16 levels
+    char *const sA0 = smem;
+    char *const sB0 = smem + 2 * kABytes;
+    float *const s_q = reinterpret_cast<float *>(smem + 2 * (kABytes + kBBytes));
+
+    if (threadIdx.x < 16) s_q[threadIdx.x] = p.lv.q[threadIdx.x];
+
+    const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.Nc + BN - 1) / BN;
+    int64_t mt, nt;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, mt, nt);
+    const int64_t m0 = mt * BM, n0 = nt * BN;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+    const int g = lane >> 4, r = lane & 15;
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t steps0 = p.seg[0].klen / kBK;
+    const int64_t steps = steps0 + (p.nseg > 1 ? p.seg[1].klen / kBK : 0);
+
+    using B0 = typename BStageOf<Mode0, BN>::T;
+    using B1 = typename BStageOf<Mode1, BN>::T;
+    AStage<BM> ra;
+    B0 rb0;
+    B1 rb1;
+
+    auto load = [&](int64_t s) {
+        if (s < steps0) {
+            ra.load(p.seg[0], m0, p.M, s * kBK);
+            rb0.load(p.seg[0], n0, p.Nc, s * kBK);
+        } else {
+            ra.load(p.seg[1], m0, p.M, (s - steps0) * kBK);
+            rb1.load(p.seg[1], n0, p.Nc, (s - steps0) * kBK);
+        }
+    };
+    auto store = [&](int64_t s, int buf) {
+        ra.store(sA0 + buf * kABytes);
+        if (s < steps0)
+            rb0.store(sB0 + buf * kBBytes, s_q);
+        else
+            rb1.store(sB0 + buf * kBBytes, s_q);
+    };
+
+    __syncthreads();  // s_q
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int64_t s = 0; s < steps; ++s) {
+        const int buf = s & 1;
+        const char *const a_t = sA0 + buf * kABytes;
+        const char *const b_t = sB0 + buf * kBBytes;
+        if (s + 1 < steps) load(s + 1);
+        // MFMAs of step s from LDS buffer buf
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(a_t + swz(wm + 16 * i + r, ks * 4 + g));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const u32x4 *>(b_t + swz(wn + 16 * j + r, ks * 4 + g));
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]),
+                                                                        acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < steps) store(s + 1, buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: D row 4 g + q, column r of each 16x16 tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn + 16 * j + r;
+            if (col >= p.Nc) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = m0 + wm + 16 * i + 4 * g + q;
+                if (row < p.M)
+                    p.c[row * p.ldc + col] = (uint16_t)(pack_bf16x2(acc[i][j][q] * p.out_scale, 0.0f) & 0xFFFFu);
+            }
+        }
+}
+
+template <int BM, int BN, int Mode0, int Mode1>
+hipError_t run(const Params &p, hipStream_t s) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.Nc + BN - 1) / BN);
+    const size_t lds = 2 * (size_t)(BM + BN) * kRowBytes + 64;
+    auto kern = gemm_kernel<BM, BN, Mode0, Mode1>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    kern<<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(p);
+    return hipGetLastError();
+}
+
+Segment nf4_segment(const uint16_t *a, int64_t lda, int64_t klen, const WView &w) {
+    Segment sg{};
+    sg.a = a;
+    sg.lda = lda;
+    sg.klen = klen;
+    sg.w = w;
+    return sg;
+}
+
+Segment bf16_segment(const uint16_t *a, int64_t lda, int64_t klen, const uint16_t *mat, int64_t ldm,
+                     int64_t rows, int64_t cols) {
+    Segment sg{};
+    sg.a = a;
+    sg.lda = lda;
+    sg.klen = klen;
+    sg.mat = mat;
+    sg.ldm = ldm;
+    sg.mat_rows = rows;
+    sg.mat_cols = cols;
+    return sg;
+}
+
+int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
+
+}  // namespace
+
+bool gemm_supported(int64_t n, int32_t r) { return n % 64 == 0 && r % 8 == 0 && r <= 256; }
+
+// Forward: T' = s X.A (when r > 0), then Y = X.W'^T + T'.B.
+hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &wt, const uint16_t *a,
+                               const uint16_t *b, int32_t r, float s_lora, uint16_t *y,
+                               uint16_t *t_ws, hipStream_t s) {
+    const WView w = make_view(wt);
+    const int64_t N = w.n, K = w.k;
+    const int64_t rp = round64(r);  // adapter width padded to the K step (zeros)
+    Params p{};
+    p.lv = levels();
+    if (r > 0) {
+        // T'[m x rp] = s * X . A : Aop = X [m x K], Bop[c][k] = A[k][c] (columns of A)
+        Params q{};
+        q.lv = p.lv;
+        q.seg[0] = bf16_segment(x, K, K, a, r, K, r);
+        q.nseg = 1;
+        q.M = m;
+        q.Nc = rp;
+        q.c = t_ws;
+        q.ldc = rp;
+        q.out_scale = s_lora;
+        hipError_t e = run<64, 64, BF16_NN, BF16_NN>(q, s);
+        if (e != hipSuccess) return e;
+    }
+    p.seg[0] = nf4_segment(x, K, K, w);
+    p.nseg = 1;
+    if (r > 0) {
+        // Y += T' . B : Aop = T' [m x rp], Bop[n][j] = B[j][n] (columns of B)
+        p.seg[1] = bf16_segment(t_ws, rp, rp, b, N, r, N);
+        p.nseg = 2;
+    }
+    p.M = m;
+    p.Nc = N;
+    p.c = y;
+    p.ldc = N;
+    p.out_scale = 1.0f;
+    return run<256, 256, NF4_NT, BF16_NN>(p, s);
+}
+
+// Input gradient: U' = s dY.B^T (when r > 0), then dX = dY.W' + U'.A^T.
+hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &wt, const uint16_t *a,
+                             const uint16_t *b, int32_t r, float s_lora, uint16_t *dx,
+                             uint16_t *u_ws, hipStream_t s) {
+    const WView w = make_view(wt);
+    const int64_t N = w.n, K = w.k;
+    const int64_t rp = round64(r);
+    Params p{};
+    p.lv = levels();
+    if (r > 0) {
+        // U'[m x rp] = s * dY . B^T : Aop = dY [m x N], Bop[c][j] = B[c][j] (rows of B)
+        Params q{};
+        q.lv = p.lv;
+        q.seg[0] = bf16_segment(dy, N, N, b, N, r, N);
+        q.nseg = 1;
+        q.M = m;
+        q.Nc = rp;
+        q.c = u_ws;
+        q.ldc = rp;
+        q.out_scale = s_lora;
+        hipError_t e = run<64, 64, BF16_NT, BF16_NT>(q, s);
+        if (e != hipSuccess) return e;
+    }
+    p.seg[0] = nf4_segment(dy, N, N, w);
+    p.nseg = 1;
+    if (r > 0) {
+        // dX += U' . A^T : Aop = U' [m x rp], Bop[c][j] = A[c][j] (rows of A)
+        p.seg[1] = bf16_segment(u_ws, rp, rp, a, r, K, r);
+        p.nseg = 2;
+    }
+    p.M = m;
+    p.Nc = K;
+    p.c = dx;
+    p.ldc = K;
+    p.out_scale = 1.0f;
+    return run<256, 256, NF4_NN, BF16_NT>(p, s);
+}
+
+}  // namespace nf4

@@ -112,7 +112,7 @@ def _w(n=256, k=512, codes=FAKE, aq=FAKE, asc=FAKE, am=None, bs=64, dq=256):
 def test_linear_validation(L, fn):
     f = getattr(L, fn)
     ws = nq.nf4_linear_workspace_size(64, 16)
-    assert ws == 64 * 16 * 2
+    assert ws == 64 * 64 * 2
 
     def call(act=FAKE, m=64, w=None, a=FAKE, b=FAKE, r=16, out=FAKE, wsp=FAKE, wsb=ws):
         w = w if w is not None else _w()
@@ -141,7 +141,8 @@ def test_linear_validation(L, fn):
 
 def test_workspace_size(L):
     assert nq.nf4_linear_workspace_size(4096, 64) == 4096 * 64 * 2
-    assert nq.nf4_linear_workspace_size(3, 5) == 256
+    assert nq.nf4_linear_workspace_size(3, 5) == 512
+    assert nq.nf4_linear_workspace_size(10, 65) == 10 * 128 * 2
     assert nq.nf4_linear_workspace_size(100, 0) == 0
 
 

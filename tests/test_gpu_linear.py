@@ -62,6 +62,13 @@ CASES = [
     (130, 96, 320, 64),
     (256, 256, 512, 64),
     (2, 4096, 128, 3),
+    # large-M shapes (N % 64 == 0, r % 8 == 0): several output tiles, ragged
+    # rows, rank not a multiple of the 64-wide K step, and the widest rank
+    (512, 1024, 256, 16),
+    (300, 512, 1024, 40),
+    (257, 2048, 512, 32),
+    (70, 320, 192, 256),
+    (200, 64, 64, 8),
     # decode-shaped (no adapter): ragged column counts and odd row counts
     (3, 100, 192, 0),
     (16, 200, 320, 0),
