@@ -115,12 +115,23 @@ def run_ahead():
 
 
 def time_op(fn, iters, warmup):
-    """Median / mean milliseconds of fn() by HIP events around each call."""
+    """Milliseconds per call of fn(i): the mean over `iters` back-to-back calls
+    between two HIP events (no event between calls, so no marker packet sits
+    between the kernels), and p10 / median / p90 from a second pass with
+    events around each call. The host runs ahead of the GPU in both passes."""
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    ev = Events(2)
+    run_ahead()
+    ev[0].record()
+    for i in range(iters):
+        fn(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    mean = ev[0].elapsed_time(ev[1]) / iters
     ev = Events(2 * iters)
     run_ahead()
     for i in range(iters):
@@ -129,7 +140,41 @@ def time_op(fn, iters, warmup):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters))
-    return ms[len(ms) // 2], sum(ms) / len(ms)
+    return mean, pct(ms)
+
+
+def pct(sorted_ms):
+    """p10 / median / p90 of an ascending list of milliseconds."""
+    n = len(sorted_ms)
+    return [round(sorted_ms[min(n - 1, int(f * n))], 5) for f in (0.1, 0.5, 0.9)]
+
+
+def sources_digest(paths):
+    """sha256 over the given source files (paths relative to the repo root)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel_key):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the same
+    counter's reading on a plain device copy of known size). Returns None
+    when no summary exists or when the kernel's sources changed since the
+    counters were taken (the summary records their sha256)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    ent = table.get(kernel_key)
+    if not ent or sources_digest(ent["sources"]) != ent["sources_sha256"]:
+        return None
+    return ent["fetch_bytes"] + ent["write_bytes"]
 
 
 def make_sets(dev, w_host_bits, nsets):
@@ -164,28 +209,30 @@ def main_step_bench(args, dev):
         qcalls[i % 4]()
         dcalls[i % 4]()
     torch.cuda.synchronize()
-    ev = Events(3 * args.steps)
+    # the step loop: K passes of quantize + dequantize, wall clock between
+    # two synchronizations (the value), and HIP events at its two ends
+    ev = Events(2)
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
-        ev[3 * i].record()
         qcalls[i % 4]()
-        ev[3 * i + 1].record()
         dcalls[i % 4]()
-        ev[3 * i + 2].record()
+    ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)]
-    d_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)]
+    gpu_ms = ev[0].elapsed_time(ev[1])
+    # each kernel of the step alone, timed the same way as every kernel bench
+    q_avg, q_pct = time_op(lambda i: qcalls[i % 4](), args.steps, 2)
+    d_avg, d_pct = time_op(lambda i: dcalls[i % 4](), args.steps, 2)
     qb = bytes_quantize(n, 2)
     db = bytes_dequantize(n, 2)
     step_bytes = qb + db
     ms_per_step = wall * 1e3 / args.steps
-    q_avg = sum(q_ms) / len(q_ms)
-    d_avg = sum(d_ms) / len(d_ms)
     res = {
         "n": n,
         "step_bytes": step_bytes,
         "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": gpu_ms / args.steps,
         "gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "quantize_ms": q_avg,
         "dequantize_ms": d_avg,
@@ -193,8 +240,9 @@ def main_step_bench(args, dev):
         "dequantize_gbs": db / (d_avg * 1e-3) / 1e9,
         "quantize_bytes": qb,
         "dequantize_bytes": db,
+        "quantize_p10_p50_p90_ms": q_pct,
+        "dequantize_p10_p50_p90_ms": d_pct,
     }
-    # parity guard on the timed buffers: the last step's codes against a fresh run
     del sets
     torch.cuda.empty_cache()
     return res, w_bits
@@ -241,10 +289,12 @@ def kernel_benches(dev, iters, warmup, with_stack):
     n1 = w1.numel()
     p1 = nq.empty_nf4(tuple(w1.shape), dev)
     o1 = torch.empty_like(w1)
-    ms, _ = time_op(prep_quantize(w1, p1), iters, warmup)
-    out["quantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_quantize(n1, 4) / ms / 1e6}
-    ms, _ = time_op(prep_dequantize(p1, n1, o1), iters, warmup)
-    out["dequantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_dequantize(n1, 4) / ms / 1e6}
+    ms, pc = time_op(prep_quantize(w1, p1), iters, warmup)
+    out["quantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_quantize(n1, 4) / ms / 1e6,
+                                     "p10_p50_p90_ms": pc}
+    ms, pc = time_op(prep_dequantize(p1, n1, o1), iters, warmup)
+    out["dequantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_dequantize(n1, 4) / ms / 1e6,
+                                       "p10_p50_p90_ms": pc}
     log(f"1024x1024: {out['quantize_1024x1024_f32']} {out['dequantize_1024x1024_f32']}")
 
     # workload 4: decode GEMV on a 28672 x 8192 NF4 weight, 4 rotating copies
@@ -261,9 +311,9 @@ def kernel_benches(dev, iters, warmup, with_stack):
     for m in workloads.GEMV_MS:
         xm = x[:m].contiguous()
         ym = [torch.empty((m, N), dtype=torch.bfloat16, device=dev) for _ in range(4)]
-        ms, _ = time_op(lambda i: nq.linear_forward(xm, wts[i % 4], out=ym[i % 4]), iters, warmup)
+        ms, pc = time_op(lambda i: nq.linear_forward(xm, wts[i % 4], out=ym[i % 4]), iters, warmup)
         byts = wbytes + m * K * 2 + m * N * 2
-        out[f"gemv_M{m}_28672x8192"] = {"ms": ms, "GB/s": byts / ms / 1e6,
+        out[f"gemv_M{m}_28672x8192"] = {"ms": ms, "p10_p50_p90_ms": pc, "GB/s": byts / ms / 1e6,
                                          "TFLOP/s": 2 * m * N * K / ms / 1e9,
                                          "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS}
         log(f"gemv M={m}: {out[f'gemv_M{m}_28672x8192']}")
@@ -286,20 +336,20 @@ def kernel_benches(dev, iters, warmup, with_stack):
     ws = torch.empty(nq.nf4_linear_workspace_size(M, r), dtype=torch.uint8, device=dev)
     flops = 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
     lin_iters = max(3, iters // 2)
-    ms, _ = time_op(lambda i: nq.linear_forward(X, wt, A, B, s, out=Y, workspace=ws), lin_iters,
-                    max(1, warmup // 2))
-    out["linear_fwd_4096x8192x8192_r64"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+    ms, pc = time_op(lambda i: nq.linear_forward(X, wt, A, B, s, out=Y, workspace=ws), lin_iters,
+                     max(1, warmup // 2))
+    out["linear_fwd_4096x8192x8192_r64"] = {"ms": ms, "p10_p50_p90_ms": pc, "TFLOP/s": flops / ms / 1e9,
                                             "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
     log(f"linear fwd: {out['linear_fwd_4096x8192x8192_r64']}")
-    ms, _ = time_op(lambda i: nq.linear_backward_input(dY, wt, A, B, s, out=dX, workspace=ws),
-                    lin_iters, max(1, warmup // 2))
-    out["linear_dgrad_4096x8192x8192_r64"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+    ms, pc = time_op(lambda i: nq.linear_backward_input(dY, wt, A, B, s, out=dX, workspace=ws),
+                     lin_iters, max(1, warmup // 2))
+    out["linear_dgrad_4096x8192x8192_r64"] = {"ms": ms, "p10_p50_p90_ms": pc, "TFLOP/s": flops / ms / 1e9,
                                               "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
     log(f"linear dgrad: {out['linear_dgrad_4096x8192x8192_r64']}")
     # practical ceiling: the vendor bf16 GEMM on a pre-dequantized weight
     Wd = nq.dequantize(wt, torch.bfloat16)
-    ms, _ = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))
-    out["hipblaslt_bf16_4096x8192x8192_reference"] = {"ms": ms,
+    ms, pc = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))
+    out["hipblaslt_bf16_4096x8192x8192_reference"] = {"ms": ms, "p10_p50_p90_ms": pc,
                                                       "TFLOP/s": 2 * M * N * K / ms / 1e9}
     del X, dY, A, B, Y, dX, ws, Wd, wt
     torch.cuda.empty_cache()
@@ -398,9 +448,11 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": counter_traffic("quantize_groups_kernel<bf16,DQ> 11008x4096"),
         "bytes_per_launch": q_bytes,
         "avg_launch_ms": round(q_ms, 5),
+        "timing": "mean of K back-to-back launches over 4 rotating inputs between two HIP "
+                  "events on the launch stream",
     }
     cpu = None if args.no_cpu_baseline else cpu_baseline(w_bits)
 
@@ -412,6 +464,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 5),
+        "gpu_ms_per_step": round(main_res["gpu_ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -428,9 +481,13 @@ def main():
         "cpu_baseline": cpu,
         "step_kernels": {
             "quantize": {"ms": round(main_res["quantize_ms"], 5),
-                         "GB/s": round(main_res["quantize_gbs"], 1)},
+                         "GB/s": round(main_res["quantize_gbs"], 1),
+                         "p10_p50_p90_ms": main_res["quantize_p10_p50_p90_ms"]},
             "dequantize": {"ms": round(main_res["dequantize_ms"], 5),
-                           "GB/s": round(main_res["dequantize_gbs"], 1)},
+                           "GB/s": round(main_res["dequantize_gbs"], 1),
+                           "hbm_frac": round(main_res["dequantize_gbs"] / HBM_PEAK_GBS, 4),
+                           "p10_p50_p90_ms": main_res["dequantize_p10_p50_p90_ms"],
+                           "traffic": counter_traffic("dequantize_chunks_kernel<bf16,DQ> 11008x4096")},
         },
         "kernels": kernels,
     }
