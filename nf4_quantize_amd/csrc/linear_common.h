@@ -49,4 +49,10 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w,
                              const uint16_t *b, int32_t r, float s_lora, uint16_t *dx,
                              uint16_t *u_ws, hipStream_t s);
 
+// Main forward GEMM of the large-M path (linear_fwd.hip): Y = X . W'^T, plus
+// T' . B when t != nullptr (T' bf16 [m x rp]). Needs K <= 2^22.
+bool fwd_main_supported(int64_t k);
+hipError_t launch_fwd_main(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *t,
+                           int64_t rp, const uint16_t *b, int32_t r, uint16_t *y, hipStream_t s);
+
 }  // namespace nf4

@@ -1,0 +1,490 @@
+// linear_fwd.hip - large-M fused NF4 linear forward for gfx950 on bf16 MFMA
+// ([MF] "Forward Pass Computation"; source key in nf4_internal.h):
+//   Y = X . W'^T + T' . B,   T' = s (X . A) (bf16, computed beforehand),
+// W' = dequantize(W), W stored [N x K] NF4 (64-blocks along K).
+//
+// Tile: a workgroup of 4 waves owns 256 rows x 256 columns of Y; wave w owns
+// all 256 rows of columns 64w .. 64w+63, as 16 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators per lane, held in AGPRs).
+// K advances 64 (one NF4 block) per step.
+//
+//  - X goes global -> LDS directly (buffer_load ... lds, no registers),
+//    double buffered, rows of 128 B with 16-byte chunks XOR-swizzled by row
+//    so the fragment reads of 16 rows hit distinct banks.
+//  - W never touches LDS: each lane loads the 8 code bytes its MFMA operands
+//    need (one weight row, 16 consecutive k) and dequantizes them in
+//    registers, bf16(q[code] * c1') as the dequantize path does, through a
+//    256-entry (low, high) level table in LDS. The 32 k of an MFMA are taken
+//    in the order that makes a lane's 16 k of one step contiguous: lane group
+//    g covers k = 16g .. 16g+15, half ks (0, 1) of it in MFMA ks. X fragments
+//    are read in the same order, so the contraction is unchanged.
+//  - Step s's MFMAs run while step s+1's operands are dequantized and step
+//    s+1's X tile and step s+2's codes are in flight.
+// All loads are raw buffer loads with per-tile descriptors whose size stops
+// at the last valid row: rows beyond M or N read as zero, the loop has no
+// branches, and the per-step advance is a scalar offset.
+#include "linear_common.h"
+
+namespace nf4 {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kTM = kBM / 16;                // 16 row tiles per wave
+constexpr int kTN = 64 / 16;                 // 4 column tiles per wave
+constexpr int kATile = kBM * kBK * 2;        // 32 KiB of bf16 per X tile
+constexpr int kXBufs = 3;                    // X tiles in flight: steps s, s+1, s+2
+constexpr int kTable = 256 * 256;            // level-pair table, one copy per lane
+constexpr int kLds = kTable + kXBufs * kATile;  // 160 KiB: table, then the X tiles
+constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
+constexpr int kFragAhead = 3;                // X fragments read this many row groups ahead
+constexpr int kLookAhead = 16;               // MFMA slots between a level read and its use
+constexpr int kLookRing = 8;                 // level reads in flight
+// The fragment ring is indexed by the row group within a step, and the next
+// step's first fragments are read at the end of the current one: the ring
+// length must divide the 32 row groups of a step to keep its phase.
+static_assert((2 * kTM) % (kFragAhead + 1) == 0, "fragment ring must divide a step");
+static_assert(kLookRing * 3 > kLookAhead, "level reads in flight exceed the ring");
+static_assert(45 + kLookAhead < 64, "half-1 operands must be finished within half 0");
+
+struct FwdParams {
+    const uint16_t *x;      // X [M x K]
+    int64_t M, K, N;
+    const uint8_t *codes;   // W codes [N x K/2]
+    const uint8_t *q8;      // E4M3 codes of c1/c2 (double quantization) or nullptr
+    const float *c2;
+    int64_t n_groups;       // entries of c2
+    const float *absmax;    // c1 (no double quantization)
+    const uint16_t *t;      // T' [M x rp] bf16, or nullptr (no adapter)
+    int64_t rp;             // adapter width padded to 64
+    const uint16_t *b;      // B [r x N] bf16
+    int32_t r;
+    uint16_t *y;            // Y [M x N] bf16
+    Levels lv;
+};
+
+__device__ __forceinline__ Rsrc rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)bytes,
+                                             kRsrcFlags);
+}
+
+// acc += a . b^T on one 16x16x32 tile. Written as an instruction so that the
+// accumulators are pinned to AGPRs; the MFMA's own hazards are respected by
+// the schedule (no two dependent MFMAs are adjacent, operands are written
+// long before use) and by explicit s_nop before the accumulators are read.
+// The statement is volatile so that it stays ordered with the wait below.
+__device__ __forceinline__ void mfma(f32x4_t &c, const u32x4 &a, const u32x4 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states after the last MFMA that writes an accumulator before any other
+// instruction reads it (more than the longest MFMA latency on gfx950).
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile(
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their no-wait maximum).
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Wait states between VALU writes of MFMA operands and the first MFMA.
+__device__ __forceinline__ void valu_to_mfma() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Level-pair table in LDS: the entry of code byte b holds (q[b & 15],
+// q[b >> 4]) as two fp16 (the LDS read bandwidth, not the arithmetic, bounds
+// this kernel: a 4-byte entry halves the bytes of an 8-byte fp32 pair). Each
+// lane has its own copy, entry b of lane l at byte 256 b + 4 l, so a wave's
+// 64 reads hit 64 distinct banks whatever the code bytes. For byte h of the
+// code dword d, v_perm builds the address (b << 8) | 4 l in one instruction.
+// The fp16 levels differ from the fp32 ones by at most 2^-12 relative, far
+// below the bf16 rounding of the operand.
+// The table sits at LDS address 0: the kernel declares no static LDS, so its
+// dynamic LDS starts there, and the perm result is the address itself.
+__device__ __forceinline__ uint32_t level_pair(const char *, uint32_t d, int h, uint32_t lane4) {
+    const uint32_t addr = __builtin_amdgcn_perm(d, lane4, 0x0C0C0400u | ((uint32_t)h << 8));
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
+}
+__device__ __forceinline__ uint32_t scale_pair(uint32_t hh, float sc) {
+    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
+    const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh >> 16));
+    return pack_bf16x2(lo * sc, hi * sc);
+}
+
+// 8 weights (one code dword, element e in bits 4e..4e+3) -> 4 dwords of bf16 pairs.
+__device__ __forceinline__ u32x4 deq8(const char *tab, uint32_t d, float sc, uint32_t lane4) {
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) o[h] = scale_pair(level_pair(tab, d, h, lane4), sc);
+    return o;
+}
+
+// Workgroup -> (m tile, n tile). Consecutive workgroups go round robin to the
+// 8 XCDs; when the tile count is a multiple of 8 each XCD is given a
+// contiguous run of the order below. The order walks bands of 8 column tiles,
+// rows fastest within a band, so the ~32 workgroups an XCD runs at once
+// cover about 4 row tiles x 8 column tiles and share X rows and W rows in
+// that XCD's L2.
+__device__ __forceinline__ void tile_of(int64_t wg, int64_t tm, int64_t tn, int64_t &mt, int64_t &nt) {
+    const int64_t total = tm * tn;
+    const int64_t L = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    constexpr int64_t kGN = 8;
+    const int64_t band = L / (kGN * tm), within = L % (kGN * tm);
+    const int64_t nb = min(kGN, tn - band * kGN);
+    mt = within / nb;
+    nt = band * kGN + within % nb;
+}
+
+// A value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Codes and scale inputs of one K-step for a lane's 4 column tiles.
+struct Raw {
+    uint2 c[kTN];     // 16 codes: k = 16g .. 16g+15 of the block
+    uint32_t q[kTN];  // E4M3 code of c1/c2 (double quantization)
+    float s[kTN];     // c2 (double quantization) or c1
+};
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
+    extern __shared__ __align__(16) char smem[];
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, g = lane >> 4;
+
+    // level-pair table: thread t writes entry t of all 64 lane copies
+    {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)p.lv.q[t & 15]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)p.lv.q[t >> 4]);
+        const uint32_t e = lo | (hi << 16);
+        u32x4 *row = reinterpret_cast<u32x4 *>(smem + 256 * t);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) row[c] = u32x4{e, e, e, e};
+    }
+    const char *const tab = smem;
+    char *const xbuf = smem + kTable;
+    const uint32_t lane4 = 4u * (uint32_t)lane;
+
+    int64_t mt, nt;
+    tile_of(blockIdx.x, (p.M + kBM - 1) / kBM, (p.N + kBN - 1) / kBN, mt, nt);
+    const int64_t m0 = uniform(mt * kBM), n0 = uniform(nt * kBN);
+    const int64_t K = p.K, steps = K / kBK, kb_row = K / kBlock;
+    const int64_t m_rows = min((int64_t)kBM, p.M - m0), n_rows = min((int64_t)kBN, p.N - n0);
+
+    // ---- X staging: wave w moves tile rows 64w .. 64w+63, 8 rows per load.
+    // Lane l of load q fills LDS row 64w + 8q + l/8, physical chunk l % 8,
+    // which holds logical chunk (l % 8) ^ ((row >> 1) & 7).
+    const Rsrc x_rs = rsrc(p.x + m0 * K, m_rows * K * 2);
+    uint32_t a_off[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 64 * w + 8 * q + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        a_off[q] = (uint32_t)(row * K * 2 + chunk * 16);
+    }
+    auto stage_x = [&](const Rsrc &rs, int64_t koff_bytes, int buf) {
+        char *dst = xbuf + buf * kATile + (64 * w) * 128;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + q * 1024), 16, a_off[q],
+                                                     (int)koff_bytes, 0, 0);
+    };
+
+    // ---- W: lane (lr, g) of column tile j holds row n0 + 64w + 16j + lr.
+    const Rsrc c_rs = rsrc(p.codes + n0 * (K / 2), n_rows * (K / 2));
+    const Rsrc q_rs = kDQ ? rsrc(p.q8 + n0 * kb_row, n_rows * kb_row)
+                          : rsrc(p.absmax + n0 * kb_row, n_rows * kb_row * 4);
+    const Rsrc s_rs = rsrc(p.c2, p.n_groups * 4);
+    uint32_t c_off[kTN], q_off[kTN], b_abs[kTN];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+        const int nl = 64 * w + 16 * j + lr;
+        c_off[j] = (uint32_t)(nl * (K / 2) + 8 * g);
+        q_off[j] = (uint32_t)(nl * kb_row * (kDQ ? 1 : 4));
+        b_abs[j] = (uint32_t)((n0 + nl) * kb_row);
+    }
+    auto load_w = [&](int64_t s, Raw &raw) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            raw.c[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(c_rs, c_off[j],
+                                                                                     (int)(s * (kBK / 2)), 0));
+            if (kDQ) {
+                raw.q[j] = __builtin_amdgcn_raw_buffer_load_b8(q_rs, q_off[j], (int)s, 0);
+                raw.s[j] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(s_rs, ((b_abs[j] + (uint32_t)s) >> 8) * 4u, 0, 0));
+            } else {
+                raw.s[j] = __builtin_bit_cast(float,
+                                              __builtin_amdgcn_raw_buffer_load_b32(q_rs, q_off[j], (int)(s * 4), 0));
+            }
+        }
+    };
+    auto scale = [&](const Raw &raw, int j) {
+        return kDQ ? __builtin_amdgcn_cvt_f32_fp8((int)raw.q[j], 0) * raw.s[j] : raw.s[j];
+    };
+
+    f32x4_t acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // fragment read offsets: tile row 16i + lr, logical chunk 2g + ks
+    uint32_t frag_off[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) frag_off[ks] = lr * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
+    auto frag = [&](const char *a_t, int idx) {
+        return *reinterpret_cast<const u32x4 *>(a_t + frag_off[idx / kTM] + (idx % kTM) * 2048);
+    };
+
+    // B operands of the MFMA halves ks = 0 (b0) and ks = 1 (b1).
+    u32x4 b0[kTN], b1[kTN];
+
+    // One K-step, scheduled by hand at the granularity of single MFMAs so
+    // that every MFMA is followed by the few other instructions that fit in
+    // its shadow (in-order issue; one wave per SIMD). Slot m (0..127) issues
+    // MFMA (row tile m/4 mod 16, column tile m%4, half m/64) and around it:
+    //  - the X fragment of row group m/4 + 2 (slots with m%4 == 0);
+    //  - the 16 code bytes of this step's half-1 operands b1 (from rc) and,
+    //    in half 1, of the next step's half-0 operands b0 (from rn): one byte
+    //    per 3 slots, its level pair read from LDS 8 slots before it is
+    //    scaled and rounded into the operand;
+    //  - the loads of later steps (first 20 slots).
+    // X fragments in flight; the first kFragAhead of a step are read at the end
+    // of the previous step (its X tile has landed by then: each step ends with
+    // the wait for the next step's tile and a barrier).
+    u32x4 af[kFragAhead + 1];
+    auto step = [&](int64_t s, const Raw &rc, const Raw &rn, Raw &rl) {
+        const char *a_t = xbuf + (int)(s % kXBufs) * kATile;
+        const char *a_next = xbuf + (int)((s + 1) % kXBufs) * kATile;
+        uint32_t lq[kLookRing];
+        float sc1[kTN], sc0[kTN];
+#pragma clang loop unroll(full)
+        for (int m = 0; m < 128; ++m) {
+            const int grp = m / 4, sub = m % 4, ks = grp / kTM, i = grp % kTM;
+            if (sub == 0) {
+                u32x4 &dst = af[(grp + kFragAhead) % (kFragAhead + 1)];
+                if (grp + kFragAhead < 2 * kTM)
+                    dst = frag(a_t, grp + kFragAhead);
+                else
+                    dst = frag(a_next, grp + kFragAhead - 2 * kTM);
+            }
+            if (m < 8) {
+                char *dst = xbuf + (int)((s + 2) % kXBufs) * kATile + (64 * w) * 128;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void *)(dst + m * 1024), 16, a_off[m],
+                                                         (int)(min(s + 2, steps - 1) * (kBK * 2)), 0, 0);
+            } else if (m < 8 + kTN) {
+                const int j = m - 8;
+                const int64_t sl = min(s + 3, steps - 1);
+                rl.c[j] = __builtin_bit_cast(
+                    uint2, __builtin_amdgcn_raw_buffer_load_b64(c_rs, c_off[j], (int)(sl * (kBK / 2)), 0));
+                if (kDQ) {
+                    rl.q[j] = __builtin_amdgcn_raw_buffer_load_b8(q_rs, q_off[j], (int)sl, 0);
+                    rl.s[j] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(s_rs, ((b_abs[j] + (uint32_t)sl) >> 8) * 4u, 0, 0));
+                } else {
+                    rl.s[j] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(q_rs, q_off[j], (int)(sl * 4), 0));
+                }
+            }
+            // level reads: unit u = 4j + h is byte h of operand j
+            const int hm = m % 64;
+            if (hm % 3 == 0 && hm / 3 < 16) {
+                const int u = hm / 3, j = u / 4, h = u % 4;
+                const uint32_t d = (m < 64) ? rc.c[j].y : rn.c[j].x;
+                lq[u % kLookRing] = level_pair(tab, d, h, lane4);
+                if (h == 0) {
+                    if (m < 64) sc1[j] = scale(rc, j);
+                    else sc0[j] = scale(rn, j);
+                }
+            }
+            if (hm >= kLookAhead && (hm - kLookAhead) % 3 == 0 && (hm - kLookAhead) / 3 < 16) {
+                const int u = (hm - kLookAhead) / 3, j = u / 4, h = u % 4;
+                const float sc = (m < 64) ? sc1[j] : sc0[j];
+                const uint32_t v = scale_pair(lq[u % kLookRing], sc);
+                if (m < 64) b1[j][h] = v;
+                else b0[j][h] = v;
+            }
+            mfma(acc[i][sub], af[grp % (kFragAhead + 1)], ks ? b1[sub] : b0[sub]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- main loop over the NF4 segment. X tiles are staged two steps ahead
+    // into 3 LDS buffers and codes three steps ahead into 4 register slots;
+    // at the end of step s only the loads issued during step s may still be
+    // in flight (X tile s+1 and the codes of s+2 have landed).
+    constexpr int kLoadsPerStep = 8 + (kDQ ? 3 : 2) * kTN;
+    Raw r0, r1, r2, r3;
+    stage_x(x_rs, 0, 0);
+    stage_x(x_rs, min((int64_t)1, steps - 1) * (kBK * 2), 1);
+    load_w(0, r0);
+    load_w(min((int64_t)1, steps - 1), r1);
+    load_w(min((int64_t)2, steps - 1), r2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // pair table, X tiles 0 and 1
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) b0[j] = deq8(tab, r0.c[j].x, scale(r0, j), lane4);
+#pragma unroll
+    for (int f = 0; f < kFragAhead; ++f) af[f] = frag(xbuf, f);
+    valu_to_mfma();
+    auto one = [&](int64_t s, const Raw &rc, const Raw &rn, Raw &rl) {
+        step(s, rc, rn, rl);
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kLoadsPerStep));
+        __syncthreads();
+    };
+    int64_t s = 0;
+    for (; s + 4 <= steps; s += 4) {
+        one(s, r0, r1, r3);
+        one(s + 1, r1, r2, r0);
+        one(s + 2, r2, r3, r1);
+        one(s + 3, r3, r0, r2);
+    }
+    if (s < steps) one(s++, r0, r1, r3);
+    if (s < steps) one(s++, r1, r2, r0);
+    if (s < steps) one(s++, r2, r3, r1);
+    __builtin_amdgcn_s_waitcnt(0);  // the clamped tail loads
+    __syncthreads();
+
+    // ---- adapter segment: + T' . B over rp / 64 steps (not pipelined)
+    if (p.t != nullptr) {
+        const Rsrc t_rs = rsrc(p.t + m0 * p.rp, m_rows * p.rp * 2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int row = 64 * w + 8 * q + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            a_off[q] = (uint32_t)(row * p.rp * 2 + chunk * 16);
+        }
+        for (int64_t sa = 0; sa < p.rp / kBK; ++sa) {
+            stage_x(t_rs, sa * (kBK * 2), 0);
+            // B operand of lane (lr, g), tile j, half ks: B[k][n], k = 64sa + 16g + 8ks + e
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const int64_t n = min(n0 + 64 * w + 16 * j + lr, p.N - 1);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const int64_t k = 64 * sa + 16 * g + 8 * ks + 2 * h;
+                        const uint32_t lo = (k < p.r) ? p.b[k * p.N + n] : 0u;
+                        const uint32_t hi = (k + 1 < p.r) ? p.b[(k + 1) * p.N + n] : 0u;
+                        d[h] = lo | (hi << 16);
+                    }
+                    (ks ? b1[j] : b0[j]) = u32x4{d[0], d[1], d[2], d[3]};
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            valu_to_mfma();
+#pragma unroll
+            for (int idx = 0; idx < 2 * kTM; ++idx) {
+                const int ks = idx / kTM, i = idx % kTM;
+                const u32x4 a = frag(xbuf, idx);
+#pragma unroll
+                for (int j = 0; j < kTN; ++j) mfma(acc[i][j], a, ks ? b1[j] : b0[j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mfma_drain();  // before the next iteration rewrites the operands
+            __syncthreads();
+        }
+    }
+
+    // ---- the accumulators are final once the last MFMA has drained; the
+    // statements below tie every accumulator to a point after that wait, so
+    // no read of them (AGPR to VGPR copies included) is placed earlier.
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < kTM; i += 2)
+        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                     "+a"(acc[i + 1][0]), "+a"(acc[i + 1][1]), "+a"(acc[i + 1][2]), "+a"(acc[i + 1][3]));
+
+    // ---- epilogue: the bf16 results go through LDS so that each lane stores
+    // 16 contiguous bytes. Wave w stages its 256 x 64 slice (32 KiB, rows of
+    // 128 B, 16-byte chunks XOR-swizzled by row / 4) at smem + 32 KiB * w; the
+    // table and the X tiles are dead by now. D element q of tile (i, j) is
+    // row 16i + 4g + q, column 16j + lr.
+    __syncthreads();
+    {
+        char *const ep = smem + w * 32768;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 16 * i + 4 * g + q, col = 16 * j + lr;
+                    const int chunk = (col >> 3) ^ ((row >> 2) & 7);
+                    *reinterpret_cast<uint16_t *>(ep + row * 128 + chunk * 16 + (col & 7) * 2) =
+                        (uint16_t)(pack_bf16x2(acc[i][j][q], 0.0f) & 0xFFFFu);
+                }
+        __syncthreads();
+        const int64_t col0 = n0 + 64 * w;
+        if (col0 < p.N) {
+#pragma unroll 4
+            for (int it = 0; it < 32; ++it) {
+                const int row = 8 * it + (lane >> 3), c = lane & 7;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * 128 + 16 * (c ^ ((row >> 2) & 7)));
+                if (m0 + row < p.M)
+                    *reinterpret_cast<u32x4 *>(p.y + (m0 + row) * p.N + col0 + 8 * c) = v;
+            }
+        }
+    }
+}
+
+template <bool kDQ>
+hipError_t run_fwd(const FwdParams &p, hipStream_t s) {
+    const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
+    auto kern = gemm_fwd_kernel<kDQ>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    kern<<<dim3((unsigned)tiles), dim3(kThreads), kLds, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_main_supported(int64_t k) { return k <= (1 << 22); }
+
+// Y = X . W'^T (+ T' . B when t != nullptr). K % 64 == 0, N % 64 == 0,
+// K <= 2^22 (each per-tile buffer descriptor spans under 4 GiB).
+hipError_t launch_fwd_main(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *t,
+                           int64_t rp, const uint16_t *b, int32_t r, uint16_t *y, hipStream_t s) {
+    FwdParams p{};
+    p.x = x;
+    p.M = m;
+    p.K = w.k_in;
+    p.N = w.n_out;
+    p.codes = w.codes;
+    p.q8 = w.absmax_q;
+    p.c2 = w.absmax_scale;
+    p.n_groups = (w.n_out * (w.k_in / kBlock) + kDqBlock - 1) / kDqBlock;
+    p.absmax = w.absmax;
+    p.t = t;
+    p.rp = rp;
+    p.b = b;
+    p.r = r;
+    p.y = y;
+    p.lv = levels();
+    return w.absmax_q ? run_fwd<true>(p, s) : run_fwd<false>(p, s);
+}
+
+}  // namespace nf4

@@ -453,6 +453,7 @@ hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w
         hipError_t e = run<64, 64, BF16_NN, BF16_NN>(q, s);
         if (e != hipSuccess) return e;
     }
+    if (fwd_main_supported(K)) return launch_fwd_main(x, m, wt, r > 0 ? t_ws : nullptr, rp, b, r, y, s);
     p.seg[0] = nf4_segment(x, K, K, w);
     p.nseg = 1;
     if (r > 0) {
