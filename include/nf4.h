@@ -126,8 +126,10 @@ typedef struct {
 } nf4_weight;
 
 /* Bytes of device workspace that nf4_linear_forward / nf4_linear_backward_input
- * need for m rows and adapter rank r: the bf16 adapter product
- * [m x (r rounded up to 64)], rounded up to 256 bytes (0 when r == 0). */
+ * need for m rows and adapter rank r (0 when r == 0): with rp = r rounded up
+ * to 64, the bf16 adapter product [m x rp] rounded up to 256 bytes, followed
+ * by 8 fp32 partial sums of it ([8 x m x rp], the split-K staging of the
+ * adapter's down-projection). */
 size_t nf4_linear_workspace_size(int64_t m, int32_t r);
 
 /* Fused QLoRA linear forward ([MF] "Forward Pass Computation"):

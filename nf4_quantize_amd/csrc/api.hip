@@ -11,7 +11,7 @@
 
 #include <mutex>
 
-#include "nf4_internal.h"
+#include "linear_common.h"
 
 #define NF4_API extern "C" __attribute__((visibility("default")))
 
@@ -223,10 +223,7 @@ NF4_API nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t block
 
 NF4_API size_t nf4_linear_workspace_size(int64_t m, int32_t r) {
     if (m <= 0 || r <= 0) return 0;
-    // bf16 [m x round64(r)] adapter product, rounded up to 256 bytes.
-    const size_t rp = ((size_t)r + 63u) / 64u * 64u;
-    const size_t bytes = (size_t)m * rp * 2u;
-    return (bytes + 255u) & ~(size_t)255u;
+    return nf4::lora_workspace_bytes(m, ((int64_t)r + 63) / 64 * 64);
 }
 
 namespace {

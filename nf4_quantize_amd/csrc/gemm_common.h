@@ -1,0 +1,90 @@
+// gemm_common.h - device helpers shared by the large-M fused NF4 linear
+// kernels (linear_fwd.hip, linear_dgrad.hip); internal.
+#pragma once
+
+#include "linear_common.h"
+
+namespace nf4 {
+namespace gemm {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ Rsrc rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)bytes,
+                                             kRsrcFlags);
+}
+
+// acc += a . b^T on one 16x16x32 tile. Written as an instruction so that the
+// accumulators are pinned to AGPRs; the MFMA's own hazards are respected by
+// the schedule (no two dependent MFMAs are adjacent, operands are written
+// long before use) and by explicit s_nop before the accumulators are read.
+// The statement is volatile so that it stays ordered with the wait below.
+__device__ __forceinline__ void mfma(f32x4_t &c, const u32x4 &a, const u32x4 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states after the last MFMA that writes an accumulator before any other
+// instruction reads it (more than the longest MFMA latency on gfx950).
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile(
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their no-wait maximum).
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Wait states between VALU writes of MFMA operands and the first MFMA.
+__device__ __forceinline__ void valu_to_mfma() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Two fp32 values as an fp16 pair (low half first).
+__device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// An fp16 pair of levels scaled by sc and rounded to a bf16 pair.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t hh, float sc) {
+    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
+    const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh >> 16));
+    return pack_bf16x2(lo * sc, hi * sc);
+}
+
+// Workgroup -> (m tile, n tile). Consecutive workgroups go round robin to the
+// 8 XCDs; when the tile count is a multiple of 8 each XCD is given a
+// contiguous run of the order below. The order walks bands of 8 column tiles,
+// rows fastest within a band, so the ~32 workgroups an XCD runs at once
+// cover about 4 row tiles x 8 column tiles and share X rows and W rows in
+// that XCD's L2.
+__device__ __forceinline__ void tile_of(int64_t wg, int64_t tm, int64_t tn, int64_t &mt, int64_t &nt) {
+    const int64_t total = tm * tn;
+    const int64_t L = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    constexpr int64_t kGN = 8;
+    const int64_t band = L / (kGN * tm), within = L % (kGN * tm);
+    const int64_t nb = min(kGN, tn - band * kGN);
+    mt = within / nb;
+    nt = band * kGN + within % nb;
+}
+
+// A value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+}  // namespace gemm
+}  // namespace nf4

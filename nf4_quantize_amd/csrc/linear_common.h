@@ -39,8 +39,15 @@ bool gemv_supported(int64_t m, int64_t k);
 hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &w, uint16_t *y,
                        hipStream_t s);
 
+// Adapter workspace: the bf16 product [m x rp] (rp = r rounded up to 64),
+// padded to 256 bytes, then room for kSplitMax fp32 partial sums of it.
+constexpr int kSplitMax = 8;
+inline size_t lora_product_bytes(int64_t m, int64_t rp) { return ((size_t)(m * rp * 2) + 255u) & ~(size_t)255u; }
+inline size_t lora_workspace_bytes(int64_t m, int64_t rp) {
+    return lora_product_bytes(m, rp) + (size_t)kSplitMax * (size_t)(m * rp) * 4u;
+}
+
 // Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
-// The workspace holds the bf16 adapter product [m x round64(r)].
 bool gemm_supported(int64_t n, int32_t r);
 hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *a,
                                const uint16_t *b, int32_t r, float s_lora, uint16_t *y,
@@ -54,5 +61,11 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w,
 bool fwd_main_supported(int64_t k);
 hipError_t launch_fwd_main(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *t,
                            int64_t rp, const uint16_t *b, int32_t r, uint16_t *y, hipStream_t s);
+
+// Main input-gradient GEMM of the large-M path (linear_dgrad.hip): dX = dY . W',
+// plus U' . A^T when u != nullptr. Needs N * K / 2 < 2^31.
+bool dgrad_main_supported(int64_t n, int64_t k);
+hipError_t launch_dgrad_main(const uint16_t *dy, int64_t m, const nf4_weight &w, const uint16_t *u,
+                             int64_t rp, const uint16_t *a, int32_t r, uint16_t *dx, hipStream_t s);
 
 }  // namespace nf4

@@ -23,14 +23,12 @@
 // All loads are raw buffer loads with per-tile descriptors whose size stops
 // at the last valid row: rows beyond M or N read as zero, the loop has no
 // branches, and the per-step advance is a scalar offset.
-#include "linear_common.h"
+#include "gemm_common.h"
 
 namespace nf4 {
 namespace {
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __amdgpu_buffer_rsrc_t Rsrc;
+using namespace gemm;
 
 constexpr int kThreads = 256;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
@@ -40,7 +38,6 @@ constexpr int kATile = kBM * kBK * 2;        // 32 KiB of bf16 per X tile
 constexpr int kXBufs = 3;                    // X tiles in flight: steps s, s+1, s+2
 constexpr int kTable = 256 * 256;            // level-pair table, one copy per lane
 constexpr int kLds = kTable + kXBufs * kATile;  // 160 KiB: table, then the X tiles
-constexpr int kRsrcFlags = 0x00020000;       // raw buffer, 32-bit data format
 constexpr int kFragAhead = 3;                // X fragments read this many row groups ahead
 constexpr int kLookAhead = 16;               // MFMA slots between a level read and its use
 constexpr int kLookRing = 8;                 // level reads in flight
@@ -67,43 +64,6 @@ struct FwdParams {
     Levels lv;
 };
 
-__device__ __forceinline__ Rsrc rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)bytes,
-                                             kRsrcFlags);
-}
-
-// acc += a . b^T on one 16x16x32 tile. Written as an instruction so that the
-// accumulators are pinned to AGPRs; the MFMA's own hazards are respected by
-// the schedule (no two dependent MFMAs are adjacent, operands are written
-// long before use) and by explicit s_nop before the accumulators are read.
-// The statement is volatile so that it stays ordered with the wait below.
-__device__ __forceinline__ void mfma(f32x4_t &c, const u32x4 &a, const u32x4 &b) {
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
-// Wait states after the last MFMA that writes an accumulator before any other
-// instruction reads it (more than the longest MFMA latency on gfx950).
-__device__ __forceinline__ void mfma_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile(
-        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory loads are
-// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt left at their no-wait maximum).
-constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// Wait states between VALU writes of MFMA operands and the first MFMA.
-__device__ __forceinline__ void valu_to_mfma() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Level-pair table in LDS: the entry of code byte b holds (q[b & 15],
 // q[b >> 4]) as two fp16 (the LDS read bandwidth, not the arithmetic, bounds
@@ -119,41 +79,12 @@ __device__ __forceinline__ uint32_t level_pair(const char *, uint32_t d, int h, 
     const uint32_t addr = __builtin_amdgcn_perm(d, lane4, 0x0C0C0400u | ((uint32_t)h << 8));
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
 }
-__device__ __forceinline__ uint32_t scale_pair(uint32_t hh, float sc) {
-    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
-    const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh >> 16));
-    return pack_bf16x2(lo * sc, hi * sc);
-}
-
 // 8 weights (one code dword, element e in bits 4e..4e+3) -> 4 dwords of bf16 pairs.
 __device__ __forceinline__ u32x4 deq8(const char *tab, uint32_t d, float sc, uint32_t lane4) {
     u32x4 o;
 #pragma unroll
     for (int h = 0; h < 4; ++h) o[h] = scale_pair(level_pair(tab, d, h, lane4), sc);
     return o;
-}
-
-// Workgroup -> (m tile, n tile). Consecutive workgroups go round robin to the
-// 8 XCDs; when the tile count is a multiple of 8 each XCD is given a
-// contiguous run of the order below. The order walks bands of 8 column tiles,
-// rows fastest within a band, so the ~32 workgroups an XCD runs at once
-// cover about 4 row tiles x 8 column tiles and share X rows and W rows in
-// that XCD's L2.
-__device__ __forceinline__ void tile_of(int64_t wg, int64_t tm, int64_t tn, int64_t &mt, int64_t &nt) {
-    const int64_t total = tm * tn;
-    const int64_t L = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
-    constexpr int64_t kGN = 8;
-    const int64_t band = L / (kGN * tm), within = L % (kGN * tm);
-    const int64_t nb = min(kGN, tn - band * kGN);
-    mt = within / nb;
-    nt = band * kGN + within % nb;
-}
-
-// A value that is the same in every lane, moved to scalar registers.
-__device__ __forceinline__ int64_t uniform(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Codes and scale inputs of one K-step for a lane's 4 column tiles.

@@ -68,6 +68,10 @@ struct Params {
     int64_t ldc;
     float out_scale;     // multiplies the fp32 accumulator before rounding
     Levels lv;
+    // split-K (grid.y = splits): when partial != nullptr, split z writes its
+    // unscaled fp32 sum to partial[(z * M + row) * ldc + col] instead of c.
+    int splits;
+    float *partial;
 };
 
 // ---------------------------------------------------------------- staging
@@ -344,15 +348,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
             rb1.store(sB0 + buf * kBBytes, s_q);
     };
 
+    // this workgroup's share of the K-steps (all of them without split-K;
+    // only the small-tile instantiations of the adapter products split K)
+    constexpr bool kSplit = (BM == 64);
+    const int64_t per = kSplit ? (steps + p.splits - 1) / p.splits : steps;
+    const int64_t s_lo = kSplit ? min(steps, (int64_t)blockIdx.y * per) : 0;
+    const int64_t s_hi = kSplit ? min(steps, s_lo + per) : steps;
+
     __syncthreads();  // s_q
-    load(0);
-    store(0, 0);
+    if (s_lo < s_hi) {
+        load(s_lo);
+        store(s_lo, 0);
+    }
     __syncthreads();
-    for (int64_t s = 0; s < steps; ++s) {
-        const int buf = s & 1;
+    for (int64_t s = s_lo; s < s_hi; ++s) {
+        const int buf = (s - s_lo) & 1;
         const char *const a_t = sA0 + buf * kABytes;
         const char *const b_t = sB0 + buf * kBBytes;
-        if (s + 1 < steps) load(s + 1);
+        if (s + 1 < s_hi) load(s + 1);
         // MFMAs of step s from LDS buffer buf
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -370,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]),
                                                                         acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < steps) store(s + 1, buf ^ 1);
+        if (s + 1 < s_hi) store(s + 1, buf ^ 1);
         __syncthreads();
     }
 
@@ -384,21 +397,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t row = m0 + wm + 16 * i + 4 * g + q;
-                if (row < p.M)
+                if (row >= p.M) continue;
+                if (kSplit && p.partial)
+                    p.partial[((int64_t)blockIdx.y * p.M + row) * p.ldc + col] = acc[i][j][q];
+                else
                     p.c[row * p.ldc + col] = (uint16_t)(pack_bf16x2(acc[i][j][q] * p.out_scale, 0.0f) & 0xFFFFu);
             }
         }
 }
 
 template <int BM, int BN, int Mode0, int Mode1>
-hipError_t run(const Params &p, hipStream_t s) {
+hipError_t run(const Params &p_in, hipStream_t s) {
+    Params p = p_in;
+    p.splits = max(1, p.splits);
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.Nc + BN - 1) / BN);
     const size_t lds = 2 * (size_t)(BM + BN) * kRowBytes + 64;
     auto kern = gemm_kernel<BM, BN, Mode0, Mode1>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    kern<<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(p);
+    kern<<<dim3((unsigned)tiles, (unsigned)max(1, p.splits)), dim3(kThreads), lds, s>>>(p);
     return hipGetLastError();
 }
 
@@ -426,6 +444,51 @@ Segment bf16_segment(const uint16_t *a, int64_t lda, int64_t klen, const uint16_
 
 int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 
+// out[i] = bf16(scale * sum over z of part[z * count + i]), 4 elements per
+// thread (count is a multiple of 64).
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ part, int splits,
+                                                              int64_t count, float scale,
+                                                              uint16_t *__restrict__ out) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= count) return;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
+    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4 *>(part + z * count + i);
+    uint2 o;
+    o.x = pack_bf16x2(scale * acc[0], scale * acc[1]);
+    o.y = pack_bf16x2(scale * acc[2], scale * acc[3]);
+    *reinterpret_cast<uint2 *>(out + i) = o;
+}
+
+// Adapter down-projection C[m x rp] = s * Aop . Bop^T (bf16) into the start of
+// the workspace. The product is thin (rp columns) and long (klen), so K is
+// split across workgroups to fill the chip; the fp32 partial sums go to the
+// workspace after C and one more pass adds, scales and rounds them.
+template <int Mode>
+hipError_t lora_down(const Segment &sg, int64_t m, int64_t rp, float s_lora, uint16_t *ws, const Levels &lv,
+                     hipStream_t s) {
+    Params q{};
+    q.lv = lv;
+    q.seg[0] = sg;
+    q.nseg = 1;
+    q.M = m;
+    q.Nc = rp;
+    q.c = ws;
+    q.ldc = rp;
+    q.out_scale = s_lora;
+    const int64_t tiles = ((m + 63) / 64) * (rp / 64), steps = sg.klen / kBK;
+    int splits = (int)min((int64_t)kSplitMax, max((int64_t)1, (512 + tiles - 1) / tiles));
+    splits = (int)min((int64_t)splits, max((int64_t)1, steps));
+    q.splits = splits;
+    if (splits == 1) return run<64, 64, Mode, Mode>(q, s);
+    q.partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + lora_product_bytes(m, rp));
+    hipError_t e = run<64, 64, Mode, Mode>(q, s);
+    if (e != hipSuccess) return e;
+    const int64_t count = m * rp;
+    reduce_partials_kernel<<<dim3((unsigned)((count / 4 + 255) / 256)), 256, 0, s>>>(q.partial, splits, count,
+                                                                                     s_lora, ws);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_supported(int64_t n, int32_t r) { return n % 64 == 0 && r % 8 == 0 && r <= 256; }
@@ -439,18 +502,10 @@ hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w
     const int64_t rp = round64(r);  // adapter width padded to the K step (zeros)
     Params p{};
     p.lv = levels();
+    p.splits = 1;
     if (r > 0) {
         // T'[m x rp] = s * X . A : Aop = X [m x K], Bop[c][k] = A[k][c] (columns of A)
-        Params q{};
-        q.lv = p.lv;
-        q.seg[0] = bf16_segment(x, K, K, a, r, K, r);
-        q.nseg = 1;
-        q.M = m;
-        q.Nc = rp;
-        q.c = t_ws;
-        q.ldc = rp;
-        q.out_scale = s_lora;
-        hipError_t e = run<64, 64, BF16_NN, BF16_NN>(q, s);
+        hipError_t e = lora_down<BF16_NN>(bf16_segment(x, K, K, a, r, K, r), m, rp, s_lora, t_ws, p.lv, s);
         if (e != hipSuccess) return e;
     }
     if (fwd_main_supported(K)) return launch_fwd_main(x, m, wt, r > 0 ? t_ws : nullptr, rp, b, r, y, s);
@@ -478,20 +533,13 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &wt
     const int64_t rp = round64(r);
     Params p{};
     p.lv = levels();
+    p.splits = 1;
     if (r > 0) {
         // U'[m x rp] = s * dY . B^T : Aop = dY [m x N], Bop[c][j] = B[c][j] (rows of B)
-        Params q{};
-        q.lv = p.lv;
-        q.seg[0] = bf16_segment(dy, N, N, b, N, r, N);
-        q.nseg = 1;
-        q.M = m;
-        q.Nc = rp;
-        q.c = u_ws;
-        q.ldc = rp;
-        q.out_scale = s_lora;
-        hipError_t e = run<64, 64, BF16_NT, BF16_NT>(q, s);
+        hipError_t e = lora_down<BF16_NT>(bf16_segment(dy, N, N, b, N, r, N), m, rp, s_lora, u_ws, p.lv, s);
         if (e != hipSuccess) return e;
     }
+    if (dgrad_main_supported(N, K)) return launch_dgrad_main(dy, m, wt, r > 0 ? u_ws : nullptr, rp, a, r, dx, s);
     p.seg[0] = nf4_segment(dy, N, N, w);
     p.nseg = 1;
     if (r > 0) {

@@ -112,7 +112,7 @@ def _w(n=256, k=512, codes=FAKE, aq=FAKE, asc=FAKE, am=None, bs=64, dq=256):
 def test_linear_validation(L, fn):
     f = getattr(L, fn)
     ws = nq.nf4_linear_workspace_size(64, 16)
-    assert ws == 64 * 64 * 2
+    assert ws == 64 * 64 * 2 + 8 * 64 * 64 * 4
 
     def call(act=FAKE, m=64, w=None, a=FAKE, b=FAKE, r=16, out=FAKE, wsp=FAKE, wsb=ws):
         w = w if w is not None else _w()
@@ -140,9 +140,10 @@ def test_linear_validation(L, fn):
 
 
 def test_workspace_size(L):
-    assert nq.nf4_linear_workspace_size(4096, 64) == 4096 * 64 * 2
-    assert nq.nf4_linear_workspace_size(3, 5) == 512
-    assert nq.nf4_linear_workspace_size(10, 65) == 10 * 128 * 2
+    # bf16 product [m x rp] padded to 256 bytes, then 8 fp32 partials [8 x m x rp]
+    assert nq.nf4_linear_workspace_size(4096, 64) == 4096 * 64 * 2 + 8 * 4096 * 64 * 4
+    assert nq.nf4_linear_workspace_size(3, 5) == 512 + 8 * 3 * 64 * 4
+    assert nq.nf4_linear_workspace_size(10, 65) == 10 * 128 * 2 + 8 * 10 * 128 * 4
     assert nq.nf4_linear_workspace_size(100, 0) == 0
 
 
