@@ -56,11 +56,14 @@ __device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
-// An fp16 pair of levels scaled by sc and rounded to a bf16 pair.
+// An fp16 pair of levels scaled by sc and rounded to a bf16 pair. Each half
+// is widened exactly and multiplied in fp32 (one rounding) by v_fma_mix_f32,
+// which reads the fp16 half directly: 3 VALU instructions for 2 weights.
 __device__ __forceinline__ uint32_t scale_pair(uint32_t hh, float sc) {
-    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh & 0xFFFFu));
-    const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(hh >> 16));
-    return pack_bf16x2(lo * sc, hi * sc);
+    float lo, hi;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hh), "v"(sc));
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(hi) : "v"(hh), "v"(sc));
+    return pack_bf16x2(lo, hi);
 }
 
 // Workgroup -> (m tile, n tile). Consecutive workgroups go round robin to the
