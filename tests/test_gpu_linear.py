@@ -78,6 +78,14 @@ CASES = [
     (9, 48, 512, 0),
     (1, 16 * 600 + 5, 256, 0),
     (16, 1000, 1280, 0),
+    # decode path with each tile count per workgroup (the grid is about one
+    # workgroup per CU, so the tile count follows from N)
+    (2, 16 * 300, 512, 0),
+    (1, 16 * 1000 + 3, 256, 0),
+    (7, 16 * 1300, 256, 0),
+    (16, 16 * 1500 + 7, 512, 0),
+    (1, 16 * 1900, 256, 0),
+    (4, 16 * 1792, 2304, 0),
 ]
 
 
