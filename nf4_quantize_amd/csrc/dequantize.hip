@@ -27,9 +27,27 @@ struct Levels {
     float q[16];
 };
 
-__device__ __forceinline__ void build_pair_table(const Levels &lv, float2 *s_pair) {
+// Entry e of the table is (q[e & 15], q[e >> 4]). The levels are kernel
+// arguments (scalar loads); a select chain copies them to LDS first, so that
+// building the table issues no vector-memory load (which would be waited on
+// together with the code loads already in flight). Ends with a barrier.
+__device__ __forceinline__ void build_pair_table(const Levels &lv, float *s_lv, float2 *s_pair) {
     const int t = threadIdx.x;  // 256 threads: one entry each
-    s_pair[t] = make_float2(lv.q[t & 15], lv.q[t >> 4]);
+    if (t < 16) {
+        // (the empty asm keeps each level an opaque scalar, so the chain is
+        // not turned back into an indexed load of the argument block)
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float q = lv.q[i];
+            asm volatile("" : "+s"(q));
+            v = t == i ? q : v;
+        }
+        s_lv[t] = v;
+    }
+    __syncthreads();
+    s_pair[t] = make_float2(s_lv[t & 15], s_lv[t >> 4]);
+    __syncthreads();
 }
 
 template <typename O> struct Out;
@@ -62,35 +80,51 @@ __global__ __launch_bounds__(kThreads) void dequantize_chunks_kernel(
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
     O *__restrict__ out, Levels lv) {
     __shared__ float2 s_pair[256];
-    build_pair_table(lv, s_pair);
-    __syncthreads();
-
+    __shared__ float s_lv[16];
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    // wave index in scalar registers: the chunk's scale data is then fetched
+    // with scalar loads (32 E4M3 codes and one c2 per chunk: a chunk of 32
+    // blocks never straddles a group of 256)
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // all code loads of the wave's chunks first (a chunk past the end reloads
+    // the last one and stores nothing)
+    uint32_t d[kCPW][4];
+#pragma unroll
+    for (int c = 0; c < kCPW; ++c) {
+        const int64_t chunk = min(wave * kCPW + c, nchunks - 1);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(codes + chunk * kChunkBytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[c][j] = __builtin_nontemporal_load(&src[j * 64 + lane]);
+    }
+    build_pair_table(lv, s_lv, s_pair);
+
 #pragma unroll
     for (int c = 0; c < kCPW; ++c) {
         const int64_t chunk = wave * kCPW + c;
         if (chunk >= nchunks) return;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(codes + chunk * kChunkBytes);
-        uint32_t d[4];
-        float s[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) d[j] = __builtin_nontemporal_load(&src[j * 64 + lane]);
         const int64_t blk0 = chunk * (kChunk / kBlock);
+        // scale of dword j: block 8 j + lane / 8 of the chunk
+        float s[4];
+        if constexpr (kDQ) {
+            const uint32_t *q32 = reinterpret_cast<const uint32_t *>(absmax_q + blk0);
+            const float c2 = absmax_scale[blk0 / kDqBlock];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t b = blk0 + j * 8 + (lane >> 3);
-            if (kDQ)
-                s[j] = e4m3_decode(absmax_q[b]) * absmax_scale[b / kDqBlock];
-            else
-                s[j] = absmax[b];
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t code8 = __builtin_amdgcn_perm(q32[2 * j + 1], q32[2 * j], (uint32_t)(lane >> 3));
+                // gfx950's fp8 -> f32 convert decodes OCP E4M3FN exactly
+                s[j] = __builtin_amdgcn_cvt_f32_fp8((int)code8, 0) * c2;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = absmax[blk0 + j * 8 + (lane >> 3)];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float v[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float2 qq = s_pair[(d[j] >> (8 * k)) & 0xFFu];
+                const float2 qq = s_pair[(d[c][j] >> (8 * k)) & 0xFFu];
                 v[2 * k] = qq.x * s[j];
                 v[2 * k + 1] = qq.y * s[j];
             }
@@ -106,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_tail_kernel(
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
     O *__restrict__ out, Levels lv) {
     __shared__ float2 s_pair[256];
-    build_pair_table(lv, s_pair);
-    __syncthreads();
+    __shared__ float s_lv[16];
+    build_pair_table(lv, s_lv, s_pair);
     const int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
     const uint32_t code = (codes[i >> 1] >> (4 * (i & 1))) & 15u;

@@ -264,9 +264,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
     // writes them to LDS so that the table is built without vector-memory
     // loads, which would wait for the units issued above.
     if (tid < 16) {
-        float v = lv.q[0];
+        // (the empty asm keeps each level an opaque scalar, so the chain is
+        // not turned back into an indexed load of the argument block)
+        float v = 0.0f;
 #pragma unroll
-        for (int i = 1; i < 16; ++i) v = tid == i ? lv.q[i] : v;
+        for (int i = 0; i < 16; ++i) {
+            float q = lv.q[i];
+            asm volatile("" : "+s"(q));
+            v = tid == i ? q : v;
+        }
         s_lv[tid] = v;
     }
     __syncthreads();

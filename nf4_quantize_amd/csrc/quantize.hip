@@ -153,11 +153,16 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     const int64_t g = blockIdx.x;
     const typename S::Vec *src = reinterpret_cast<const typename S::Vec *>(w + g * kGroup);
 
+    // The table comes from the argument block through a vector load: issued
+    // first and stored to LDS after the weight loads are on their way, so its
+    // wait does not cover them.
+    const LutEntry le = lut.e[t % kLutEntries];
+    __builtin_amdgcn_sched_barrier(0);
     typename S::Vec v[ITERS];
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * TH + t]);
-
-    load_lut(lut, s_lut);
+    // (every thread stores its entry; the copies are identical)
+    s_lut[t % kLutEntries] = make_float2(le.thr, __int_as_float(le.base));
     __syncthreads();
 
 #pragma unroll
