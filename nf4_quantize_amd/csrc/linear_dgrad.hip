@@ -34,7 +34,7 @@ constexpr int kTM = kBM / 16;              // 16 row tiles per wave
 constexpr int kTN = 64 / 16;               // 4 column tiles per wave
 constexpr int kATile = kBM * kBK * 2;      // 32 KiB of bf16 dY per step
 constexpr int kBTile = kBN * kBK * 2;      // 32 KiB of bf16 W' per step
-constexpr int kTable = 256 * 32 * 4;       // level-pair table, one copy per lane pair
+constexpr int kTable = 256 * 32 * 4;       // level-pair table, one copy per half-wave lane
 constexpr int kLds = kTable + 2 * kATile + 2 * kBTile;  // 160 KiB
 constexpr int kFragAhead = 3;              // dY fragments read this many row groups ahead
 constexpr int kLookAhead = 16;             // MFMA slots between a level read and its use
@@ -93,15 +93,16 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     const int lr = lane & 15, g = lane >> 4;
 
     // level-pair table at LDS address 0 (no static LDS in this kernel): the
-    // fp16 pair of code byte b for lane pair p at byte 128 b + 4 p, so a
-    // wave's 64 reads touch each bank from at most two lanes.
+    // fp16 pair of code byte b for copy p at byte 128 b + 4 p. Lane l reads
+    // copy l % 32: LDS serves a wave's 32-bit reads one half-wave at a time,
+    // and the 32 lanes of a half-wave then read 32 distinct banks.
     {
         const uint32_t e = f16_pair(p.lv.q[t & 15], p.lv.q[t >> 4]);
         u32x4 *row = reinterpret_cast<u32x4 *>(smem + 128 * t);
 #pragma unroll
         for (int c = 0; c < 8; ++c) row[c] = u32x4{e, e, e, e};
     }
-    const uint32_t pair4 = 4u * (uint32_t)(lane >> 1);
+    const uint32_t pair4 = 4u * (uint32_t)(lane & 31);
     auto level = [&](uint32_t d, int h) {
         const uint32_t addr = (((d >> (8 * h)) & 0xFFu) << 7) | pair4;
         return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);

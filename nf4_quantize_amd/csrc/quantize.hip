@@ -2,7 +2,7 @@
 // for gfx950 ([MF] "Block-Wise Quantization Mechanics" and "Double
 // Quantization (DQ)", see nf4_internal.h for the source key).
 //
-// Work split: one workgroup of 256 threads per group of 256 blocks (16384
+// Work split: one workgroup of 512 threads per group of 256 blocks (16384
 // weights), so c2 = max c1 of the group is a workgroup reduction and never
 // leaves the chip. Each lane owns one 16-byte slice of a block (8 bf16 or 4
 // fp32 weights); consecutive lanes own consecutive slices, so every wave
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void double_quantize_kernel(
 }
 
 // Threads per group workgroup.
-constexpr int kGroupThreads = 256;
+constexpr int kGroupThreads = 512;
 
 template <typename T>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
