@@ -49,6 +49,9 @@ constexpr int kBpu = 4;      // blocks per unit (K chunk of 256 weights)
 constexpr int kChunk = kBpu * kBlock;
 constexpr int kMaxNT = 8;    // column tiles per workgroup
 constexpr int kWaves = 8;    // waves per workgroup (the K split)
+constexpr int kMaxK = 32768; // longest row: its E4M3 codes for 16 kMaxNT rows fill kQ8Words
+constexpr int kQ8Words = 16 * kMaxNT * (kMaxK / kBlock) / 4 + 64;  // staged E4M3 code dwords
+constexpr int kC2Words = 16 * kMaxNT * (kMaxK / kBlock) / 256 + 2;  // staged c2 values
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -64,16 +67,26 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // One unit's operands for this lane: two 16-byte pieces of codes of weight
 // row r (blocks 0-1 and 2-3 of the chunk, lane group g's quarter of each
-// pair) and the raw scale data of the row's 4 blocks: the E4M3 codes and the
-// group's c2 with double quantization, else the fp32 absmax values.
+// pair), and without double quantization the fp32 absmax values of the
+// row's 4 blocks. With double quantization the scale data of the
+// workgroup's rows is staged in LDS once (see gemv_kernel) and read per unit.
 template <bool kDQ> struct Unit;
 template <> struct Unit<true> {
     u32x4 c[2];
-    uint32_t q8;
-    float c2;
 };
 template <> struct Unit<false> {
     u32x4 c[2];
+    f32x4 am;
+};
+
+// Scale data of one unit for this lane's weight row: the 4 E4M3 codes and
+// the group's c2, or the 4 fp32 absmax values.
+template <bool kDQ> struct Scales;
+template <> struct Scales<true> {
+    uint32_t q8;
+    float c2;
+};
+template <> struct Scales<false> {
     f32x4 am;
 };
 
@@ -86,10 +99,9 @@ template <> struct Unit<false> {
 // same on every path, but through `none`, an empty descriptor, so they return
 // zeros without touching memory.
 struct Stream {
-    Rsrc codes, q, sc, x, none;
+    Rsrc codes, q, x, none;
     uint32_t c_off;    // r * K/2 + 16 g
-    uint32_t q_off;    // r * nblk (bytes of E4M3 codes), or 4 r * nblk (absmax bytes)
-    uint32_t flat0;    // block index of row n_base + r, block 0, from the group of row n_base
+    uint32_t q_off;    // 4 r * nblk: bytes of absmax before row r (without double quantization)
     uint32_t x_off;    // bytes of X row r at k = 16 s(g)
     uint32_t tile_c;   // 16 * K/2: bytes of codes per 16 rows
     uint32_t tile_b;   // 16 * nblk: blocks per 16 rows
@@ -101,14 +113,8 @@ __device__ __forceinline__ void issue_unit(Unit<kDQ> &u, const Stream &st, int t
     const uint32_t vo = st.c_off + (uint32_t)t * st.tile_c;
     u.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, vo, (int)(128u * chunk), 0));
     u.c[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, vo + 64u, (int)(128u * chunk), 0));
-    const uint32_t tb = (uint32_t)t * st.tile_b;  // block of row 16 t + r, block 0, relative to row r
-    if constexpr (kDQ) {
-        // the 4 blocks share one aligned word of E4M3 codes and one group
-        const Rsrc qr = live ? st.q : st.none, sr = live ? st.sc : st.none;
-        u.q8 = __builtin_amdgcn_raw_buffer_load_b32(qr, st.q_off + tb, (int)(kBpu * chunk), 0);
-        const uint32_t grp = (st.flat0 + tb + kBpu * chunk) >> 8;
-        u.c2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, grp * 4u, 0, 0));
-    } else {
+    if constexpr (!kDQ) {
+        const uint32_t tb = (uint32_t)t * st.tile_b;  // block of row 16 t + r, block 0, relative to row r
         const Rsrc ar = live ? st.q : st.none;
         u.am = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, st.q_off + 4u * tb, (int)(4u * kBpu * chunk), 0));
@@ -129,10 +135,10 @@ __device__ __forceinline__ void issue_x(u32x4 (&xa)[kBpu], u32x4 (&xb)[kBpu], co
 }
 
 template <bool kDQ, int J>
-__device__ __forceinline__ float unit_scale(const Unit<kDQ> &u) {
+__device__ __forceinline__ float unit_scale(const Scales<kDQ> &sc) {
     // gfx950's fp8 -> f32 convert decodes OCP E4M3FN exactly
-    if constexpr (kDQ) return __builtin_amdgcn_cvt_f32_fp8((int)u.q8, J) * u.c2;
-    else return u.am[J];
+    if constexpr (kDQ) return __builtin_amdgcn_cvt_f32_fp8((int)sc.q8, J) * sc.c2;
+    else return sc.am[J];
 }
 
 // bf16 pairs of the 4 code bytes of d: table words at byte 256 * byte + lane4.
@@ -146,14 +152,9 @@ __device__ __forceinline__ u32x4 lookup4(const char *lds, uint32_t d, uint32_t l
 }
 
 template <bool kDQ, int J, int kMI>
-__device__ __forceinline__ void block_mac(f32x4_t &acc, const Unit<kDQ> &u, uint32_t ev, uint32_t od, const u32x4 &xa,
-                                          const u32x4 &xb, const char *lds, uint32_t lane4) {
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 lo = lookup4(lds, ev, lane4), hi = lookup4(lds, od, lane4);
-    f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(lo), z, 0, 0, 0);
-    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), as_bf16x8(hi), p, 0, 0, 0);
+__device__ __forceinline__ void block_scale(f32x4_t &acc, const Scales<kDQ> &sc, const f32x4_t &p) {
     // D row 4 g + i, column r: that column is weight row n, scaled by c1'(n, b)
-    const float s = unit_scale<kDQ, J>(u);
+    const float s = unit_scale<kDQ, J>(sc);
     if constexpr (kMI == 1) {
         acc[0] += p[0] * s;  // one activation row: only element 0 of lane group 0 is kept
     } else {
@@ -161,12 +162,21 @@ __device__ __forceinline__ void block_mac(f32x4_t &acc, const Unit<kDQ> &u, uint
     }
 }
 
+__device__ __forceinline__ f32x4_t mfma(const u32x4 &x, const u32x4 &w, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x), as_bf16x8(w), c, 0, 0, 0);
+}
+
 // One unit: regroup the code words so that each register holds one block
 // (the lower half-wave of block 2p's word pair and the upper half-wave of
-// block 2p + 1's are exchanged), then 2 MFMAs per block.
+// block 2p + 1's are exchanged), then 2 MFMAs per block (first half of the
+// block's k with a zero accumulator, then the second half), then the
+// block's scale. The order is fixed by scheduling barriers so that table
+// reads run a block ahead of the MFMAs that use them and the scaling waits
+// on MFMA results that have had time to complete.
 template <bool kDQ, int kMI>
-__device__ __forceinline__ void unit_mac(f32x4_t &acc, const Unit<kDQ> &u, const u32x4 (&xa)[kBpu],
-                                         const u32x4 (&xb)[kBpu], const char *lds, uint32_t lane4) {
+__device__ __forceinline__ void unit_mac(f32x4_t &acc, const Unit<kDQ> &u, const Scales<kDQ> &sc,
+                                         const u32x4 (&xa)[kBpu], const u32x4 (&xb)[kBpu], const char *lds,
+                                         uint32_t lane4) {
     uint32_t ev[kBpu], od[kBpu];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -177,10 +187,37 @@ __device__ __forceinline__ void unit_mac(f32x4_t &acc, const Unit<kDQ> &u, const
         od[2 * p] = o[0];
         od[2 * p + 1] = o[1];
     }
-    block_mac<kDQ, 0, kMI>(acc, u, ev[0], od[0], xa[0], xb[0], lds, lane4);
-    block_mac<kDQ, 1, kMI>(acc, u, ev[1], od[1], xa[1], xb[1], lds, lane4);
-    block_mac<kDQ, 2, kMI>(acc, u, ev[2], od[2], xa[2], xb[2], lds, lane4);
-    block_mac<kDQ, 3, kMI>(acc, u, ev[3], od[3], xa[3], xb[3], lds, lane4);
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    u32x4 lo[kBpu], hi[kBpu];
+    f32x4_t p[kBpu];
+    lo[0] = lookup4(lds, ev[0], lane4);
+    lo[1] = lookup4(lds, ev[1], lane4);
+    hi[0] = lookup4(lds, od[0], lane4);
+    hi[1] = lookup4(lds, od[1], lane4);
+    __builtin_amdgcn_sched_barrier(0);
+    p[0] = mfma(xa[0], lo[0], z);
+    p[1] = mfma(xa[1], lo[1], z);
+    __builtin_amdgcn_sched_barrier(0);
+    lo[2] = lookup4(lds, ev[2], lane4);
+    lo[3] = lookup4(lds, ev[3], lane4);
+    __builtin_amdgcn_sched_barrier(0);
+    p[0] = mfma(xb[0], hi[0], p[0]);
+    p[1] = mfma(xb[1], hi[1], p[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    hi[2] = lookup4(lds, od[2], lane4);
+    hi[3] = lookup4(lds, od[3], lane4);
+    __builtin_amdgcn_sched_barrier(0);
+    p[2] = mfma(xa[2], lo[2], z);
+    p[3] = mfma(xa[3], lo[3], z);
+    __builtin_amdgcn_sched_barrier(0);
+    block_scale<kDQ, 0, kMI>(acc, sc, p[0]);
+    block_scale<kDQ, 1, kMI>(acc, sc, p[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    p[2] = mfma(xb[2], hi[2], p[2]);
+    p[3] = mfma(xb[3], hi[3], p[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    block_scale<kDQ, 2, kMI>(acc, sc, p[2]);
+    block_scale<kDQ, 3, kMI>(acc, sc, p[3]);
 }
 
 template <int NT, bool kDQ, int kMI>
@@ -196,12 +233,21 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
     constexpr int kRing = kR * NT;
     constexpr int kNX = kR + 1;
     constexpr int kUnroll = NT * (kR == 1 ? 2 : 6);
+    // vector-memory loads of the prologue (units 0 .. kRing - 2 and the X of
+    // the chunks they start)
+    constexpr int kPrologueLoads = (kRing - 1) * (kDQ ? 2 : 3) + 2 * kBpu * ((kRing - 2) / NT + 1);
+    static_assert(kPrologueLoads < 64, "vmcnt range");
     static_assert(kUnroll % kRing == 0 && (kUnroll / NT) % kNX == 0, "unroll must align ring and X buffers");
     static_assert(kWaves * NT * 256 <= 256 * 64, "partial tiles must fit the table's LDS");
 
     // 64 KiB: the lane-replicated code table, then the partial tiles
     __shared__ uint32_t s_lds[256 * 64];
     __shared__ float s_lv[16];
+    // with double quantization: the E4M3 codes of the workgroup's rows (row
+    // rho's dword d at rho * K/256 + (d ^ (rho & qmask))) and the c2 values
+    // of its groups
+    __shared__ uint32_t s_q8[kDQ ? kQ8Words : 1];
+    __shared__ float s_c2[kDQ ? kC2Words : 1];
     const char *lds = reinterpret_cast<const char *>(s_lds);
 
     const int tid = threadIdx.x;
@@ -219,20 +265,48 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
     st.tile_b = (uint32_t)(16 * nblk);
     st.none = rsrc(w.codes, 0);
     st.codes = rsrc(w.codes + n_base * (K / 2), rows * (K / 2));
+    st.x = rsrc(x, (int64_t)m * K * 2);
+    st.c_off = (uint32_t)(r * (K / 2) + 16 * g);
+    st.x_off = (uint32_t)(2 * (r * K + 16 * sg));
+
+    // Scale data. With double quantization the workgroup's E4M3 codes (rows
+    // x K/64 bytes, contiguous in memory) and its groups' c2 values are
+    // copied to LDS by direct-to-LDS loads issued before anything else, so
+    // every scale line is fetched once per workgroup instead of once per unit.
+    // A row's dwords are XOR-swizzled by the row index (within aligned runs of
+    // up to 32 dwords) so that the 16 rows a unit reads fall in distinct banks.
+    const uint32_t rowdw = (uint32_t)(nblk / 4);  // E4M3 code dwords per row
+    const uint32_t qmask = std::min(rowdw & (0u - rowdw), 32u) - 1u;
+    uint32_t c2_row0 = 0;  // block index of row n_base + r, block 0, counted from the first staged group
     if constexpr (kDQ) {
-        st.q = rsrc(w.q + n_base * nblk, rows * nblk);
-        // the groups holding the workgroup's blocks
         const int64_t g0 = n_base * nblk / 256, g1 = ((n_base + rows) * nblk - 1) / 256;
-        st.sc = rsrc(w.scale + g0, (g1 - g0 + 1) * 4);
-        st.q_off = (uint32_t)(r * nblk);
+        c2_row0 = (uint32_t)((n_base + r) * nblk - g0 * 256);
+        const Rsrc qsrc = rsrc(w.q + n_base * nblk, rows * nblk);
+        const uint32_t total = (uint32_t)rows * rowdw;
+        constexpr uint32_t kStep = 64u * kWaves;
+        uint32_t rho = (uint32_t)(wave * 64 + lane) / rowdw;
+        uint32_t d = (uint32_t)(wave * 64 + lane) - rho * rowdw;
+        const uint32_t sq = kStep / rowdw, sr = kStep - sq * rowdw;
+        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < total; p0 += kStep) {
+            // dwords p0 + lane of the staged array; past `total` the source is
+            // outside the descriptor and zeros are written (inside s_q8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qsrc, (gemm::lds_void *)(s_q8 + p0), 4,
+                                                     (rho * rowdw + (d ^ (rho & qmask))) * 4u, 0, 0, 0);
+            rho += sq;
+            d += sr;
+            if (d >= rowdw) {
+                d -= rowdw;
+                ++rho;
+            }
+        }
+        const Rsrc csrc = rsrc(w.scale + g0, (g1 - g0 + 1) * 4);
+        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < (uint32_t)(g1 - g0 + 1); p0 += kStep)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(csrc, (gemm::lds_void *)(s_c2 + p0), 4, (p0 + lane) * 4u, 0,
+                                                     0, 0);
     } else {
         st.q = rsrc(w.absmax + n_base * nblk, rows * nblk * 4);
         st.q_off = (uint32_t)(r * nblk * 4);
     }
-    st.x = rsrc(x, (int64_t)m * K * 2);
-    st.c_off = (uint32_t)(r * (K / 2) + 16 * g);
-    st.flat0 = (uint32_t)((n_base + r) * nblk - (n_base * nblk / 256) * 256);
-    st.x_off = (uint32_t)(2 * (r * K + 16 * sg));
 
     // this wave's chunks: wave, wave + kWaves, ...; unit u = (chunk u / NT, tile u % NT)
     const int64_t chunks = K / kChunk;
@@ -280,6 +354,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
         const int e = i >> 6;
         s_lds[i] = pack_bf16x2(s_lv[e & 15], s_lv[e >> 4]);
     }
+    // this wave's scale copies have landed once at most the prologue's
+    // vector-memory loads (issued after them) are outstanding; the barrier
+    // then publishes every wave's copies
+    if constexpr (kDQ) __builtin_amdgcn_s_waitcnt(gemm::vmcnt_at_most(kPrologueLoads));
     __syncthreads();
 
     for (int u0 = 0; u0 < units; u0 += kUnroll) {
@@ -292,8 +370,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
             } else {
                 issue(u0 + kUnroll, std::integral_constant<int, J + kRing - 1 - kUnroll>{});
             }
-            if (u0 + J < units)
-                unit_mac<kDQ, kMI>(acc[t], ring[J % kRing], xa[ci % kNX], xb[ci % kNX], lds, lane4);
+            if (u0 + J < units) {
+                Scales<kDQ> sc;
+                if constexpr (kDQ) {
+                    const uint32_t chunk = (uint32_t)(wave + kWaves * ((u0 + J) / NT));
+                    const uint32_t row = 16u * t + r;
+                    sc.q8 = s_q8[row * rowdw + (chunk ^ (row & qmask))];
+                    sc.c2 = s_c2[(c2_row0 + (uint32_t)t * st.tile_b + kBpu * chunk) >> 8];
+                } else {
+                    sc.am = ring[J % kRing].am;
+                }
+                unit_mac<kDQ, kMI>(acc[t], ring[J % kRing], sc, xa[ci % kNX], xb[ci % kNX], lds, lane4);
+            }
         });
     }
 
@@ -342,11 +430,8 @@ void launch_mi(int nt, dim3 grid, const uint16_t *x, int m, const WView &w, uint
 
 }  // namespace
 
-// The descriptors address each workgroup's rows with 32-bit offsets:
-// 128 rows of K/2 bytes, and 16 rows of X.
-bool gemv_supported(int64_t m, int64_t k) {
-    return m >= 1 && m <= 16 && k % kChunk == 0 && k <= (int64_t)1 << 24;
-}
+// K at most kMaxK: the staged scale data of a workgroup's rows fits LDS.
+bool gemv_supported(int64_t m, int64_t k) { return m >= 1 && m <= 16 && k % kChunk == 0 && k <= kMaxK; }
 
 hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint16_t *y, hipStream_t s) {
     const WView w = make_view(wt);
