@@ -13,8 +13,8 @@
 //    so the fragment reads of 16 rows hit distinct banks.
 //  - W never touches LDS: each lane loads the 8 code bytes its MFMA operands
 //    need (one weight row, 16 consecutive k) and dequantizes them in
-//    registers, bf16(q[code] * c1') as the dequantize path does, through a
-//    256-entry (low, high) level table in LDS. The 32 k of an MFMA are taken
+//    registers to bf16(q[code] * c1') through a 256-entry (low, high) level
+//    table in LDS, the levels held as fp16 (see level_pair). The 32 k of an MFMA are taken
 //    in the order that makes a lane's 16 k of one step contiguous: lane group
 //    g covers k = 16g .. 16g+15, half ks (0, 1) of it in MFMA ks. X fragments
 //    are read in the same order, so the contraction is unchanged.
@@ -68,8 +68,9 @@ struct FwdParams {
 // Level-pair table in LDS: the entry of code byte b holds (q[b & 15],
 // q[b >> 4]) as two fp16 (the LDS read bandwidth, not the arithmetic, bounds
 // this kernel: a 4-byte entry halves the bytes of an 8-byte fp32 pair). Each
-// lane has its own copy, entry b of lane l at byte 256 b + 4 l, so a wave's
-// 64 reads hit 64 distinct banks whatever the code bytes. For byte h of the
+// lane has its own copy, entry b of lane l at byte 256 b + 4 l, so the 32
+// lanes of each half-wave (LDS serves 32-bit reads a half-wave at a time)
+// hit 32 distinct banks whatever the code bytes. For byte h of the
 // code dword d, v_perm builds the address (b << 8) | 4 l in one instruction.
 // The fp16 levels differ from the fp32 ones by at most 2^-12 relative, far
 // below the bf16 rounding of the operand.
