@@ -406,6 +406,183 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
     }
 }
 
+// ---- one activation row (m == 1): VALU dot products over row-linear loads
+//
+// With a single activation row the MFMA's 16-row A operand is 1/16 used and
+// the 16-row tile makes every load touch 16 weight rows. Here each wave owns
+// a contiguous range of weight rows - a contiguous range of codes - and
+// streams it linearly, 1 KiB per load instruction: in piece p of a row, lane
+// l holds the 16 code bytes of weights k = 2048 p + 32 l + [0, 32), one half
+// of block 32 p + l/2. Code bytes become bf16 level pairs through the same
+// lane-private table, v_dot2c_f32_bf16 multiplies them with the lane's x
+// pairs (16 registers per piece, loaded once), and the half-block sum is
+// scaled by its c1' (one FMA). At the end of a row a wave reduction adds the
+// 64 lanes and lane 0 stores y. Requires K = P * 2048 with P <= 4 (the x
+// registers).
+constexpr int kWaves1 = 8;
+constexpr int kRing1 = 4;      // pieces in flight per wave
+constexpr int kPiece = 2048;   // weights per piece: one 1 KiB load instruction
+constexpr int kMaxP1 = 4;      // pieces per row (x registers: 16 per piece)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool kDQ> struct Piece;
+template <> struct Piece<true> {
+    u32x4 c;
+    uint32_t q8;  // E4M3 code of the lane's block in the low byte
+    float c2;
+};
+template <> struct Piece<false> {
+    u32x4 c;
+    float am;
+};
+
+// Sum over the 64 lanes (every lane gets the sum).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);  // rows 0+1 and 2+3
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int P, bool kDQ>
+__global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__restrict__ x, WView w,
+                                                              uint16_t *__restrict__ y, Levels lv) {
+    static_assert(kRing1 % P == 0, "ring must hold whole rows' pieces in phase");
+    __shared__ uint32_t s_lds[256 * 64];
+    __shared__ float s_lv[16];
+    const char *lds = reinterpret_cast<const char *>(s_lds);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lane4 = 4u * lane;
+    const int64_t K = w.k, nblk = K / kBlock;
+    const int64_t W = (int64_t)gridDim.x * kWaves1, gw = (int64_t)blockIdx.x * kWaves1 + wave;
+    const int64_t r0 = gw * w.n / W, r1 = (gw + 1) * w.n / W;  // this wave's rows
+    const int nrows = (int)(r1 - r0), npieces = nrows * P;
+
+    // x pairs of every piece: x[2048 p + 32 lane + 2 m], m = 0..15
+    u32x4 xv[P][4];
+    {
+        const Rsrc xr = rsrc(x, K * 2);
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xv[pp][i] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(2 * (kPiece * pp + 32 * lane) + 16 * i), 0, 0));
+    }
+
+    // descriptors over this wave's rows; loads of pieces past the end go
+    // through an empty descriptor (the wait counts then match on every path)
+    const Rsrc none = rsrc(w.codes, 0);
+    const Rsrc cr = rsrc(w.codes + r0 * (K / 2), (int64_t)nrows * (K / 2));
+    Rsrc qr, sr;
+    int64_t g0 = 0;
+    if constexpr (kDQ) {
+        qr = rsrc(w.q + r0 * nblk, (int64_t)nrows * nblk);
+        g0 = r0 * nblk / 256;
+        const int64_t g1 = nrows > 0 ? (r1 * nblk - 1) / 256 : g0;
+        sr = rsrc(w.scale + g0, (g1 - g0 + 1) * 4);
+    } else {
+        qr = rsrc(w.absmax + r0 * nblk, (int64_t)nrows * nblk * 4);
+    }
+    const uint32_t half_blk = (uint32_t)(lane >> 1);  // lane's block within a piece
+    const uint32_t flat0 = (uint32_t)(r0 * nblk - g0 * 256);
+
+    Piece<kDQ> ring[kRing1];
+    auto issue = [&](int j0, auto JC) {
+        constexpr int J = decltype(JC)::value;
+        constexpr int pp = J % P;
+        const int j = j0 + J;
+        const bool live = j < npieces;
+        const uint32_t row = (uint32_t)(j / P);
+        Piece<kDQ> &pc = ring[J % kRing1];
+        pc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? cr : none, 16u * lane,
+                                                                               (int)(1024u * (uint32_t)j), 0));
+        const uint32_t blk = row * (uint32_t)nblk + 32u * pp + half_blk;  // block, from the wave's first row
+        if constexpr (kDQ) {
+            pc.q8 = __builtin_amdgcn_raw_buffer_load_b8(live ? qr : none, blk, 0, 0);
+            pc.c2 = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(live ? sr : none, ((flat0 + blk) >> 8) * 4u, 0, 0));
+        } else {
+            pc.am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(live ? qr : none, 4u * blk, 0, 0));
+        }
+    };
+
+    static_for<kRing1 - 1>([&](auto JC) { issue(0, JC); });
+
+    if (tid < 16) {
+        // (the empty asm keeps each level an opaque scalar, so the chain is
+        // not turned back into an indexed load of the argument block)
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float q = lv.q[i];
+            asm volatile("" : "+s"(q));
+            v = tid == i ? q : v;
+        }
+        s_lv[tid] = v;
+    }
+    __syncthreads();
+    for (int i = tid; i < 256 * 64; i += 64 * kWaves1) {
+        const int e = i >> 6;
+        s_lds[i] = pack_bf16x2(s_lv[e & 15], s_lv[e >> 4]);
+    }
+    __syncthreads();
+
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < npieces; j0 += kRing1) {
+        static_for<kRing1>([&](auto JC) {
+            constexpr int J = decltype(JC)::value;
+            constexpr int pp = J % P;
+            if constexpr (J + kRing1 - 1 < kRing1) {
+                issue(j0, std::integral_constant<int, J + kRing1 - 1>{});
+            } else {
+                issue(j0 + kRing1, std::integral_constant<int, J - 1>{});
+            }
+            if (j0 + J < npieces) {
+                const Piece<kDQ> &pc = ring[J % kRing1];
+                float part = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 lv4 = lookup4(lds, pc.c[i], lane4);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // (vector elements are copied to scalars first: a bit cast of
+                        // an element expression reads element 0 with this compiler)
+                        const uint32_t lw = lv4[b], xw = xv[pp][i][b];
+                        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lw),
+                                                               __builtin_bit_cast(bf16x2_t, xw), part, false);
+                    }
+                }
+                float sc;
+                if constexpr (kDQ) sc = __builtin_amdgcn_cvt_f32_fp8((int)pc.q8, 0) * pc.c2;
+                else sc = pc.am;
+                acc = fmaf(part, sc, acc);
+                if constexpr (pp == P - 1) {
+                    const float sum = wave_sum(acc);
+                    if (lane == 0) y[r0 + (j0 + J) / P] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
+                    acc = 0.0f;
+                }
+            }
+        });
+    }
+}
+
+template <bool kDQ>
+void launch_gemv1(int p, dim3 grid, const uint16_t *x, const WView &w, uint16_t *y, hipStream_t s) {
+    switch (p) {
+        case 1: gemv1_kernel<1, kDQ><<<grid, dim3(64 * kWaves1), 0, s>>>(x, w, y, levels()); break;
+        case 2: gemv1_kernel<2, kDQ><<<grid, dim3(64 * kWaves1), 0, s>>>(x, w, y, levels()); break;
+        default: gemv1_kernel<4, kDQ><<<grid, dim3(64 * kWaves1), 0, s>>>(x, w, y, levels()); break;
+    }
+}
+
 template <int NT, int kMI>
 void launch_nt(dim3 grid, const uint16_t *x, int m, const WView &w, uint16_t *y, hipStream_t s) {
     if (w.q)
@@ -439,6 +616,16 @@ hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint1
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
+    if (m == 1 && w.k % kPiece == 0 && w.k / kPiece <= kMaxP1 && w.k / kPiece != 3) {
+        // rows split over the waves of two workgroups per CU
+        const int p = (int)(w.k / kPiece);
+        const dim3 grid1((unsigned)std::max<int64_t>(1, std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1)));
+        if (w.q)
+            launch_gemv1<true>(p, grid1, x, w, y, s);
+        else
+            launch_gemv1<false>(p, grid1, x, w, y, s);
+        return hipGetLastError();
+    }
     const int64_t tiles = (w.n + 15) / 16;
     const int nt = (int)std::min<int64_t>(std::max<int64_t>((tiles + cus - 1) / cus, 1), kMaxNT);
     const dim3 grid((unsigned)((tiles + nt - 1) / nt));

@@ -86,6 +86,14 @@ CASES = [
     (16, 16 * 1500 + 7, 512, 0),
     (1, 16 * 1900, 256, 0),
     (4, 16 * 1792, 2304, 0),
+    # one activation row with K a multiple of 2048 (the row-streaming
+    # kernel): 1, 2 and 4 pieces per row, fewer rows than waves, and K = 6144
+    # (3 pieces, which the 16-row kernel takes)
+    (1, 1000, 2048, 0),
+    (1, 300, 4096, 0),
+    (1, 77, 8192, 0),
+    (1, 5000, 8192, 0),
+    (1, 640, 6144, 0),
 ]
 
 
