@@ -23,6 +23,8 @@
 // All loads are raw buffer loads with per-tile descriptors whose size stops
 // at the last valid row: rows beyond M or N read as zero, the loop has no
 // branches, and the per-step advance is a scalar offset.
+#include <utility>
+
 #include "gemm_common.h"
 
 namespace nf4 {
@@ -37,7 +39,7 @@ constexpr int kTN = 64 / 16;                 // 4 column tiles per wave
 constexpr int kATile = kBM * kBK * 2;        // 32 KiB of bf16 per X tile
 constexpr int kXBufs = 3;                    // X tiles in flight: steps s, s+1, s+2
 constexpr int kTable = 256 * 256;            // level-pair table, one copy per lane
-constexpr int kLds = kTable + kXBufs * kATile;  // 160 KiB: table, then the X tiles
+constexpr int kLds = kTable + kXBufs * kATile;  // 160 KiB: table and X tiles, all static
 constexpr int kFragAhead = 3;                // X fragments read this many row groups ahead
 constexpr int kLookAhead = 16;               // MFMA slots between a level read and its use
 constexpr int kLookRing = 8;                 // level reads in flight
@@ -45,6 +47,7 @@ constexpr int kLookRing = 8;                 // level reads in flight
 // step's first fragments are read at the end of the current one: the ring
 // length must divide the 32 row groups of a step to keep its phase.
 static_assert((2 * kTM) % (kFragAhead + 1) == 0, "fragment ring must divide a step");
+constexpr int kBarrierSlot = 4 * (2 * kTM - kFragAhead);  // first slot reading the next step's tile
 static_assert(kLookRing * 3 > kLookAhead, "level reads in flight exceed the ring");
 static_assert(45 + kLookAhead < 64, "half-1 operands must be finished within half 0");
 
@@ -74,11 +77,10 @@ struct FwdParams {
 // code dword d, v_perm builds the address (b << 8) | 4 l in one instruction.
 // The fp16 levels differ from the fp32 ones by at most 2^-12 relative, far
 // below the bf16 rounding of the operand.
-// The table sits at LDS address 0: the kernel declares no static LDS, so its
-// dynamic LDS starts there, and the perm result is the address itself.
-__device__ __forceinline__ uint32_t level_pair(const char *, uint32_t d, int h, uint32_t lane4) {
+// The table is a static LDS array: its base folds into the read's offset.
+__device__ __forceinline__ uint32_t level_pair(const char *tab, uint32_t d, int h, uint32_t lane4) {
     const uint32_t addr = __builtin_amdgcn_perm(d, lane4, 0x0C0C0400u | ((uint32_t)h << 8));
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
+    return *reinterpret_cast<const uint32_t *>(tab + addr);
 }
 // 8 weights (one code dword, element e in bits 4e..4e+3) -> 4 dwords of bf16 pairs.
 __device__ __forceinline__ u32x4 deq8(const char *tab, uint32_t d, float sc, uint32_t lane4) {
@@ -97,7 +99,13 @@ struct Raw {
 
 template <bool kDQ>
 __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
-    extern __shared__ __align__(16) char smem[];
+    // Static LDS: the table and three X tiles as separate objects, so that the
+    // compiler's waits for a direct-to-LDS load cover only reads of its tile.
+    __shared__ __align__(16) char s_tab[kTable];
+    __shared__ __align__(16) char s_x0[kATile];
+    __shared__ __align__(16) char s_x1[kATile];
+    __shared__ __align__(16) char s_x2[kATile];
+    static_assert(kTable + 3 * kATile == kLds && kXBufs == 3, "LDS layout");
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lr = lane & 15, g = lane >> 4;
@@ -107,12 +115,21 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
         const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)p.lv.q[t & 15]);
         const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)p.lv.q[t >> 4]);
         const uint32_t e = lo | (hi << 16);
-        u32x4 *row = reinterpret_cast<u32x4 *>(smem + 256 * t);
+        u32x4 *row = reinterpret_cast<u32x4 *>(s_tab + 256 * t);
 #pragma unroll
         for (int c = 0; c < 16; ++c) row[c] = u32x4{e, e, e, e};
     }
-    const char *const tab = smem;
-    char *const xbuf = smem + kTable;
+    const char *const tab = s_tab;
+    // X tile buffer b (b a compile-time constant)
+    auto xbuf = [&](auto BC) -> char * {
+        constexpr int b = decltype(BC)::value;
+        if constexpr (b == 0) return s_x0;
+        else if constexpr (b == 1) return s_x1;
+        else return s_x2;
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
     const uint32_t lane4 = 4u * (uint32_t)lane;
 
     int64_t mt, nt;
@@ -132,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
         a_off[q] = (uint32_t)(row * K * 2 + chunk * 16);
     }
-    auto stage_x = [&](const Rsrc &rs, int64_t koff_bytes, int buf) {
-        char *dst = xbuf + buf * kATile + (64 * w) * 128;
+    auto stage_x = [&](const Rsrc &rs, int64_t koff_bytes, auto BC) {
+        char *dst = xbuf(BC) + (64 * w) * 128;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + q * 1024), 16, a_off[q],
@@ -203,14 +220,32 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
     // of the previous step (its X tile has landed by then: each step ends with
     // the wait for the next step's tile and a barrier).
     u32x4 af[kFragAhead + 1];
-    auto step = [&](int64_t s, const Raw &rc, const Raw &rn, Raw &rl) {
-        const char *a_t = xbuf + (int)(s % kXBufs) * kATile;
-        const char *a_next = xbuf + (int)((s + 1) % kXBufs) * kATile;
+    // Loads issued after step s-1's X tile load, by the barrier slot of step s:
+    // step s-1's code loads, then step s's X tile and code loads.
+    constexpr int kLoadsPerStep = 8 + (kDQ ? 3 : 2) * kTN;
+    constexpr int kAfterTile = 2 * kLoadsPerStep - 8;
+    auto step = [&](int64_t s, auto BC, const Raw &rc, const Raw &rn, Raw &rl) {
+        constexpr int b = decltype(BC)::value;  // s % 3
+        const char *a_t = xbuf(std::integral_constant<int, b>{});
+        const char *a_next = xbuf(std::integral_constant<int, (b + 1) % 3>{});
+        char *const x_dst = xbuf(std::integral_constant<int, (b + 2) % 3>{}) + (64 * w) * 128;
         uint32_t lq[kLookRing];
         float sc1[kTN], sc0[kTN];
 #pragma clang loop unroll(full)
         for (int m = 0; m < 128; ++m) {
             const int grp = m / 4, sub = m % 4, ks = grp / kTM, i = grp % kTM;
+            if (m == kBarrierSlot) {
+                // This wave's part of the next step's X tile (loaded during step
+                // s-1) has landed and its reads of tiles before it are done; the
+                // barrier makes that true of every wave, so the next tile can be
+                // read and the tile loaded at the start of step s+1 can reuse the
+                // buffer of step s-1. A plain s_barrier: the fence of
+                // __syncthreads would also wait for the tile loaded during step s.
+                __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterTile) & ~(0xF << 8));
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
             if (sub == 0) {
                 u32x4 &dst = af[(grp + kFragAhead) % (kFragAhead + 1)];
                 if (grp + kFragAhead < 2 * kTM)
@@ -219,12 +254,11 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
                     dst = frag(a_next, grp + kFragAhead - 2 * kTM);
             }
             if (m < 8) {
-                char *dst = xbuf + (int)((s + 2) % kXBufs) * kATile + (64 * w) * 128;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void *)(dst + m * 1024), 16, a_off[m],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void *)(x_dst + m * 1024), 16, a_off[m],
                                                          (int)(min(s + 2, steps - 1) * (kBK * 2)), 0, 0);
             } else if (m < 8 + kTN) {
                 const int j = m - 8;
-                const int64_t sl = min(s + 3, steps - 1);
+                const int64_t sl = min(s + 2, steps - 1);
                 rl.c[j] = __builtin_bit_cast(
                     uint2, __builtin_amdgcn_raw_buffer_load_b64(c_rs, c_off[j], (int)(sl * (kBK / 2)), 0));
                 if (kDQ) {
@@ -260,38 +294,29 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
     };
 
     // ---- main loop over the NF4 segment. X tiles are staged two steps ahead
-    // into 3 LDS buffers and codes three steps ahead into 4 register slots;
-    // at the end of step s only the loads issued during step s may still be
-    // in flight (X tile s+1 and the codes of s+2 have landed).
-    constexpr int kLoadsPerStep = 8 + (kDQ ? 3 : 2) * kTN;
-    Raw r0, r1, r2, r3;
-    stage_x(x_rs, 0, 0);
-    stage_x(x_rs, min((int64_t)1, steps - 1) * (kBK * 2), 1);
+    // into 3 LDS buffers and codes two steps ahead into 3 register slots; one
+    // barrier per step, at kBarrierSlot (see step). The loop is unrolled by
+    // 3 so that every buffer and slot index is a compile-time constant.
+    Raw r0, r1, r2;
+    stage_x(x_rs, 0, B0{});
+    stage_x(x_rs, min((int64_t)1, steps - 1) * (kBK * 2), B1{});
     load_w(0, r0);
     load_w(min((int64_t)1, steps - 1), r1);
-    load_w(min((int64_t)2, steps - 1), r2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // pair table, X tiles 0 and 1
 #pragma unroll
     for (int j = 0; j < kTN; ++j) b0[j] = deq8(tab, r0.c[j].x, scale(r0, j), lane4);
 #pragma unroll
-    for (int f = 0; f < kFragAhead; ++f) af[f] = frag(xbuf, f);
+    for (int f = 0; f < kFragAhead; ++f) af[f] = frag(xbuf(B0{}), f);
     valu_to_mfma();
-    auto one = [&](int64_t s, const Raw &rc, const Raw &rn, Raw &rl) {
-        step(s, rc, rn, rl);
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kLoadsPerStep));
-        __syncthreads();
-    };
     int64_t s = 0;
-    for (; s + 4 <= steps; s += 4) {
-        one(s, r0, r1, r3);
-        one(s + 1, r1, r2, r0);
-        one(s + 2, r2, r3, r1);
-        one(s + 3, r3, r0, r2);
+    for (; s + 3 <= steps; s += 3) {
+        step(s, B0{}, r0, r1, r2);
+        step(s + 1, B1{}, r1, r2, r0);
+        step(s + 2, B2{}, r2, r0, r1);
     }
-    if (s < steps) one(s++, r0, r1, r3);
-    if (s < steps) one(s++, r1, r2, r0);
-    if (s < steps) one(s++, r2, r3, r1);
+    if (s < steps) step(s++, B0{}, r0, r1, r2);
+    if (s < steps) step(s++, B1{}, r1, r2, r0);
     __builtin_amdgcn_s_waitcnt(0);  // the clamped tail loads
     __syncthreads();
 
@@ -305,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
             a_off[q] = (uint32_t)(row * p.rp * 2 + chunk * 16);
         }
         for (int64_t sa = 0; sa < p.rp / kBK; ++sa) {
-            stage_x(t_rs, sa * (kBK * 2), 0);
+            stage_x(t_rs, sa * (kBK * 2), B0{});
             // B operand of lane (lr, g), tile j, half ks: B[k][n], k = 64sa + 16g + 8ks + e
 #pragma unroll
             for (int j = 0; j < kTN; ++j) {
@@ -329,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int idx = 0; idx < 2 * kTM; ++idx) {
                 const int ks = idx / kTM, i = idx % kTM;
-                const u32x4 a = frag(xbuf, idx);
+                const u32x4 a = frag(xbuf(B0{}), idx);
 #pragma unroll
                 for (int j = 0; j < kTN; ++j) mfma(acc[i][j], a, ks ? b1[j] : b0[j]);
                 __builtin_amdgcn_sched_barrier(0);
@@ -350,12 +375,12 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
 
     // ---- epilogue: the bf16 results go through LDS so that each lane stores
     // 16 contiguous bytes. Wave w stages its 256 x 64 slice (32 KiB, rows of
-    // 128 B, 16-byte chunks XOR-swizzled by row / 4) at smem + 32 KiB * w; the
-    // table and the X tiles are dead by now. D element q of tile (i, j) is
-    // row 16i + 4g + q, column 16j + lr.
+    // 128 B, 16-byte chunks XOR-swizzled by row / 4) in the table's two
+    // halves (waves 0, 1) and X tiles 0, 1 (waves 2, 3), all dead by now. D
+    // element q of tile (i, j) is row 16i + 4g + q, column 16j + lr.
     __syncthreads();
     {
-        char *const ep = smem + w * 32768;
+        char *const ep = w < 2 ? s_tab + w * 32768 : (w == 2 ? s_x0 : s_x1);
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -384,11 +409,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
 template <bool kDQ>
 hipError_t run_fwd(const FwdParams &p, hipStream_t s) {
     const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
-    auto kern = gemm_fwd_kernel<kDQ>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    kern<<<dim3((unsigned)tiles), dim3(kThreads), kLds, s>>>(p);
+    gemm_fwd_kernel<kDQ><<<dim3((unsigned)tiles), dim3(kThreads), 0, s>>>(p);
     return hipGetLastError();
 }
 
