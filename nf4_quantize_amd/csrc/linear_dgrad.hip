@@ -44,6 +44,7 @@ static_assert(2 * kLookRing >= kLookAhead, "level reads in flight exceed the rin
 static_assert(62 + kLookAhead < 96, "the patch must be finished before it is written");
 static_assert((2 * kTM) % (kFragAhead + 1) == 0, "fragment ring must divide a step");
 // the last fragments of a step are read before the barrier, the next step's first after it
+static_assert(32 + 10 * 7 < kBarrierSlot, "all loads of a step before its barrier");
 static_assert(4 * (2 * kTM - kFragAhead) - 4 < kBarrierSlot && 4 * (2 * kTM - kFragAhead) >= kBarrierSlot,
               "fragment prefetch must straddle the barrier");
 
@@ -225,13 +226,19 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_at_most(8 * (kDQ ? 3 : 2)));
                 __syncthreads();
             }
-            if (m < 8) {
+            // loads spread over the step (the four waves run this schedule in
+            // step, so bunched loads would meet at the memory pipeline
+            // together): part q of dY tile s+1 at slot 4q + 1, then the patch
+            // row r8 of step s+2 at slot 32 + 10 r8, all before the barrier
+            if (m % 4 == 1 && m / 4 < 8) {
+                const int q = m / 4;
                 char *dst = ybuf + nxt * kATile + (64 * w) * 128;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(y_rs, (lds_void *)(dst + m * 1024), 16, a_off[m],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(y_rs, (lds_void *)(dst + q * 1024), 16, a_off[q],
                                                          (int)(min(s + 1, steps - 1) * (kBK * 2)), 0, 0);
-            } else if (m < 16) {
+            }
+            if (m >= 32 && (m - 32) % 10 == 0 && (m - 32) / 10 < 8) {
                 // patch loads of step s+2, one row per slot
-                const int r8 = m - 8;
+                const int r8 = (m - 32) / 10;
                 const int64_t j0 = min(s + 2, steps - 1) * kBK;
                 pl.c[r8] = __builtin_amdgcn_raw_buffer_load_b32(c_rs, c_off[r8], (int)(j0 * (K / 2)), 0);
                 if (kDQ) {

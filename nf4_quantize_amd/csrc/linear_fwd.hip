@@ -215,15 +215,16 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
     //    in half 1, of the next step's half-0 operands b0 (from rn): one byte
     //    per 3 slots, its level pair read from LDS 8 slots before it is
     //    scaled and rounded into the operand;
-    //  - the loads of later steps (first 20 slots).
+    //  - the loads of the step after next (spread over the step, see below).
     // X fragments in flight; the first kFragAhead of a step are read at the end
     // of the previous step (its X tile has landed by then: each step ends with
     // the wait for the next step's tile and a barrier).
     u32x4 af[kFragAhead + 1];
-    // Loads issued after step s-1's X tile load, by the barrier slot of step s:
-    // step s-1's code loads, then step s's X tile and code loads.
+    // Loads issued after the last load of step s-1 by the barrier slot of step
+    // s: all of step s's (X tile and codes are issued by slot 115).
     constexpr int kLoadsPerStep = 8 + (kDQ ? 3 : 2) * kTN;
-    constexpr int kAfterTile = 2 * kLoadsPerStep - 8;
+    constexpr int kAfterTile = kLoadsPerStep;
+    static_assert(16 * 7 + 3 < kBarrierSlot && 32 * (kTN - 1) + 1 < kBarrierSlot, "loads before the barrier");
     auto step = [&](int64_t s, auto BC, const Raw &rc, const Raw &rn, Raw &rl) {
         constexpr int b = decltype(BC)::value;  // s % 3
         const char *a_t = xbuf(std::integral_constant<int, b>{});
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
             const int grp = m / 4, sub = m % 4, ks = grp / kTM, i = grp % kTM;
             if (m == kBarrierSlot) {
                 // This wave's part of the next step's X tile (loaded during step
-                // s-1) has landed and its reads of tiles before it are done; the
+                // s-1, like everything before this step's loads) has landed and
+                // its reads of tiles before it are done; the
                 // barrier makes that true of every wave, so the next tile can be
                 // read and the tile loaded at the start of step s+1 can reuse the
                 // buffer of step s-1. A plain s_barrier: the fence of
@@ -253,11 +255,17 @@ __global__ __launch_bounds__(kThreads) void gemm_fwd_kernel(FwdParams p) {
                 else
                     dst = frag(a_next, grp + kFragAhead - 2 * kTM);
             }
-            if (m < 8) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void *)(x_dst + m * 1024), 16, a_off[m],
+            // loads spread over the step (all four waves run this schedule in
+            // step with each other, so bunched loads would meet at the memory
+            // pipeline and the LDS together): part q of the next-but-one X tile
+            // at slot 16q + 3, the codes of column tile j at slot 32j + 1
+            if (m % 16 == 3) {
+                const int q = m / 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void *)(x_dst + q * 1024), 16, a_off[q],
                                                          (int)(min(s + 2, steps - 1) * (kBK * 2)), 0, 0);
-            } else if (m < 8 + kTN) {
-                const int j = m - 8;
+            }
+            if (m % 32 == 1) {
+                const int j = m / 32;
                 const int64_t sl = min(s + 2, steps - 1);
                 rl.c[j] = __builtin_bit_cast(
                     uint2, __builtin_amdgcn_raw_buffer_load_b64(c_rs, c_off[j], (int)(sl * (kBK / 2)), 0));
