@@ -93,8 +93,8 @@ bool build_lut(CodeLut *lut) {
         if (bucket_of(lo) != (uint32_t)k || bucket_of(hi) != (uint32_t)k) return false;
         const int c_lo = nearest_by_search(lo);
         const int c_hi = nearest_by_search(hi);
-        lut->e[k].base = c_lo;
-        lut->e[k].thr = 2.0f;
+        lut->e[k].hi = c_hi;
+        lut->e[k].thr = -2.0f;
         if (c_hi != c_lo) {
             if (c_hi != c_lo + 1) return false;  // more than one switch in a bucket
             int64_t u = f2ord(lo), v = f2ord(hi);  // code(u) == c_lo, code(v) == c_lo + 1
@@ -111,9 +111,10 @@ bool build_lut(CodeLut *lut) {
         }
         start = a + 1;
     }
-    for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{2.0f, 15};
-    return lut->e[kLutUsed - 1].base == 15 && nearest_by_search(0.0f) == 7 &&
-           lut->e[bucket_of(0.0f)].base == 7;
+    for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{-2.0f, 15};
+    const LutEntry &z = lut->e[bucket_of(0.0f)];
+    return lut->e[kLutUsed - 1].hi == 15 && nearest_by_search(0.0f) == 7 &&
+           z.hi - (0.0f < z.thr ? 1 : 0) == 7;
 }
 
 }  // namespace

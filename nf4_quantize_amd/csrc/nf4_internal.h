@@ -26,8 +26,11 @@ extern const float kLevels[16];
 // low mantissa bits hold i = round(128 v + 128) and the mask keeps 8 * (i / 8),
 // the byte offset of an 8-byte table entry (bucket k = i / 8, about 1/16 wide).
 // No bucket holds more than one switch point of the code function, so
-//   code(v) = base[k] + (v >= thr[k]),
-// with thr = 2.0 in a bucket without a switch point. For |v| <= 1 + 2^-20
+//   code(v) = hi[k] - (v < thr[k]),
+// where hi[k] is the code at the top of the bucket and thr = -2.0 in a bucket
+// without a switch point (hi - 1 >= 0 wherever v < thr can hold, so a word of
+// packed hi nibbles minus the packed comparison bits never borrows across
+// nibbles). For |v| <= 1 + 2^-20
 // the bucket is 0..32; any input, NaN included, gives an offset below 512,
 // so the table has 64 entries. Built on the host from the codebook by
 // nf4::code_lut() (which buckets with this same fp32 formula) and passed to
@@ -36,7 +39,7 @@ constexpr int kLutEntries = 64;
 constexpr int kLutUsed = 33;
 struct LutEntry {
     float thr;
-    int32_t base;
+    int32_t hi;
 };
 struct CodeLut {
     LutEntry e[kLutEntries];

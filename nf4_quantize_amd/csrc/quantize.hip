@@ -9,12 +9,15 @@
 // load is one contiguous 1 KiB run. A block's absmax is a DPP max across the
 // 8 (bf16) or 16 (fp32) lanes that hold it.
 //
-// The nearest level is found without a 16-way search: n is approximated by
-// q = fl(w * fl(1/c1)) (one multiply), bucketed (one fma + convert), and the
-// code is base + (q >= thr) from a 33-entry LDS table. q differs from the
-// exact fl(w / c1) by < 1.8e-7; lanes with q within 2^-20 of a switch point
-// redo their slice with the correctly rounded division, so codes are exactly
-// those of the definition.
+// The nearest level is found without a 16-way search: n = fl(w / c1) is
+// approximated by x = w * rcp(c1), which is bucketed (one fma + mask) into a
+// 33-entry LDS table giving the bucket's switch point thr and top code hi;
+// the code is hi - (x < thr), with d = x - thr from one more fma. x differs
+// from n by < 1.5e-7; lanes with |d| < 2^-20 redo their slice with the
+// correctly rounded division, so codes are exactly those of the definition.
+// The table is held in 8 (bf16) or 4 (fp32) copies, copy e with hi shifted to
+// nibble e, so a slice's codes are the OR of its entries' hi fields minus the
+// sign bits of its d values gathered to nibble positions.
 #pragma clang fp contract(off)
 
 #include "nf4_internal.h"
@@ -24,12 +27,36 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Max over the whole workgroup of T threads; every thread gets the result.
+// Max of non-negative floats via their bit patterns (monotone as unsigned),
+// with the neighbour lane brought in by DPP (0 is the identity of the max, so
+// the move folds into the max instruction).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, true));
+}
+
+// Max over the wave of non-negative floats, returned to every lane: DPP
+// within each row of 16 lanes, then the four row results by v_readlane.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_umax<0x141>(v);  // row_half_mirror
+    v = dpp_umax<0x140>(v);  // row_mirror
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return __uint_as_float(max(a, b));
+}
+
+// Max over the whole workgroup of T threads of non-negative floats; every
+// thread gets the result.
 template <int T = kThreads>
 __device__ __forceinline__ float wg_max(float v, float *s_red) {
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    const float m = wave_max_nonneg(v);
     const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) s_red[wave] = v;
+    if ((threadIdx.x & 63) == 0) s_red[wave] = m;
     __syncthreads();
     float r = s_red[0];
 #pragma unroll
@@ -41,15 +68,13 @@ __device__ __forceinline__ float wg_max(float v, float *s_red) {
 __device__ __forceinline__ uint32_t lut_offset(float v) {
     return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f));
 }
-__device__ __forceinline__ float2 lut_entry(const float2 *s_lut, float v) {
-    return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(s_lut) + lut_offset(v));
+__device__ __forceinline__ float2 lut_at(const float2 *s_lut, uint32_t off) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(s_lut) + off);
 }
-
-// Max of non-negative floats via their bit patterns (monotone as unsigned),
-// with the neighbour lane brought in by DPP.
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-    return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, false));
+// Code of an exactly normalised value (the definition's fl32(w / c1)).
+__device__ __forceinline__ uint32_t exact_code(const float2 *s_lut, float nrm) {
+    const float2 ent = lut_at(s_lut, lut_offset(nrm));
+    return (uint32_t)__float_as_int(ent.y) - (nrm < ent.x ? 1u : 0u);
 }
 
 // Input traits: one 16-byte slice per lane.
@@ -72,46 +97,73 @@ template <> struct Slice<float> {
     }
 };
 
+// Bit 4e of the result is the sign bit of d[e] (E = 4 or 8). v_perm_b32
+// selectors 9 and 11 give a byte of copies of bit 31 of the second and the
+// first source, 12 a zero byte: each v_perm gathers two signs.
+template <int E>
+__device__ __forceinline__ uint32_t sign_nibbles(const float (&d)[E]) {
+    auto u = [&](int e) { return __float_as_uint(d[e]); };
+    if constexpr (E == 8) {
+        const uint32_t ev = __builtin_amdgcn_perm(u(2), u(0), 0x0C0C0B09u) |
+                            __builtin_amdgcn_perm(u(6), u(4), 0x0B090C0Cu);
+        const uint32_t od = __builtin_amdgcn_perm(u(3), u(1), 0x0C0C0B09u) |
+                            __builtin_amdgcn_perm(u(7), u(5), 0x0B090C0Cu);
+        return (ev & 0x01010101u) | (od & 0x10101010u);
+    } else {
+        const uint32_t ev = __builtin_amdgcn_perm(u(2), u(0), 0x0C0C0B09u);
+        const uint32_t od = __builtin_amdgcn_perm(u(3), u(1), 0x0C0C0B09u);
+        return (ev & 0x0101u) | (od & 0x1010u);
+    }
+}
+
 // Codes of one lane's slice. c1 is the block absmax (all lanes of the block
-// hold the same value). Returns the packed nibbles, element e at bits 4e.
+// hold the same value). s_lut holds E copies of the table, copy e with the
+// top code shifted to nibble e. Returns the packed nibbles, element e at
+// bits 4e.
 template <int E>
 __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, const float2 *s_lut) {
-    // rcp ~ 1/c1 from v_rcp_f32 (within 1 ulp for a normal result): then
-    // |q - fl(w/c1)| stays below 2.4e-7 for |w| <= c1, well inside kNearTol.
-    // Blocks with c1 == 0 (all zero) take rcp = 0 (q = 0 -> code 7). A c1
-    // outside [2^-125, 2^125] - whose reciprocal would overflow or fall into
-    // the subnormal range, where v_rcp_f32 is not that accurate - takes the
-    // exact path for the whole slice.
-    const bool in_range = (c1 >= 0x1p-125f) & (c1 <= 0x1p125f);
+    // rcp ~ 1/c1 from v_rcp_f32 (within 1 ulp for a normal result). With
+    // x = w * rcp as a real number, |x - fl(w/c1)| < 1.5e-7 for |w| <= c1.
+    // The bucket is that of x (one fma with 128 rcp, a power-of-two multiple)
+    // and d = fl(x - thr) (one fma). Whenever |d| >= kNearTol, x and
+    // fl(w/c1) lie on the same side of thr, and as every switch point sits
+    // at least 2^-16 inside its bucket, x's entry gives fl(w/c1)'s code.
+    // Blocks with c1 == 0 (all zero) take rcp = 0 (x = 0 -> code 7). A c1
+    // outside [2^-118, 2^125] - where 128 rcp would overflow, or rcp fall
+    // into the subnormal range where v_rcp_f32 is not that accurate - takes
+    // the exact path for the whole slice.
+    const bool in_range = (c1 >= 0x1p-118f) & (c1 <= 0x1p125f);
     const bool outside = (c1 > 0.0f) & !in_range;
     const float rcp = in_range ? __builtin_amdgcn_rcpf(c1) : 0.0f;
-    uint32_t packed = 0;
-    float dmin = __builtin_inff();
+    const float rcp128 = rcp * 128.0f;
+    uint32_t top = 0;
+    float d[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const float q = f[e] * rcp;
-        const float2 ent = lut_entry(s_lut, q);
-        const float d = q - ent.x;
-        const uint32_t code = (uint32_t)__float_as_int(ent.y) + (d >= 0.0f ? 1u : 0u);
-        dmin = fminf(dmin, fabsf(d));
-        packed |= code << (4 * e);
+        const float2 ent = lut_at(s_lut + e * kLutEntries,
+                                  lut_offset_bits(fmaf(f[e], rcp128, 128.0f + 0x1p23f)));
+        d[e] = fmaf(f[e], rcp, -ent.x);
+        top |= __float_as_uint(ent.y);
     }
+    float dmin = fabsf(d[0]);
+#pragma unroll
+    for (int e = 1; e < E; ++e) dmin = fminf(dmin, fabsf(d[e]));
+    uint32_t packed = top - sign_nibbles<E>(d);
     if (outside | !(dmin >= kNearTol)) {  // rare: redo with the correctly rounded division
         packed = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float nrm = f[e] / c1;
-            const float2 ent = lut_entry(s_lut, nrm);
-            const uint32_t code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
-            packed |= code << (4 * e);
-        }
+        for (int e = 0; e < E; ++e) packed |= exact_code(s_lut, f[e] / c1) << (4 * e);
     }
     return packed;
 }
 
+// Entry i of the table copies (copy i / kLutEntries, see slice_codes).
+__device__ __forceinline__ float2 lut_copy_entry(const LutEntry &le, int i) {
+    return make_float2(le.thr, __int_as_float(le.hi << (4 * (i / kLutEntries))));
+}
+
 __device__ __forceinline__ void load_lut(const CodeLut &lut, float2 *s_lut) {
-    if (threadIdx.x < kLutEntries)
-        s_lut[threadIdx.x] = make_float2(lut.e[threadIdx.x].thr, __int_as_float(lut.e[threadIdx.x].base));
+    if (threadIdx.x < kLutEntries) s_lut[threadIdx.x] = lut_copy_entry(lut.e[threadIdx.x], 0);
 }
 
 // Double quantization of the group's 256 c1 values held in s_c1 (threads
@@ -144,7 +196,9 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     constexpr int ITERS = SLICES / TH;         // slices per thread
     constexpr int BPI = TH / LPB;              // blocks per iteration
 
-    __shared__ float2 s_lut[kLutEntries];
+    constexpr int kTab = E * kLutEntries;       // entries of the E table copies
+    static_assert(kTab <= TH, "one table entry per thread");
+    __shared__ float2 s_lut[kTab];
     __shared__ float s_c1[kDqBlock];
     __shared__ float s_red[TH / 64];
     __shared__ uint32_t s_q8[kDqBlock / 4];
@@ -161,17 +215,17 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     typename S::Vec v[ITERS];
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * TH + t]);
-    // (every thread stores its entry; the copies are identical)
-    s_lut[t % kLutEntries] = make_float2(le.thr, __int_as_float(le.base));
+    // (threads past the table store a duplicate of an entry, unconditionally)
+    s_lut[t % kTab] = lut_copy_entry(le, t % kTab);
     __syncthreads();
 
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
         float f[E];
         S::widen(v[i], f);
-        float mf = fabsf(f[0]);
+        float mf = 0.0f;
 #pragma unroll
-        for (int e = 1; e < E; ++e) mf = fmaxf(mf, fabsf(f[e]));
+        for (int e = 0; e < E; ++e) mf = fmaxf(mf, fabsf(f[e]));
         uint32_t mb = __float_as_uint(mf);
         mb = dpp_umax<0xB1>(mb);   // quad_perm [1,0,3,2]
         mb = dpp_umax<0x4E>(mb);   // quad_perm [2,3,0,1]
@@ -223,12 +277,7 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
     for (int64_t i = lo; i < hi; i += 2) {
         uint32_t byte = 0;
         for (int j = 0; j < 2 && i + j < hi; ++j) {
-            uint32_t code = 7;
-            if (c1 > 0.0f) {
-                const float nrm = elem(i + j) / c1;
-                const float2 ent = lut_entry(s_lut, nrm);
-                code = (uint32_t)__float_as_int(ent.y) + (nrm >= ent.x ? 1u : 0u);
-            }
+            const uint32_t code = (c1 > 0.0f) ? exact_code(s_lut, elem(i + j) / c1) : 7u;
             byte |= code << (4 * j);
         }
         codes[i / 2] = (uint8_t)byte;
