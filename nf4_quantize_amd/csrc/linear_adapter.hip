@@ -1,0 +1,296 @@
+// linear_adapter.hip - the low-rank adapter's down-projection in the fused
+// QLoRA linear for gfx950: the factor s (X A) of the forward ([MF] "Forward
+// Pass Computation") and s (dY B^T) of the input gradient ([MF] "Gradient
+// Computation"; source key in nf4_internal.h):
+//   C[m x rp] = s * Aop[m x K] . Bop[rp x K]^T   (bf16 operands, fp32 sums)
+// with Bop[c][k] = A[k][c] (forward, A [K x r]) or Bop[c][k] = B[c][k]
+// (input gradient, B [r x N]); columns c >= r are zero.
+//
+// The product is thin (rp <= 256 columns) and long: it reads Aop (64 MiB at
+// 4096 x 8192) once from HBM, so it is bound by that stream. A workgroup of
+// 4 waves owns 64 rows x 64 columns and a slice of K (K is split over up to
+// kSplitMax workgroups; the fp32 partial sums are added by a second pass).
+// K advances 64 per step. Each step's Aop tile (64 rows x 128 B) goes global
+// -> LDS by direct-to-LDS loads into a ring of kStages slots, issued
+// kStages - 1 steps ahead; so does the Bop tile of the input gradient (rows
+// of B). The forward's Bop tile is a column slice of A: each thread loads two
+// 16-byte row pieces and writes their 8 column pairs (v_perm_b32) to LDS, a
+// step before use. Tiles are stored [row][64] with 16-byte chunks XOR-
+// swizzled by row. The four waves split the 64 x 64 output 2 x 2 and run
+// v_mfma_f32_16x16x32_bf16.
+#include <type_traits>
+
+#include "gemm_common.h"
+
+namespace nf4 {
+namespace {
+
+using gemm::f32x4_t;
+using gemm::lds_void;
+using gemm::Rsrc;
+using gemm::rsrc;
+using gemm::vmcnt_at_most;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kBM = 64;                 // Aop rows per workgroup
+constexpr int kBC = 64;                 // output columns per workgroup
+constexpr int kBK = 64;                 // K step
+constexpr int kStages = 4;              // LDS ring slots
+constexpr int kTile = kBM * kBK * 2;    // one tile: 64 rows x 128 B
+constexpr int kLoads = 4;               // vector-memory instructions per wave per step
+static_assert(kBC == kBM, "Aop and Bop tiles share one layout");
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+    return (uint32_t)row * 128u + 16u * (uint32_t)(chunk ^ ((row >> 1) & 7));
+}
+
+struct AdapterParams {
+    const uint16_t *a;   // Aop, row-major [m x lda]
+    int64_t lda;
+    const uint16_t *mat; // A [K x r] (forward) or B [r x ldm] (input gradient)
+    int64_t ldm;
+    int64_t m, klen, rp;
+    int32_t r;
+    int splits;
+    float *partial;      // [splits][m][rp] fp32 sums, or nullptr
+    uint16_t *c;         // [m][rp] bf16 = scale * sum when partial == nullptr
+    float scale;
+};
+
+template <bool kNN>
+__global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p) {
+    // One static object per ring slot, so that the compiler's waits for a
+    // direct-to-LDS load cover only reads of its own slot.
+    __shared__ __align__(16) char s_x0[kTile], s_x1[kTile], s_x2[kTile], s_x3[kTile];
+    __shared__ __align__(16) char s_b0[kTile], s_b1[kTile], s_b2[kTile], s_b3[kTile];
+    auto xs = [&](auto SC) -> char * {
+        constexpr int s = decltype(SC)::value;
+        if constexpr (s == 0) return s_x0;
+        else if constexpr (s == 1) return s_x1;
+        else if constexpr (s == 2) return s_x2;
+        else return s_x3;
+    };
+    auto bs = [&](auto SC) -> char * {
+        constexpr int s = decltype(SC)::value;
+        if constexpr (s == 0) return s_b0;
+        else if constexpr (s == 1) return s_b1;
+        else if constexpr (s == 2) return s_b2;
+        else return s_b3;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, g = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * kBM;
+    const int cg = blockIdx.z;  // 64-column group of C
+    const int64_t steps = p.klen / kBK;
+    const int64_t per = (steps + p.splits - 1) / p.splits;
+    const int64_t s_lo = min(steps, (int64_t)blockIdx.y * per);
+    const int n = (int)(min(steps, s_lo + per) - s_lo);
+    const int64_t m_rows = min((int64_t)kBM, p.m - m0);
+    const Rsrc none = rsrc(p.a, 0);
+
+    // Aop tile: wave w moves rows 16w .. 16w+15, 8 rows per load; lane l of
+    // load q fills row 16w + 8q + l/8, physical chunk l % 8, which holds
+    // logical chunk (l % 8) ^ ((row >> 1) & 7). Rows past m read as zeros
+    // (the row is in the range-checked lane offset, K in the scalar offset).
+    const Rsrc x_rs = rsrc(p.a + m0 * p.lda, m_rows * p.lda * 2);
+    uint32_t x_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = 16 * w + 8 * q + (lane >> 3);
+        x_off[q] = (uint32_t)(row * p.lda * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
+    }
+
+    // Bop tile, input gradient: rows c of B, moved like the Aop tile.
+    const int64_t c_rows = max((int64_t)0, min((int64_t)kBC, (int64_t)p.r - (int64_t)cg * kBC));
+    const Rsrc bt_rs = rsrc(p.mat + (int64_t)cg * kBC * p.ldm, kNN ? 0 : c_rows * p.ldm * 2);
+    uint32_t bt_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = 16 * w + 8 * q + (lane >> 3);
+        bt_off[q] = (uint32_t)(row * p.ldm * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
+    }
+
+    // Bop tile, forward: thread (kp = lane % 32, cc = 2w + lane / 32) loads
+    // A rows 2kp and 2kp + 1 of the step, columns 64 cg + 8cc .. + 7 (all
+    // valid or all past r, as r % 8 == 0).
+    // A column chunk past r takes the lane offset num_records, out of range
+    // with or without the scalar offset (the descriptor stays wave-uniform).
+    const int kp = lane & 31, cc = 2 * w + (lane >> 5);
+    const bool cc_live = (int64_t)cg * kBC + 8 * cc < p.r;
+    const int64_t bn_bytes = kNN ? p.klen * p.ldm * 2 : 0;
+    const Rsrc bn_rs = rsrc(p.mat, bn_bytes);
+    const uint32_t bn_off = cc_live ? (uint32_t)((2 * kp * p.ldm + (int64_t)cg * kBC + 8 * cc) * 2)
+                                    : (uint32_t)bn_bytes;
+    const uint32_t bn_off1 = cc_live ? bn_off + (uint32_t)(p.ldm * 2) : bn_off;
+    u32x4 braw[kStages][2];
+
+    // Loads of this workgroup's step i into ring slot SC (i % kStages): always
+    // issued, through the empty descriptor for steps past the slice.
+    auto issue = [&](int i, auto SC) {
+        const bool live = i < n;
+        const int64_t k0 = (s_lo + (live ? i : 0)) * kBK;
+        // (scalar offsets: uniform by construction, said so for the compiler)
+        const int so_k = __builtin_amdgcn_readfirstlane((int)(k0 * 2));
+        const Rsrc xr = live ? x_rs : none;
+        char *xd = xs(SC) + 16 * w * 128;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(xd + q * 1024), 16, x_off[q], so_k, 0,
+                                                     0);
+        if constexpr (!kNN) {
+            const Rsrc br = live ? bt_rs : none;
+            char *bd = bs(SC) + 16 * w * 128;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(bd + q * 1024), 16, bt_off[q], so_k,
+                                                         0, 0);
+        } else {
+            constexpr int s = decltype(SC)::value;
+            const Rsrc br = live ? bn_rs : none;
+            const int so = __builtin_amdgcn_readfirstlane((int)(k0 * p.ldm * 2));
+            braw[s][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off, so, 0));
+            braw[s][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off1, so, 0));
+        }
+    };
+    // Forward: the column pairs of the step in slot SC to its Bop tile.
+    auto write_bn = [&](auto SC) {
+        if constexpr (kNN) {
+            constexpr int s = decltype(SC)::value;
+            char *bd = bs(SC);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = braw[s][0][j >> 1], hi = braw[s][1][j >> 1];
+                const uint32_t d = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                *reinterpret_cast<uint32_t *>(bd + swz(8 * cc + j, kp >> 2) + 4 * (kp & 3)) = d;
+            }
+        }
+    };
+
+    // MFMA fragments: wave (wr, wc) owns rows 32 wr .. +31, columns 32 wc .. +31;
+    // tile row 16i + lr, logical chunk 2g + ks.
+    const int wr = w >> 1, wc = w & 1;
+    uint32_t fa[2][2], fb[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
+            fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
+        }
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Step i from slot SC; the loads of step i + kStages - 1 go to slot SI.
+    auto step = [&](int i, auto SC, auto SN, auto SI) {
+        // This wave's loads of step i have landed once at most the loads of
+        // the two later steps are outstanding; LDS writes are done too. The
+        // barrier then makes every wave's part of the tiles visible, and all
+        // waves have finished step i - 1, so its slot can be refilled.
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kStages - 2) * kLoads) & ~(0xF << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(i + kStages - 1, SI);
+        write_bn(SN);  // forward: Bop tile of step i + 1
+        if (i < n) {
+            const char *xa = xs(SC), *xb = bs(SC);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 a[2], b[2];
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
+                    b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+                }
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, a[i2]), __builtin_bit_cast(bf16x8_t, b[j]),
+                            acc[i2][j], 0, 0, 0);
+            }
+        }
+    };
+
+    issue(0, S0{});
+    issue(1, S1{});
+    issue(2, S2{});
+    write_bn(S0{});
+    for (int i = 0; i < n; i += kStages) {
+        step(i, S0{}, S1{}, S3{});
+        step(i + 1, S1{}, S2{}, S0{});
+        step(i + 2, S2{}, S3{}, S1{});
+        step(i + 3, S3{}, S0{}, S2{});
+    }
+    // no direct-to-LDS load may still be in flight when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+
+    // D row 4g + q, column lr of each 16 x 16 tile; columns from r to rp are
+    // written as zeros whatever the padding rows of the tiles held.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = (int64_t)cg * kBC + 32 * wc + 16 * j + lr;
+            const bool col_live = col < p.r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = m0 + 32 * wr + 16 * i + 4 * g + q;
+                if (row >= p.m) continue;
+                const float v = col_live ? acc[i][j][q] : 0.0f;
+                if (p.partial)
+                    p.partial[((int64_t)blockIdx.y * p.m + row) * p.rp + col] = v;
+                else
+                    p.c[row * p.rp + col] = (uint16_t)(pack_bf16x2(v * p.scale, 0.0f) & 0xFFFFu);
+            }
+        }
+}
+
+}  // namespace
+
+bool adapter_down_supported(bool nn, int64_t lda, int64_t klen, int64_t ldm, int32_t r) {
+    // 32-bit buffer offsets: a tile's 64 rows of Aop (or of B), and all of A
+    if (lda > ((int64_t)1 << 23) || klen % kBK != 0) return false;
+    if (nn) return klen * ldm * 2 < ((int64_t)1 << 31);
+    return ldm <= ((int64_t)1 << 23) && (int64_t)r * ldm * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_t m, int64_t klen,
+                               const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
+                               float *partial, uint16_t *c, float scale, hipStream_t s) {
+    AdapterParams p{};
+    p.a = aop;
+    p.lda = lda;
+    p.mat = mat;
+    p.ldm = ldm;
+    p.m = m;
+    p.klen = klen;
+    p.rp = rp;
+    p.r = r;
+    p.splits = max(1, splits);
+    p.partial = partial;
+    p.c = c;
+    p.scale = scale;
+    const dim3 grid((unsigned)((m + kBM - 1) / kBM), (unsigned)p.splits, (unsigned)(rp / kBC));
+    if (nn)
+        adapter_down_kernel<true><<<grid, kThreads, 0, s>>>(p);
+    else
+        adapter_down_kernel<false><<<grid, kThreads, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace nf4

@@ -47,6 +47,15 @@ inline size_t lora_workspace_bytes(int64_t m, int64_t rp) {
     return lora_product_bytes(m, rp) + (size_t)kSplitMax * (size_t)(m * rp) * 4u;
 }
 
+// Adapter down-projection C[m x rp] = scale * Aop . Bop^T (linear_adapter.hip):
+// Bop[c][k] = mat[k][c] (nn: A [klen x r], ldm = r) or mat[c][k] (B [r x ldm]).
+// With partial != nullptr, split z of `splits` writes its fp32 sum to
+// partial[z][m][rp] instead of c. Needs r % 8 == 0 and rp % 64 == 0.
+bool adapter_down_supported(bool nn, int64_t lda, int64_t klen, int64_t ldm, int32_t r);
+hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_t m, int64_t klen,
+                               const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
+                               float *partial, uint16_t *c, float scale, hipStream_t s);
+
 // Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
 bool gemm_supported(int64_t n, int32_t r);
 hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *a,

@@ -479,12 +479,24 @@ hipError_t lora_down(const Segment &sg, int64_t m, int64_t rp, float s_lora, uin
     int splits = (int)min((int64_t)kSplitMax, max((int64_t)1, (512 + tiles - 1) / tiles));
     splits = (int)min((int64_t)splits, max((int64_t)1, steps));
     q.splits = splits;
-    if (splits == 1) return run<64, 64, Mode, Mode>(q, s);
-    q.partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + lora_product_bytes(m, rp));
-    hipError_t e = run<64, 64, Mode, Mode>(q, s);
-    if (e != hipSuccess) return e;
+    float *const partial =
+        splits > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + lora_product_bytes(m, rp)) : nullptr;
+    // the streaming kernel of linear_adapter.hip; the generic one otherwise
+    constexpr bool kNN = (Mode == BF16_NN);
+    const int32_t r = (int32_t)(kNN ? sg.mat_cols : sg.mat_rows);
+    hipError_t e;
+    if (adapter_down_supported(kNN, sg.lda, sg.klen, sg.ldm, r)) {
+        e = launch_adapter_down(kNN, sg.a, sg.lda, m, sg.klen, sg.mat, sg.ldm, r, rp, splits, partial, ws,
+                                s_lora, s);
+        if (e != hipSuccess || splits == 1) return e;
+    } else {
+        if (splits == 1) return run<64, 64, Mode, Mode>(q, s);
+        q.partial = partial;
+        e = run<64, 64, Mode, Mode>(q, s);
+        if (e != hipSuccess) return e;
+    }
     const int64_t count = m * rp;
-    reduce_partials_kernel<<<dim3((unsigned)((count / 4 + 255) / 256)), 256, 0, s>>>(q.partial, splits, count,
+    reduce_partials_kernel<<<dim3((unsigned)((count / 4 + 255) / 256)), 256, 0, s>>>(partial, splits, count,
                                                                                      s_lora, ws);
     return hipGetLastError();
 }

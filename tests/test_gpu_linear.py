@@ -69,6 +69,12 @@ CASES = [
     (257, 2048, 512, 32),
     (70, 320, 192, 256),
     (200, 64, 64, 8),
+    # adapter down-projection split over K: slices of 3 and 6 steps (not a
+    # multiple of the 4-slot ring), empty trailing slices, and a rank that
+    # leaves the second 64-column group mostly padding
+    (64, 1344, 1408, 24),
+    (100, 640, 2880, 48),
+    (96, 1024, 1024, 72),
     # decode-shaped (no adapter): ragged column counts and odd row counts
     (3, 100, 192, 0),
     (16, 200, 320, 0),
