@@ -5,10 +5,14 @@
 // W' = dequantize(W), W stored [N x K] NF4 (64-blocks along K); the
 // contraction runs over N, the rows of W.
 //
-// Tile: a workgroup of 4 waves owns 256 rows x 256 columns of dX; wave w owns
-// all 256 rows of columns 64w .. 64w+63 as 16 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16 (accumulators in AGPRs). A step contracts 64 rows
-// of W (one NF4 block width of dX columns per row).
+// Tile: a workgroup of 4 waves owns 256 rows x 256 columns of dX; wave
+// w = 2 wr + wc owns rows 128 wr .. +127 and columns 128 wc .. +127 as 8 x 8
+// tiles of v_mfma_f32_16x16x32_bf16 (accumulators in AGPRs). A step contracts
+// 64 rows of W (one NF4 block width of dX columns per row). W' is dequantized
+// once per workgroup into an LDS tile, so the 2 x 2 split of the waves costs
+// no extra dequantization; it halves the dY operand reads (each wave reads
+// 128 rows, not 256) for twice the W' operand reads: per step the CU's LDS
+// moves 224 KiB instead of 256 KiB.
 //
 //  - dY goes global -> LDS directly (buffer_load ... lds), double buffered,
 //    like X in the forward kernel.
@@ -30,8 +34,8 @@ using namespace gemm;
 
 constexpr int kThreads = 256;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kTM = kBM / 16;              // 16 row tiles per wave
-constexpr int kTN = 64 / 16;               // 4 column tiles per wave
+constexpr int kTM = 128 / 16;             // 8 row tiles per wave
+constexpr int kTN = 128 / 16;             // 8 column tiles per wave
 constexpr int kATile = kBM * kBK * 2;      // 32 KiB of bf16 dY per step
 constexpr int kBTile = kBN * kBK * 2;      // 32 KiB of bf16 W' per step
 constexpr int kTable = 256 * 32 * 4;       // level-pair table, one copy per half-wave lane
@@ -39,14 +43,14 @@ constexpr int kLds = kTable + 2 * kATile + 2 * kBTile;  // 160 KiB
 constexpr int kFragAhead = 3;              // dY fragments read this many row groups ahead
 constexpr int kLookAhead = 16;             // MFMA slots between a level read and its use
 constexpr int kLookRing = 8;
-constexpr int kBarrierSlot = 116;
+// the first slot that reads the next step's dY tile (a row group is kTN slots)
+constexpr int kBarrierSlot = kTN * (2 * kTM - kFragAhead);
 static_assert(2 * kLookRing >= kLookAhead, "level reads in flight exceed the ring");
 static_assert(62 + kLookAhead < 96, "the patch must be finished before it is written");
 static_assert((2 * kTM) % (kFragAhead + 1) == 0, "fragment ring must divide a step");
-// the last fragments of a step are read before the barrier, the next step's first after it
-static_assert(32 + 10 * 7 < kBarrierSlot, "all loads of a step before its barrier");
-static_assert(4 * (2 * kTM - kFragAhead) - 4 < kBarrierSlot && 4 * (2 * kTM - kFragAhead) >= kBarrierSlot,
-              "fragment prefetch must straddle the barrier");
+static_assert(kTM * kTN * 2 == 128, "128 MFMA slots per step");
+static_assert(32 + 10 * 7 < kBarrierSlot && 96 < kBarrierSlot, "all loads and the W' write of a step before its barrier");
+static_assert(kBarrierSlot + kTN < 128, "next step's first W' operands read within the step");
 
 struct DgradParams {
     const uint16_t *dy;     // dY [M x N]
@@ -179,13 +183,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         }
     };
 
-    // ---- MFMA operands
+    // ---- MFMA operands: dY tile row 128 wr + 16 i + lr and W tile row
+    // 128 wc + 16 jt + lr, logical chunk 2g + ks (the swizzle of such a row is
+    // (lr >> 1) & 7)
+    const int wr = w >> 1, wc = w & 1;
     uint32_t frag_off[2], bfrag_off[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        frag_off[ks] = lr * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
-        // B: W tile row 64w + 16jt + lr (swizzle of that row: ((64w + 16jt + lr) >> 1) & 7 = (lr >> 1) & 7)
-        bfrag_off[ks] = (64 * w + lr) * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
+        frag_off[ks] = (128 * wr + lr) * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
+        bfrag_off[ks] = (128 * wc + lr) * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
     }
     auto afrag = [&](const char *a_t, int idx) {
         return *reinterpret_cast<const u32x4 *>(a_t + frag_off[idx / kTM] + (idx % kTM) * 2048);
@@ -203,7 +209,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     u32x4 af[kFragAhead + 1];
     u32x4 bq0[kTN], bq1[kTN];  // B operands of halves 0 and 1
 
-    // One step s: 128 MFMA slots (as in the forward kernel) with, around them,
+    // One step s: 128 MFMA slots (row group grp = m / 8 of dY operands, W'
+    // column tile m % 8) with, around them,
     // the dY tile s+1 DMA, the patch loads of step s+2, the dequantization,
     // transpose and LDS write of step s+1's patch (from pc), the barrier, and
     // the first operands of step s+1.
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         float sc[8];
 #pragma clang loop unroll(full)
         for (int m = 0; m < 128; ++m) {
-            const int grp = m / 4, sub = m % 4, ks = grp / kTM, i = grp % kTM;
+            const int grp = m / kTN, sub = m % kTN, ks = grp / kTM, i = grp % kTM;
             if (m == kBarrierSlot) {
                 // dY tile s+1 has landed (only this step's patch loads may be
                 // in flight), W tile s+1 is written, and every read of the
@@ -229,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
             // loads spread over the step (the four waves run this schedule in
             // step, so bunched loads would meet at the memory pipeline
             // together): part q of dY tile s+1 at slot 4q + 1, then the patch
-            // row r8 of step s+2 at slot 32 + 10 r8, all before the barrier
+            // row r8 of step s+2 at slot 32 + 10 r8, all before the barrier.
+            // The W' operands of half 1 are read at slots 16 .. 23 (used from
+            // slot 64), those of the next step's half 0 right after the barrier.
             if (m % 4 == 1 && m / 4 < 8) {
                 const int q = m / 4;
                 char *dst = ybuf + nxt * kATile + (64 * w) * 128;
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                                                          (int)(sa * (kBK * 2)), 0, 0);
 #pragma unroll
             for (int jt = 0; jt < kTN; ++jt) {
-                const int64_t c = c0 + 64 * w + 16 * jt + lr;
+                const int64_t c = c0 + 128 * wc + 16 * jt + lr;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int64_t k = 64 * sa + 16 * g + 8 * ks;
@@ -367,11 +376,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     // ---- accumulators final (see the forward kernel), then the epilogue
     mfma_drain();
 #pragma unroll
-    for (int i = 0; i < kTM; i += 2)
+    for (int i = 0; i < kTM; ++i)
         asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
-                     "+a"(acc[i + 1][0]), "+a"(acc[i + 1][1]), "+a"(acc[i + 1][2]), "+a"(acc[i + 1][3]));
+                     "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
     __syncthreads();
     {
+        // the wave's 128 x 128 bf16 block through LDS: row stride 256 B,
+        // 16-byte chunks XOR-swizzled by row, then 16-byte stores along rows
         char *const ep = smem + w * 32768;
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -380,18 +391,19 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int row = 16 * i + 4 * g + q, cc = 16 * j + lr;
-                    const int chunk = (cc >> 3) ^ ((row >> 2) & 7);
-                    *reinterpret_cast<uint16_t *>(ep + row * 128 + chunk * 16 + (cc & 7) * 2) =
+                    const int chunk = (cc >> 3) ^ ((row >> 2) & 15);
+                    *reinterpret_cast<uint16_t *>(ep + row * 256 + chunk * 16 + (cc & 7) * 2) =
                         (uint16_t)(pack_bf16x2(acc[i][j][q], 0.0f) & 0xFFFFu);
                 }
         __syncthreads();
-        const int64_t colw = c0 + 64 * w;
-        if (colw < K) {
+        const int64_t rw = m0 + 128 * wr, colw = c0 + 128 * wc;
+        const int c = lane & 15;
+        if (colw + 8 * c < K) {
 #pragma unroll 4
             for (int it = 0; it < 32; ++it) {
-                const int row = 8 * it + (lane >> 3), c = lane & 7;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * 128 + 16 * (c ^ ((row >> 2) & 7)));
-                if (m0 + row < p.M) *reinterpret_cast<u32x4 *>(p.dx + (m0 + row) * K + colw + 8 * c) = v;
+                const int row = 4 * it + (lane >> 4);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * 256 + 16 * (c ^ ((row >> 2) & 15)));
+                if (rw + row < p.M) *reinterpret_cast<u32x4 *>(p.dx + (rw + row) * K + colw + 8 * c) = v;
             }
         }
     }
