@@ -50,8 +50,11 @@ constexpr int kChunk = kBpu * kBlock;
 constexpr int kMaxNT = 8;    // column tiles per workgroup
 constexpr int kWaves = 8;    // waves per workgroup (the K split)
 constexpr int kMaxK = 32768; // longest row: its E4M3 codes for 16 kMaxNT rows fill kQ8Words
-constexpr int kQ8Words = 16 * kMaxNT * (kMaxK / kBlock) / 4 + 64;  // staged E4M3 code dwords
-constexpr int kC2Words = 16 * kMaxNT * (kMaxK / kBlock) / 256 + 2;  // staged c2 values
+// Staging areas filled by direct-to-LDS loads, which write all 64 lanes'
+// dwords (zeros past the source), so each is a whole number of 64-dword loads.
+constexpr int round64w(int n) { return (n + 63) / 64 * 64; }
+constexpr int kQ8Words = round64w(16 * kMaxNT * (kMaxK / kBlock) / 4 + 64);  // staged E4M3 code dwords
+constexpr int kC2Words = round64w(16 * kMaxNT * (kMaxK / kBlock) / 256 + 2);  // staged c2 values
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -418,19 +421,21 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
 // pairs (16 registers per piece, loaded once), and the half-block sum is
 // scaled by its c1' (one FMA). At the end of a row a wave reduction adds the
 // 64 lanes and lane 0 stores y. Requires K = P * 2048 with P <= 4 (the x
-// registers).
+// registers). With double quantization the workgroup's E4M3 codes and c2
+// values are copied to LDS once, at the start, by direct-to-LDS loads: two
+// small loads per 1 KiB piece had cost 1.5 us of the 25.5 us at
+// 28672 x 8192.
 constexpr int kWaves1 = 8;
 constexpr int kRing1 = 4;      // pieces in flight per wave
 constexpr int kPiece = 2048;   // weights per piece: one 1 KiB load instruction
 constexpr int kMaxP1 = 4;      // pieces per row (x registers: 16 per piece)
+constexpr int kQ8Stage1 = 12288;  // staged E4M3 code bytes per workgroup (the grid is sized for it)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool kDQ> struct Piece;
 template <> struct Piece<true> {
     u32x4 c;
-    uint32_t q8;  // E4M3 code of the lane's block in the low byte
-    float c2;
 };
 template <> struct Piece<false> {
     u32x4 c;
@@ -455,6 +460,11 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     static_assert(kRing1 % P == 0, "ring must hold whole rows' pieces in phase");
     __shared__ uint32_t s_lds[256 * 64];
     __shared__ float s_lv[16];
+    // with double quantization: the E4M3 codes of the workgroup's rows
+    // (contiguous in memory) and the c2 values of its groups
+    // (whole 64-dword loads: a direct-to-LDS load writes every lane's dword)
+    __shared__ uint32_t s_q8[kDQ ? round64w(kQ8Stage1 / 4) : 1];
+    __shared__ float s_c2[kDQ ? round64w(kQ8Stage1 / 256 + 2) : 1];
     const char *lds = reinterpret_cast<const char *>(s_lds);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -464,6 +474,27 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     const int64_t W = (int64_t)gridDim.x * kWaves1, gw = (int64_t)blockIdx.x * kWaves1 + wave;
     const int64_t r0 = gw * w.n / W, r1 = (gw + 1) * w.n / W;  // this wave's rows
     const int nrows = (int)(r1 - r0), npieces = nrows * P;
+    // the workgroup's rows (its waves' ranges are consecutive)
+    const int64_t wg0 = (int64_t)blockIdx.x * kWaves1;
+    const int64_t R0 = wg0 * w.n / W, R1 = (wg0 + kWaves1) * w.n / W;
+
+    // Stage the workgroup's scale data first (before any other vector-memory
+    // load, so the wait before the main loop counts only the pieces after it).
+    int64_t g0 = 0;
+    if constexpr (kDQ) {
+        g0 = R0 * nblk / 256;
+        const int64_t g1 = R1 > R0 ? (R1 * nblk - 1) / 256 : g0;
+        const uint32_t qdw = (uint32_t)((R1 - R0) * nblk / 4);  // nblk % 4 == 0 (K % 256 == 0)
+        const Rsrc qsrc = rsrc(w.q + R0 * nblk, (R1 - R0) * nblk);
+        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < qdw; p0 += 64u * kWaves1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qsrc, (gemm::lds_void *)(s_q8 + p0), 4, (p0 + lane) * 4u, 0, 0,
+                                                     0);
+        const uint32_t ng = (uint32_t)(g1 - g0 + 1);
+        const Rsrc csrc = rsrc(w.scale + g0, (int64_t)ng * 4);
+        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < ng; p0 += 64u * kWaves1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(csrc, (gemm::lds_void *)(s_c2 + p0), 4, (p0 + lane) * 4u, 0, 0,
+                                                     0);
+    }
 
     // x pairs of every piece: x[2048 p + 32 lane + 2 m], m = 0..15
     u32x4 xv[P][4];
@@ -481,17 +512,12 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     // through an empty descriptor (the wait counts then match on every path)
     const Rsrc none = rsrc(w.codes, 0);
     const Rsrc cr = rsrc(w.codes + r0 * (K / 2), (int64_t)nrows * (K / 2));
-    Rsrc qr, sr;
-    int64_t g0 = 0;
-    if constexpr (kDQ) {
-        qr = rsrc(w.q + r0 * nblk, (int64_t)nrows * nblk);
-        g0 = r0 * nblk / 256;
-        const int64_t g1 = nrows > 0 ? (r1 * nblk - 1) / 256 : g0;
-        sr = rsrc(w.scale + g0, (g1 - g0 + 1) * 4);
-    } else {
-        qr = rsrc(w.absmax + r0 * nblk, (int64_t)nrows * nblk * 4);
-    }
+    Rsrc qr = none;
+    if constexpr (!kDQ) qr = rsrc(w.absmax + r0 * nblk, (int64_t)nrows * nblk * 4);
     const uint32_t half_blk = (uint32_t)(lane >> 1);  // lane's block within a piece
+    // block index of this wave's first row, block 0: within the staged codes
+    // and counted from the first staged group
+    const uint32_t q8_0 = (uint32_t)((r0 - R0) * nblk);
     const uint32_t flat0 = (uint32_t)(r0 * nblk - g0 * 256);
 
     Piece<kDQ> ring[kRing1];
@@ -504,12 +530,8 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
         Piece<kDQ> &pc = ring[J % kRing1];
         pc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? cr : none, 16u * lane,
                                                                                (int)(1024u * (uint32_t)j), 0));
-        const uint32_t blk = row * (uint32_t)nblk + 32u * pp + half_blk;  // block, from the wave's first row
-        if constexpr (kDQ) {
-            pc.q8 = __builtin_amdgcn_raw_buffer_load_b8(live ? qr : none, blk, 0, 0);
-            pc.c2 = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(live ? sr : none, ((flat0 + blk) >> 8) * 4u, 0, 0));
-        } else {
+        if constexpr (!kDQ) {
+            const uint32_t blk = row * (uint32_t)nblk + 32u * pp + half_blk;  // block, from the wave's first row
             pc.am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(live ? qr : none, 4u * blk, 0, 0));
         }
     };
@@ -533,6 +555,10 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
         const int e = i >> 6;
         s_lds[i] = pack_bf16x2(s_lv[e & 15], s_lv[e >> 4]);
     }
+    // this wave's scale copies have landed once at most the prologue's piece
+    // loads (issued after them) are outstanding; the barrier publishes every
+    // wave's copies
+    if constexpr (kDQ) __builtin_amdgcn_s_waitcnt(gemm::vmcnt_at_most(kRing1 - 1));
     __syncthreads();
 
     float acc = 0.0f;
@@ -547,23 +573,36 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
             }
             if (j0 + J < npieces) {
                 const Piece<kDQ> &pc = ring[J % kRing1];
-                float part = 0.0f;
+                // all LDS reads of the piece first (the 16 level-pair lookups
+                // and the scale data), then the dot products on two chains
+                uint32_t q8 = 0;
+                float c2 = 0.0f;
+                if constexpr (kDQ) {
+                    const uint32_t blk = (uint32_t)((j0 + J) / P) * (uint32_t)nblk + 32u * pp + half_blk;
+                    q8 = reinterpret_cast<const uint8_t *>(s_q8)[q8_0 + blk];
+                    c2 = s_c2[(flat0 + blk) >> 8];
+                }
+                u32x4 lv4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lv4[i] = lookup4(lds, pc.c[i], lane4);
+                __builtin_amdgcn_sched_barrier(0);
+                float part[2] = {0.0f, 0.0f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const u32x4 lv4 = lookup4(lds, pc.c[i], lane4);
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         // (vector elements are copied to scalars first: a bit cast of
                         // an element expression reads element 0 with this compiler)
-                        const uint32_t lw = lv4[b], xw = xv[pp][i][b];
-                        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lw),
-                                                               __builtin_bit_cast(bf16x2_t, xw), part, false);
+                        const uint32_t lw = lv4[i][b], xw = xv[pp][i][b];
+                        part[b & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lw),
+                                                                      __builtin_bit_cast(bf16x2_t, xw), part[b & 1],
+                                                                      false);
                     }
                 }
                 float sc;
-                if constexpr (kDQ) sc = __builtin_amdgcn_cvt_f32_fp8((int)pc.q8, 0) * pc.c2;
+                if constexpr (kDQ) sc = __builtin_amdgcn_cvt_f32_fp8((int)q8, 0) * c2;
                 else sc = pc.am;
-                acc = fmaf(part, sc, acc);
+                acc = fmaf(part[0] + part[1], sc, acc);
                 if constexpr (pp == P - 1) {
                     const float sum = wave_sum(acc);
                     if (lane == 0) y[r0 + (j0 + J) / P] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
@@ -618,8 +657,14 @@ hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint1
         cus = 256;
     if (m == 1 && w.k % kPiece == 0 && w.k / kPiece <= kMaxP1 && w.k / kPiece != 3) {
         // rows split over the waves of two workgroups per CU
+        // two workgroups per CU, or more when a workgroup's E4M3 codes would
+        // not fit its staging area (the rows split evenly over all waves)
         const int p = (int)(w.k / kPiece);
-        const dim3 grid1((unsigned)std::max<int64_t>(1, std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1)));
+        const int64_t nblk = w.k / kBlock;
+        const int64_t per_row_wg = (kQ8Stage1 / nblk - 2) / kWaves1 * kWaves1;  // rows per workgroup that fit
+        int64_t g1n = std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1);
+        if (w.q) g1n = std::max<int64_t>(g1n, (w.n + per_row_wg - 1) / per_row_wg);
+        const dim3 grid1((unsigned)std::max<int64_t>(1, g1n));
         if (w.q)
             launch_gemv1<true>(p, grid1, x, w, y, s);
         else

@@ -168,6 +168,40 @@ def test_decode_gemv_sampled(dev, m, gemv_case):
     assert e <= TOL
 
 
+def test_decode_gemv_longest_rows_sampled(dev):
+    """The 16-row decode kernel at its longest rows (K = 32768) with 8 tiles of
+    16 rows per workgroup, where a workgroup's staged scale data is largest
+    (more than 256 c2 groups). The packed weight is random storage: any code
+    bytes, finite E4M3 scale codes and positive c2 values. Checked on sampled
+    output columns (including the ragged last tile) against the oracle."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K = 32768
+    N = 16 * (7 * cus + 1) + 5  # more than 7 tiles per CU: 8 per workgroup; ragged last tile
+    rng = np.random.Generator(np.random.PCG64(77))
+    codes = rng.integers(0, 256, size=N * K // 2, dtype=np.uint8)
+    nblk = N * K // 64
+    q8 = rng.integers(0x20, 0x7F, size=nblk, dtype=np.uint8)  # 0x7F would be NaN
+    scale = (rng.random((nblk + 255) // 256, dtype=np.float32) * np.float32(0.05) + np.float32(0.01))
+    log(f"gemv longest rows: N={N} K={K} ({N * K // 2} code bytes)")
+    t = nq.NF4Tensor(to_dev(codes, dev), None, to_dev(q8, dev), to_dev(scale, dev), (N, K))
+    host = dict(codes=codes, absmax=None, q=q8, scale=scale)
+    cols = np.unique(np.concatenate([rng.choice(N, 250, replace=False), np.arange(N - 6, N)]))
+    wd = oracle_wdeq(host, (N, K), rows=cols)
+    for m in (4, 16):
+        x = workloads.to_bf16_bits(rng.standard_normal((m, K), dtype=np.float32))
+        y = nq.linear_forward(to_dev(x, dev), t)
+        torch.cuda.synchronize()
+        ref = oracle.linear_forward(x, wd)
+        got = _bf16_to_f32(to_host(y))[:, cols]
+        e, nw = rel_err_metric(got, ref)
+        log(f"  M={m}: err {e:.3e} normwise {nw:.3e}")
+        assert e <= TOL
+    del t
+    torch.cuda.empty_cache()
+
+
 @pytest.fixture(scope="module")
 def gemv_case(dev):
     log("preparing 28672x8192 NF4 weight on the oracle")
