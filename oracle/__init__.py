@@ -62,6 +62,8 @@ def lib():
         for name in ("nf4ref_linear_forward", "nf4ref_linear_backward_input"):
             getattr(L, name).argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i32,
                                          ctypes.c_double, _p, _i64, _p, _i64, _p]
+        L.nf4ref_lora_grads.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _i32, ctypes.c_double,
+                                        _p, _i64, _p, _p, _i64, _p]
         _lib = L
     return _lib
 
@@ -248,3 +250,26 @@ def linear_backward_input(dy, wdeq, A=None, B=None, s=1.0, rows=None, cols=None)
                                               r, float(s), _ptr(rows), nr, _ptr(cols), nc,
                                               _ptr(out)), "linear_backward_input")
     return out
+
+
+def lora_grads(x, dy, A, B, s=1.0, a_rows=None, b_cols=None):
+    """Adapter gradients ([MF] "Gradient Computation"): dA = s X^T (dY B^T) and
+    dB = s (X A)^T dY in double. x: uint16 bf16 bits [m,K]; dy: [m,N]; A: [K,r];
+    B: [r,N]. Returns (dA [len(a_rows), r], dB [r, len(b_cols)]) as float64."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    m, K = x.shape
+    N = dy.shape[1]
+    r = A.shape[1]
+    assert dy.shape[0] == m and A.shape[0] == K and B.shape == (r, N)
+    a_rows, b_cols = _index(a_rows), _index(b_cols)
+    na = K if a_rows is None else a_rows.size
+    nb = N if b_cols is None else b_cols.size
+    da = np.zeros((na, r), np.float64)
+    db = np.zeros((r, nb), np.float64)
+    _check(lib().nf4ref_lora_grads(_ptr(x), _ptr(dy), m, K, N, _ptr(A), _ptr(B), r, float(s),
+                                   _ptr(a_rows), na, _ptr(da), _ptr(b_cols), nb, _ptr(db)),
+           "lora_grads")
+    return da, db

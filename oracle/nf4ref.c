@@ -24,6 +24,7 @@
 #include <float.h>
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 _Static_assert(FLT_EVAL_METHOD == 0, "float expressions must evaluate in binary32");
@@ -420,4 +421,73 @@ int nf4ref_linear_backward_input(const uint16_t *dy, int64_t m, int64_t K, int64
         }
     }
     return 0;
+}
+
+/* [MF] "Gradient Computation": with T = X A and U = dY B^T (m x r, exact in
+ * double), dA = s X^T U and dB = s T^T dY, each a plain sum over the m rows. */
+int nf4ref_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                      const uint16_t *A, const uint16_t *B, int32_t r, double s,
+                      const int64_t *a_rows, int64_t na, double *da, const int64_t *b_cols,
+                      int64_t nb, double *db) {
+    if (!x || !dy || !A || !B || m < 0 || K < 0 || N < 0 || r <= 0) return -1;
+    if (!a_rows) na = K;
+    if (!b_cols) nb = N;
+    double *T = (double *)calloc((size_t)(m > 0 ? m : 1) * (size_t)r, sizeof(double));
+    double *U = (double *)calloc((size_t)(m > 0 ? m : 1) * (size_t)r, sizeof(double));
+    double *acc = (double *)calloc((size_t)r, sizeof(double));
+    if (!T || !U || !acc) {
+        free(T);
+        free(U);
+        free(acc);
+        return -1;
+    }
+    for (int64_t i = 0; i < m; ++i) {
+        double *t = T + i * r;  /* T[i][c] = sum_k x[i][k] A[k][c] */
+        for (int64_t k = 0; k < K; ++k) {
+            const double xv = (double)nf4ref_bf16_to_f32(x[i * K + k]);
+            for (int32_t c = 0; c < r; ++c) t[c] += xv * (double)nf4ref_bf16_to_f32(A[k * r + c]);
+        }
+        double *u = U + i * r;  /* U[i][c] = sum_n dy[i][n] B[c][n] */
+        for (int32_t c = 0; c < r; ++c) {
+            double a = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                a += (double)nf4ref_bf16_to_f32(dy[i * N + n]) * (double)nf4ref_bf16_to_f32(B[(int64_t)c * N + n]);
+            u[c] = a;
+        }
+    }
+    int rc = 0;
+    if (da) {
+        for (int64_t j = 0; j < na && rc == 0; ++j) {
+            const int64_t k = a_rows ? a_rows[j] : j;
+            if (k < 0 || k >= K) {
+                rc = -1;
+                break;
+            }
+            for (int32_t c = 0; c < r; ++c) acc[c] = 0.0;
+            for (int64_t i = 0; i < m; ++i) {
+                const double xv = (double)nf4ref_bf16_to_f32(x[i * K + k]);
+                for (int32_t c = 0; c < r; ++c) acc[c] += xv * U[i * r + c];
+            }
+            for (int32_t c = 0; c < r; ++c) da[j * r + c] = s * acc[c];
+        }
+    }
+    if (db) {
+        for (int64_t j = 0; j < nb && rc == 0; ++j) {
+            const int64_t n = b_cols ? b_cols[j] : j;
+            if (n < 0 || n >= N) {
+                rc = -1;
+                break;
+            }
+            for (int32_t c = 0; c < r; ++c) acc[c] = 0.0;
+            for (int64_t i = 0; i < m; ++i) {
+                const double g = (double)nf4ref_bf16_to_f32(dy[i * N + n]);
+                for (int32_t c = 0; c < r; ++c) acc[c] += T[i * r + c] * g;
+            }
+            for (int32_t c = 0; c < r; ++c) db[c * nb + j] = s * acc[c];
+        }
+    }
+    free(T);
+    free(U);
+    free(acc);
+    return rc;
 }

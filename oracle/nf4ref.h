@@ -120,6 +120,19 @@ int nf4ref_linear_backward_input(const uint16_t *dy, int64_t m, int64_t K, int64
                                  int32_t r, double s, const int64_t *rows, int64_t nrows,
                                  const int64_t *cols, int64_t ncols, double *out);
 
+/* Gradients of the adapter ([MF] "Gradient Computation", the two adapter
+ * equations), in double with no intermediate rounding:
+ *   dA = s * X^T (dY B^T)     [K x r]   (the gradient of L1 = A)
+ *   dB = s * (X A)^T dY       [r x N]   (the gradient of L2 = B)
+ * x: bf16 [m x K]; dy: bf16 [m x N]; A: bf16 [K x r]; B: bf16 [r x N].
+ * a_rows (na indices into K) selects the rows of dA, b_cols (nb indices into
+ * N) the columns of dB; NULL means all. da: double [na x r] (may be NULL),
+ * db: double [r x nb] (may be NULL). Returns 0, or -1 on invalid arguments. */
+int nf4ref_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                      const uint16_t *A, const uint16_t *B, int32_t r, double s,
+                      const int64_t *a_rows, int64_t na, double *da, const int64_t *b_cols,
+                      int64_t nb, double *db);
+
 #ifdef __cplusplus
 }
 #endif
