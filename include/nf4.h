@@ -155,6 +155,30 @@ nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf4_weight
                                      float lora_scale, void *dx, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace that nf4_lora_backward needs: with rp = r rounded
+ * up to 64, the bf16 products X.A and dY.B^T ([m x rp] each, rounded up to 256
+ * bytes) followed by 8 fp32 partial sums of the largest of [m x rp], [k_in x r]
+ * and [r x n_out]. Returns 0 for invalid sizes. */
+size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, int32_t r);
+
+/* Gradients of the low-rank adapter of the same linear ([MF] "Gradient
+ * Computation", the two adapter equations; A = L1 [k_in x r], B = L2 [r x n_out]):
+ *   grad_a = lora_scale * X^T . (dY . B^T)      [k_in x r]
+ *   grad_b = lora_scale * (X . A)^T . dY        [r x n_out]
+ *   x        device bf16 [m x k_in] row-major (the forward's input)
+ *   dy       device bf16 [m x n_out] (the gradient of the forward's output)
+ *   lora_a   device bf16 [k_in x r];  lora_b  device bf16 [r x n_out]
+ *   grad_a, grad_b  device out, row-major, fp32 or bf16 (grad_dtype); either may
+ *            be NULL to skip it
+ * bf16 operands; X.A and dY.B^T are rounded to bf16, the sums over the m
+ * tokens accumulate in fp32. k_in % 64 == 0, n_out % 64 == 0, r % 8 == 0,
+ * 8 <= r <= 256. m == 0 gives zero gradients. workspace: device, 256-byte
+ * aligned, >= nf4_lora_backward_workspace_size(m, k_in, n_out, r) bytes. */
+nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k_in, int64_t n_out,
+                             const void *lora_a, const void *lora_b, int32_t r, float lora_scale,
+                             void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

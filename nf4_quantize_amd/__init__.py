@@ -44,6 +44,8 @@ EXPORTS = (
     "nf4_linear_workspace_size",
     "nf4_linear_forward",
     "nf4_linear_backward_input",
+    "nf4_lora_backward_workspace_size",
+    "nf4_lora_backward",
 )
 
 
@@ -102,6 +104,11 @@ def lib():
         fn.argtypes = [p, i64, ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p,
                        ctypes.c_size_t, p]
         fn.restype = ctypes.c_int
+    L.nf4_lora_backward_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.nf4_lora_backward_workspace_size.restype = ctypes.c_size_t
+    L.nf4_lora_backward.argtypes = [p, p, i64, i64, i64, p, p, i32, f32, p, p, ctypes.c_int, p,
+                                    ctypes.c_size_t, p]
+    L.nf4_lora_backward.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -331,5 +338,52 @@ def nf4_linear_backward_input(dy, w: NF4Tensor, lora_a=None, lora_b=None, lora_s
                    out, workspace)
 
 
+def nf4_lora_backward_workspace_size(m, k_in, n_out, r):
+    return int(lib().nf4_lora_backward_workspace_size(int(m), int(k_in), int(n_out), int(r)))
+
+
+def nf4_lora_backward(x, dy, lora_a, lora_b, lora_scale=1.0, grad_dtype=None, grad_a=True,
+                      grad_b=True, workspace=None):
+    """Adapter gradients: dA = lora_scale * X^T (dY B^T) [K x r] and
+    dB = lora_scale * (X A)^T dY [r x N]; x bf16 [m x K], dy bf16 [m x N],
+    lora_a [K x r], lora_b [r x N]. grad_a / grad_b: True (allocate), False
+    (skip) or an output tensor. Returns (dA or None, dB or None)."""
+    import torch
+
+    if grad_dtype is None:
+        grad_dtype = torch.float32
+    _need_cuda(x, dy, lora_a, lora_b, workspace)
+    for t in (x, dy, lora_a, lora_b):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("activations, gradients and adapters are bfloat16")
+    m, K = x.shape
+    N = dy.shape[1]
+    r = lora_a.shape[1]
+    dev = x.device
+
+    def out(spec, shape):
+        if spec is True:
+            return torch.empty(shape, dtype=grad_dtype, device=dev)
+        if spec is False or spec is None:
+            return None
+        _need_cuda(spec)
+        return spec
+
+    ga, gb = out(grad_a, (K, r)), out(grad_b, (r, N))
+    for g in (ga, gb):
+        if g is not None and g.dtype != grad_dtype:
+            raise TypeError("gradient outputs must have grad_dtype")
+    ws_bytes = nf4_lora_backward_workspace_size(m, K, N, r)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    st = lib().nf4_lora_backward(_ptr(x), _ptr(dy), m, K, N, _ptr(lora_a), _ptr(lora_b), r,
+                                 float(lora_scale), _ptr(ga), _ptr(gb), _dtype_code(grad_dtype),
+                                 _ptr(workspace), ws_len, _stream(dev))
+    _check(st, "nf4_lora_backward")
+    return ga, gb
+
+
 linear_forward = nf4_linear_forward
 linear_backward_input = nf4_linear_backward_input
+lora_backward = nf4_lora_backward

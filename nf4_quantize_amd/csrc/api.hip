@@ -288,3 +288,31 @@ NF4_API nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf
         static_cast<const uint16_t *>(lora_b), r, lora_scale, static_cast<uint16_t *>(dx),
         workspace, static_cast<hipStream_t>(stream)));
 }
+
+NF4_API size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, int32_t r) {
+    if (m < 0 || k_in <= 0 || n_out <= 0 || r <= 0 || r > 256) return 0;
+    return nf4::lora_grads_workspace_bytes(m, k_in, n_out, ((int64_t)r + 63) / 64 * 64, r);
+}
+
+NF4_API nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k_in, int64_t n_out,
+                                     const void *lora_a, const void *lora_b, int32_t r, float lora_scale,
+                                     void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (m < 0 || k_in <= 0 || n_out <= 0 || (k_in % 64) != 0 || (n_out % 64) != 0) return NF4_ERR_SIZE;
+    if (r <= 0 || r > 256 || (r % 8) != 0) return NF4_ERR_SIZE;
+    if (m > (int64_t(1) << 31) || m * k_in > kMaxElems || m * n_out > kMaxElems) return NF4_ERR_SIZE;
+    if (k_in * r > kMaxElems || n_out * r > kMaxElems) return NF4_ERR_SIZE;
+    if (grad_dtype != NF4_F32 && grad_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    if (!grad_a && !grad_b) return NF4_OK;
+    if (!lora_a || !lora_b || (m > 0 && (!x || !dy))) return NF4_ERR_NULL;
+    if ((x && !aligned(x, 16)) || (dy && !aligned(dy, 16)) || !aligned(lora_a, 16) || !aligned(lora_b, 16) ||
+        (grad_a && !aligned(grad_a, 16)) || (grad_b && !aligned(grad_b, 16)))
+        return NF4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nf4_lora_backward_workspace_size(m, k_in, n_out, r))
+        return NF4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return NF4_ERR_ALIGN;
+    return launch_status(nf4::launch_lora_grads(
+        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dy), m, k_in, n_out,
+        static_cast<const uint16_t *>(lora_a), static_cast<const uint16_t *>(lora_b), r, lora_scale, grad_a,
+        grad_b, grad_dtype == NF4_F32, workspace, static_cast<hipStream_t>(stream)));
+}

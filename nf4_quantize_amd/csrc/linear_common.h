@@ -2,6 +2,8 @@
 // linear kernels (internal).
 #pragma once
 
+#include <algorithm>
+
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -64,6 +66,17 @@ hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w
 hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w, const uint16_t *a,
                              const uint16_t *b, int32_t r, float s_lora, uint16_t *dx,
                              uint16_t *u_ws, hipStream_t s);
+
+// Adapter gradients dA = s X^T (dY B^T) [K x r] and dB = s (X A)^T dY [r x N]
+// (linear_gemm.hip); da or db may be nullptr. Needs K % 64 == 0, N % 64 == 0,
+// r % 8 == 0, r <= 256, and a workspace of lora_grads_workspace_bytes.
+inline size_t lora_grads_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t rp, int64_t r) {
+    const int64_t most = std::max(m * rp, std::max(k * r, r * n));
+    return 2 * lora_product_bytes(m, rp) + (size_t)kSplitMax * (size_t)most * 4u;
+}
+hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                             const uint16_t *a, const uint16_t *b, int32_t r, float s_lora, void *da, void *db,
+                             bool f32_out, void *ws, hipStream_t s);
 
 // Main forward GEMM of the large-M path (linear_fwd.hip): Y = X . W'^T, plus
 // T' . B when t != nullptr (T' bf16 [m x rp]). Needs K <= 2^22.

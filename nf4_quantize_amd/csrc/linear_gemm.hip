@@ -26,6 +26,7 @@
 // does it: bf16(q[code] * c1'). The next K-step's global loads are issued
 // before the current step's MFMAs; LDS is double buffered.
 #include <algorithm>
+#include <type_traits>
 
 #include "linear_common.h"
 
@@ -50,9 +51,10 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
 
 // One K-segment: C += Aop . Bop^T over ksteps of 64.
 struct Segment {
-    const uint16_t *a;   // Aop, row-major [M x lda]
+    const uint16_t *a;   // Aop, row-major [M x lda] (transposed A: [a_krows x lda], Aop[i][k] = a[k][i])
     int64_t lda;
     int64_t klen;        // contraction length of the segment (multiple of 64)
+    int64_t a_krows;     // transposed A: rows of a (contraction values past it read as zero)
     // B source
     WView w;             // NF4 modes
     const uint16_t *mat; // bf16 modes
@@ -116,6 +118,41 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
         }
         out[j] = u32x4{d[0], d[1], d[2], d[3]};
     }
+}
+
+// A tile read across rows: Aop[i][k] = a[k][i] for BM rows i and 64
+// contraction values k (the token sums of the adapter gradients). Thread t
+// owns an 8 (k) x 8 (i) patch, loaded as 8 row pieces and transposed in
+// registers; needs M % 8 == 0 and lda % 8 == 0.
+template <int BM>
+struct AStageT {
+    static constexpr int kPatches = BM * kBK / 64;  // threads beyond this idle
+    static_assert(kPatches <= kThreads, "at most one 8x8 patch per thread");
+    u32x4 r[8];
+    __device__ void load(const Segment &sg, int64_t m0, int64_t M, int64_t k0) {
+        const int t = threadIdx.x;
+        if (t >= kPatches) return;
+        const int kp = t & 7, ip = t >> 3;
+        const int64_t i = m0 + ip * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = k0 + kp * 8 + e;
+            r[e] = u32x4{0, 0, 0, 0};
+            if (k < sg.a_krows && i < M) r[e] = *reinterpret_cast<const u32x4 *>(sg.a + k * sg.lda + i);
+        }
+    }
+    __device__ void store(char *lds) const;
+};
+
+template <int BM>
+__device__ void AStageT<BM>::store(char *lds) const {
+    const int t = threadIdx.x;
+    if (t >= kPatches) return;
+    const int kp = t & 7, ip = t >> 3;
+    u32x4 cols[8];
+    transpose8x8(r, cols);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(lds + swz(ip * 8 + j, kp)) = cols[j];
 }
 
 // B tile, NF4 read along K (forward): BN weight rows x one 64-block.
@@ -294,7 +331,7 @@ __device__ __forceinline__ void tile_coords(int64_t wg, int64_t tm, int64_t tn, 
     nt = group * gn + within % ncols;
 }
 
-template <int BM, int BN, int Mode0, int Mode1>
+template <int BM, int BN, int Mode0, int Mode1, bool kAT = false>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
     constexpr int TM = WM / 16, TN = WN / 16; // 16x16 MFMA tiles per wave
@@ -327,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 
     using B0 = typename BStageOf<Mode0, BN>::T;
     using B1 = typename BStageOf<Mode1, BN>::T;
-    AStage<BM> ra;
+    std::conditional_t<kAT, AStageT<BM>, AStage<BM>> ra;
     B0 rb0;
     B1 rb1;
 
@@ -406,13 +443,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
         }
 }
 
-template <int BM, int BN, int Mode0, int Mode1>
+template <int BM, int BN, int Mode0, int Mode1, bool kAT = false>
 hipError_t run(const Params &p_in, hipStream_t s) {
     Params p = p_in;
     p.splits = max(1, p.splits);
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.Nc + BN - 1) / BN);
     const size_t lds = 2 * (size_t)(BM + BN) * kRowBytes + 64;
-    auto kern = gemm_kernel<BM, BN, Mode0, Mode1>;
+    auto kern = gemm_kernel<BM, BN, Mode0, Mode1, kAT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -444,19 +481,23 @@ Segment bf16_segment(const uint16_t *a, int64_t lda, int64_t klen, const uint16_
 
 int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 
-// out[i] = bf16(scale * sum over z of part[z * count + i]), 4 elements per
-// thread (count is a multiple of 64).
+// out[i] = scale * sum over z of part[z * count + i], rounded to bf16 or kept
+// fp32, 4 elements per thread (count is a multiple of 4).
+template <bool kF32 = false>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ part, int splits,
-                                                              int64_t count, float scale,
-                                                              uint16_t *__restrict__ out) {
+                                                              int64_t count, float scale, void *__restrict__ out) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= count) return;
     f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
     for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4 *>(part + z * count + i);
-    uint2 o;
-    o.x = pack_bf16x2(scale * acc[0], scale * acc[1]);
-    o.y = pack_bf16x2(scale * acc[2], scale * acc[3]);
-    *reinterpret_cast<uint2 *>(out + i) = o;
+    if constexpr (kF32) {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + i) = acc * scale;
+    } else {
+        uint2 o;
+        o.x = pack_bf16x2(scale * acc[0], scale * acc[1]);
+        o.y = pack_bf16x2(scale * acc[2], scale * acc[3]);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + i) = o;
+    }
 }
 
 // Adapter down-projection C[m x rp] = s * Aop . Bop^T (bf16) into the start of
@@ -465,7 +506,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
 // workspace after C and one more pass adds, scales and rounds them.
 template <int Mode>
 hipError_t lora_down(const Segment &sg, int64_t m, int64_t rp, float s_lora, uint16_t *ws, const Levels &lv,
-                     hipStream_t s) {
+                     hipStream_t s, float *partial_area = nullptr) {
     Params q{};
     q.lv = lv;
     q.seg[0] = sg;
@@ -479,8 +520,8 @@ hipError_t lora_down(const Segment &sg, int64_t m, int64_t rp, float s_lora, uin
     int splits = (int)min((int64_t)kSplitMax, max((int64_t)1, (512 + tiles - 1) / tiles));
     splits = (int)min((int64_t)splits, max((int64_t)1, steps));
     q.splits = splits;
-    float *const partial =
-        splits > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + lora_product_bytes(m, rp)) : nullptr;
+    if (!partial_area) partial_area = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + lora_product_bytes(m, rp));
+    float *const partial = splits > 1 ? partial_area : nullptr;
     // the streaming kernel of linear_adapter.hip; the generic one otherwise
     constexpr bool kNN = (Mode == BF16_NN);
     const int32_t r = (int32_t)(kNN ? sg.mat_cols : sg.mat_rows);
@@ -565,6 +606,77 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &wt
     p.ldc = K;
     p.out_scale = 1.0f;
     return run<256, 256, NF4_NN, BF16_NT>(p, s);
+}
+
+// Adapter gradients ([MF] "Gradient Computation"): T = X.A and U = dY.B^T
+// (bf16, unscaled) by the down-projection, then two token sums on the generic
+// kernel with a transposed A tile:
+//   dA = s X^T U   [K x r]: Aop[k][i] = X[i][k], Bop[c][i] = U[i][c]
+//   dB = s T^T dY  [r x N]: Aop[c][i] = T[i][c], Bop[n][i] = dY[i][n]
+// Each token sum is split over up to kSplitMax workgroups per tile; its fp32
+// partial sums are added, scaled by s and stored (bf16 or fp32) by one more
+// pass. Workspace: T, U (lora_product_bytes each), then the partial sums.
+hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
+                             const uint16_t *a, const uint16_t *b, int32_t r, float s_lora, void *da, void *db,
+                             bool f32_out, void *ws, hipStream_t s) {
+    const int64_t rp = round64(r);
+    char *const base = static_cast<char *>(ws);
+    uint16_t *const T = reinterpret_cast<uint16_t *>(base);
+    uint16_t *const U = reinterpret_cast<uint16_t *>(base + lora_product_bytes(m, rp));
+    float *const part = reinterpret_cast<float *>(base + 2 * lora_product_bytes(m, rp));
+    const Levels lv = levels();
+    hipError_t e = hipSuccess;
+    if (m > 0) {
+        if (db) {
+            e = lora_down<BF16_NN>(bf16_segment(x, K, K, a, r, K, r), m, rp, 1.0f, T, lv, s, part);
+            if (e != hipSuccess) return e;
+        }
+        if (da) {
+            e = lora_down<BF16_NT>(bf16_segment(dy, N, N, b, N, r, N), m, rp, 1.0f, U, lv, s, part);
+            if (e != hipSuccess) return e;
+        }
+    }
+    const int64_t mk = round64(m);  // token steps of 64 (tokens past m read as zero)
+    auto token_sum = [&](const uint16_t *at, int64_t lda, int64_t rows, const uint16_t *mat, int64_t ldm,
+                         int64_t cols, void *out) -> hipError_t {
+        Params q{};
+        q.lv = lv;
+        Segment sg{};
+        sg.a = at;
+        sg.lda = lda;
+        sg.klen = mk;
+        sg.a_krows = m;
+        sg.mat = mat;
+        sg.ldm = ldm;
+        sg.mat_rows = m;
+        sg.mat_cols = cols;
+        q.seg[0] = sg;
+        q.nseg = 1;
+        q.M = rows;
+        q.Nc = cols;
+        q.ldc = cols;
+        q.out_scale = s_lora;
+        const int64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64), steps = mk / kBK;
+        int splits = (int)min((int64_t)kSplitMax, max((int64_t)1, (512 + tiles - 1) / tiles));
+        splits = (int)min((int64_t)splits, max((int64_t)1, steps));
+        q.splits = splits;
+        q.partial = part;
+        hipError_t e2 = run<64, 64, BF16_NN, BF16_NN, true>(q, s);
+        if (e2 != hipSuccess) return e2;
+        const int64_t count = rows * cols;
+        const dim3 grid((unsigned)((count / 4 + 255) / 256));
+        if (f32_out)
+            reduce_partials_kernel<true><<<grid, 256, 0, s>>>(part, splits, count, s_lora, out);
+        else
+            reduce_partials_kernel<false><<<grid, 256, 0, s>>>(part, splits, count, s_lora, out);
+        return hipGetLastError();
+    };
+    if (da) {
+        e = token_sum(x, K, K, U, rp, r, da);
+        if (e != hipSuccess) return e;
+    }
+    if (db) e = token_sum(T, rp, r, dy, N, N, db);
+    return e;
 }
 
 }  // namespace nf4

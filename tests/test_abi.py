@@ -160,3 +160,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(nq, "_lib", None)
     with pytest.raises(nq.NF4LibraryMissing):
         nq.lib()
+
+
+def test_lora_backward_validation(L):
+    f = L.nf4_lora_backward
+    ws = nq.nf4_lora_backward_workspace_size(64, 512, 256, 16)
+    # X.A and dY.B^T as bf16 [64 x 64], then 8 fp32 partial sums of the largest
+    # of [64 x 64], [512 x 16] and [16 x 256]
+    assert ws == 2 * 64 * 64 * 2 + 8 * 64 * 128 * 4
+    assert nq.nf4_lora_backward_workspace_size(64, 512, 256, 0) == 0
+    assert nq.nf4_lora_backward_workspace_size(-1, 512, 256, 16) == 0
+
+    def call(x=FAKE, dy=FAKE, m=64, k=512, n=256, a=FAKE, b=FAKE, r=16, ga=FAKE, gb=FAKE, dt=0,
+             wsp=FAKE, wsb=ws):
+        return f(x, dy, m, k, n, a, b, r, 2.0, ga, gb, dt, wsp, wsb, None)
+
+    assert call(m=-1) == 2
+    assert call(k=100) == 2  # k_in % 64 != 0
+    assert call(n=96) == 2   # n_out % 64 != 0
+    assert call(r=12) == 2   # r % 8 != 0
+    assert call(r=264) == 2
+    assert call(r=0) == 2
+    assert call(dt=7) == 3
+    assert call(ga=None, gb=None) == 0  # nothing asked: OK, nothing launched
+    assert call(x=None) == 1
+    assert call(dy=None) == 1
+    assert call(a=None) == 1
+    assert call(b=None) == 1
+    assert call(x=FAKE + 2) == 4
+    assert call(gb=FAKE + 4) == 4
+    assert call(wsp=None) == 5
+    assert call(wsb=ws - 1) == 5
+    assert call(wsp=FAKE + 16) == 4  # the workspace is 256-byte aligned
