@@ -12,8 +12,9 @@ Printed: one JSON line with the contract fields, plus
   cpu_baseline  the CPU oracle on the same workload (single thread)
   kernels       every kernel of the path measured alone: quantize and
                 dequantize on the 1024x1024 fp32 and 11008x4096 bf16 weights,
-                the decode GEMV (M = 1, 4, 16 on 28672 x 8192) and the QLoRA
-                linear forward / input gradient (4096 x 8192 x 8192, r = 64).
+                the decode GEMV (M = 1, 4, 16 on 28672 x 8192), the QLoRA
+                linear forward / input gradient (4096 x 8192 x 8192, r = 64)
+                and the adapter gradients at that shape.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-kernels]
                        [--no-cpu-baseline] [--stack]
@@ -346,6 +347,20 @@ def kernel_benches(dev, iters, warmup, with_stack):
     out["linear_dgrad_4096x8192x8192_r64"] = {"ms": ms, "p10_p50_p90_ms": pc, "TFLOP/s": flops / ms / 1e9,
                                               "mfma_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
     log(f"linear dgrad: {out['linear_dgrad_4096x8192x8192_r64']}")
+    # adapter gradients (fp32 out): bound by reading X and dY; the algorithmic
+    # bytes read each of X, dY, A, B once and write dA and dB once
+    gA = torch.empty((K, r), dtype=torch.float32, device=dev)
+    gB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    lws = torch.empty(nq.nf4_lora_backward_workspace_size(M, K, N, r), dtype=torch.uint8, device=dev)
+    ms, pc = time_op(lambda i: nq.lora_backward(X, dY, A, B, s, grad_a=gA, grad_b=gB, workspace=lws),
+                     lin_iters, max(1, warmup // 2))
+    lbytes = 2 * (M * K + M * N + K * r + r * N) + 4 * (K * r + r * N)
+    lflops = 4 * M * r * (K + N)  # X.A, dY.B^T, X^T.U, T^T.dY
+    out["lora_backward_4096x8192x8192_r64"] = {"ms": ms, "p10_p50_p90_ms": pc, "GB/s": lbytes / ms / 1e6,
+                                               "hbm_frac": lbytes / ms / 1e6 / HBM_PEAK_GBS,
+                                               "GFLOP/s": lflops / ms / 1e6, "bytes": lbytes}
+    log(f"lora backward: {out['lora_backward_4096x8192x8192_r64']}")
+    del gA, gB, lws
     # practical ceiling: the vendor bf16 GEMM on a pre-dequantized weight
     Wd = nq.dequantize(wt, torch.bfloat16)
     ms, pc = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))

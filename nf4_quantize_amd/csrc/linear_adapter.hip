@@ -119,12 +119,13 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p)
         bt_off[q] = (uint32_t)(row * p.ldm * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
     }
 
-    // Bop tile, forward: thread (kp = lane % 32, cc = 2w + lane / 32) loads
-    // A rows 2kp and 2kp + 1 of the step, columns 64 cg + 8cc .. + 7 (all
-    // valid or all past r, as r % 8 == 0).
-    // A column chunk past r takes the lane offset num_records, out of range
-    // with or without the scalar offset (the descriptor stays wave-uniform).
-    const int kp = lane & 31, cc = 2 * w + (lane >> 5);
+    // Bop tile, forward: thread (kp = 8w + lane / 8, cc = lane % 8) loads A
+    // rows 2kp and 2kp + 1 of the step, columns 64 cg + 8cc .. + 7 (all
+    // valid or all past r, as r % 8 == 0); each octet of lanes reads one
+    // row's 128 contiguous bytes. A column chunk past r takes the lane offset
+    // num_records, out of range with or without the scalar offset (the
+    // descriptor stays wave-uniform).
+    const int kp = 8 * w + (lane >> 3), cc = lane & 7;
     const bool cc_live = (int64_t)cg * kBC + 8 * cc < p.r;
     const int64_t bn_bytes = kNN ? p.klen * p.ldm * 2 : 0;
     const Rsrc bn_rs = rsrc(p.mat, bn_bytes);
@@ -260,7 +261,210 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p)
         }
 }
 
+// ---- token sums of the adapter gradients ([MF] "Gradient Computation"):
+//   C[o][j] = sum over tokens t of P[t][o] * Q[t][j]
+// with P = X, Q = dY.B^T (dA = s X^T (dY B^T), C = dA, [O x r]) or P = dY,
+// Q = X.A (dB = s (X A)^T dY, C^T = dB, [r x O]). Both operands have the
+// tokens as rows, so both are transposed on the way into LDS: each thread
+// loads two token rows of 8 columns of P and of Q and writes their 8 column
+// pairs. A workgroup of 4 waves owns 64 x 64 of C and a slice of the tokens;
+// loads run 3 steps of 64 tokens ahead through a register ring, and the LDS
+// tiles of a step are written one step before use.
+struct TokenSumParams {
+    const uint16_t *p;  // [m x O] row-major
+    const uint16_t *q;  // [m x rp] row-major
+    int64_t m, O, rp;
+    int32_t r;
+    int splits;
+    float *partial;     // [splits][O][r] (or [splits][r][O] when transposed), or nullptr
+    void *out;          // final C (splits == 1): fp32 or bf16, [O x r] or [r x O]
+    bool f32, transposed;
+    float scale;
+};
+
+__global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p) {
+    __shared__ __align__(16) char s_p0[kTile], s_p1[kTile], s_q0[kTile], s_q1[kTile];
+    auto ps = [&](auto SC) -> char * {
+        if constexpr (decltype(SC)::value == 0) return s_p0;
+        else return s_p1;
+    };
+    auto qs = [&](auto SC) -> char * {
+        if constexpr (decltype(SC)::value == 0) return s_q0;
+        else return s_q1;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, g = lane >> 4;
+    const int64_t o0 = (int64_t)blockIdx.x * kBM;
+    const int cg = blockIdx.z;
+    const int64_t steps = (p.m + kBK - 1) / kBK;
+    const int64_t per = (steps + p.splits - 1) / p.splits;
+    const int64_t s_lo = min(steps, (int64_t)blockIdx.y * per);
+    const int n = (int)(min(steps, s_lo + per) - s_lo);
+    const Rsrc none = rsrc(p.p, 0);
+
+    // thread (kp, cc): token rows 2kp and 2kp + 1 of the step, columns
+    // 8cc .. 8cc + 7 of the tile (of P: o0 + 8cc; of Q: 64 cg + 8cc, which
+    // are all valid or all past r as r % 8 == 0: past r the lane offset is
+    // pushed out of the descriptor's range). Each octet of lanes reads one
+    // row's 128 contiguous bytes, so a load instruction covers 8 rows x 128 B.
+    const int kp = 8 * w + (lane >> 3), cc = lane & 7;
+    const bool q_live = (int64_t)cg * kBC + 8 * cc < p.r;
+    const uint32_t p_off = (uint32_t)((2 * kp * p.O + o0 + 8 * cc) * 2);
+    const uint32_t q_off = q_live ? (uint32_t)((2 * kp * p.rp + (int64_t)cg * kBC + 8 * cc) * 2) : 0xFFFFFFF0u;
+    u32x4 raw[4][4];  // [ring slot][P row 0, P row 1, Q row 0, Q row 1]
+
+    // Loads of step i (ring slot SC): descriptors start at the step's first
+    // token and end at token m, so tokens past m read as zeros.
+    auto issue = [&](int i, auto SC) {
+        constexpr int sl = decltype(SC)::value;
+        const bool live = i < n;
+        const int64_t tok0 = (s_lo + (live ? i : 0)) * kBK;
+        const int64_t rows = live ? min((int64_t)kBK, p.m - tok0) : 0;
+        const Rsrc pr = live ? rsrc(p.p + tok0 * p.O, rows * p.O * 2) : none;
+        const Rsrc qr = live ? rsrc(p.q + tok0 * p.rp, rows * p.rp * 2) : none;
+        raw[sl][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off, 0, 0));
+        raw[sl][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off + (uint32_t)(p.O * 2), 0, 0));
+        raw[sl][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_off, 0, 0));
+        raw[sl][3] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_live ? q_off + (uint32_t)(p.rp * 2) : q_off, 0, 0));
+    };
+    // The column pairs of ring slot SR to LDS slot SL ([column][token] tiles).
+    auto write = [&](auto SR, auto SL) {
+        constexpr int sl = decltype(SR)::value;
+        char *pd = ps(SL), *qd = qs(SL);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t off = swz(8 * cc + j, kp >> 2) + 4 * (kp & 3);
+            const uint32_t a0 = raw[sl][0][j >> 1], a1 = raw[sl][1][j >> 1];
+            const uint32_t b0 = raw[sl][2][j >> 1], b1 = raw[sl][3][j >> 1];
+            *reinterpret_cast<uint32_t *>(pd + off) = __builtin_amdgcn_perm(a1, a0, sel);
+            *reinterpret_cast<uint32_t *>(qd + off) = __builtin_amdgcn_perm(b1, b0, sel);
+        }
+    };
+
+    const int wr = w >> 1, wc = w & 1;
+    uint32_t fa[2][2], fb[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
+            fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
+        }
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Step i: the tiles of step i are in LDS slot i & 1 (written last step);
+    // issue the loads of step i + 3 into ring slot SI, write step i + 1's
+    // tiles (ring slot SN) to the other LDS slot, then the MFMAs.
+    auto step = [&](int i, auto SC, auto SN, auto SI, auto LC, auto LN) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile writes are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(i + 3, SI);
+        write(SN, LN);
+        if (i < n) {
+            const char *xa = ps(LC), *xb = qs(LC);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 a[2], b[2];
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
+                    b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+                }
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, a[i2]), __builtin_bit_cast(bf16x8_t, b[j]),
+                            acc[i2][j], 0, 0, 0);
+            }
+        }
+        (void)SC;
+    };
+
+    issue(0, S0{});
+    issue(1, S1{});
+    issue(2, S2{});
+    write(S0{}, S0{});
+    for (int i = 0; i < n; i += 4) {
+        step(i, S0{}, S1{}, S3{}, S0{}, S1{});
+        step(i + 1, S1{}, S2{}, S0{}, S1{}, S0{});
+        step(i + 2, S2{}, S3{}, S1{}, S0{}, S1{});
+        step(i + 3, S3{}, S0{}, S2{}, S1{}, S0{});
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // the loads of steps past the slice
+
+    // D row 4g + q (o), column lr (j) of each 16 x 16 tile; columns past r
+    // are not stored
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int64_t j = (int64_t)cg * kBC + 32 * wc + 16 * jt + lr;
+            const int64_t o = o0 + 32 * wr + 16 * i + 4 * g;
+            if (j >= p.r) continue;
+            const f32x4_t v = acc[i][jt];
+            if (p.partial) {
+                float *dst = p.partial + (int64_t)blockIdx.y * p.O * p.r;
+                if (p.transposed) {
+                    *reinterpret_cast<f32x4_t *>(dst + j * p.O + o) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dst[(o + q) * p.r + j] = v[q];
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t idx = p.transposed ? j * p.O + o + q : (o + q) * p.r + j;
+                    const float x = v[q] * p.scale;
+                    if (p.f32) static_cast<float *>(p.out)[idx] = x;
+                    else static_cast<uint16_t *>(p.out)[idx] = (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+                }
+            }
+        }
+}
+
 }  // namespace
+
+bool token_sum_supported(int64_t m, int64_t O, int64_t rp) {
+    // 32-bit buffer offsets within one step's 64 token rows
+    return O % kBM == 0 && 64 * O * 2 < ((int64_t)1 << 31) && 64 * rp * 2 < ((int64_t)1 << 31) && m >= 0;
+}
+
+hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
+                            int splits, float *partial, void *out, bool f32, bool transposed, float scale,
+                            hipStream_t s) {
+    TokenSumParams p{};
+    p.p = pm;
+    p.q = qm;
+    p.m = m;
+    p.O = O;
+    p.rp = rp;
+    p.r = r;
+    p.splits = max(1, splits);
+    p.partial = partial;
+    p.out = out;
+    p.f32 = f32;
+    p.transposed = transposed;
+    p.scale = scale;
+    const dim3 grid((unsigned)(O / kBM), (unsigned)p.splits, (unsigned)(rp / kBC));
+    token_sum_kernel<<<grid, kThreads, 0, s>>>(p);
+    return hipGetLastError();
+}
 
 bool adapter_down_supported(bool nn, int64_t lda, int64_t klen, int64_t ldm, int32_t r) {
     // 32-bit buffer offsets: a tile's 64 rows of Aop (or of B), and all of A

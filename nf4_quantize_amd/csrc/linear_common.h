@@ -58,6 +58,17 @@ hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_
                                const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
                                float *partial, uint16_t *c, float scale, hipStream_t s);
 
+// Token sums of the adapter gradients (linear_adapter.hip): C[o][j] =
+// sum over the m tokens of P[t][o] * Q[t][j], P [m x O] (O % 64 == 0),
+// Q [m x rp] bf16 (columns past r unused). With partial != nullptr split z of
+// `splits` writes its fp32 sum to partial[z] ([O x r], or [r x O] when
+// transposed); otherwise scale * C goes to out (fp32 or bf16, [O x r] or
+// [r x O]).
+bool token_sum_supported(int64_t m, int64_t O, int64_t rp);
+hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
+                            int splits, float *partial, void *out, bool f32, bool transposed, float scale,
+                            hipStream_t s);
+
 // Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
 bool gemm_supported(int64_t n, int32_t r);
 hipError_t launch_gemm_forward(const uint16_t *x, int64_t m, const nf4_weight &w, const uint16_t *a,

@@ -637,6 +637,24 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         }
     }
     const int64_t mk = round64(m);  // token steps of 64 (tokens past m read as zero)
+    // the streaming kernel of linear_adapter.hip: C[o][j] = sum_t P[t][o] Q[t][j]
+    auto stream_sum = [&](const uint16_t *pm, int64_t O, const uint16_t *qm, bool transposed,
+                          void *out) -> hipError_t {
+        const int64_t tiles = (O / 64) * (rp / 64), steps = mk / kBK;
+        int splits = (int)min((int64_t)kSplitMax, max((int64_t)1, (1024 + tiles - 1) / tiles));
+        splits = (int)min((int64_t)splits, max((int64_t)1, steps));
+        hipError_t e2 = launch_token_sum(pm, qm, m, O, rp, r, splits, splits > 1 ? part : nullptr, out, f32_out,
+                                         transposed, s_lora, s);
+        if (e2 != hipSuccess || splits == 1) return e2;
+        const int64_t count = O * (int64_t)r;
+        const dim3 grid((unsigned)((count / 4 + 255) / 256));
+        if (f32_out)
+            reduce_partials_kernel<true><<<grid, 256, 0, s>>>(part, splits, count, s_lora, out);
+        else
+            reduce_partials_kernel<false><<<grid, 256, 0, s>>>(part, splits, count, s_lora, out);
+        return hipGetLastError();
+    };
+    // the generic kernel with a transposed A tile otherwise
     auto token_sum = [&](const uint16_t *at, int64_t lda, int64_t rows, const uint16_t *mat, int64_t ldm,
                          int64_t cols, void *out) -> hipError_t {
         Params q{};
@@ -672,10 +690,10 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         return hipGetLastError();
     };
     if (da) {
-        e = token_sum(x, K, K, U, rp, r, da);
+        e = token_sum_supported(m, K, rp) ? stream_sum(x, K, U, false, da) : token_sum(x, K, K, U, rp, r, da);
         if (e != hipSuccess) return e;
     }
-    if (db) e = token_sum(T, rp, r, dy, N, N, db);
+    if (db) e = token_sum_supported(m, N, rp) ? stream_sum(dy, N, T, true, db) : token_sum(T, rp, r, dy, N, N, db);
     return e;
 }
 
