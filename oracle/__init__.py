@@ -62,6 +62,20 @@ def lib():
         for name in ("nf4ref_linear_forward", "nf4ref_linear_backward_input"):
             getattr(L, name).argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i32,
                                          ctypes.c_double, _p, _i64, _p, _i64, _p]
+        L.nf4ref_quantize_bs.argtypes = [_p, ctypes.c_int, _i64, _i32, _p, _p]
+        L.nf4ref_e5m2_encode.argtypes = [ctypes.c_float]
+        L.nf4ref_e5m2_encode.restype = ctypes.c_uint8
+        L.nf4ref_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.nf4ref_e5m2_decode.restype = ctypes.c_float
+        L.nf4ref_e5m2_encode_array.argtypes = [_p, _i64, _p]
+        L.nf4ref_pairwise_sum.argtypes = [_p, _i64]
+        L.nf4ref_pairwise_sum.restype = ctypes.c_float
+        L.nf4ref_double_quantize_ex.argtypes = [_p, _i64, _i32, ctypes.c_int, ctypes.c_int, _p,
+                                                _p, _p]
+        L.nf4ref_block_scale_ex.argtypes = [_i64, _i32, ctypes.c_int, _p, _p, _p, _p]
+        L.nf4ref_block_scale_ex.restype = ctypes.c_float
+        L.nf4ref_dequantize_range_ex.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, ctypes.c_int,
+                                                 _p, _p, _p, _p, _p, ctypes.c_int]
         L.nf4ref_lora_grads.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _i32, ctypes.c_double,
                                         _p, _i64, _p, _p, _i64, _p]
         _lib = L
@@ -200,6 +214,88 @@ def dequantize_rows(codes, shape, rows, absmax=None, q=None, scale=None):
     out = np.zeros((len(rows), K), np.float32)
     for i, r in enumerate(rows):
         out[i] = dequantize_range(codes, N * K, int(r) * K, K, absmax, q, scale)
+    return out
+
+
+# ---- variants of the storage format (block sizes, DQ code formats, mean offset) ----
+
+DQ_FORMATS = {"e4m3": 0, "e5m2": 1, "linear8": 2}
+
+
+def _fmt(f):
+    if isinstance(f, str):
+        return DQ_FORMATS[f]
+    return int(f)
+
+
+def quantize_bs(w, blocksize=BLOCK):
+    """Blockwise NF4 with block size B1: (codes uint8[ceil(n/2)], absmax float32[ceil(n/B1)])."""
+    w, dt = _as_bits(w)
+    n = w.size
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    absmax = np.zeros((n + blocksize - 1) // blocksize, np.float32)
+    _check(lib().nf4ref_quantize_bs(_ptr(w), dt, n, int(blocksize), _ptr(codes), _ptr(absmax)),
+           "quantize_bs")
+    return codes, absmax
+
+
+def e5m2_encode(r):
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    out = np.zeros(r.shape, np.uint8)
+    _check(lib().nf4ref_e5m2_encode_array(_ptr(r), r.size, _ptr(out)), "e5m2_encode")
+    return out
+
+
+def e5m2_decode(c):
+    f = lib().nf4ref_e5m2_decode
+    return np.array([f(int(v)) for v in np.asarray(c).ravel()], np.float32)
+
+
+def pairwise_sum(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return np.float32(lib().nf4ref_pairwise_sum(_ptr(x), x.size))
+
+
+def double_quantize_ex(absmax, dq_blocksize=DQ_BLOCK, dq_format="e4m3", mean_offset=False):
+    """Returns (q uint8[nblocks], scale float32[ceil(nblocks/B2)], offset float32 or None)."""
+    absmax = np.ascontiguousarray(absmax, dtype=np.float32)
+    nb = absmax.size
+    q = np.zeros(nb, np.uint8)
+    scale = np.zeros((nb + dq_blocksize - 1) // dq_blocksize, np.float32)
+    off = np.zeros(1, np.float32)
+    _check(lib().nf4ref_double_quantize_ex(_ptr(absmax), nb, int(dq_blocksize), _fmt(dq_format),
+                                           1 if mean_offset else 0, _ptr(q), _ptr(scale),
+                                           _ptr(off)), "double_quantize_ex")
+    return q, scale, (off[0] if mean_offset else None)
+
+
+def block_scales_ex(nblocks, dq_blocksize=DQ_BLOCK, dq_format="e4m3", absmax=None, q=None,
+                    scale=None, offset=None):
+    """The reconstructed scale of every block."""
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    off = None if offset is None else np.array([offset], np.float32)
+    f = lib().nf4ref_block_scale_ex
+    return np.array([f(b, int(dq_blocksize), _fmt(dq_format), _ptr(absmax), _ptr(q), _ptr(scale),
+                       _ptr(off)) for b in range(nblocks)], np.float32)
+
+
+def dequantize_ex(codes, n, blocksize=BLOCK, dq_blocksize=DQ_BLOCK, dq_format="e4m3",
+                  absmax=None, q=None, scale=None, offset=None, out_dtype=F32, start=0,
+                  count=None):
+    """Elements [start, start+count) of the n-element tensor under the variant."""
+    count = n - start if count is None else count
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    off = None if offset is None else np.array([offset], np.float32)
+    out = np.zeros(count, np.float32 if out_dtype == F32 else np.uint16)
+    _check(lib().nf4ref_dequantize_range_ex(_ptr(codes), n, start, count, int(blocksize),
+                                            int(dq_blocksize), _fmt(dq_format), _ptr(absmax),
+                                            _ptr(q), _ptr(scale), _ptr(off), _ptr(out),
+                                            out_dtype), "dequantize_range_ex")
     return out
 
 

@@ -179,16 +179,21 @@ static float load_elem(const void *w, int dtype, int64_t i) {
     return nf4ref_bf16_to_f32(((const uint16_t *)w)[i]);
 }
 
-int nf4ref_quantize(const void *w, int dtype, int64_t n, uint8_t *codes, float *absmax) {
-    if (n < 0) return -1;
+static int pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+int nf4ref_quantize_bs(const void *w, int dtype, int64_t n, int32_t blocksize, uint8_t *codes,
+                       float *absmax) {
+    if (n < 0 || !pow2_in(blocksize, 16, 4096)) return -1;
     if (n == 0) return 0;
     if (!w || !codes || !absmax) return -1;
     if (dtype != NF4REF_F32 && dtype != NF4REF_BF16) return -1;
-    int64_t nblocks = (n + NF4REF_BLOCK - 1) / NF4REF_BLOCK;
+    int64_t nblocks = (n + blocksize - 1) / blocksize;
     memset(codes, 0, (size_t)((n + 1) / 2));
     for (int64_t b = 0; b < nblocks; ++b) {
-        int64_t lo = b * NF4REF_BLOCK;
-        int64_t hi = lo + NF4REF_BLOCK < n ? lo + NF4REF_BLOCK : n;
+        int64_t lo = b * blocksize;
+        int64_t hi = lo + blocksize < n ? lo + blocksize : n;
         /* c1 = max |w| over the block. */
         float c1 = 0.0f;
         for (int64_t i = lo; i < hi; ++i) {
@@ -209,6 +214,10 @@ int nf4ref_quantize(const void *w, int dtype, int64_t n, uint8_t *codes, float *
         }
     }
     return 0;
+}
+
+int nf4ref_quantize(const void *w, int dtype, int64_t n, uint8_t *codes, float *absmax) {
+    return nf4ref_quantize_bs(w, dtype, n, NF4REF_BLOCK, codes, absmax);
 }
 
 /* ---- OCP FP8 E4M3FN ---- */
@@ -321,6 +330,161 @@ int nf4ref_dequantize_range(const uint8_t *codes, int64_t n, int64_t start, int6
 int nf4ref_dequantize(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *q,
                       const float *scale, void *out, int out_dtype) {
     return nf4ref_dequantize_range(codes, n, 0, n, absmax, q, scale, out, out_dtype);
+}
+
+/* ---- variants of double quantization (see nf4ref.h) ---- */
+
+/* OCP FP8 E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent
+ * field 31 holds infinities and NaNs, the largest finite value is 57344.
+ * Exponent field 0 is subnormal, m * 2^-16. */
+uint8_t nf4ref_e5m2_encode(float r) {
+    uint8_t sign = 0;
+    double v = (double)r;
+    if (isnan(r)) return 0x7F;
+    if (v < 0) {
+        sign = 0x80;
+        v = -v;
+    }
+    if (v == 0.0) return sign;
+    if (v >= 61440.0) return (uint8_t)(sign | 0x7B); /* beyond max + half step: saturate */
+    int code;
+    if (v < ldexp(1.0, -14)) {
+        code = (int)rint(v * 65536.0); /* m = 4 is code 0x04 = 2^-14 */
+    } else {
+        int e2;
+        double f = frexp(v, &e2);
+        int e = e2 - 1;
+        int mant = (int)rint((2.0 * f - 1.0) * 4.0);
+        code = ((e + 15) << 2) + mant;
+        if (code > 0x7B) code = 0x7B;
+    }
+    return (uint8_t)(sign | code);
+}
+
+float nf4ref_e5m2_decode(uint8_t c) {
+    int s = (c >> 7) & 1;
+    int e = (c >> 2) & 31;
+    int m = c & 3;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -16);
+    else v = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return (float)(s ? -v : v);
+}
+
+int nf4ref_e5m2_encode_array(const float *r, int64_t n, uint8_t *out) {
+    if (n < 0 || (n > 0 && (!r || !out))) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = nf4ref_e5m2_encode(r[i]);
+    return 0;
+}
+
+static float pairwise_node(const float *x, int64_t n, int64_t lo, int64_t len) {
+    if (lo >= n) return 0.0f;
+    if (len == 1) return x[lo];
+    return pairwise_node(x, n, lo, len / 2) + pairwise_node(x, n, lo + len / 2, len / 2);
+}
+
+float nf4ref_pairwise_sum(const float *x, int64_t n) {
+    if (n <= 0) return 0.0f;
+    int64_t p = 1;
+    while (p < n) p *= 2;
+    return pairwise_node(x, n, 0, p);
+}
+
+/* Levels of the linear code: 255 unsigned, 127 signed. */
+static float linear_levels(int mean_offset) { return mean_offset ? 127.0f : 255.0f; }
+
+/* The 8-bit code of value x in the group with stored value sc (c2, or the
+ * step u of the linear code). */
+static uint8_t dq_encode(float x, float sc, int fmt, int mean_offset) {
+    if (fmt == NF4REF_DQ_LINEAR8) {
+        float lv = linear_levels(mean_offset);
+        if (sc == 0.0f) return 0;
+        float t = rintf(x / sc); /* nearest integer, ties to even */
+        if (t > lv) t = lv;
+        if (t < -lv) t = -lv;
+        return (uint8_t)(int8_t)(int)t; /* two's complement when signed */
+    }
+    float ratio = (sc == 0.0f) ? 0.0f : x / sc;
+    return fmt == NF4REF_DQ_E5M2 ? nf4ref_e5m2_encode(ratio) : nf4ref_e4m3_encode(ratio);
+}
+
+static float dq_decode(uint8_t c, int fmt, int mean_offset) {
+    if (fmt == NF4REF_DQ_LINEAR8) return mean_offset ? (float)(int8_t)c : (float)c;
+    return fmt == NF4REF_DQ_E5M2 ? nf4ref_e5m2_decode(c) : nf4ref_e4m3_decode(c);
+}
+
+int nf4ref_double_quantize_ex(const float *absmax, int64_t nblocks, int32_t dq_blocksize,
+                              int dq_format, int mean_offset, uint8_t *q, float *scale,
+                              float *offset) {
+    if (nblocks < 0 || !pow2_in(dq_blocksize, 1, 4096)) return -1;
+    if (dq_format < NF4REF_DQ_E4M3 || dq_format > NF4REF_DQ_LINEAR8) return -1;
+    if (mean_offset && !offset) return -1;
+    if (nblocks == 0) {
+        if (mean_offset) *offset = 0.0f;
+        return 0;
+    }
+    if (!absmax || !q || !scale) return -1;
+    for (int64_t b = 0; b < nblocks; ++b)
+        if (!isfinite(absmax[b])) return -2;
+    float mu = 0.0f;
+    if (mean_offset) {
+        mu = nf4ref_pairwise_sum(absmax, nblocks) / (float)nblocks;
+        if (!isfinite(mu)) return -2;
+        *offset = mu;
+    }
+    int64_t ngroups = (nblocks + dq_blocksize - 1) / dq_blocksize;
+    for (int64_t g = 0; g < ngroups; ++g) {
+        int64_t lo = g * dq_blocksize;
+        int64_t hi = lo + dq_blocksize < nblocks ? lo + dq_blocksize : nblocks;
+        /* c2 = max |x| over the group, x = c1 (or c1 - mu) */
+        float c2 = 0.0f;
+        for (int64_t b = lo; b < hi; ++b) {
+            float x = mean_offset ? absmax[b] - mu : absmax[b];
+            if (fabsf(x) > c2) c2 = fabsf(x);
+        }
+        float sc = (dq_format == NF4REF_DQ_LINEAR8) ? c2 / linear_levels(mean_offset) : c2;
+        scale[g] = sc;
+        for (int64_t b = lo; b < hi; ++b) {
+            float x = mean_offset ? absmax[b] - mu : absmax[b];
+            q[b] = dq_encode(x, sc, dq_format, mean_offset);
+        }
+    }
+    return 0;
+}
+
+float nf4ref_block_scale_ex(int64_t b, int32_t dq_blocksize, int dq_format, const float *absmax,
+                            const uint8_t *q, const float *scale, const float *offset) {
+    if (!q) return absmax[b];
+    float v = dq_decode(q[b], dq_format, offset != NULL) * scale[b / dq_blocksize];
+    if (offset) v = v + *offset;
+    return v;
+}
+
+int nf4ref_dequantize_range_ex(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                               int32_t blocksize, int32_t dq_blocksize, int dq_format,
+                               const float *absmax, const uint8_t *q, const float *scale,
+                               const float *offset, void *out, int out_dtype) {
+    if (n < 0 || start < 0 || count < 0 || start + count > n) return -1;
+    if (!pow2_in(blocksize, 16, 4096) || !pow2_in(dq_blocksize, 1, 4096)) return -1;
+    if (dq_format < NF4REF_DQ_E4M3 || dq_format > NF4REF_DQ_LINEAR8) return -1;
+    if (count == 0) return 0;
+    if (!codes || !out) return -1;
+    if (!q && !absmax) return -1;
+    if (q && !scale) return -1;
+    if (out_dtype != NF4REF_F32 && out_dtype != NF4REF_BF16) return -1;
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t i = start + j;
+        int code = (codes[i / 2] >> (4 * (int)(i & 1))) & 15;
+        float c1 = nf4ref_block_scale_ex(i / blocksize, dq_blocksize, dq_format, absmax, q, scale,
+                                         offset);
+        float v = NF4_Q[code] * c1;
+        if (out_dtype == NF4REF_F32)
+            ((float *)out)[j] = v;
+        else
+            ((uint16_t *)out)[j] = nf4ref_f32_to_bf16(v);
+    }
+    return 0;
 }
 
 /* ---- storage footprint ([L15] "Double quantisation" per-parameter tables) ---- */

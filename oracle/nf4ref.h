@@ -133,6 +133,60 @@ int nf4ref_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t 
                       const int64_t *a_rows, int64_t na, double *da, const int64_t *b_cols,
                       int64_t nb, double *db);
 
+/* ---- Variants of the storage format ([MF] "Block-Wise Quantization
+ * Mechanics": 64 is the typical block size, so B1 is a parameter; [MF]
+ * "Double Quantization (DQ)": the 8-bit float format of the second step is
+ * not named, and the step's prose mentions an asymmetric bias / mean
+ * subtraction). Readings:
+ *   - B1 (blocksize) and B2 (dq_blocksize) are powers of two, B1 in
+ *     [16, 4096], B2 in [1, 4096];
+ *   - dq_format: NF4REF_DQ_E4M3 (OCP E4M3FN of c1/c2, the default),
+ *     NF4REF_DQ_E5M2 (OCP E5M2 of c1/c2, round to nearest even), or
+ *     NF4REF_DQ_LINEAR8 (a uniform integer code: the stored group value is the
+ *     step u = fl32(c2 / L) with L = 255, or 127 for signed codes; the code is
+ *     the nearest integer to fl32(c1 / u), clamped to [0, L] (or [-L, L]);
+ *     the scale is reconstructed as fl32(code * u));
+ *   - mean offset: mu = fl32(S / fl32(nblocks)), S the pairwise sum of all
+ *     c1 of the tensor (nf4ref_pairwise_sum); double quantization then acts on
+ *     x = fl32(c1 - mu): c2 = max |x| over the group, the code is the signed
+ *     code of fl32(x / c2) (or of fl32(x / u)), and the reconstructed scale is
+ *     fl32(fl32(decode * c2) + mu). One fp32 mu per tensor, so the
+ *     per-parameter footprint is unchanged. */
+enum { NF4REF_DQ_E4M3 = 0, NF4REF_DQ_E5M2 = 1, NF4REF_DQ_LINEAR8 = 2 };
+
+/* nf4ref_quantize with block size B1. absmax: ceil(n/B1) floats. */
+int nf4ref_quantize_bs(const void *w, int dtype, int64_t n, int32_t blocksize, uint8_t *codes,
+                       float *absmax);
+
+/* OCP FP8 E5M2 encode (round to nearest even; beyond the largest finite value
+ * saturates to it) / decode. */
+uint8_t nf4ref_e5m2_encode(float r);
+float nf4ref_e5m2_decode(uint8_t c);
+int nf4ref_e5m2_encode_array(const float *r, int64_t n, uint8_t *out);
+
+/* Pairwise sum in fp32: the values padded with zeros to a power-of-two
+ * count, then adjacent pairs added level by level until one value remains. */
+float nf4ref_pairwise_sum(const float *x, int64_t n);
+
+/* Double quantization with a block B2, a code format and an optional mean
+ * offset (see above). q: nblocks bytes; scale: ceil(nblocks/B2) floats (c2, or
+ * the step u for NF4REF_DQ_LINEAR8); offset: one float, written iff
+ * mean_offset (may be NULL otherwise). */
+int nf4ref_double_quantize_ex(const float *absmax, int64_t nblocks, int32_t dq_blocksize,
+                              int dq_format, int mean_offset, uint8_t *q, float *scale,
+                              float *offset);
+
+/* The reconstructed scale of block b under the variant; offset == NULL means
+ * no mean offset, q == NULL means no double quantization (absmax[b]). */
+float nf4ref_block_scale_ex(int64_t b, int32_t dq_blocksize, int dq_format, const float *absmax,
+                            const uint8_t *q, const float *scale, const float *offset);
+
+/* nf4ref_dequantize_range with block size B1 and the DQ variant. */
+int nf4ref_dequantize_range_ex(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                               int32_t blocksize, int32_t dq_blocksize, int dq_format,
+                               const float *absmax, const uint8_t *q, const float *scale,
+                               const float *offset, void *out, int out_dtype);
+
 #ifdef __cplusplus
 }
 #endif
