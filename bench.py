@@ -369,8 +369,73 @@ def kernel_benches(dev, iters, warmup, with_stack):
     del X, dY, A, B, Y, dX, ws, Wd, wt
     torch.cuda.empty_cache()
 
+    out.update(variant_benches(dev, iters, warmup))
     if with_stack:
         out.update(stack_bench(dev))
+    return out
+
+
+VARIANTS = (
+    # label, (B1, B2, DQ code format, mean offset)
+    ("e5m2", (64, 256, "e5m2", False)),
+    ("linear8", (64, 256, "linear8", False)),
+    ("e4m3_offset", (64, 256, "e4m3", True)),
+    ("b128", (128, 256, "e4m3", False)),
+    ("b16", (16, 256, "e4m3", False)),
+    ("b4096_e5m2_offset", (4096, 256, "e5m2", True)),
+)
+
+
+def variant_storage_bytes(n, f):
+    nb = f.nblocks(n)
+    return (n + 1) // 2 + nb + 4 * f.ngroups(n) + (4 if f.mean_offset else 0)
+
+
+def variant_benches(dev, iters, warmup):
+    """Storage-format variants on the 11008 x 4096 bf16 weight (4 rotating
+    copies, 361 MB, more than the last-level cache): quantize with fused or
+    two-pass double quantization, and dequantize to bf16."""
+    import ctypes
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    shape = workloads.MLP_SHAPE
+    n = shape[0] * shape[1]
+    ws_in = [(torch.randn(shape, generator=g, device=dev) * workloads.SIGMA_W).to(torch.bfloat16)
+             for _ in range(4)]
+    L = nq.lib()
+    for label, spec in VARIANTS:
+        f = nq.NF4Format(*spec)
+        fs = f.struct()
+        ts = [nq.empty_nf4(shape, dev, fmt=f) for _ in range(4)]
+        wsz = nq.nf4_quantize_ex_workspace_size(n, f)
+        wsp = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+        qargs = [(_p(ws_in[i]), 1, n, ctypes.byref(fs), _p(ts[i].codes), None, _p(ts[i].absmax_q),
+                  _p(ts[i].absmax_scale), _p(ts[i].absmax_offset), _p(wsp), wsp.numel(), _stream())
+                 for i in range(4)]
+        qcalls = [Prepared(L.nf4_quantize_ex, *a) for a in qargs]
+        ms, pc = time_op(lambda i: qcalls[i % 4](), iters, warmup)
+        byts = n * 2 + variant_storage_bytes(n, f)
+        key = f"quantize_{label}_11008x4096_bf16"
+        out[key] = {"ms": ms, "p10_p50_p90_ms": pc, "GB/s": byts / ms / 1e6,
+                    "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS, "format": list(spec)}
+        log(f"{key}: {out[key]}")
+        outs = [torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        dcalls = [Prepared(L.nf4_dequantize_ex, _p(ts[i].codes), n, ctypes.byref(fs), None,
+                           _p(ts[i].absmax_q), _p(ts[i].absmax_scale), _p(ts[i].absmax_offset),
+                           _p(outs[i]), 1, _stream()) for i in range(4)]
+        ms, pc = time_op(lambda i: dcalls[i % 4](), iters, warmup)
+        key = f"dequantize_{label}_11008x4096_bf16"
+        out[key] = {"ms": ms, "p10_p50_p90_ms": pc, "GB/s": byts / ms / 1e6,
+                    "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS, "format": list(spec)}
+        log(f"{key}: {out[key]}")
+        del ts, outs, wsp
+    del ws_in
+    torch.cuda.empty_cache()
     return out
 
 

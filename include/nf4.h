@@ -179,6 +179,74 @@ nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k
                              void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ---- Storage-format variants ----
+ * The entry points above fix B1 = 64, B2 = 256 and the E4M3FN code. [MF]
+ * "Block-Wise Quantization Mechanics" gives 64 as the typical block size, and
+ * [MF] "Double Quantization (DQ)" names neither the 8-bit float format nor
+ * how its prose's asymmetric bias / mean subtraction is applied; the calls
+ * below take these as parameters.
+ *
+ * Format of the second-level (8-bit) code of c1:
+ *   NF4_DQ_E4M3     OCP FP8 E4M3FN of fl32(x / c2), round to nearest even
+ *   NF4_DQ_E5M2     OCP FP8 E5M2 of fl32(x / c2), round to nearest even
+ *   NF4_DQ_LINEAR8  uniform integer code: absmax_scale holds the step
+ *                   u = fl32(c2 / L), L = 255 (127 with the mean offset), and
+ *                   the code is rint(fl32(x / u)) clamped to [-L, L]
+ * where x = c1, or x = fl32(c1 - mu) with the mean offset, and c2 = max |x|
+ * over the group. With the mean offset the codes are signed (FP8 sign bit, or
+ * int8 two's complement for NF4_DQ_LINEAR8) and mu = fl32(S / fl32(nblocks))
+ * is one fp32 per tensor, S the pairwise fp32 sum of all c1 (the values
+ * padded with zeros to a power-of-two count, adjacent pairs added level by
+ * level). The reconstructed scale is
+ *   scale(b) = fl32(decode(absmax_q[b]) * absmax_scale[b / B2])     (+ mu: one more fl32 add)
+ * and the weight fl32(q[code] * scale(i / B1)) as before. */
+typedef enum { NF4_DQ_E4M3 = 0, NF4_DQ_E5M2 = 1, NF4_DQ_LINEAR8 = 2 } nf4_dq_format;
+
+typedef struct {
+    int32_t blocksize;      /* B1: a power of two in [16, 4096] */
+    int32_t dq_blocksize;   /* B2: a power of two in [1, 4096] */
+    int32_t dq_format;      /* an nf4_dq_format */
+    int32_t dq_mean_offset; /* 0, or 1 for the tensor-wide mean offset */
+} nf4_format;
+
+/* Device workspace bytes of nf4_quantize_ex for an n-element tensor: fp32
+ * block scales when the call runs in two passes (B1 != 64, B2 != 256 or the
+ * mean offset, with double quantization) plus, with the mean offset, the
+ * partial sums of mu. 0 when none is needed; (size_t)-1 for invalid args. */
+size_t nf4_quantize_ex_workspace_size(int64_t n, const nf4_format *f);
+
+/* Blockwise NF4 quantization with block size f->blocksize and, when absmax_q
+ * and absmax_scale are given, double quantization in f's format (see above).
+ *   w, codes, absmax, absmax_q, absmax_scale  as nf4_quantize, with B1, B2 of f
+ *   absmax_offset  device out, one float (mu); required iff f->dq_mean_offset
+ *                  and double quantization is on, else ignored
+ *   workspace      device, 256-byte aligned, >= nf4_quantize_ex_workspace_size
+ *                  bytes (may be NULL when that is 0)
+ * f = {64, 256, NF4_DQ_E4M3, 0} computes exactly what nf4_quantize does. */
+nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, const nf4_format *f,
+                           uint8_t *codes, float *absmax, uint8_t *absmax_q, float *absmax_scale,
+                           float *absmax_offset, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Device workspace bytes of nf4_double_quantize_ex (the partial sums of mu;
+ * 0 without the mean offset); (size_t)-1 for invalid args. */
+size_t nf4_double_quantize_ex_workspace_size(int64_t nblocks, const nf4_format *f);
+
+/* Double quantization of nblocks existing fp32 block scales in f's format
+ * (f->blocksize is not used). absmax_offset: device out, one float, required
+ * iff f->dq_mean_offset. */
+nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, const nf4_format *f,
+                                  uint8_t *absmax_q, float *absmax_scale, float *absmax_offset,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Dequantization of a tensor stored in format f: scale(b) as above, absmax
+ * (fp32, no double quantization) when absmax_q == NULL. absmax_offset: device,
+ * one float, required iff f->dq_mean_offset and absmax_q != NULL. */
+nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format *f,
+                             const float *absmax, const uint8_t *absmax_q,
+                             const float *absmax_scale, const float *absmax_offset, void *out,
+                             nf4_dtype out_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,7 +46,15 @@ EXPORTS = (
     "nf4_linear_backward_input",
     "nf4_lora_backward_workspace_size",
     "nf4_lora_backward",
+    "nf4_quantize_ex_workspace_size",
+    "nf4_quantize_ex",
+    "nf4_double_quantize_ex_workspace_size",
+    "nf4_double_quantize_ex",
+    "nf4_dequantize_ex",
 )
+
+# nf4_dq_format: the 8-bit code of double quantization.
+DQ_FORMATS = {"e4m3": 0, "e5m2": 1, "linear8": 2}
 
 
 class NF4LibraryMissing(RuntimeError):
@@ -69,6 +77,15 @@ class nf4_weight(ctypes.Structure):
         ("k_in", ctypes.c_int64),
         ("blocksize", ctypes.c_int32),
         ("dq_blocksize", ctypes.c_int32),
+    ]
+
+
+class nf4_format(ctypes.Structure):
+    _fields_ = [
+        ("blocksize", ctypes.c_int32),
+        ("dq_blocksize", ctypes.c_int32),
+        ("dq_format", ctypes.c_int32),
+        ("dq_mean_offset", ctypes.c_int32),
     ]
 
 
@@ -109,6 +126,17 @@ def lib():
     L.nf4_lora_backward.argtypes = [p, p, i64, i64, i64, p, p, i32, f32, p, p, ctypes.c_int, p,
                                     ctypes.c_size_t, p]
     L.nf4_lora_backward.restype = ctypes.c_int
+    fmt_p = ctypes.POINTER(nf4_format)
+    L.nf4_quantize_ex_workspace_size.argtypes = [i64, fmt_p]
+    L.nf4_quantize_ex_workspace_size.restype = ctypes.c_size_t
+    L.nf4_double_quantize_ex_workspace_size.argtypes = [i64, fmt_p]
+    L.nf4_double_quantize_ex_workspace_size.restype = ctypes.c_size_t
+    L.nf4_quantize_ex.argtypes = [p, ctypes.c_int, i64, fmt_p, p, p, p, p, p, p, ctypes.c_size_t, p]
+    L.nf4_quantize_ex.restype = ctypes.c_int
+    L.nf4_double_quantize_ex.argtypes = [p, i64, fmt_p, p, p, p, p, ctypes.c_size_t, p]
+    L.nf4_double_quantize_ex.restype = ctypes.c_int
+    L.nf4_dequantize_ex.argtypes = [p, i64, fmt_p, p, p, p, p, p, ctypes.c_int, p]
+    L.nf4_dequantize_ex.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -187,6 +215,88 @@ def nf4_linear_workspace_size(m, r):
     return int(lib().nf4_linear_workspace_size(m, r))
 
 
+@dataclass(frozen=True)
+class NF4Format:
+    """Storage-format variant (nf4_format in nf4.h): block size B1, DQ block
+    B2, the 8-bit code format of double quantization ("e4m3", "e5m2",
+    "linear8") and the tensor-wide mean offset."""
+    blocksize: int = BLOCK
+    dq_blocksize: int = DQ_BLOCK
+    dq_format: str = "e4m3"
+    mean_offset: bool = False
+
+    @property
+    def is_default(self):
+        return self == NF4Format()
+
+    def struct(self):
+        if self.dq_format not in DQ_FORMATS:
+            raise ValueError(f"dq_format must be one of {sorted(DQ_FORMATS)}")
+        return nf4_format(self.blocksize, self.dq_blocksize, DQ_FORMATS[self.dq_format],
+                          1 if self.mean_offset else 0)
+
+    def nblocks(self, n):
+        return (n + self.blocksize - 1) // self.blocksize
+
+    def ngroups(self, n):
+        return (self.nblocks(n) + self.dq_blocksize - 1) // self.dq_blocksize
+
+
+def _ws_size(fn, n, fmt):
+    size = fn(n, ctypes.byref(fmt.struct()))
+    if size == ctypes.c_size_t(-1).value:
+        raise NF4Error(3, fn.__name__)
+    return int(size)
+
+
+def nf4_quantize_ex_workspace_size(n, fmt: NF4Format):
+    return _ws_size(lib().nf4_quantize_ex_workspace_size, n, fmt)
+
+
+def nf4_double_quantize_ex_workspace_size(nblocks, fmt: NF4Format):
+    return _ws_size(lib().nf4_double_quantize_ex_workspace_size, nblocks, fmt)
+
+
+def _workspace(size, device):
+    import torch
+
+    return torch.empty(max(size, 1), dtype=torch.uint8, device=device) if size else None
+
+
+def nf4_quantize_ex(w, fmt: NF4Format, codes, absmax=None, absmax_q=None, absmax_scale=None,
+                    absmax_offset=None, workspace=None):
+    _need_cuda(w, codes, absmax, absmax_q, absmax_scale, absmax_offset, workspace)
+    if workspace is None and absmax_q is not None:
+        workspace = _workspace(nf4_quantize_ex_workspace_size(w.numel(), fmt), w.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().nf4_quantize_ex(_ptr(w), _dtype_code(w.dtype), w.numel(), ctypes.byref(fmt.struct()),
+                               _ptr(codes), _ptr(absmax), _ptr(absmax_q), _ptr(absmax_scale),
+                               _ptr(absmax_offset), _ptr(workspace), ws_bytes, _stream(w.device))
+    _check(st, "nf4_quantize_ex")
+
+
+def nf4_double_quantize_ex(absmax, fmt: NF4Format, absmax_q, absmax_scale, absmax_offset=None,
+                           workspace=None):
+    _need_cuda(absmax, absmax_q, absmax_scale, absmax_offset, workspace)
+    if workspace is None:
+        workspace = _workspace(nf4_double_quantize_ex_workspace_size(absmax.numel(), fmt),
+                               absmax.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().nf4_double_quantize_ex(_ptr(absmax), absmax.numel(), ctypes.byref(fmt.struct()),
+                                      _ptr(absmax_q), _ptr(absmax_scale), _ptr(absmax_offset),
+                                      _ptr(workspace), ws_bytes, _stream(absmax.device))
+    _check(st, "nf4_double_quantize_ex")
+
+
+def nf4_dequantize_ex(codes, n, fmt: NF4Format, out, absmax=None, absmax_q=None,
+                      absmax_scale=None, absmax_offset=None):
+    _need_cuda(codes, out, absmax, absmax_q, absmax_scale, absmax_offset)
+    st = lib().nf4_dequantize_ex(_ptr(codes), n, ctypes.byref(fmt.struct()), _ptr(absmax),
+                                 _ptr(absmax_q), _ptr(absmax_scale), _ptr(absmax_offset),
+                                 _ptr(out), _dtype_code(out.dtype), _stream(codes.device))
+    _check(st, "nf4_dequantize_ex")
+
+
 # ------------------------------------------------------------- convenience
 
 @dataclass
@@ -200,6 +310,8 @@ class NF4Config:
     compute_dtype: str = "bfloat16"
     blocksize: int = BLOCK
     dq_blocksize: int = DQ_BLOCK
+    dq_format: str = "e4m3"
+    dq_mean_offset: bool = False
 
     def validate(self):
         if not self.load_in_4bit:
@@ -208,9 +320,16 @@ class NF4Config:
             raise ValueError("only quant_type='nf4' is implemented")
         if str(self.compute_dtype).replace("torch.", "") != "bfloat16":
             raise ValueError("only bfloat16 compute is implemented")
-        if self.blocksize != BLOCK or self.dq_blocksize != DQ_BLOCK:
-            raise ValueError("block sizes 64 / 256 only")
+        self.format().struct()
+        if self.blocksize not in (16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+            raise ValueError("blocksize: a power of two in [16, 4096]")
+        if self.dq_blocksize < 1 or self.dq_blocksize > 4096 or \
+                self.dq_blocksize & (self.dq_blocksize - 1):
+            raise ValueError("dq_blocksize: a power of two in [1, 4096]")
         return self
+
+    def format(self):
+        return NF4Format(self.blocksize, self.dq_blocksize, self.dq_format, self.dq_mean_offset)
 
 
 @dataclass
@@ -221,6 +340,8 @@ class NF4Tensor:
     absmax_q: Optional["object"]
     absmax_scale: Optional["object"]
     shape: Tuple[int, ...]
+    fmt: NF4Format = NF4Format()
+    absmax_offset: Optional["object"] = None
 
     @property
     def numel(self):
@@ -235,12 +356,16 @@ class NF4Tensor:
 
     def storage_bytes(self):
         return sum(t.numel() * t.element_size() for t in
-                   (self.codes, self.absmax, self.absmax_q, self.absmax_scale) if t is not None)
+                   (self.codes, self.absmax, self.absmax_q, self.absmax_scale, self.absmax_offset)
+                   if t is not None)
 
     def weight_struct(self):
         """nf4_weight view of a 2-D [N x K] weight (keep self alive while used)."""
         if len(self.shape) != 2:
             raise ValueError("a linear weight is 2-D [n_out x k_in]")
+        if not self.fmt.is_default:
+            raise ValueError("the fused linear kernels take the default storage format "
+                             "(B1 = 64, B2 = 256, E4M3, no mean offset)")
         return nf4_weight(
             codes=self.codes.data_ptr(),
             absmax_q=self.absmax_q.data_ptr() if self.absmax_q is not None else None,
@@ -257,35 +382,55 @@ def ngroups(n):
     return (nblocks(n) + DQ_BLOCK - 1) // DQ_BLOCK
 
 
-def empty_nf4(shape, device, double_quant=True, keep_absmax=False):
+def empty_nf4(shape, device, double_quant=True, keep_absmax=False, fmt: NF4Format = None):
     import torch
 
+    fmt = fmt or NF4Format()
     n = 1
     for d in shape:
         n *= d
+    nb, ng = fmt.nblocks(n), fmt.ngroups(n)
     codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
-    absmax = (torch.empty(nblocks(n), dtype=torch.float32, device=device)
+    absmax = (torch.empty(nb, dtype=torch.float32, device=device)
               if (keep_absmax or not double_quant) else None)
-    q = torch.empty(nblocks(n), dtype=torch.uint8, device=device) if double_quant else None
-    sc = torch.empty(ngroups(n), dtype=torch.float32, device=device) if double_quant else None
-    return NF4Tensor(codes, absmax, q, sc, tuple(shape))
+    q = torch.empty(nb, dtype=torch.uint8, device=device) if double_quant else None
+    sc = torch.empty(ng, dtype=torch.float32, device=device) if double_quant else None
+    off = (torch.empty(1, dtype=torch.float32, device=device)
+           if (double_quant and fmt.mean_offset) else None)
+    return NF4Tensor(codes, absmax, q, sc, tuple(shape), fmt, off)
 
 
-def quantize(w, double_quant=True, keep_absmax=False, out: Optional[NF4Tensor] = None):
-    """Blockwise NF4 (+ double quantization) of a float32/bfloat16 device tensor."""
-    t = out if out is not None else empty_nf4(tuple(w.shape), w.device, double_quant, keep_absmax)
-    nf4_quantize(w.contiguous(), t.codes, t.absmax, t.absmax_q, t.absmax_scale)
+def quantize(w, double_quant=True, keep_absmax=False, out: Optional[NF4Tensor] = None,
+             fmt: NF4Format = None):
+    """Blockwise NF4 (+ double quantization) of a float32/bfloat16 device tensor,
+    in the default storage format or the variant `fmt`."""
+    fmt = out.fmt if out is not None else (fmt or NF4Format())
+    t = out if out is not None else empty_nf4(tuple(w.shape), w.device, double_quant, keep_absmax,
+                                               fmt)
+    if fmt.is_default:
+        nf4_quantize(w.contiguous(), t.codes, t.absmax, t.absmax_q, t.absmax_scale)
+    else:
+        nf4_quantize_ex(w.contiguous(), fmt, t.codes, t.absmax, t.absmax_q, t.absmax_scale,
+                        t.absmax_offset)
     return t
 
 
-def double_quantize(absmax):
+def double_quantize(absmax, fmt: NF4Format = None):
+    """Returns (absmax_q, absmax_scale), plus the offset tensor when fmt has
+    the mean offset."""
     import torch
 
-    q = torch.empty(absmax.numel(), dtype=torch.uint8, device=absmax.device)
-    sc = torch.empty((absmax.numel() + DQ_BLOCK - 1) // DQ_BLOCK, dtype=torch.float32,
+    fmt = fmt or NF4Format()
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.uint8, device=absmax.device)
+    sc = torch.empty((nb + fmt.dq_blocksize - 1) // fmt.dq_blocksize, dtype=torch.float32,
                      device=absmax.device)
-    nf4_double_quantize(absmax, q, sc)
-    return q, sc
+    if fmt == NF4Format(blocksize=fmt.blocksize):
+        nf4_double_quantize(absmax, q, sc)
+        return q, sc
+    off = torch.empty(1, dtype=torch.float32, device=absmax.device) if fmt.mean_offset else None
+    nf4_double_quantize_ex(absmax, fmt, q, sc, off)
+    return (q, sc, off) if fmt.mean_offset else (q, sc)
 
 
 def dequantize(t: NF4Tensor, out_dtype=None, out=None):
@@ -294,7 +439,13 @@ def dequantize(t: NF4Tensor, out_dtype=None, out=None):
     out_dtype = out_dtype or torch.bfloat16
     if out is None:
         out = torch.empty(t.shape, dtype=out_dtype, device=t.codes.device)
-    if t.double_quant:
+    if not t.fmt.is_default:
+        if t.double_quant:
+            nf4_dequantize_ex(t.codes, t.numel, t.fmt, out, absmax_q=t.absmax_q,
+                              absmax_scale=t.absmax_scale, absmax_offset=t.absmax_offset)
+        else:
+            nf4_dequantize_ex(t.codes, t.numel, t.fmt, out, absmax=t.absmax)
+    elif t.double_quant:
         nf4_dequantize(t.codes, t.numel, out, absmax_q=t.absmax_q, absmax_scale=t.absmax_scale)
     else:
         nf4_dequantize(t.codes, t.numel, out, absmax=t.absmax)

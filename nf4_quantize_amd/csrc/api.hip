@@ -316,3 +316,110 @@ NF4_API nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, i
         static_cast<const uint16_t *>(lora_a), static_cast<const uint16_t *>(lora_b), r, lora_scale, grad_a,
         grad_b, grad_dtype == NF4_F32, workspace, static_cast<hipStream_t>(stream)));
 }
+
+// ---- storage-format variants ----
+
+namespace {
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+nf4_status check_format(const nf4_format *f) {
+    if (!f) return NF4_ERR_NULL;
+    if (!pow2_in(f->blocksize, 16, 4096) || !pow2_in(f->dq_blocksize, 1, 4096))
+        return NF4_ERR_UNSUPPORTED;
+    if (f->dq_format < NF4_DQ_E4M3 || f->dq_format > NF4_DQ_LINEAR8) return NF4_ERR_UNSUPPORTED;
+    if (f->dq_mean_offset != 0 && f->dq_mean_offset != 1) return NF4_ERR_UNSUPPORTED;
+    return NF4_OK;
+}
+
+nf4_status check_workspace(size_t need, const void *ws, size_t ws_bytes) {
+    if (need == 0) return NF4_OK;
+    if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return NF4_ERR_ALIGN;
+    return NF4_OK;
+}
+
+}  // namespace
+
+NF4_API size_t nf4_quantize_ex_workspace_size(int64_t n, const nf4_format *f) {
+    if (check_format(f) != NF4_OK || n < 0 || n > kMaxElems) return (size_t)-1;
+    return nf4::quantize_ex_workspace(n, *f);
+}
+
+NF4_API size_t nf4_double_quantize_ex_workspace_size(int64_t nblocks, const nf4_format *f) {
+    if (check_format(f) != NF4_OK || nblocks < 0 || nblocks > kMaxElems / 16) return (size_t)-1;
+    return nf4::double_quantize_ex_workspace(nblocks, *f);
+}
+
+NF4_API nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, const nf4_format *f,
+                                   uint8_t *codes, float *absmax, uint8_t *absmax_q,
+                                   float *absmax_scale, float *absmax_offset, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    nf4_status st = check_format(f);
+    if (st != NF4_OK) return st;
+    if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
+    if (w_dtype != NF4_F32 && w_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    if (!code_lut()) return NF4_ERR_UNSUPPORTED;
+    const bool dq = absmax_q != nullptr || absmax_scale != nullptr;
+    if (n == 0) return NF4_OK;
+    if (!w || !codes) return NF4_ERR_NULL;
+    if (dq && (!absmax_q || !absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !absmax) return NF4_ERR_NULL;
+    if (dq && f->dq_mean_offset && !absmax_offset) return NF4_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codes, 16)) return NF4_ERR_ALIGN;
+    if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
+        (absmax_scale && !aligned(absmax_scale, 4)) || (absmax_offset && !aligned(absmax_offset, 4)))
+        return NF4_ERR_ALIGN;
+    if (dq && (st = check_workspace(nf4::quantize_ex_workspace(n, *f), workspace,
+                                    workspace_bytes)) != NF4_OK)
+        return st;
+    return launch_status(nf4::launch_quantize_ex(w, w_dtype, n, *f, codes, absmax,
+                                                 dq ? absmax_q : nullptr,
+                                                 dq ? absmax_scale : nullptr, absmax_offset,
+                                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, const nf4_format *f,
+                                          uint8_t *absmax_q, float *absmax_scale,
+                                          float *absmax_offset, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    nf4_status st = check_format(f);
+    if (st != NF4_OK) return st;
+    if (nblocks < 0 || nblocks > kMaxElems / 16) return NF4_ERR_SIZE;
+    if (nblocks == 0) return NF4_OK;
+    if (!absmax || !absmax_q || !absmax_scale) return NF4_ERR_NULL;
+    if (f->dq_mean_offset && !absmax_offset) return NF4_ERR_NULL;
+    if (!aligned(absmax, 4) || !aligned(absmax_q, 4) || !aligned(absmax_scale, 4) ||
+        (absmax_offset && !aligned(absmax_offset, 4)))
+        return NF4_ERR_ALIGN;
+    if ((st = check_workspace(nf4::double_quantize_ex_workspace(nblocks, *f), workspace,
+                              workspace_bytes)) != NF4_OK)
+        return st;
+    return launch_status(nf4::launch_double_quantize_ex(absmax, nblocks, *f, absmax_q,
+                                                        absmax_scale, absmax_offset, workspace,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format *f,
+                                     const float *absmax, const uint8_t *absmax_q,
+                                     const float *absmax_scale, const float *absmax_offset,
+                                     void *out, nf4_dtype out_dtype, void *stream) {
+    nf4_status st = check_format(f);
+    if (st != NF4_OK) return st;
+    if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
+    if (out_dtype != NF4_F32 && out_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    const bool dq = absmax_q != nullptr || absmax_scale != nullptr;
+    if (n == 0) return NF4_OK;
+    if (!codes || !out) return NF4_ERR_NULL;
+    if (dq && (!absmax_q || !absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !absmax) return NF4_ERR_NULL;
+    if (dq && f->dq_mean_offset && !absmax_offset) return NF4_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(out, 16)) return NF4_ERR_ALIGN;
+    if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
+        (absmax_scale && !aligned(absmax_scale, 4)) || (absmax_offset && !aligned(absmax_offset, 4)))
+        return NF4_ERR_ALIGN;
+    return launch_status(nf4::launch_dequantize_ex(
+        codes, n, *f, dq ? nullptr : absmax, dq ? absmax_q : nullptr, dq ? absmax_scale : nullptr,
+        (dq && f->dq_mean_offset) ? absmax_offset : nullptr, out, out_dtype,
+        static_cast<hipStream_t>(stream)));
+}

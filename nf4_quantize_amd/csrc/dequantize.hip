@@ -175,6 +175,138 @@ hipError_t launch_t(const uint8_t *codes, int64_t n, const float *absmax, const 
     return hipGetLastError();
 }
 
+// ---- storage-format variants: any block sizes, the 8-bit code format F
+// and the mean offset (kS) ----
+
+// Scale of block blk: absmax (kDQ false), or decode(q) * group value (+ mu).
+template <int F, bool kS, bool kDQ>
+struct VariantScale {
+    const float *absmax;
+    const uint8_t *q;
+    const float *sc;
+    float mu;
+    int lb2;
+    __device__ __forceinline__ float operator()(int64_t blk) const {
+        if constexpr (!kDQ) {
+            return absmax[blk];
+        } else {
+            float v = dq_decode<F, kS>((uint32_t)q[blk]) * sc[blk >> lb2];
+            if constexpr (kS) v = v + mu;
+            return v;
+        }
+    }
+};
+
+// The chunk kernel's layout (a wave owns 2048-weight chunks, lane l reads
+// code dwords j * 256 + 4 l) with each lane's scale looked up per dword: the
+// 8 weights of a dword lie in one block for every B1 >= 16.
+template <typename O, int F, bool kS, bool kDQ, int kCPW>
+__global__ __launch_bounds__(kThreads) void dequantize_variant_kernel(
+    const uint8_t *__restrict__ codes, int64_t nchunks, int lb1, int lb2,
+    const float *__restrict__ absmax, const uint8_t *__restrict__ absmax_q,
+    const float *__restrict__ absmax_scale, const float *__restrict__ mu_p, O *__restrict__ out,
+    Levels lv) {
+    __shared__ float2 s_pair[256];
+    __shared__ float s_lv[16];
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    uint32_t d[kCPW][4];
+#pragma unroll
+    for (int c = 0; c < kCPW; ++c) {
+        const int64_t chunk = min(wave * kCPW + c, nchunks - 1);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(codes + chunk * kChunkBytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[c][j] = __builtin_nontemporal_load(&src[j * 64 + lane]);
+    }
+    const VariantScale<F, kS, kDQ> scale{absmax, absmax_q, absmax_scale,
+                                         (kDQ && kS) ? *mu_p : 0.0f, lb2};
+    build_pair_table(lv, s_lv, s_pair);
+
+#pragma unroll
+    for (int c = 0; c < kCPW; ++c) {
+        const int64_t chunk = wave * kCPW + c;
+        if (chunk >= nchunks) return;
+        float s[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[j] = scale((chunk * kChunk + j * 512 + lane * 8) >> lb1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float2 qq = s_pair[(d[c][j] >> (8 * k)) & 0xFFu];
+                v[2 * k] = qq.x * s[j];
+                v[2 * k + 1] = qq.y * s[j];
+            }
+            Out<O>::store8(out + chunk * kChunk + j * 512 + lane * 8, v);
+        }
+    }
+}
+
+template <typename O, int F, bool kS, bool kDQ>
+__global__ __launch_bounds__(kThreads) void dequantize_variant_tail_kernel(
+    const uint8_t *__restrict__ codes, int64_t start, int64_t n, int lb1, int lb2,
+    const float *__restrict__ absmax, const uint8_t *__restrict__ absmax_q,
+    const float *__restrict__ absmax_scale, const float *__restrict__ mu_p, O *__restrict__ out,
+    Levels lv) {
+    __shared__ float2 s_pair[256];
+    __shared__ float s_lv[16];
+    build_pair_table(lv, s_lv, s_pair);
+    const int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const VariantScale<F, kS, kDQ> scale{absmax, absmax_q, absmax_scale,
+                                         (kDQ && kS) ? *mu_p : 0.0f, lb2};
+    const uint32_t code = (codes[i >> 1] >> (4 * (i & 1))) & 15u;
+    Out<O>::store1(out + i, s_pair[code].x * scale(i >> lb1));
+}
+
+template <typename O, int F, bool kS, bool kDQ>
+hipError_t launch_variant(const uint8_t *codes, int64_t n, int lb1, int lb2, const float *absmax,
+                          const uint8_t *q, const float *sc, const float *mu, O *out,
+                          hipStream_t s) {
+    Levels lv;
+    for (int i = 0; i < 16; ++i) lv.q[i] = kLevels[i];
+    constexpr int kCPW = 2;
+    const int64_t nchunks = n / kChunk;
+    if (nchunks > 0) {
+        const int64_t waves = (nchunks + kCPW - 1) / kCPW;
+        const int64_t wgs = (waves + (kThreads / 64) - 1) / (kThreads / 64);
+        dequantize_variant_kernel<O, F, kS, kDQ, kCPW><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
+            codes, nchunks, lb1, lb2, absmax, q, sc, mu, out, lv);
+    }
+    const int64_t start = nchunks * kChunk;
+    if (start < n) {
+        const int64_t rem = n - start;
+        dequantize_variant_tail_kernel<O, F, kS, kDQ>
+            <<<dim3((unsigned)((rem + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(
+                codes, start, n, lb1, lb2, absmax, q, sc, mu, out, lv);
+    }
+    return hipGetLastError();
+}
+
+template <typename O>
+hipError_t launch_variant_o(const uint8_t *codes, int64_t n, const nf4_format &f,
+                            const float *absmax, const uint8_t *q, const float *sc,
+                            const float *mu, O *out, hipStream_t s) {
+    int lb1 = 0, lb2 = 0;
+    while ((1 << lb1) < f.blocksize) ++lb1;
+    while ((1 << lb2) < f.dq_blocksize) ++lb2;
+    if (!q) return launch_variant<O, kFmtE4M3, false, false>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+    if (f.dq_mean_offset) {
+        switch (f.dq_format) {
+            case kFmtE5M2: return launch_variant<O, kFmtE5M2, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+            case kFmtLin8: return launch_variant<O, kFmtLin8, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+            default: return launch_variant<O, kFmtE4M3, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+        }
+    }
+    switch (f.dq_format) {
+        case kFmtE5M2: return launch_variant<O, kFmtE5M2, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+        case kFmtLin8: return launch_variant<O, kFmtLin8, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+        default: return launch_variant<O, kFmtE4M3, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absmax,
@@ -184,6 +316,22 @@ hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absma
         return launch_t<uint16_t>(codes, n, absmax, absmax_q, absmax_scale,
                                   static_cast<uint16_t *>(out), s);
     return launch_t<float>(codes, n, absmax, absmax_q, absmax_scale, static_cast<float *>(out), s);
+}
+
+
+hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format &f,
+                                const float *absmax, const uint8_t *absmax_q,
+                                const float *absmax_scale, const float *absmax_offset, void *out,
+                                nf4_dtype dt, hipStream_t s) {
+    const bool plain = f.blocksize == kBlock &&
+                       (!absmax_q || (f.dq_blocksize == kDqBlock && f.dq_format == kFmtE4M3 &&
+                                      !f.dq_mean_offset));
+    if (plain) return launch_dequantize(codes, n, absmax, absmax_q, absmax_scale, out, dt, s);
+    if (dt == NF4_BF16)
+        return launch_variant_o<uint16_t>(codes, n, f, absmax, absmax_q, absmax_scale,
+                                          absmax_offset, static_cast<uint16_t *>(out), s);
+    return launch_variant_o<float>(codes, n, f, absmax, absmax_q, absmax_scale, absmax_offset,
+                                   static_cast<float *>(out), s);
 }
 
 }  // namespace nf4

@@ -65,6 +65,23 @@ hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t 
 hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absmax,
                              const uint8_t *absmax_q, const float *absmax_scale, void *out,
                              nf4_dtype dt, hipStream_t s);
+// Storage-format variants: block size B1, DQ block B2, the 8-bit code format
+// of double quantization and the tensor-wide mean offset (nf4_format).
+hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_format &f,
+                              uint8_t *codes, float *absmax, uint8_t *absmax_q,
+                              float *absmax_scale, float *absmax_offset, void *workspace,
+                              hipStream_t s);
+hipError_t launch_double_quantize_ex(const float *absmax, int64_t nblocks, const nf4_format &f,
+                                     uint8_t *absmax_q, float *absmax_scale,
+                                     float *absmax_offset, void *workspace, hipStream_t s);
+hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format &f,
+                                const float *absmax, const uint8_t *absmax_q,
+                                const float *absmax_scale, const float *absmax_offset, void *out,
+                                nf4_dtype dt, hipStream_t s);
+// Workspace of the variants: fp32 block scales (when they are not an output
+// of a two-pass quantization) and the partial sums of the mean offset.
+size_t quantize_ex_workspace(int64_t n, const nf4_format &f);
+size_t double_quantize_ex_workspace(int64_t nblocks, const nf4_format &f);
 hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s);
@@ -110,6 +127,49 @@ __device__ __forceinline__ uint32_t e4m3_encode_unit(float r) {
     uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
     uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & (keep & 1u));
     return (uint32_t)((e + 7) << 3) + keep + up;
+}
+
+// OCP FP8 E5M2 encode of r in [0, 1], round to nearest, ties to even (5
+// exponent bits, bias 15, 2 mantissa bits; below 2^-14 uniform with step 2^-16).
+__device__ __forceinline__ uint32_t e5m2_encode_unit(float r) {
+    uint32_t u = __float_as_uint(r);
+    if (u < 0x38800000u) return (uint32_t)__builtin_rintf(r * 65536.0f);
+    int e = (int)(u >> 23) - 127;
+    uint32_t mant = u & 0x7FFFFFu;
+    uint32_t keep = mant >> 21, rest = mant & 0x1FFFFFu;
+    uint32_t up = (rest > 0x100000u) | ((rest == 0x100000u) & (keep & 1u));
+    return (uint32_t)((e + 15) << 2) + keep + up;
+}
+
+// The 8-bit code of double quantization (nf4_dq_format), kS = signed codes
+// (mean offset on). x is c1 (or c1 - mu), sc the stored group value: c2 for
+// the float formats, the step c2 / L for the linear code (L = 255, 127 signed).
+enum : int { kFmtE4M3 = NF4_DQ_E4M3, kFmtE5M2 = NF4_DQ_E5M2, kFmtLin8 = NF4_DQ_LINEAR8 };
+template <bool kS> constexpr float lin_levels() { return kS ? 127.0f : 255.0f; }
+
+template <int F, bool kS>
+__device__ __forceinline__ uint32_t dq_encode(float x, float sc) {
+    if constexpr (F == kFmtLin8) {
+        if (sc == 0.0f) return 0u;
+        const float l = lin_levels<kS>();
+        const float t = fminf(fmaxf(__builtin_rintf(x / sc), -l), l);
+        return (uint32_t)(int)t & 0xFFu;
+    } else {
+        const float r = (sc == 0.0f) ? 0.0f : x / sc;
+        const uint32_t sign = (kS && r < 0.0f) ? 0x80u : 0u;
+        const float a = kS ? fabsf(r) : r;
+        return sign | (F == kFmtE5M2 ? e5m2_encode_unit(a) : e4m3_encode_unit(a));
+    }
+}
+
+// Decode of the code in byte J of v (gfx950's fp8 / bf8 converts decode OCP
+// E4M3FN / E5M2, sign included).
+template <int F, bool kS, int J = 0>
+__device__ __forceinline__ float dq_decode(uint32_t v) {
+    if constexpr (F == kFmtE4M3) return __builtin_amdgcn_cvt_f32_fp8((int)v, J);
+    else if constexpr (F == kFmtE5M2) return __builtin_amdgcn_cvt_f32_bf8((int)v, J);
+    else if constexpr (kS) return (float)(int)(int8_t)(uint8_t)(v >> (8 * J));
+    else return (float)((v >> (8 * J)) & 0xFFu);
 }
 
 // Reconstructed first-level scale c1' of one block.

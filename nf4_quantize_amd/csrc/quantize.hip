@@ -20,6 +20,8 @@
 // sign bits of its d values gathered to nibble positions.
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -166,26 +168,29 @@ __device__ __forceinline__ void load_lut(const CodeLut &lut, float2 *s_lut) {
     if (threadIdx.x < kLutEntries) s_lut[threadIdx.x] = lut_copy_entry(lut.e[threadIdx.x], 0);
 }
 
+// The stored group value of unsigned codes: c2, or the linear code's step.
+template <int F>
+__device__ __forceinline__ float group_value(float c2) {
+    return F == kFmtLin8 ? c2 / lin_levels<false>() : c2;
+}
+
 // Double quantization of the group's 256 c1 values held in s_c1 (threads
 // 0..255 each own one block; a larger workgroup's other threads only join
-// the barriers).
-template <int T>
+// the barriers), 8-bit codes in format F.
+template <int T, int F>
 __device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32_t *s_q8,
                                          uint8_t *absmax_q, float *absmax_scale, int64_t g) {
     const int t = threadIdx.x;
     const float c1 = (t < kDqBlock) ? s_c1[t] : 0.0f;
-    const float c2 = wg_max<T>(c1, s_red);
-    if (t < kDqBlock) {
-        const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
-        reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)e4m3_encode_unit(ratio);
-    }
+    const float sc = group_value<F>(wg_max<T>(c1, s_red));
+    if (t < kDqBlock) reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)dq_encode<F, false>(c1, sc);
     __syncthreads();
     if (t < kDqBlock / 4) reinterpret_cast<uint32_t *>(absmax_q + g * kDqBlock)[t] = s_q8[t];
-    if (t == 0) absmax_scale[g] = c2;
+    if (t == 0) absmax_scale[g] = sc;
 }
 
 // One workgroup of TH threads per full group of 16384 weights.
-template <typename T, bool kDQ, int TH>
+template <typename T, bool kDQ, int TH, int F>
 __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
     uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, CodeLut lut) {
@@ -246,13 +251,13 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     }
     if (kDQ) {
         __syncthreads();
-        group_dq<TH>(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
+        group_dq<TH, F>(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
     }
 }
 
 // The final partial group: thread t owns block t of the group and works
 // element by element with guarded accesses.
-template <typename T>
+template <typename T, int F>
 __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
     const T *__restrict__ w, int64_t n, int64_t g, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale,
@@ -284,13 +289,10 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
     }
     if (absmax_q) {
         __syncthreads();
-        const float c2 = wg_max(s_c1[t], s_red);
+        const float sc = group_value<F>(wg_max(s_c1[t], s_red));
         const int64_t nblocks = (n + kBlock - 1) / kBlock;
-        if (b < nblocks) {
-            const float ratio = (c2 > 0.0f) ? s_c1[t] / c2 : 0.0f;
-            absmax_q[b] = (uint8_t)e4m3_encode_unit(ratio);
-        }
-        if (t == 0) absmax_scale[g] = c2;
+        if (b < nblocks) absmax_q[b] = (uint8_t)dq_encode<F, false>(s_c1[t], sc);
+        if (t == 0) absmax_scale[g] = sc;
     }
 }
 
@@ -314,7 +316,9 @@ __global__ __launch_bounds__(kThreads) void double_quantize_kernel(
 // Threads per group workgroup.
 constexpr int kGroupThreads = 512;
 
-template <typename T>
+// B1 = 64 (and, with double quantization, B2 = 256 without the mean
+// offset): the fused group kernel, 8-bit codes in format F.
+template <typename T, int F>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
                              uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
     const CodeLut &lut = *code_lut();
@@ -322,16 +326,257 @@ hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absma
     constexpr int TH = kGroupThreads;
     if (full > 0) {
         if (absmax_q)
-            quantize_groups_kernel<T, true, TH><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
+            quantize_groups_kernel<T, true, TH, F><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
                 w, codes, absmax, absmax_q, absmax_scale, lut);
         else
-            quantize_groups_kernel<T, false, TH><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
+            quantize_groups_kernel<T, false, TH, kFmtE4M3><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
                 w, codes, absmax, nullptr, nullptr, lut);
     }
     if (n % kGroup)
-        quantize_tail_kernel<T><<<1, kThreads, 0, s>>>(w, n, full, codes, absmax, absmax_q,
-                                                       absmax_scale, lut);
+        quantize_tail_kernel<T, F><<<1, kThreads, 0, s>>>(w, n, full, codes, absmax, absmax_q,
+                                                          absmax_scale, lut);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_quantize_fmt(const T *w, int64_t n, uint8_t *codes, float *absmax,
+                               uint8_t *absmax_q, float *absmax_scale, int fmt, hipStream_t s) {
+    if (fmt == kFmtE5M2)
+        return launch_quantize_t<T, kFmtE5M2>(w, n, codes, absmax, absmax_q, absmax_scale, s);
+    if (fmt == kFmtLin8)
+        return launch_quantize_t<T, kFmtLin8>(w, n, codes, absmax, absmax_q, absmax_scale, s);
+    return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, absmax_q, absmax_scale, s);
+}
+
+// ---- storage-format variants: block sizes other than 64, the mean offset ----
+
+// Blockwise quantization with block size B1 (codes and fp32 absmax; double
+// quantization follows in its own kernel). A wave works on units of
+// U = max(B1, 64 E) weights: one block, or 64 E / B1 whole blocks. Each lane
+// holds S = U / (64 E) slices of a unit, slice i at i * 64 + lane, so every
+// wave load is one contiguous 1 KiB run as in the group kernel. A block's
+// absmax is a DPP max over its B1 / E lanes, or a whole-wave max.
+template <typename T, int B1>
+__global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
+    const T *__restrict__ w, int64_t nunits, uint8_t *__restrict__ codes,
+    float *__restrict__ absmax, CodeLut lut) {
+    using Sl = Slice<T>;
+    constexpr int E = Sl::kElems;
+    constexpr int U = B1 > 64 * E ? B1 : 64 * E;  // weights per unit
+    constexpr int S = U / (64 * E);                // slices per lane and unit
+    constexpr int UPW = S >= 4 ? 1 : 4 / S;        // units per wave
+    constexpr int LPB = B1 / E;                    // lanes per block (S == 1)
+    constexpr int kTab = E * kLutEntries;
+    __shared__ float2 s_lut[kTab];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int64_t unit0 = ((int64_t)blockIdx.x * (kThreads / 64) +
+                           __builtin_amdgcn_readfirstlane(t >> 6)) * UPW;
+    // all loads first (a unit past the end reloads the last one and stores nothing)
+    typename Sl::Vec v[UPW][S];
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+        const int64_t unit = min(unit0 + u, nunits - 1);
+        const typename Sl::Vec *src = reinterpret_cast<const typename Sl::Vec *>(w + unit * U);
+#pragma unroll
+        for (int i = 0; i < S; ++i) v[u][i] = __builtin_nontemporal_load(&src[i * 64 + lane]);
+    }
+    for (int i = t; i < kTab; i += kThreads) s_lut[i] = lut_copy_entry(lut.e[i % kLutEntries], i);
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+        const int64_t unit = unit0 + u;
+        if (unit >= nunits) break;  // uniform over the wave
+        float f[S][E];
+        float mf = 0.0f;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            Sl::widen(v[u][i], f[i]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) mf = fmaxf(mf, fabsf(f[i][e]));
+        }
+        float m;
+        if constexpr (U == B1) {
+            m = wave_max_nonneg(mf);
+            if (lane == 0) absmax[unit] = m;
+        } else {
+            uint32_t mb = __float_as_uint(mf);
+            mb = dpp_umax<0xB1>(mb);                           // quad_perm [1,0,3,2]
+            if (LPB >= 4) mb = dpp_umax<0x4E>(mb);             // quad_perm [2,3,0,1]
+            if (LPB >= 8) mb = dpp_umax<0x141>(mb);            // row_half_mirror
+            if (LPB >= 16) mb = dpp_umax<0x140>(mb);           // row_mirror
+            if (LPB >= 32) mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+            m = __uint_as_float(mb);
+            if ((lane % LPB) == 0) absmax[unit * (U / B1) + lane / LPB] = m;
+        }
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const uint32_t packed = slice_codes<E>(f[i], m, s_lut);
+            const int64_t slice = unit * (U / E) + i * 64 + lane;
+            if (E == 8)
+                reinterpret_cast<uint32_t *>(codes)[slice] = packed;
+            else
+                reinterpret_cast<uint16_t *>(codes)[slice] = (uint16_t)packed;
+        }
+    }
+}
+
+// The blocks after the last full unit: one thread per block, element by
+// element with the correctly rounded division.
+template <typename T>
+__global__ __launch_bounds__(64) void quantize_blocks_tail_kernel(
+    const T *__restrict__ w, int64_t n, int64_t b0, int64_t nblocks, int32_t bs,
+    uint8_t *__restrict__ codes, float *__restrict__ absmax, CodeLut lut) {
+    __shared__ float2 s_lut[kLutEntries];
+    load_lut(lut, s_lut);
+    __syncthreads();
+    const int64_t b = b0 + (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (b >= nblocks) return;
+    const int64_t lo = b * bs;
+    const int64_t hi = min(lo + bs, n);
+    auto elem = [&](int64_t i) -> float {
+        if constexpr (sizeof(T) == 2) return __uint_as_float((uint32_t)w[i] << 16);
+        else return w[i];
+    };
+    float c1 = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) c1 = fmaxf(c1, fabsf(elem(i)));
+    absmax[b] = c1;
+    for (int64_t i = lo; i < hi; i += 2) {
+        uint32_t byte = 0;
+        for (int j = 0; j < 2 && i + j < hi; ++j) {
+            const uint32_t code = (c1 > 0.0f) ? exact_code(s_lut, elem(i + j) / c1) : 7u;
+            byte |= code << (4 * j);
+        }
+        codes[i / 2] = (uint8_t)byte;
+    }
+}
+
+// Pairwise fp32 sum of an aligned chunk of 4096 values (zeros past n), the
+// subtree of the sum over the whole array padded to a power of two: each
+// thread adds its 16 values as a tree, then lanes pair up by XOR shuffles
+// (x + y == y + x, so both lanes of a pair hold the same node) and the four
+// wave sums pair up last. final_mean: one workgroup, writes sum / nf.
+constexpr int kSumChunk = 4096;
+__global__ __launch_bounds__(kThreads) void pairwise_sum_kernel(const float *__restrict__ x,
+                                                                int64_t n, float *__restrict__ out,
+                                                                float nf, int final_mean) {
+    __shared__ float s_w[kThreads / 64];
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * kSumChunk + 16 * t;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (base + i < n) ? x[base + i] : 0.0f;
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * h) v[i] = v[i] + v[i + h];
+    float sum = v[0];
+#pragma unroll
+    for (int k = 1; k < 64; k *= 2) sum = sum + __shfl_xor(sum, k);
+    if ((t & 63) == 0) s_w[t >> 6] = sum;
+    __syncthreads();
+    if (t == 0) {
+        const float tot = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+        out[blockIdx.x] = final_mean ? tot / nf : tot;
+    }
+}
+
+// Double quantization with group size 2^lb2 in format F (kS: mean offset,
+// signed codes). A group of 64 or more blocks is one wave's; smaller groups
+// are aligned lane segments of a wave of 64 consecutive blocks.
+template <int F, bool kS>
+__global__ __launch_bounds__(kThreads) void dq_generic_kernel(
+    const float *__restrict__ absmax, int64_t nblocks, int lb2, const float *__restrict__ mu_p,
+    uint8_t *__restrict__ q, float *__restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const float mu = kS ? *mu_p : 0.0f;
+    const int b2 = 1 << lb2;
+    auto xval = [&](int64_t b) -> float {
+        const float c = absmax[b];
+        return kS ? c - mu : c;
+    };
+    if (b2 >= 64) {
+        const int64_t g = wave;
+        if (g >= ((nblocks + b2 - 1) >> lb2)) return;  // uniform over the wave
+        const int64_t b0 = g << lb2;
+        float m = 0.0f;
+        for (int j = lane; j < b2; j += 64)
+            if (b0 + j < nblocks) m = fmaxf(m, fabsf(xval(b0 + j)));
+        float sc = wave_max_nonneg(m);
+        if (F == kFmtLin8) sc = sc / lin_levels<kS>();
+        if (lane == 0) scale[g] = sc;
+        for (int j = lane; j < b2; j += 64)
+            if (b0 + j < nblocks) q[b0 + j] = (uint8_t)dq_encode<F, kS>(xval(b0 + j), sc);
+    } else {
+        const int64_t b = wave * 64 + lane;
+        const bool live = b < nblocks;
+        const float x = live ? xval(b) : 0.0f;
+        uint32_t mb = __float_as_uint(fabsf(x));
+        for (int k = 1; k < b2; k *= 2) mb = max(mb, (uint32_t)__shfl_xor((int)mb, k));
+        float sc = __uint_as_float(mb);
+        if (F == kFmtLin8) sc = sc / lin_levels<kS>();
+        if (live) {
+            q[b] = (uint8_t)dq_encode<F, kS>(x, sc);
+            if ((lane & (b2 - 1)) == 0) scale[b >> lb2] = sc;
+        }
+    }
+}
+
+template <typename T, int B1>
+hipError_t launch_blocks(const T *w, int64_t n, uint8_t *codes, float *absmax, hipStream_t s) {
+    const CodeLut &lut = *code_lut();
+    constexpr int E = Slice<T>::kElems;
+    constexpr int U = B1 > 64 * E ? B1 : 64 * E;
+    constexpr int S = U / (64 * E);
+    constexpr int UPW = S >= 4 ? 1 : 4 / S;
+    const int64_t nunits = n / U;
+    if (nunits > 0) {
+        const int64_t waves = (nunits + UPW - 1) / UPW;
+        const int64_t wgs = (waves + 3) / 4;
+        quantize_blocks_kernel<T, B1><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
+            w, nunits, codes, absmax, lut);
+    }
+    const int64_t nb = (n + B1 - 1) / B1;
+    const int64_t b0 = nunits * (U / B1);
+    if (b0 < nb)
+        quantize_blocks_tail_kernel<T><<<dim3((unsigned)((nb - b0 + 63) / 64)), dim3(64), 0, s>>>(
+            w, n, b0, nb, B1, codes, absmax, lut);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_blocks_bs(const T *w, int64_t n, int32_t bs, uint8_t *codes, float *absmax,
+                            hipStream_t s) {
+    switch (bs) {
+        case 16: return launch_blocks<T, 16>(w, n, codes, absmax, s);
+        case 32: return launch_blocks<T, 32>(w, n, codes, absmax, s);
+        case 64: return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, nullptr, nullptr, s);
+        case 128: return launch_blocks<T, 128>(w, n, codes, absmax, s);
+        case 256: return launch_blocks<T, 256>(w, n, codes, absmax, s);
+        case 512: return launch_blocks<T, 512>(w, n, codes, absmax, s);
+        case 1024: return launch_blocks<T, 1024>(w, n, codes, absmax, s);
+        case 2048: return launch_blocks<T, 2048>(w, n, codes, absmax, s);
+        default: return launch_blocks<T, 4096>(w, n, codes, absmax, s);
+    }
+}
+
+int ilog2(int64_t v) {
+    int l = 0;
+    while ((int64_t(1) << l) < v) ++l;
+    return l;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+template <int F, bool kS>
+void launch_dq_generic(const float *absmax, int64_t nb, int lb2, const float *mu, uint8_t *q,
+                       float *scale, hipStream_t s) {
+    const int64_t waves = lb2 >= 6 ? ((nb + (int64_t(1) << lb2) - 1) >> lb2) : (nb + 63) / 64;
+    dq_generic_kernel<F, kS><<<dim3((unsigned)((waves + 3) / 4)), dim3(kThreads), 0, s>>>(
+        absmax, nb, lb2, mu, q, scale);
 }
 
 }  // namespace
@@ -339,10 +584,10 @@ hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absma
 hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *codes, float *absmax,
                            uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
     if (dt == NF4_BF16)
-        return launch_quantize_t<uint16_t>(static_cast<const uint16_t *>(w), n, codes, absmax,
-                                           absmax_q, absmax_scale, s);
-    return launch_quantize_t<float>(static_cast<const float *>(w), n, codes, absmax, absmax_q,
-                                    absmax_scale, s);
+        return launch_quantize_t<uint16_t, kFmtE4M3>(static_cast<const uint16_t *>(w), n, codes,
+                                                     absmax, absmax_q, absmax_scale, s);
+    return launch_quantize_t<float, kFmtE4M3>(static_cast<const float *>(w), n, codes, absmax,
+                                              absmax_q, absmax_scale, s);
 }
 
 hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t *absmax_q,
@@ -351,6 +596,86 @@ hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t 
     double_quantize_kernel<<<dim3((unsigned)groups), dim3(kThreads), 0, s>>>(absmax, nblocks,
                                                                              absmax_q, absmax_scale);
     return hipGetLastError();
+}
+
+
+size_t double_quantize_ex_workspace(int64_t nblocks, const nf4_format &f) {
+    if (!f.dq_mean_offset) return 0;
+    const int64_t l1 = std::max<int64_t>(1, (nblocks + kSumChunk - 1) / kSumChunk);
+    const int64_t l2 = std::max<int64_t>(1, (l1 + kSumChunk - 1) / kSumChunk);
+    return round256(4 * (size_t)l1) + round256(4 * (size_t)l2);
+}
+
+size_t quantize_ex_workspace(int64_t n, const nf4_format &f) {
+    const int64_t nb = (n + f.blocksize - 1) / f.blocksize;
+    const bool fused = f.blocksize == kBlock && f.dq_blocksize == kDqBlock && !f.dq_mean_offset;
+    return (fused ? 0 : round256(4 * (size_t)nb)) + double_quantize_ex_workspace(nb, f);
+}
+
+hipError_t launch_double_quantize_ex(const float *absmax, int64_t nb, const nf4_format &f,
+                                     uint8_t *absmax_q, float *absmax_scale,
+                                     float *absmax_offset, void *workspace, hipStream_t s) {
+    const int lb2 = ilog2(f.dq_blocksize);
+    if (f.dq_mean_offset) {
+        // mu: the pairwise sum level by level (ping-pong between two partial
+        // buffers), the last level divides by the block count
+        const int64_t l1 = std::max<int64_t>(1, (nb + kSumChunk - 1) / kSumChunk);
+        float *buf[2] = {static_cast<float *>(workspace),
+                         static_cast<float *>(workspace) + round256(4 * (size_t)l1) / 4};
+        const float *src = absmax;
+        int64_t len = nb;
+        for (int lvl = 0; len > kSumChunk; ++lvl) {
+            const int64_t outlen = (len + kSumChunk - 1) / kSumChunk;
+            pairwise_sum_kernel<<<dim3((unsigned)outlen), dim3(kThreads), 0, s>>>(
+                src, len, buf[lvl & 1], 0.0f, 0);
+            src = buf[lvl & 1];
+            len = outlen;
+        }
+        pairwise_sum_kernel<<<1, kThreads, 0, s>>>(src, len, absmax_offset, (float)nb, 1);
+        switch (f.dq_format) {
+            case kFmtE5M2: launch_dq_generic<kFmtE5M2, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s); break;
+            case kFmtLin8: launch_dq_generic<kFmtLin8, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s); break;
+            default: launch_dq_generic<kFmtE4M3, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s);
+        }
+    } else {
+        switch (f.dq_format) {
+            case kFmtE5M2: launch_dq_generic<kFmtE5M2, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s); break;
+            case kFmtLin8: launch_dq_generic<kFmtLin8, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s); break;
+            default: launch_dq_generic<kFmtE4M3, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_format &f,
+                              uint8_t *codes, float *absmax, uint8_t *absmax_q,
+                              float *absmax_scale, float *absmax_offset, void *workspace,
+                              hipStream_t s) {
+    const bool dq = absmax_q != nullptr;
+    const bool bf = dt == NF4_BF16;
+    const bool fused = f.blocksize == kBlock &&
+                       (!dq || (f.dq_blocksize == kDqBlock && !f.dq_mean_offset));
+    if (fused) {
+        if (bf)
+            return launch_quantize_fmt<uint16_t>(static_cast<const uint16_t *>(w), n, codes,
+                                                 absmax, absmax_q, absmax_scale, f.dq_format, s);
+        return launch_quantize_fmt<float>(static_cast<const float *>(w), n, codes, absmax,
+                                          absmax_q, absmax_scale, f.dq_format, s);
+    }
+    // two passes: codes and fp32 absmax, then double quantization
+    const int64_t nb = (n + f.blocksize - 1) / f.blocksize;
+    float *am = absmax;
+    void *rest = workspace;
+    if (dq) {
+        if (!am) am = static_cast<float *>(workspace);
+        rest = static_cast<char *>(workspace) + round256(4 * (size_t)nb);
+    }
+    hipError_t e = bf ? launch_blocks_bs<uint16_t>(static_cast<const uint16_t *>(w), n,
+                                                   f.blocksize, codes, am, s)
+                      : launch_blocks_bs<float>(static_cast<const float *>(w), n, f.blocksize,
+                                                codes, am, s);
+    if (e != hipSuccess || !dq) return e;
+    return launch_double_quantize_ex(am, nb, f, absmax_q, absmax_scale, absmax_offset, rest, s);
 }
 
 }  // namespace nf4

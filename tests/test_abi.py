@@ -149,8 +149,8 @@ def test_workspace_size(L):
 
 def test_config_surface():
     nq.NF4Config().validate()
-    for bad in (dict(quant_type="fp4"), dict(compute_dtype="float32"), dict(blocksize=128),
-                dict(load_in_4bit=False)):
+    for bad in (dict(quant_type="fp4"), dict(compute_dtype="float32"), dict(blocksize=96),
+                dict(load_in_4bit=False), dict(dq_format="int8")):
         with pytest.raises(ValueError):
             nq.NF4Config(**bad).validate()
 
@@ -192,3 +192,75 @@ def test_lora_backward_validation(L):
     assert call(wsp=None) == 5
     assert call(wsb=ws - 1) == 5
     assert call(wsp=FAKE + 16) == 4  # the workspace is 256-byte aligned
+
+
+def _fmt(bs=64, dq=256, f=0, off=0):
+    return ctypes.byref(nq.nf4_format(bs, dq, f, off))
+
+
+def test_format_variant_validation(L):
+    """nf4_quantize_ex / nf4_double_quantize_ex / nf4_dequantize_ex reject bad
+    formats, sizes, pointers, alignment and workspace before any HIP call."""
+    q = L.nf4_quantize_ex
+    ok = dict(w=FAKE, dt=nq.NF4_BF16, n=1024, codes=FAKE, am=None, aq=FAKE, asc=FAKE, off=FAKE,
+              ws=FAKE, wsb=1 << 20)
+
+    def call_q(fmt, **kw):
+        a = dict(ok, **kw)
+        return q(a["w"], a["dt"], a["n"], fmt, a["codes"], a["am"], a["aq"], a["asc"], a["off"],
+                 a["ws"], a["wsb"], None)
+
+    assert call_q(None) == 1
+    for bad in (_fmt(bs=8), _fmt(bs=96), _fmt(bs=8192), _fmt(dq=0), _fmt(dq=3), _fmt(dq=8192),
+                _fmt(f=3), _fmt(f=-1), _fmt(off=2)):
+        assert call_q(bad) == 3
+    assert call_q(_fmt(), n=-1) == 2
+    assert call_q(_fmt(), dt=7) == 3
+    assert call_q(_fmt(bs=128), n=0) == 0
+    assert call_q(_fmt(), w=None) == 1
+    assert call_q(_fmt(), aq=None) == 1  # one of the two DQ outputs missing
+    assert call_q(_fmt(), aq=None, asc=None) == 1  # no DQ and no absmax
+    assert call_q(_fmt(off=1), off=None) == 1
+    assert call_q(_fmt(), w=FAKE + 4) == 4
+    assert call_q(_fmt(), off=FAKE + 2) == 4
+    # two-pass formats need a workspace: missing, too small, misaligned
+    need = L.nf4_quantize_ex_workspace_size(1024, _fmt(bs=128))
+    assert need == 256 * ((1024 // 128 * 4 + 255) // 256)
+    assert call_q(_fmt(bs=128), ws=None) == 5
+    assert call_q(_fmt(bs=128), wsb=need - 1) == 5
+    assert call_q(_fmt(bs=128), ws=FAKE + 16) == 4
+    assert L.nf4_quantize_ex_workspace_size(1024, _fmt()) == 0
+    assert L.nf4_quantize_ex_workspace_size(1024, _fmt(f=2)) == 0
+    assert L.nf4_quantize_ex_workspace_size(1024, _fmt(bs=48)) == ctypes.c_size_t(-1).value
+    # the mean offset: block scales, then two partial-sum buffers
+    assert L.nf4_quantize_ex_workspace_size(1 << 20, _fmt(off=1)) == 4 * (1 << 14) + 256 + 256
+    assert L.nf4_double_quantize_ex_workspace_size(5000, _fmt(off=1)) == 256 + 256
+    assert L.nf4_double_quantize_ex_workspace_size(5000, _fmt(f=1)) == 0
+
+    dq = L.nf4_double_quantize_ex
+    assert dq(FAKE, 100, _fmt(dq=5), FAKE, FAKE, None, None, 0, None) == 3
+    assert dq(FAKE, -1, _fmt(), FAKE, FAKE, None, None, 0, None) == 2
+    assert dq(None, 100, _fmt(), FAKE, FAKE, None, None, 0, None) == 1
+    assert dq(FAKE, 100, _fmt(off=1), FAKE, FAKE, None, FAKE, 1024, None) == 1
+    assert dq(FAKE, 100, _fmt(off=1), FAKE, FAKE, FAKE, None, 0, None) == 5
+    assert dq(FAKE + 2, 100, _fmt(), FAKE, FAKE, None, None, 0, None) == 4
+
+    dz = L.nf4_dequantize_ex
+    assert dz(FAKE, 1024, _fmt(bs=32), None, FAKE, FAKE, None, FAKE, 9, None) == 3
+    assert dz(FAKE, 1024, _fmt(bs=32, off=1), None, FAKE, FAKE, None, FAKE, 1, None) == 1
+    assert dz(FAKE, 1024, _fmt(bs=32), None, None, None, None, FAKE, 1, None) == 1
+    assert dz(FAKE + 8, 1024, _fmt(bs=32), FAKE, None, None, None, FAKE, 1, None) == 4
+    assert dz(FAKE, 1024, None, FAKE, None, None, None, FAKE, 1, None) == 1
+    assert dz(FAKE, 0, _fmt(bs=32), None, None, None, None, None, 1, None) == 0
+
+
+def test_format_surface():
+    f = nq.NF4Format(blocksize=128, dq_format="e5m2", mean_offset=True)
+    assert not f.is_default and nq.NF4Format().is_default
+    assert f.nblocks(1000) == 8 and f.ngroups(1 << 20) == 32
+    with pytest.raises(ValueError):
+        nq.NF4Format(dq_format="fp8").struct()
+    assert nq.NF4Config(blocksize=128, dq_format="linear8").validate().format() == \
+        nq.NF4Format(128, 256, "linear8", False)
+    with pytest.raises(ValueError):
+        nq.NF4Config(blocksize=96).validate()
