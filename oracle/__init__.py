@@ -76,6 +76,8 @@ def lib():
         L.nf4ref_block_scale_ex.restype = ctypes.c_float
         L.nf4ref_dequantize_range_ex.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, ctypes.c_int,
                                                  _p, _p, _p, _p, _p, ctypes.c_int]
+        L.nf4ref_merged_weight.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i32,
+                                           ctypes.c_float, _p, _i64, _p]
         L.nf4ref_lora_grads.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _i32, ctypes.c_double,
                                         _p, _i64, _p, _p, _i64, _p]
         _lib = L
@@ -297,6 +299,38 @@ def dequantize_ex(codes, n, blocksize=BLOCK, dq_blocksize=DQ_BLOCK, dq_format="e
                                             _ptr(q), _ptr(scale), _ptr(off), _ptr(out),
                                             out_dtype), "dequantize_range_ex")
     return out
+
+
+# ---- merging the adapter into the quantized base ----
+
+def merged_weight(codes, shape, A, B, s, absmax=None, q=None, scale=None, rows=None):
+    """fp32 rows of Wm = dequantize(W) + s (A B)^T (see nf4ref_merged_weight)."""
+    N, K = shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    r = A.shape[1]
+    rows = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = N if rows is None else rows.size
+    out = np.zeros((nr, K), np.float32)
+    _check(lib().nf4ref_merged_weight(_ptr(codes), _ptr(absmax), _ptr(q), _ptr(scale), N, K,
+                                      _ptr(A), _ptr(B), r, float(np.float32(s)), _ptr(rows), nr,
+                                      _ptr(out)), "merged_weight")
+    return out
+
+
+def merge_lora(codes, shape, A, B, s, absmax=None, q=None, scale=None, dq=True):
+    """Merge and re-quantize: returns (codes, absmax, q, scale) of the merged
+    weight (q and scale None when dq is False) and the fp32 merged weight."""
+    wm = merged_weight(codes, shape, A, B, s, absmax, q, scale)
+    nc, na = quantize(wm.ravel())
+    if not dq:
+        return nc, na, None, None, wm
+    nq8, nsc = double_quantize(na)
+    return nc, na, nq8, nsc, wm
 
 
 def storage_bytes(n, dq):

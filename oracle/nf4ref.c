@@ -487,6 +487,37 @@ int nf4ref_dequantize_range_ex(const uint8_t *codes, int64_t n, int64_t start, i
     return 0;
 }
 
+/* ---- merging the adapter into the quantized base (see nf4ref.h) ---- */
+
+int nf4ref_merged_weight(const uint8_t *codes, const float *absmax, const uint8_t *q,
+                         const float *scale, int64_t N, int64_t K, const uint16_t *A,
+                         const uint16_t *B, int32_t r, float s, const int64_t *rows,
+                         int64_t nrows, float *wm) {
+    if (N <= 0 || K <= 0 || r < 0 || (r > 0 && (!A || !B)) || !codes || !wm) return -1;
+    if (!q && !absmax) return -1;
+    if (q && !scale) return -1;
+    if (!rows) nrows = N;
+    if (nrows < 0) return -1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t n = rows ? rows[i] : i;
+        if (n < 0 || n >= N) return -1;
+        /* the dequantized row of the base */
+        if (nf4ref_dequantize_range(codes, N * K, n * K, K, absmax, q, scale, wm + i * K,
+                                    NF4REF_F32) != 0)
+            return -1;
+        for (int64_t k = 0; k < K; ++k) {
+            double d = 0.0;
+            for (int32_t j = 0; j < r; ++j)
+                d += (double)nf4ref_bf16_to_f32(A[k * r + j]) *
+                     (double)nf4ref_bf16_to_f32(B[(int64_t)j * N + n]);
+            float d32 = (float)d;
+            float delta = s * d32;
+            wm[i * K + k] = wm[i * K + k] + delta;
+        }
+    }
+    return 0;
+}
+
 /* ---- storage footprint ([L15] "Double quantisation" per-parameter tables) ---- */
 
 int64_t nf4ref_storage_bytes(int64_t n, int dq) {

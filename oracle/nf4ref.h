@@ -187,6 +187,24 @@ int nf4ref_dequantize_range_ex(const uint8_t *codes, int64_t n, int64_t start, i
                                const float *absmax, const uint8_t *q, const float *scale,
                                const float *offset, void *out, int out_dtype);
 
+/* ---- Merging the adapter into the quantized base ([QP] "Step 4: Merging and
+ * Inference"; "QLoRA: quantising the part you are not training" (addaly),
+ * "What it costs", item 3: a merge into the quantized base must re-quantize).
+ * With Y = X W'^T + s (X A) B, the merged weight is
+ *   Wm[n][k] = fl32(W'[n][k] + fl32(s * fl32(d[n][k]))),  d[n][k] = sum_j A[k][j] B[j][n]
+ * with d summed in double (every product of two bf16 values is exact) and
+ * rounded once to fp32, and W' the fp32 dequantized base. The
+ * merged weight is then re-quantized blockwise (and double-quantized) as by
+ * nf4ref_quantize / nf4ref_double_quantize.
+ *   codes, q, scale, absmax: the base ([N x K], q == NULL: plain absmax)
+ *   A bf16 [K x r], B bf16 [r x N], s = alpha / r
+ *   rows (nrows indices into N, NULL = all): the rows written to wm, fp32
+ *   [nrows x K]. Returns 0, or -1 on invalid arguments. */
+int nf4ref_merged_weight(const uint8_t *codes, const float *absmax, const uint8_t *q,
+                         const float *scale, int64_t N, int64_t K, const uint16_t *A,
+                         const uint16_t *B, int32_t r, float s, const int64_t *rows,
+                         int64_t nrows, float *wm);
+
 #ifdef __cplusplus
 }
 #endif
