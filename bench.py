@@ -361,6 +361,21 @@ def kernel_benches(dev, iters, warmup, with_stack):
                                                "GFLOP/s": lflops / ms / 1e6, "bytes": lbytes}
     log(f"lora backward: {out['lora_backward_4096x8192x8192_r64']}")
     del gA, gB, lws
+    # merging the adapter into the quantized base and re-quantizing, over 4
+    # rotating copies of the base (4 x 2 x 34.6 MB in and out, more than the
+    # last-level cache); in + out storage and the adapter once
+    bases = [wt] + [nq.quantize((torch.randn((N, K), generator=g, device=dev) * 0.02)
+                                .to(torch.bfloat16)) for _ in range(3)]
+    merged = [nq.empty_nf4((N, K), dev) for _ in range(4)]
+    mws = torch.empty(nq.nf4_merge_lora_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    ms, pc = time_op(lambda i: nq.nf4_merge_lora(bases[i % 4], A, B, s, merged[i % 4], workspace=mws),
+                     lin_iters, max(1, warmup // 2))
+    mbytes = 2 * nq.nf4_storage_bytes(N * K) + 2 * (K * r + r * N)
+    out["merge_lora_8192x8192_r64"] = {"ms": ms, "p10_p50_p90_ms": pc, "GB/s": mbytes / ms / 1e6,
+                                       "hbm_frac": mbytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": mbytes,
+                                       "TFLOP/s": 2 * N * K * r / ms / 1e9}
+    log(f"merge: {out['merge_lora_8192x8192_r64']}")
+    del bases[1:], merged, mws
     # practical ceiling: the vendor bf16 GEMM on a pre-dequantized weight
     Wd = nq.dequantize(wt, torch.bfloat16)
     ms, pc = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))

@@ -179,6 +179,36 @@ nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k
                              void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace nf4_merge_lora needs: the fp32 block scales of the
+ * merged weight (n_out * k_in / 64 floats, rounded up to 256 bytes), used when
+ * the merged weight is double-quantized and absmax_out is NULL. Returns 0 for
+ * invalid sizes. */
+size_t nf4_merge_lora_workspace_size(int64_t n_out, int64_t k_in);
+
+/* Merges the low-rank adapter into the quantized base and re-quantizes
+ * ([QP] "Step 4: Merging and Inference"; "QLoRA: quantising the part you are
+ * not training" (addaly), "What it costs", item 3: merging into the quantized
+ * base has to re-quantize). With W' = dequantize(w) in fp32:
+ *   Wm[n][k] = fl32(W'[n][k] + fl32(lora_scale * d[n][k])),  d = (A . B)^T [N x K]
+ * d is accumulated in fp32 on the matrix cores from the bf16 adapter (every
+ * product exact, the order of the sum over the rank unspecified), then Wm is
+ * quantized blockwise exactly as nf4_quantize does (codes_out, absmax_out),
+ * and double-quantized as nf4_double_quantize does when absmax_q_out and
+ * absmax_scale_out are given.
+ *   w          the base: default format (B1 = 64; B2 = 256 if double-quantized)
+ *   lora_a     device bf16 [k_in x r], 16-byte aligned; lora_b device bf16 [r x n_out]
+ *   codes_out  device out, n_out * k_in / 2 bytes, 16-byte aligned
+ *   absmax_out device out or NULL, one float per 64 weights
+ *   absmax_q_out, absmax_scale_out  device out or both NULL (then absmax_out is required)
+ *   workspace  >= nf4_merge_lora_workspace_size bytes, 256-byte aligned, when
+ *              double quantization is requested without absmax_out; else may be NULL
+ * The outputs may be the base's own buffers (in-place merge). k_in % 64 == 0,
+ * r % 8 == 0, 8 <= r <= 256. */
+nf4_status nf4_merge_lora(const nf4_weight *w, const void *lora_a, const void *lora_b, int32_t r,
+                          float lora_scale, uint8_t *codes_out, float *absmax_out,
+                          uint8_t *absmax_q_out, float *absmax_scale_out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* ---- Storage-format variants ----
  * The entry points above fix B1 = 64, B2 = 256 and the E4M3FN code. [MF]
  * "Block-Wise Quantization Mechanics" gives 64 as the typical block size, and

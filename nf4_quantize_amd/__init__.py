@@ -51,6 +51,8 @@ EXPORTS = (
     "nf4_double_quantize_ex_workspace_size",
     "nf4_double_quantize_ex",
     "nf4_dequantize_ex",
+    "nf4_merge_lora_workspace_size",
+    "nf4_merge_lora",
 )
 
 # nf4_dq_format: the 8-bit code of double quantization.
@@ -137,6 +139,11 @@ def lib():
     L.nf4_double_quantize_ex.restype = ctypes.c_int
     L.nf4_dequantize_ex.argtypes = [p, i64, fmt_p, p, p, p, p, p, ctypes.c_int, p]
     L.nf4_dequantize_ex.restype = ctypes.c_int
+    L.nf4_merge_lora_workspace_size.argtypes = [i64, i64]
+    L.nf4_merge_lora_workspace_size.restype = ctypes.c_size_t
+    L.nf4_merge_lora.argtypes = [ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p, p, p, p,
+                                 ctypes.c_size_t, p]
+    L.nf4_merge_lora.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -538,3 +545,40 @@ def nf4_lora_backward(x, dy, lora_a, lora_b, lora_scale=1.0, grad_dtype=None, gr
 linear_forward = nf4_linear_forward
 linear_backward_input = nf4_linear_backward_input
 lora_backward = nf4_lora_backward
+
+
+# ------------------------------------------------- merging the adapter
+
+def nf4_merge_lora_workspace_size(n_out, k_in):
+    return int(lib().nf4_merge_lora_workspace_size(n_out, k_in))
+
+
+def nf4_merge_lora(w: NF4Tensor, lora_a, lora_b, lora_scale, out: NF4Tensor, workspace=None):
+    """W_out = quantize(dequantize(w) + lora_scale (A B)^T) into out's buffers
+    (out may be w itself: an in-place merge)."""
+    _need_cuda(lora_a, lora_b, out.codes, out.absmax, out.absmax_q, out.absmax_scale, workspace)
+    if out.absmax_q is not None and out.absmax is None and workspace is None:
+        workspace = _workspace(nf4_merge_lora_workspace_size(*w.shape), lora_a.device)
+    ws = w.weight_struct()
+    st = lib().nf4_merge_lora(ctypes.byref(ws), _ptr(lora_a), _ptr(lora_b), lora_a.shape[1],
+                              float(lora_scale), _ptr(out.codes), _ptr(out.absmax),
+                              _ptr(out.absmax_q), _ptr(out.absmax_scale), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(),
+                              _stream(lora_a.device))
+    _check(st, "nf4_merge_lora")
+    return out
+
+
+def merge_lora(w: NF4Tensor, lora_a, lora_b, lora_scale=1.0, out: Optional[NF4Tensor] = None,
+               double_quant=None, keep_absmax=False, workspace=None):
+    """Merges the adapter (A [K x r], B [r x N] bf16) into the NF4 weight w
+    [N x K] and re-quantizes; returns the merged NF4Tensor (new buffers unless
+    `out` is given; `out=w` merges in place)."""
+    if out is None:
+        dq = w.double_quant if double_quant is None else double_quant
+        out = empty_nf4(w.shape, w.codes.device, dq, keep_absmax)
+    return nf4_merge_lora(w, lora_a, lora_b, lora_scale, out, workspace)
+
+
+lora_merge = merge_lora
+

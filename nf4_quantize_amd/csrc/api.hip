@@ -423,3 +423,49 @@ NF4_API nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_
         (dq && f->dq_mean_offset) ? absmax_offset : nullptr, out, out_dtype,
         static_cast<hipStream_t>(stream)));
 }
+
+// ---- merging the adapter into the quantized base ----
+
+NF4_API size_t nf4_merge_lora_workspace_size(int64_t n_out, int64_t k_in) {
+    if (n_out <= 0 || k_in <= 0 || (k_in % kBlock) != 0 || n_out * k_in > kMaxElems) return 0;
+    return nf4::merge_workspace(n_out, k_in);
+}
+
+NF4_API nf4_status nf4_merge_lora(const nf4_weight *w, const void *lora_a, const void *lora_b,
+                                  int32_t r, float lora_scale, uint8_t *codes_out, float *absmax_out,
+                                  uint8_t *absmax_q_out, float *absmax_scale_out, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (!w) return NF4_ERR_NULL;
+    if (w->n_out <= 0 || w->k_in <= 0 || (w->k_in % kBlock) != 0) return NF4_ERR_SIZE;
+    if (w->n_out * w->k_in > kMaxElems) return NF4_ERR_SIZE;
+    if (r < 8 || r > 256 || (r % 8) != 0) return NF4_ERR_SIZE;
+    if (w->blocksize != kBlock) return NF4_ERR_UNSUPPORTED;
+    if (!code_lut()) return NF4_ERR_UNSUPPORTED;
+    const bool dq_in = w->absmax_q != nullptr || w->absmax_scale != nullptr;
+    if (dq_in && w->dq_blocksize != kDqBlock) return NF4_ERR_UNSUPPORTED;
+    if (!w->codes || !lora_a || !lora_b || !codes_out) return NF4_ERR_NULL;
+    if (dq_in && (!w->absmax_q || !w->absmax_scale)) return NF4_ERR_NULL;
+    if (!dq_in && !w->absmax) return NF4_ERR_NULL;
+    const bool dq_out = absmax_q_out != nullptr || absmax_scale_out != nullptr;
+    if (dq_out && (!absmax_q_out || !absmax_scale_out)) return NF4_ERR_NULL;
+    if (!dq_out && !absmax_out) return NF4_ERR_NULL;
+    if (!aligned(w->codes, 16) || !aligned(codes_out, 16) || !aligned(lora_a, 16) ||
+        !aligned(lora_b, 2))
+        return NF4_ERR_ALIGN;
+    if ((w->absmax && !aligned(w->absmax, 4)) || (w->absmax_q && !aligned(w->absmax_q, 4)) ||
+        (w->absmax_scale && !aligned(w->absmax_scale, 4)) || (absmax_out && !aligned(absmax_out, 4)) ||
+        (absmax_q_out && !aligned(absmax_q_out, 4)) ||
+        (absmax_scale_out && !aligned(absmax_scale_out, 4)))
+        return NF4_ERR_ALIGN;
+    if (dq_out && !absmax_out) {
+        const size_t need = nf4::merge_workspace(w->n_out, w->k_in);
+        if (!workspace || workspace_bytes < need) return NF4_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return NF4_ERR_ALIGN;
+    }
+    nf4_weight wv = *w;
+    if (!dq_in) wv.absmax_q = nullptr, wv.absmax_scale = nullptr;
+    return launch_status(nf4::launch_merge(
+        wv, static_cast<const uint16_t *>(lora_a), static_cast<const uint16_t *>(lora_b), r,
+        lora_scale, codes_out, absmax_out, absmax_q_out, absmax_scale_out, workspace,
+        static_cast<hipStream_t>(stream)));
+}

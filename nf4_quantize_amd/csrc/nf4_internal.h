@@ -82,6 +82,11 @@ hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_forma
 // of a two-pass quantization) and the partial sums of the mean offset.
 size_t quantize_ex_workspace(int64_t n, const nf4_format &f);
 size_t double_quantize_ex_workspace(int64_t nblocks, const nf4_format &f);
+// Merging the adapter into the quantized base (W [N x K] default format).
+size_t merge_workspace(int64_t n_out, int64_t k_in);
+hipError_t launch_merge(const nf4_weight &w, const uint16_t *a, const uint16_t *b, int32_t r,
+                        float s_lora, uint8_t *codes_out, float *absmax_out, uint8_t *absmax_q_out,
+                        float *absmax_scale_out, void *workspace, hipStream_t s);
 hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s);

@@ -579,6 +579,209 @@ void launch_dq_generic(const float *absmax, int64_t nb, int lb2, const float *mu
         absmax, nb, lb2, mu, q, scale);
 }
 
+// ---- merging the adapter into the quantized base ----
+//
+// W_new = quantize(fl32(W' + fl32(s * fl32(d)))), d[n][k] = sum_j A[k][j] B[j][n],
+// W' the dequantized base [N x K]. A workgroup owns 64 weight rows and walks a
+// run of 256-column tiles; in each tile wave w owns the 64-column block
+// kb = k0 + 64 w of the 64 rows. B^T for the 64 rows is transposed into LDS
+// once. Per tile and wave:
+//   - the delta D[n][k] = sum_j B^T[n][j] A[k][j] on the matrix cores
+//     (v_mfma_f32_16x16x32_bf16; A's rows hold the rank index contiguously,
+//     so its fragments come straight from memory);
+//   - two passes of 32 rows: the delta rows go through LDS so that lane l
+//     holds half h = l & 1 of row l / 2's block (32 weights, one 16-byte code
+//     load); the lane dequantizes them, adds s * d, the block max is the max
+//     of the lane pair, and the merged values get their codes from the same
+//     nearest-level search as the quantize kernels.
+// The next tile's A fragments, codes and scales are loaded while the current
+// tile is computed; waves never wait for each other inside the loop. The new
+// fp32 block scales go to absmax (or the workspace) for double quantization.
+typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMergeRows = 64;
+constexpr int kMergeCols = 256;
+constexpr int kMergeRankMax = 256;
+constexpr int kCStride = 68;  // fp32 row stride of a delta tile (rows 4 apart hit other banks)
+
+struct MergeParams {
+    const uint8_t *codes;  // base codes
+    const uint8_t *q8;     // base E4M3 scale codes, or nullptr
+    const float *c2;       // base second-level scales
+    const float *absmax;   // base fp32 block scales (when q8 == nullptr)
+    const uint16_t *a;     // bf16 [K x r]
+    const uint16_t *b;     // bf16 [r x N]
+    int64_t n_rows, k_cols;
+    int32_t col_tiles, tiles_per_wg, chunks;
+    int32_t r, rp;         // rank, and the rank rounded up to 32
+    float s;
+    uint8_t *new_codes;
+    float *new_absmax;
+    float lv[16];
+};
+
+// Global data of one tile for one lane: A fragments of the first two rank
+// steps, and for each 32-row pass the lane's 16 code bytes and block scale.
+struct MergeTile {
+    u32x4 bo[2][4];
+    u32x4 code[2];
+    float c1o[2];
+};
+
+__global__ __launch_bounds__(kThreads) void merge_requantize_kernel(MergeParams p, CodeLut lut) {
+    constexpr int kTab = 8 * kLutEntries;
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_bt[];  // [64][rp + 8]
+    __shared__ __attribute__((aligned(16))) float s_c[4][32 * kCStride];
+    __shared__ float2 s_lut[kTab];
+    __shared__ float s_lv[16];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lr = lane & 15, g = lane >> 4, h = lane & 1;
+    const int64_t rt = blockIdx.x / p.chunks;
+    const int ct0 = (int)(blockIdx.x % p.chunks) * p.tiles_per_wg;
+    const int ct1 = min(ct0 + p.tiles_per_wg, p.col_tiles);
+    const int64_t n0 = rt * kMergeRows;
+    const int bts = p.rp + 8;
+
+    auto load_tile = [&](int ct) {
+        MergeTile d;
+        const int64_t kb = (int64_t)ct * kMergeCols + 64 * w;
+        const bool live = kb < p.k_cols;  // uniform over the wave
+        const int64_t kl = live ? kb : 0;
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+            for (int tk = 0; tk < 4; ++tk) {
+                const int j0 = 32 * js + 8 * g;
+                d.bo[js][tk] = (live && j0 < p.r)
+                                   ? *reinterpret_cast<const u32x4 *>(p.a + (kl + 16 * tk + lr) * p.r + j0)
+                                   : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const int64_t n = n0 + 32 * ps + (lane >> 1);
+            const int64_t nl = n < p.n_rows ? n : 0;  // rows past N reload row 0, store nothing
+            d.code[ps] = *reinterpret_cast<const u32x4 *>(p.codes + nl * (p.k_cols / 2) + kl / 2 + 16 * h);
+            const int64_t ob = nl * (p.k_cols / kBlock) + kl / kBlock;
+            d.c1o[ps] = p.q8 ? __builtin_amdgcn_cvt_f32_fp8((int)p.q8[ob], 0) * p.c2[ob / kDqBlock]
+                             : p.absmax[ob];
+        }
+        return d;
+    };
+
+    MergeTile cur = load_tile(ct0);
+
+    // B^T tile: Bt[n][j] = B[j][n0 + n], zero past N and past the rank
+    // (16 loads per thread in flight, then 16 stores; one pass for r <= 64)
+    for (int base = 0; base < kMergeRows * p.rp; base += 16 * kThreads) {
+        uint16_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int idx = base + u * kThreads + t;
+            const int nn = idx & 63, j = idx >> 6;
+            v[u] = (j < p.r && n0 + nn < p.n_rows) ? p.b[(int64_t)j * p.n_rows + n0 + nn] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int idx = base + u * kThreads + t;
+            if (idx < kMergeRows * p.rp) s_bt[(idx & 63) * bts + (idx >> 6)] = v[u];
+        }
+    }
+    for (int i = t; i < kTab; i += kThreads) s_lut[i] = lut_copy_entry(lut.e[i % kLutEntries], i);
+    if (t < 16) s_lv[t] = p.lv[t];
+    __syncthreads();
+
+    float *cw = s_c[w];
+    for (int ct = ct0; ct < ct1; ++ct) {
+        const MergeTile nxt = load_tile(min(ct + 1, ct1 - 1));
+        const int64_t kb = (int64_t)ct * kMergeCols + 64 * w;
+        if (kb >= p.k_cols) continue;  // uniform over the wave
+
+        // the delta of the wave's block: D[16 tn + 4 g + q][16 tk + lr] in acc[tn][tk][q]
+        mf32x4_t acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int js = 0; js < p.rp / 32; ++js) {
+            const int j0 = 32 * js + 8 * g;
+            u32x4 bq[4], ao[4];
+#pragma unroll
+            for (int tk = 0; tk < 4; ++tk) {
+                if (js < 2)
+                    bq[tk] = cur.bo[js & 1][tk];
+                else
+                    bq[tk] = j0 < p.r
+                                 ? *reinterpret_cast<const u32x4 *>(p.a + (kb + 16 * tk + lr) * p.r + j0)
+                                 : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+                ao[tn] = *reinterpret_cast<const u32x4 *>(s_bt + (16 * tn + lr) * bts + j0);
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+                for (int tk = 0; tk < 4; ++tk)
+                    acc[tn][tk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(mbf16x8_t, ao[tn]), __builtin_bit_cast(mbf16x8_t, bq[tk]),
+                        acc[tn][tk], 0, 0, 0);
+        }
+
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            // rows 32 ps .. +31 of the delta into the wave's LDS tile (a wave's
+            // LDS accesses complete in order, so no barrier is needed between
+            // its writes, its reads and the next pass's writes)
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int tk = 0; tk < 4; ++tk)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        cw[(16 * tn + 4 * g + q) * kCStride + 16 * tk + lr] = acc[2 * ps + tn][tk][q];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+            const int64_t n = n0 + 32 * ps + (lane >> 1);
+            const float *crow = cw + (lane >> 1) * kCStride + 32 * h;
+            const u32x4 oc = cur.code[ps];
+            const uint32_t dw[4] = {oc.x, oc.y, oc.z, oc.w};
+            const float c1o = cur.c1o[ps];
+            float wm[4][8];
+            float m = 0.0f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const f32x4 da = *reinterpret_cast<const f32x4 *>(crow + 8 * d);
+                const f32x4 db = *reinterpret_cast<const f32x4 *>(crow + 8 * d + 4);
+                const float dl[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float wold = s_lv[(dw[d] >> (4 * e)) & 15u] * c1o;
+                    const float delta = p.s * dl[e];
+                    wm[d][e] = wold + delta;
+                    m = fmaxf(m, fabsf(wm[d][e]));
+                }
+            }
+            m = __uint_as_float(dpp_umax<0xB1>(__float_as_uint(m)));  // the lane pair's max
+            uint32_t packed[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) packed[d] = slice_codes<8>(wm[d], m, s_lut);
+            if (n < p.n_rows) {
+                *reinterpret_cast<u32x4 *>(p.new_codes + n * (p.k_cols / 2) + kb / 2 + 16 * h) =
+                    u32x4{packed[0], packed[1], packed[2], packed[3]};
+                if (h == 0) p.new_absmax[n * (p.k_cols / kBlock) + kb / kBlock] = m;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        cur = nxt;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *codes, float *absmax,
@@ -676,6 +879,50 @@ hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_
                                                 codes, am, s);
     if (e != hipSuccess || !dq) return e;
     return launch_double_quantize_ex(am, nb, f, absmax_q, absmax_scale, absmax_offset, rest, s);
+}
+
+
+size_t merge_workspace(int64_t n_out, int64_t k_in) {
+    return round256(4 * (size_t)(n_out * (k_in / kBlock)));
+}
+
+hipError_t launch_merge(const nf4_weight &w, const uint16_t *a, const uint16_t *b, int32_t r,
+                        float s_lora, uint8_t *codes_out, float *absmax_out, uint8_t *absmax_q_out,
+                        float *absmax_scale_out, void *workspace, hipStream_t s) {
+    MergeParams p;
+    p.codes = w.codes;
+    p.q8 = w.absmax_q;
+    p.c2 = w.absmax_scale;
+    p.absmax = w.absmax;
+    p.a = a;
+    p.b = b;
+    p.n_rows = w.n_out;
+    p.k_cols = w.k_in;
+    p.col_tiles = (int32_t)((w.k_in + kMergeCols - 1) / kMergeCols);
+    p.r = r;
+    p.rp = (r + 31) / 32 * 32;
+    p.s = s_lora;
+    p.new_codes = codes_out;
+    p.new_absmax = absmax_out ? absmax_out : static_cast<float *>(workspace);
+    for (int i = 0; i < 16; ++i) p.lv[i] = kLevels[i];
+    // two workgroups per CU (the register budget's occupancy), each walking a
+    // run of column tiles
+    const int64_t row_tiles = (w.n_out + kMergeRows - 1) / kMergeRows;
+    const int64_t target = 2 * 256;
+    int64_t per = (row_tiles * p.col_tiles + target - 1) / target;
+    per = std::max<int64_t>(1, std::min<int64_t>(per, p.col_tiles));
+    p.tiles_per_wg = (int32_t)per;
+    p.chunks = (int32_t)((p.col_tiles + per - 1) / per);
+    const size_t lds = (size_t)kMergeRows * (p.rp + 8) * 2;
+    merge_requantize_kernel<<<dim3((unsigned)(row_tiles * p.chunks)), dim3(kThreads), lds, s>>>(
+        p, *code_lut());
+    if (absmax_q_out) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_double_quantize(p.new_absmax, w.n_out * (w.k_in / kBlock), absmax_q_out,
+                                      absmax_scale_out, s);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace nf4

@@ -264,3 +264,31 @@ def test_format_surface():
         nq.NF4Format(128, 256, "linear8", False)
     with pytest.raises(ValueError):
         nq.NF4Config(blocksize=96).validate()
+
+
+def test_merge_lora_validation(L):
+    m = L.nf4_merge_lora
+    w = _w(n=256, k=512)
+    ok = dict(w=ctypes.byref(w), a=FAKE, b=FAKE, r=64, s=2.0, c=FAKE, am=None, aq=FAKE, asc=FAKE,
+              ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return m(a["w"], a["a"], a["b"], a["r"], a["s"], a["c"], a["am"], a["aq"], a["asc"],
+                 a["ws"], a["wsb"], None)
+
+    assert call(w=None) == 1
+    assert call(w=ctypes.byref(_w(n=256, k=96))) == 2
+    assert call(w=ctypes.byref(_w(n=0, k=512))) == 2
+    for r in (0, 4, 12, 264):
+        assert call(r=r) == 2
+    assert call(w=ctypes.byref(_w(bs=32))) == 3
+    assert call(w=ctypes.byref(_w(dq=128))) == 3
+    assert call(a=None) == 1 and call(b=None) == 1 and call(c=None) == 1
+    assert call(aq=None) == 1
+    assert call(aq=None, asc=None) == 1  # no output scales at all
+    assert call(a=FAKE + 8) == 4 and call(b=FAKE + 1) == 4 and call(c=FAKE + 4) == 4
+    need = L.nf4_merge_lora_workspace_size(256, 512)
+    assert need == 256 * 512 // 64 * 4
+    assert call(ws=None) == 5 and call(wsb=need - 1) == 5 and call(ws=FAKE + 64) == 4
+    assert L.nf4_merge_lora_workspace_size(256, 96) == 0
