@@ -78,6 +78,10 @@ def lib():
                                                  _p, _p, _p, _p, _p, ctypes.c_int]
         L.nf4ref_merged_weight.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i32,
                                            ctypes.c_float, _p, _i64, _p]
+        L.nf4ref_codebook_levels.argtypes = [ctypes.c_int, _p]
+        L.nf4ref_quantize_cb.argtypes = [_p, ctypes.c_int, _i64, _i32, ctypes.c_int, _p, _p]
+        L.nf4ref_dequantize_range_cb.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, ctypes.c_int,
+                                                 ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int]
         L.nf4ref_lora_grads.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _i32, ctypes.c_double,
                                         _p, _i64, _p, _p, _i64, _p]
         _lib = L
@@ -331,6 +335,49 @@ def merge_lora(codes, shape, A, B, s, absmax=None, q=None, scale=None, dq=True):
         return nc, na, None, None, wm
     nq8, nsc = double_quantize(na)
     return nc, na, nq8, nsc, wm
+
+
+# ---- codebook swaps ----
+
+CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
+
+
+def _cb(c):
+    return CODEBOOKS[c] if isinstance(c, str) else int(c)
+
+
+def codebook_levels(codebook):
+    q = np.zeros(16, np.float32)
+    _check(lib().nf4ref_codebook_levels(_cb(codebook), _ptr(q)), "codebook_levels")
+    return q
+
+
+def quantize_cb(w, blocksize=BLOCK, codebook="nf4"):
+    """Blockwise quantization to the codebook's 16 levels: (codes, absmax)."""
+    w, dt = _as_bits(w)
+    n = w.size
+    codes = np.zeros((n + 1) // 2, np.uint8)
+    absmax = np.zeros((n + blocksize - 1) // blocksize, np.float32)
+    _check(lib().nf4ref_quantize_cb(_ptr(w), dt, n, int(blocksize), _cb(codebook), _ptr(codes),
+                                    _ptr(absmax)), "quantize_cb")
+    return codes, absmax
+
+
+def dequantize_cb(codes, n, blocksize=BLOCK, dq_blocksize=DQ_BLOCK, dq_format="e4m3",
+                  codebook="nf4", absmax=None, q=None, scale=None, offset=None, out_dtype=F32,
+                  start=0, count=None):
+    count = n - start if count is None else count
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    absmax = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if q is None else np.ascontiguousarray(q, dtype=np.uint8)
+    scale = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    off = None if offset is None else np.array([offset], np.float32)
+    out = np.zeros(count, np.float32 if out_dtype == F32 else np.uint16)
+    _check(lib().nf4ref_dequantize_range_cb(_ptr(codes), n, start, count, int(blocksize),
+                                            int(dq_blocksize), _fmt(dq_format), _cb(codebook),
+                                            _ptr(absmax), _ptr(q), _ptr(scale), _ptr(off),
+                                            _ptr(out), out_dtype), "dequantize_range_cb")
+    return out
 
 
 def storage_bytes(n, dq):

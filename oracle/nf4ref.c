@@ -518,6 +518,96 @@ int nf4ref_merged_weight(const uint8_t *codes, const float *absmax, const uint8_
     return 0;
 }
 
+/* ---- codebook swaps (see nf4ref.h) ---- */
+
+int nf4ref_codebook_levels(int codebook, float q[16]) {
+    if (!q) return -1;
+    if (codebook == NF4REF_CB_NF4) {
+        for (int i = 0; i < 16; ++i) q[i] = NF4_Q[i];
+    } else if (codebook == NF4REF_CB_FP4) {
+        static const float mag[8] = {6.0f, 4.0f, 3.0f, 2.0f, 1.5f, 1.0f, 0.5f, 0.0f};
+        for (int i = 0; i < 8; ++i) {
+            q[i] = -(mag[i] / 6.0f);      /* -1 .. -0 */
+            q[15 - i] = mag[i] / 6.0f;    /* +0 .. 1 */
+        }
+    } else if (codebook == NF4REF_CB_INT4) {
+        for (int k = 0; k < 16; ++k) q[k] = (float)(2 * k - 15) / 15.0f;
+    } else {
+        return -1;
+    }
+    return 0;
+}
+
+static int nearest_in(const float q[16], float n) {
+    int best = 0;
+    float best_d = fabsf(n - q[0]);
+    for (int i = 1; i < 16; ++i) {
+        float d = fabsf(n - q[i]);
+        if (d < best_d) {
+            best_d = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+int nf4ref_quantize_cb(const void *w, int dtype, int64_t n, int32_t blocksize, int codebook,
+                       uint8_t *codes, float *absmax) {
+    float q[16];
+    if (nf4ref_codebook_levels(codebook, q) != 0) return -1;
+    if (n < 0 || !pow2_in(blocksize, 16, 4096)) return -1;
+    if (n == 0) return 0;
+    if (!w || !codes || !absmax) return -1;
+    if (dtype != NF4REF_F32 && dtype != NF4REF_BF16) return -1;
+    const int zero_code = nearest_in(q, 0.0f);
+    int64_t nblocks = (n + blocksize - 1) / blocksize;
+    memset(codes, 0, (size_t)((n + 1) / 2));
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int64_t lo = b * blocksize;
+        int64_t hi = lo + blocksize < n ? lo + blocksize : n;
+        float c1 = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            float v = load_elem(w, dtype, i);
+            if (!isfinite(v)) return -2;
+            if (fabsf(v) > c1) c1 = fabsf(v);
+        }
+        absmax[b] = c1;
+        for (int64_t i = lo; i < hi; ++i) {
+            int code = (c1 == 0.0f) ? zero_code : nearest_in(q, load_elem(w, dtype, i) / c1);
+            codes[i / 2] |= (uint8_t)(code << (4 * (int)(i & 1)));
+        }
+    }
+    return 0;
+}
+
+int nf4ref_dequantize_range_cb(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                               int32_t blocksize, int32_t dq_blocksize, int dq_format, int codebook,
+                               const float *absmax, const uint8_t *q, const float *scale,
+                               const float *offset, void *out, int out_dtype) {
+    float lv[16];
+    if (nf4ref_codebook_levels(codebook, lv) != 0) return -1;
+    if (n < 0 || start < 0 || count < 0 || start + count > n) return -1;
+    if (!pow2_in(blocksize, 16, 4096) || !pow2_in(dq_blocksize, 1, 4096)) return -1;
+    if (dq_format < NF4REF_DQ_E4M3 || dq_format > NF4REF_DQ_LINEAR8) return -1;
+    if (count == 0) return 0;
+    if (!codes || !out) return -1;
+    if (!q && !absmax) return -1;
+    if (q && !scale) return -1;
+    if (out_dtype != NF4REF_F32 && out_dtype != NF4REF_BF16) return -1;
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t i = start + j;
+        int code = (codes[i / 2] >> (4 * (int)(i & 1))) & 15;
+        float c1 = nf4ref_block_scale_ex(i / blocksize, dq_blocksize, dq_format, absmax, q, scale,
+                                         offset);
+        float v = lv[code] * c1;
+        if (out_dtype == NF4REF_F32)
+            ((float *)out)[j] = v;
+        else
+            ((uint16_t *)out)[j] = nf4ref_f32_to_bf16(v);
+    }
+    return 0;
+}
+
 /* ---- storage footprint ([L15] "Double quantisation" per-parameter tables) ---- */
 
 int64_t nf4ref_storage_bytes(int64_t n, int dq) {

@@ -205,6 +205,34 @@ int nf4ref_merged_weight(const uint8_t *codes, const float *absmax, const uint8_
                          const uint16_t *B, int32_t r, float s, const int64_t *rows,
                          int64_t nrows, float *wm);
 
+/* ---- Codebook swaps ([MF] "Empirical Performance and Architectural
+ * Guidelines", finding 2: NF4 against 4-bit floating point (FP4) and 4-bit
+ * integer (Int4); [QP] "1. 4-bit NormalFloat (NF4)", the numpy comparison's
+ * naive uniform 4-bit quantizer). The same blockwise scheme with
+ * another sorted set of 16 levels in [-1, 1]:
+ *   NF4REF_CB_NF4   the printed NF4 list
+ *   NF4REF_CB_FP4   the OCP FP4 (E2M1) values {0, .5, 1, 1.5, 2, 3, 4, 6} with
+ *                   both signs, divided by 6 (fl32(v / 6)); -0 and +0 are both
+ *                   levels (indices 7 and 8; the tie rule never picks 8).
+ *                   PARITY UNPINNED: the pages name FP4 without defining it.
+ *   NF4REF_CB_INT4  16 evenly spaced levels fl32((2k - 15) / 15), k = 0..15:
+ *                   the dequantized values (k' + 1/2) / 7.5, k' = -8..7, of the
+ *                   uniform toy
+ * A block with c1 == 0 gets the code of the level nearest 0. */
+enum { NF4REF_CB_NF4 = 0, NF4REF_CB_FP4 = 1, NF4REF_CB_INT4 = 2 };
+
+int nf4ref_codebook_levels(int codebook, float q[16]);
+
+/* nf4ref_quantize_bs with the codebook's levels. */
+int nf4ref_quantize_cb(const void *w, int dtype, int64_t n, int32_t blocksize, int codebook,
+                       uint8_t *codes, float *absmax);
+
+/* nf4ref_dequantize_range_ex with the codebook's levels. */
+int nf4ref_dequantize_range_cb(const uint8_t *codes, int64_t n, int64_t start, int64_t count,
+                               int32_t blocksize, int32_t dq_blocksize, int dq_format, int codebook,
+                               const float *absmax, const uint8_t *q, const float *scale,
+                               const float *offset, void *out, int out_dtype);
+
 #ifdef __cplusplus
 }
 #endif
