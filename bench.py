@@ -398,6 +398,8 @@ VARIANTS = (
     ("b128", (128, 256, "e4m3", False)),
     ("b16", (16, 256, "e4m3", False)),
     ("b4096_e5m2_offset", (4096, 256, "e5m2", True)),
+    ("fp4", (64, 256, "e4m3", False, "fp4")),
+    ("int4", (64, 256, "e4m3", False, "int4")),
 )
 
 
@@ -409,7 +411,8 @@ def variant_storage_bytes(n, f):
 def variant_benches(dev, iters, warmup):
     """Storage-format variants on the 11008 x 4096 bf16 weight (4 rotating
     copies, 361 MB, more than the last-level cache): quantize with fused or
-    two-pass double quantization, and dequantize to bf16."""
+    two-pass double quantization, and dequantize to bf16; the FP4 and Int4
+    codebooks on the same kernels, and the three codebooks' quantization MSE."""
     import ctypes
     import torch
     import nf4_quantize_amd as nq
@@ -449,6 +452,11 @@ def variant_benches(dev, iters, warmup):
                     "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS, "format": list(spec)}
         log(f"{key}: {out[key]}")
         del ts, outs, wsp
+    # the codebook comparison: mean squared error of NF4, FP4 and Int4 (B1 = 64,
+    # double quantization) on the same Gaussian weight
+    out["codebook_mse_11008x4096_bf16"] = {
+        cb: nq.quantization_mse(ws_in[0], nq.NF4Format(codebook=cb)) for cb in ("nf4", "fp4", "int4")}
+    log(f"codebook MSE: {out['codebook_mse_11008x4096_bf16']}")
     del ws_in
     torch.cuda.empty_cache()
     return out

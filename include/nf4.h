@@ -232,12 +232,29 @@ nf4_status nf4_merge_lora(const nf4_weight *w, const void *lora_a, const void *l
  * and the weight fl32(q[code] * scale(i / B1)) as before. */
 typedef enum { NF4_DQ_E4M3 = 0, NF4_DQ_E5M2 = 1, NF4_DQ_LINEAR8 = 2 } nf4_dq_format;
 
+/* The 16 levels of the 4-bit code ([MF] "Empirical Performance and
+ * Architectural Guidelines" compares NF4 with FP4 and Int4; [QP] "1. 4-bit
+ * NormalFloat (NF4)" compares it with a naive uniform 4-bit quantizer):
+ *   NF4_CODEBOOK_NF4   the printed NF4 list (nf4_codebook())
+ *   NF4_CODEBOOK_FP4   the OCP FP4 (E2M1) values 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *                      with both signs, each fl32(v / 6): the 15 distinct
+ *                      values ascending at codes 0..14 (0 at 7), and -0 at
+ *                      code 15 (equal to level 7, so never chosen)
+ *   NF4_CODEBOOK_INT4  fl32((2k - 15) / 15), k = 0..15: evenly spaced, no zero
+ * A code is the index of the nearest level (lower index on a tie), and a
+ * block with c1 == 0 gets the code of the level nearest 0. */
+typedef enum { NF4_CODEBOOK_NF4 = 0, NF4_CODEBOOK_FP4 = 1, NF4_CODEBOOK_INT4 = 2 } nf4_codebook_id;
+
 typedef struct {
     int32_t blocksize;      /* B1: a power of two in [16, 4096] */
     int32_t dq_blocksize;   /* B2: a power of two in [1, 4096] */
     int32_t dq_format;      /* an nf4_dq_format */
     int32_t dq_mean_offset; /* 0, or 1 for the tensor-wide mean offset */
+    int32_t codebook;       /* an nf4_codebook_id */
 } nf4_format;
+
+/* The 16 levels of a codebook (static host array), NULL for an unknown id. */
+const float *nf4_codebook_levels(int32_t codebook);
 
 /* Device workspace bytes of nf4_quantize_ex for an n-element tensor: fp32
  * block scales when the call runs in two passes (B1 != 64, B2 != 256 or the
@@ -252,7 +269,9 @@ size_t nf4_quantize_ex_workspace_size(int64_t n, const nf4_format *f);
  *                  and double quantization is on, else ignored
  *   workspace      device, 256-byte aligned, >= nf4_quantize_ex_workspace_size
  *                  bytes (may be NULL when that is 0)
- * f = {64, 256, NF4_DQ_E4M3, 0} computes exactly what nf4_quantize does. */
+ * The 4-bit codes index f->codebook's levels.
+ * f = {64, 256, NF4_DQ_E4M3, 0, NF4_CODEBOOK_NF4} computes exactly what
+ * nf4_quantize does. */
 nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, const nf4_format *f,
                            uint8_t *codes, float *absmax, uint8_t *absmax_q, float *absmax_scale,
                            float *absmax_offset, void *workspace, size_t workspace_bytes,
@@ -269,7 +288,8 @@ nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, const nf
                                   uint8_t *absmax_q, float *absmax_scale, float *absmax_offset,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Dequantization of a tensor stored in format f: scale(b) as above, absmax
+/* Dequantization of a tensor stored in format f (levels of f->codebook):
+ * scale(b) as above, absmax
  * (fp32, no double quantization) when absmax_q == NULL. absmax_offset: device,
  * one float, required iff f->dq_mean_offset and absmax_q != NULL. */
 nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format *f,

@@ -37,6 +37,7 @@ STATUS = {
 EXPORTS = (
     "nf4_status_string",
     "nf4_codebook",
+    "nf4_codebook_levels",
     "nf4_storage_bytes",
     "nf4_quantize",
     "nf4_double_quantize",
@@ -57,6 +58,8 @@ EXPORTS = (
 
 # nf4_dq_format: the 8-bit code of double quantization.
 DQ_FORMATS = {"e4m3": 0, "e5m2": 1, "linear8": 2}
+# nf4_codebook_id: the 16 levels of the 4-bit code.
+CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
 
 
 class NF4LibraryMissing(RuntimeError):
@@ -88,6 +91,7 @@ class nf4_format(ctypes.Structure):
         ("dq_blocksize", ctypes.c_int32),
         ("dq_format", ctypes.c_int32),
         ("dq_mean_offset", ctypes.c_int32),
+        ("codebook", ctypes.c_int32),
     ]
 
 
@@ -108,6 +112,8 @@ def lib():
     L.nf4_status_string.restype = ctypes.c_char_p
     L.nf4_codebook.argtypes = []
     L.nf4_codebook.restype = ctypes.POINTER(ctypes.c_float)
+    L.nf4_codebook_levels.argtypes = [i32]
+    L.nf4_codebook_levels.restype = ctypes.POINTER(ctypes.c_float)
     L.nf4_storage_bytes.argtypes = [i64, i32, i32, i32]
     L.nf4_storage_bytes.restype = i64
     L.nf4_quantize.argtypes = [p, ctypes.c_int, i64, i32, p, p, i32, p, p, p]
@@ -188,6 +194,13 @@ def nf4_codebook():
     return [cb[i] for i in range(16)]
 
 
+def nf4_codebook_levels(codebook="nf4"):
+    cb = lib().nf4_codebook_levels(CODEBOOKS[codebook] if isinstance(codebook, str) else codebook)
+    if not cb:
+        raise ValueError(f"unknown codebook {codebook!r}")
+    return [cb[i] for i in range(16)]
+
+
 def nf4_storage_bytes(n, double_quant=True, blocksize=BLOCK, dq_blocksize=DQ_BLOCK):
     return int(lib().nf4_storage_bytes(n, blocksize, dq_blocksize, 1 if double_quant else 0))
 
@@ -226,11 +239,13 @@ def nf4_linear_workspace_size(m, r):
 class NF4Format:
     """Storage-format variant (nf4_format in nf4.h): block size B1, DQ block
     B2, the 8-bit code format of double quantization ("e4m3", "e5m2",
-    "linear8") and the tensor-wide mean offset."""
+    "linear8"), the tensor-wide mean offset, and the 4-bit codebook ("nf4",
+    "fp4", "int4")."""
     blocksize: int = BLOCK
     dq_blocksize: int = DQ_BLOCK
     dq_format: str = "e4m3"
     mean_offset: bool = False
+    codebook: str = "nf4"
 
     @property
     def is_default(self):
@@ -239,8 +254,10 @@ class NF4Format:
     def struct(self):
         if self.dq_format not in DQ_FORMATS:
             raise ValueError(f"dq_format must be one of {sorted(DQ_FORMATS)}")
+        if self.codebook not in CODEBOOKS:
+            raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}")
         return nf4_format(self.blocksize, self.dq_blocksize, DQ_FORMATS[self.dq_format],
-                          1 if self.mean_offset else 0)
+                          1 if self.mean_offset else 0, CODEBOOKS[self.codebook])
 
     def nblocks(self, n):
         return (n + self.blocksize - 1) // self.blocksize
@@ -581,4 +598,18 @@ def merge_lora(w: NF4Tensor, lora_a, lora_b, lora_scale=1.0, out: Optional[NF4Te
 
 
 lora_merge = merge_lora
+
+
+# ------------------------------------------------- codebook comparison
+
+def quantization_mse(w, fmt: NF4Format = None, double_quant=True):
+    """Mean squared error of quantizing then dequantizing the device tensor w
+    in format `fmt` (the codebook comparison of NF4 against FP4 and Int4).
+    Quantization and dequantization run in the library's kernels; the error
+    is reduced with torch on the device (float64)."""
+    import torch
+
+    t = quantize(w, double_quant=double_quant, fmt=fmt)
+    d = dequantize(t, out_dtype=torch.float32)
+    return float(((d.double() - w.double()) ** 2).mean())
 

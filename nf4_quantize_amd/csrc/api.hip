@@ -40,14 +40,36 @@ const float kLevels[16] = {
 
 namespace {
 
+// The other codebooks (nf4.h, nf4_codebook_id): OCP FP4 E2M1 values / 6
+// (the 15 distinct ones ascending, then -0) and evenly spaced Int4 levels,
+// each rounded once to fp32.
+struct OtherLevels {
+    float fp4[16];
+    float int4[16];
+    OtherLevels() {
+        const float e2m1[7] = {0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+        fp4[7] = 0.0f;
+        for (int i = 0; i < 7; ++i) {
+            fp4[8 + i] = e2m1[i] / 6.0f;
+            fp4[6 - i] = -(e2m1[i] / 6.0f);
+        }
+        fp4[15] = -0.0f;
+        for (int k = 0; k < 16; ++k) int4[k] = (float)(2 * k - 15) / 15.0f;
+    }
+};
+const OtherLevels &other_levels() {
+    static const OtherLevels l;
+    return l;
+}
+
 // Nearest level of a normalised value by direct search: the first index with
 // the smallest |fl32(n - q_i)| ([MF] "Block-Wise Quantization Mechanics").
 // Host-side only, used to build the bucket table.
-int nearest_by_search(float n) {
+int nearest_by_search(const float *lv, float n) {
     int best = 0;
-    float bd = fabsf(n - kLevels[0]);
+    float bd = fabsf(n - lv[0]);
     for (int i = 1; i < 16; ++i) {
-        const float d = fabsf(n - kLevels[i]);
+        const float d = fabsf(n - lv[i]);
         if (d < bd) {
             bd = d;
             best = i;
@@ -72,7 +94,7 @@ float ord2f(int64_t o) {
 // Bucket of v, with the same fp32 formula as the kernels (see CodeLut).
 uint32_t bucket_of(float v) { return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f)) >> 3; }
 
-bool build_lut(CodeLut *lut) {
+bool build_lut(CodeLut *lut, const float *lv) {
     const float vmin = -1.0f - 0x1p-20f, vmax = 1.0f + 0x1p-20f;
     // bucket_of is non-decreasing in v, so each bucket is an interval of floats.
     int64_t start = f2ord(vmin);
@@ -91,8 +113,8 @@ bool build_lut(CodeLut *lut) {
         }
         const float lo = ord2f(start), hi = ord2f(a);
         if (bucket_of(lo) != (uint32_t)k || bucket_of(hi) != (uint32_t)k) return false;
-        const int c_lo = nearest_by_search(lo);
-        const int c_hi = nearest_by_search(hi);
+        const int c_lo = nearest_by_search(lv, lo);
+        const int c_hi = nearest_by_search(lv, hi);
         lut->e[k].hi = c_hi;
         lut->e[k].thr = -2.0f;
         if (c_hi != c_lo) {
@@ -100,7 +122,7 @@ bool build_lut(CodeLut *lut) {
             int64_t u = f2ord(lo), v = f2ord(hi);  // code(u) == c_lo, code(v) == c_lo + 1
             while (v - u > 1) {
                 const int64_t mid = u + (v - u) / 2;
-                if (nearest_by_search(ord2f(mid)) > c_lo) v = mid; else u = mid;
+                if (nearest_by_search(lv, ord2f(mid)) > c_lo) v = mid; else u = mid;
             }
             const float thr = ord2f(v);
             // A switch point must sit inside its bucket by more than the
@@ -111,21 +133,34 @@ bool build_lut(CodeLut *lut) {
         }
         start = a + 1;
     }
-    for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{-2.0f, 15};
+    for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{-2.0f, nearest_by_search(lv, 1.0f)};
+    // the code of 0 (a block with c1 == 0) must come out of the table
     const LutEntry &z = lut->e[bucket_of(0.0f)];
-    return lut->e[kLutUsed - 1].hi == 15 && nearest_by_search(0.0f) == 7 &&
-           z.hi - (0.0f < z.thr ? 1 : 0) == 7;
+    return lut->e[kLutUsed - 1].hi == nearest_by_search(lv, 1.0f) &&
+           z.hi - (0.0f < z.thr ? 1 : 0) == nearest_by_search(lv, 0.0f);
 }
 
 }  // namespace
 
-const CodeLut *code_lut() {
-    static CodeLut lut;
-    static bool ok = false;
-    static std::once_flag once;
-    std::call_once(once, [] { ok = build_lut(&lut); });
-    return ok ? &lut : nullptr;
+const float *levels_for(int cb) {
+    switch (cb) {
+        case NF4_CODEBOOK_NF4: return kLevels;
+        case NF4_CODEBOOK_FP4: return other_levels().fp4;
+        case NF4_CODEBOOK_INT4: return other_levels().int4;
+        default: return nullptr;
+    }
 }
+
+const CodeLut *code_lut_for(int cb) {
+    static CodeLut lut[3];
+    static bool ok[3] = {false, false, false};
+    static std::once_flag once[3];
+    if (cb < 0 || cb > 2) return nullptr;
+    std::call_once(once[cb], [cb] { ok[cb] = build_lut(&lut[cb], levels_for(cb)); });
+    return ok[cb] ? &lut[cb] : nullptr;
+}
+
+const CodeLut *code_lut() { return code_lut_for(NF4_CODEBOOK_NF4); }
 
 }  // namespace nf4
 
@@ -157,6 +192,8 @@ NF4_API const char *nf4_status_string(int status) {
 }
 
 NF4_API const float *nf4_codebook(void) { return kLevels; }
+
+NF4_API const float *nf4_codebook_levels(int32_t codebook) { return levels_for(codebook); }
 
 NF4_API int64_t nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t dq_blocksize,
                                   int32_t double_quant) {
@@ -329,6 +366,7 @@ nf4_status check_format(const nf4_format *f) {
         return NF4_ERR_UNSUPPORTED;
     if (f->dq_format < NF4_DQ_E4M3 || f->dq_format > NF4_DQ_LINEAR8) return NF4_ERR_UNSUPPORTED;
     if (f->dq_mean_offset != 0 && f->dq_mean_offset != 1) return NF4_ERR_UNSUPPORTED;
+    if (!code_lut_for(f->codebook)) return NF4_ERR_UNSUPPORTED;
     return NF4_OK;
 }
 

@@ -151,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_tail_kernel(
 
 template <typename O>
 hipError_t launch_t(const uint8_t *codes, int64_t n, const float *absmax, const uint8_t *absmax_q,
-                    const float *absmax_scale, O *out, hipStream_t s) {
+                    const float *absmax_scale, O *out, const float *levels, hipStream_t s) {
     Levels lv;
-    for (int i = 0; i < 16; ++i) lv.q[i] = kLevels[i];
+    for (int i = 0; i < 16; ++i) lv.q[i] = levels[i];
     constexpr int kCPW = 2;
     const int64_t nchunks = n / kChunk;
     if (nchunks > 0) {
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_variant_tail_kernel(
 template <typename O, int F, bool kS, bool kDQ>
 hipError_t launch_variant(const uint8_t *codes, int64_t n, int lb1, int lb2, const float *absmax,
                           const uint8_t *q, const float *sc, const float *mu, O *out,
-                          hipStream_t s) {
+                          const float *levels, hipStream_t s) {
     Levels lv;
-    for (int i = 0; i < 16; ++i) lv.q[i] = kLevels[i];
+    for (int i = 0; i < 16; ++i) lv.q[i] = levels[i];
     constexpr int kCPW = 2;
     const int64_t nchunks = n / kChunk;
     if (nchunks > 0) {
@@ -289,21 +289,22 @@ template <typename O>
 hipError_t launch_variant_o(const uint8_t *codes, int64_t n, const nf4_format &f,
                             const float *absmax, const uint8_t *q, const float *sc,
                             const float *mu, O *out, hipStream_t s) {
+    const float *levels = levels_for(f.codebook);
     int lb1 = 0, lb2 = 0;
     while ((1 << lb1) < f.blocksize) ++lb1;
     while ((1 << lb2) < f.dq_blocksize) ++lb2;
-    if (!q) return launch_variant<O, kFmtE4M3, false, false>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+    if (!q) return launch_variant<O, kFmtE4M3, false, false>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
     if (f.dq_mean_offset) {
         switch (f.dq_format) {
-            case kFmtE5M2: return launch_variant<O, kFmtE5M2, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
-            case kFmtLin8: return launch_variant<O, kFmtLin8, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
-            default: return launch_variant<O, kFmtE4M3, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+            case kFmtE5M2: return launch_variant<O, kFmtE5M2, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
+            case kFmtLin8: return launch_variant<O, kFmtLin8, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
+            default: return launch_variant<O, kFmtE4M3, true, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
         }
     }
     switch (f.dq_format) {
-        case kFmtE5M2: return launch_variant<O, kFmtE5M2, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
-        case kFmtLin8: return launch_variant<O, kFmtLin8, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
-        default: return launch_variant<O, kFmtE4M3, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, s);
+        case kFmtE5M2: return launch_variant<O, kFmtE5M2, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
+        case kFmtLin8: return launch_variant<O, kFmtLin8, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
+        default: return launch_variant<O, kFmtE4M3, false, true>(codes, n, lb1, lb2, absmax, q, sc, mu, out, levels, s);
     }
 }
 
@@ -314,8 +315,9 @@ hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absma
                              nf4_dtype dt, hipStream_t s) {
     if (dt == NF4_BF16)
         return launch_t<uint16_t>(codes, n, absmax, absmax_q, absmax_scale,
-                                  static_cast<uint16_t *>(out), s);
-    return launch_t<float>(codes, n, absmax, absmax_q, absmax_scale, static_cast<float *>(out), s);
+                                  static_cast<uint16_t *>(out), kLevels, s);
+    return launch_t<float>(codes, n, absmax, absmax_q, absmax_scale, static_cast<float *>(out),
+                           kLevels, s);
 }
 
 
@@ -326,7 +328,14 @@ hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_forma
     const bool plain = f.blocksize == kBlock &&
                        (!absmax_q || (f.dq_blocksize == kDqBlock && f.dq_format == kFmtE4M3 &&
                                       !f.dq_mean_offset));
-    if (plain) return launch_dequantize(codes, n, absmax, absmax_q, absmax_scale, out, dt, s);
+    if (plain) {
+        const float *levels = levels_for(f.codebook);
+        if (dt == NF4_BF16)
+            return launch_t<uint16_t>(codes, n, absmax, absmax_q, absmax_scale,
+                                      static_cast<uint16_t *>(out), levels, s);
+        return launch_t<float>(codes, n, absmax, absmax_q, absmax_scale, static_cast<float *>(out),
+                               levels, s);
+    }
     if (dt == NF4_BF16)
         return launch_variant_o<uint16_t>(codes, n, f, absmax, absmax_q, absmax_scale,
                                           absmax_offset, static_cast<uint16_t *>(out), s);

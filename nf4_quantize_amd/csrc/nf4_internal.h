@@ -47,9 +47,13 @@ struct CodeLut {
 __host__ __device__ __forceinline__ uint32_t lut_offset_bits(float fma_result) {
     return __builtin_bit_cast(uint32_t, fma_result) & 0x1F8u;
 }
-// Returns the table (built once, thread-safe), or nullptr if the codebook
-// failed the construction checks.
+// Returns the table of the NF4 levels, or of codebook `cb` (nf4_codebook_id),
+// built once (thread-safe); nullptr if the codebook failed the construction
+// checks or is unknown.
 const CodeLut *code_lut();
+const CodeLut *code_lut_for(int cb);
+// The 16 levels of codebook `cb`, or nullptr.
+const float *levels_for(int cb);
 
 // |q - n| bound used by the quantize kernels: with r within 1 ulp of 1/c1,
 // q = fl(w * r) and n = fl(w / c1) differ by less than 2.4e-7 for |w| <= c1;

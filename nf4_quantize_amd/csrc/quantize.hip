@@ -154,7 +154,8 @@ __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, c
     if (outside | !(dmin >= kNearTol)) {  // rare: redo with the correctly rounded division
         packed = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) packed |= exact_code(s_lut, f[e] / c1) << (4 * e);
+        for (int e = 0; e < E; ++e)
+            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f) << (4 * e);
     }
     return packed;
 }
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
     for (int64_t i = lo; i < hi; i += 2) {
         uint32_t byte = 0;
         for (int j = 0; j < 2 && i + j < hi; ++j) {
-            const uint32_t code = (c1 > 0.0f) ? exact_code(s_lut, elem(i + j) / c1) : 7u;
+            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f);
             byte |= code << (4 * j);
         }
         codes[i / 2] = (uint8_t)byte;
@@ -320,8 +321,8 @@ constexpr int kGroupThreads = 512;
 // offset): the fused group kernel, 8-bit codes in format F.
 template <typename T, int F>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
-                             uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
-    const CodeLut &lut = *code_lut();
+                             uint8_t *absmax_q, float *absmax_scale, const CodeLut &lut,
+                             hipStream_t s) {
     const int64_t full = n / kGroup;
     constexpr int TH = kGroupThreads;
     if (full > 0) {
@@ -340,12 +341,13 @@ hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absma
 
 template <typename T>
 hipError_t launch_quantize_fmt(const T *w, int64_t n, uint8_t *codes, float *absmax,
-                               uint8_t *absmax_q, float *absmax_scale, int fmt, hipStream_t s) {
+                               uint8_t *absmax_q, float *absmax_scale, int fmt, const CodeLut &lut,
+                               hipStream_t s) {
     if (fmt == kFmtE5M2)
-        return launch_quantize_t<T, kFmtE5M2>(w, n, codes, absmax, absmax_q, absmax_scale, s);
+        return launch_quantize_t<T, kFmtE5M2>(w, n, codes, absmax, absmax_q, absmax_scale, lut, s);
     if (fmt == kFmtLin8)
-        return launch_quantize_t<T, kFmtLin8>(w, n, codes, absmax, absmax_q, absmax_scale, s);
-    return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, absmax_q, absmax_scale, s);
+        return launch_quantize_t<T, kFmtLin8>(w, n, codes, absmax, absmax_q, absmax_scale, lut, s);
+    return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, absmax_q, absmax_scale, lut, s);
 }
 
 // ---- storage-format variants: block sizes other than 64, the mean offset ----
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(64) void quantize_blocks_tail_kernel(
     for (int64_t i = lo; i < hi; i += 2) {
         uint32_t byte = 0;
         for (int j = 0; j < 2 && i + j < hi; ++j) {
-            const uint32_t code = (c1 > 0.0f) ? exact_code(s_lut, elem(i + j) / c1) : 7u;
+            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f);
             byte |= code << (4 * j);
         }
         codes[i / 2] = (uint8_t)byte;
@@ -526,8 +528,8 @@ __global__ __launch_bounds__(kThreads) void dq_generic_kernel(
 }
 
 template <typename T, int B1>
-hipError_t launch_blocks(const T *w, int64_t n, uint8_t *codes, float *absmax, hipStream_t s) {
-    const CodeLut &lut = *code_lut();
+hipError_t launch_blocks(const T *w, int64_t n, uint8_t *codes, float *absmax, const CodeLut &lut,
+                         hipStream_t s) {
     constexpr int E = Slice<T>::kElems;
     constexpr int U = B1 > 64 * E ? B1 : 64 * E;
     constexpr int S = U / (64 * E);
@@ -549,17 +551,17 @@ hipError_t launch_blocks(const T *w, int64_t n, uint8_t *codes, float *absmax, h
 
 template <typename T>
 hipError_t launch_blocks_bs(const T *w, int64_t n, int32_t bs, uint8_t *codes, float *absmax,
-                            hipStream_t s) {
+                            const CodeLut &lut, hipStream_t s) {
     switch (bs) {
-        case 16: return launch_blocks<T, 16>(w, n, codes, absmax, s);
-        case 32: return launch_blocks<T, 32>(w, n, codes, absmax, s);
-        case 64: return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, nullptr, nullptr, s);
-        case 128: return launch_blocks<T, 128>(w, n, codes, absmax, s);
-        case 256: return launch_blocks<T, 256>(w, n, codes, absmax, s);
-        case 512: return launch_blocks<T, 512>(w, n, codes, absmax, s);
-        case 1024: return launch_blocks<T, 1024>(w, n, codes, absmax, s);
-        case 2048: return launch_blocks<T, 2048>(w, n, codes, absmax, s);
-        default: return launch_blocks<T, 4096>(w, n, codes, absmax, s);
+        case 16: return launch_blocks<T, 16>(w, n, codes, absmax, lut, s);
+        case 32: return launch_blocks<T, 32>(w, n, codes, absmax, lut, s);
+        case 64: return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, nullptr, nullptr, lut, s);
+        case 128: return launch_blocks<T, 128>(w, n, codes, absmax, lut, s);
+        case 256: return launch_blocks<T, 256>(w, n, codes, absmax, lut, s);
+        case 512: return launch_blocks<T, 512>(w, n, codes, absmax, lut, s);
+        case 1024: return launch_blocks<T, 1024>(w, n, codes, absmax, lut, s);
+        case 2048: return launch_blocks<T, 2048>(w, n, codes, absmax, lut, s);
+        default: return launch_blocks<T, 4096>(w, n, codes, absmax, lut, s);
     }
 }
 
@@ -788,9 +790,9 @@ hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *code
                            uint8_t *absmax_q, float *absmax_scale, hipStream_t s) {
     if (dt == NF4_BF16)
         return launch_quantize_t<uint16_t, kFmtE4M3>(static_cast<const uint16_t *>(w), n, codes,
-                                                     absmax, absmax_q, absmax_scale, s);
+                                                     absmax, absmax_q, absmax_scale, *code_lut(), s);
     return launch_quantize_t<float, kFmtE4M3>(static_cast<const float *>(w), n, codes, absmax,
-                                              absmax_q, absmax_scale, s);
+                                              absmax_q, absmax_scale, *code_lut(), s);
 }
 
 hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t *absmax_q,
@@ -856,14 +858,15 @@ hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_
                               hipStream_t s) {
     const bool dq = absmax_q != nullptr;
     const bool bf = dt == NF4_BF16;
+    const CodeLut &lut = *code_lut_for(f.codebook);
     const bool fused = f.blocksize == kBlock &&
                        (!dq || (f.dq_blocksize == kDqBlock && !f.dq_mean_offset));
     if (fused) {
         if (bf)
             return launch_quantize_fmt<uint16_t>(static_cast<const uint16_t *>(w), n, codes,
-                                                 absmax, absmax_q, absmax_scale, f.dq_format, s);
+                                                 absmax, absmax_q, absmax_scale, f.dq_format, lut, s);
         return launch_quantize_fmt<float>(static_cast<const float *>(w), n, codes, absmax,
-                                          absmax_q, absmax_scale, f.dq_format, s);
+                                          absmax_q, absmax_scale, f.dq_format, lut, s);
     }
     // two passes: codes and fp32 absmax, then double quantization
     const int64_t nb = (n + f.blocksize - 1) / f.blocksize;
@@ -874,9 +877,9 @@ hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_
         rest = static_cast<char *>(workspace) + round256(4 * (size_t)nb);
     }
     hipError_t e = bf ? launch_blocks_bs<uint16_t>(static_cast<const uint16_t *>(w), n,
-                                                   f.blocksize, codes, am, s)
+                                                   f.blocksize, codes, am, lut, s)
                       : launch_blocks_bs<float>(static_cast<const float *>(w), n, f.blocksize,
-                                                codes, am, s);
+                                                codes, am, lut, s);
     if (e != hipSuccess || !dq) return e;
     return launch_double_quantize_ex(am, nb, f, absmax_q, absmax_scale, absmax_offset, rest, s);
 }

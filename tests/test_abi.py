@@ -194,8 +194,8 @@ def test_lora_backward_validation(L):
     assert call(wsp=FAKE + 16) == 4  # the workspace is 256-byte aligned
 
 
-def _fmt(bs=64, dq=256, f=0, off=0):
-    return ctypes.byref(nq.nf4_format(bs, dq, f, off))
+def _fmt(bs=64, dq=256, f=0, off=0, cb=0):
+    return ctypes.byref(nq.nf4_format(bs, dq, f, off, cb))
 
 
 def test_format_variant_validation(L):
@@ -212,7 +212,7 @@ def test_format_variant_validation(L):
 
     assert call_q(None) == 1
     for bad in (_fmt(bs=8), _fmt(bs=96), _fmt(bs=8192), _fmt(dq=0), _fmt(dq=3), _fmt(dq=8192),
-                _fmt(f=3), _fmt(f=-1), _fmt(off=2)):
+                _fmt(f=3), _fmt(f=-1), _fmt(off=2), _fmt(cb=3), _fmt(cb=-1)):
         assert call_q(bad) == 3
     assert call_q(_fmt(), n=-1) == 2
     assert call_q(_fmt(), dt=7) == 3
@@ -292,3 +292,12 @@ def test_merge_lora_validation(L):
     assert need == 256 * 512 // 64 * 4
     assert call(ws=None) == 5 and call(wsb=need - 1) == 5 and call(ws=FAKE + 64) == 4
     assert L.nf4_merge_lora_workspace_size(256, 96) == 0
+
+
+def test_codebook_levels(L, oracle_mod):
+    """The library's codebooks hold the same levels as the oracle's (each
+    built by its own code from the same definitions)."""
+    for name in ("nf4", "fp4", "int4"):
+        got = np.array(nq.nf4_codebook_levels(name), np.float32)
+        assert np.array_equal(got.view(np.uint32), oracle_mod.codebook_levels(name).view(np.uint32))
+    assert not L.nf4_codebook_levels(3)

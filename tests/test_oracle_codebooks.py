@@ -46,7 +46,12 @@ def test_int4_is_the_uniform_quantizer_of_the_comparison(oracle_mod):
 def test_codebook_brute_force(oracle_mod, cb):
     rng = np.random.Generator(np.random.PCG64(len(cb)))
     lv = oracle_mod.codebook_levels(cb)
-    assert np.all(np.diff(lv) >= 0) and lv[0] == -1 and lv[-1] == 1
+    used = lv[:15] if cb == "fp4" else lv  # FP4's index 15 is its -0, equal to level 7
+    assert np.all(np.diff(used) > 0) and used[0] == -1 and used[-1] == 1
+    if cb == "fp4":
+        assert lv[15] == 0 and np.signbit(lv[15]) and lv[7] == 0 and not np.signbit(lv[7])
+        assert np.array_equal(np.sort(np.abs(lv[:15] * 6).astype(np.float64))[::2],
+                              [0, 0.5, 1, 1.5, 2, 3, 4, 6])
     n = 64 * 40 + 9
     w = rng.standard_normal(n, dtype=np.float32)
     w[:64] = 0.0
