@@ -77,7 +77,8 @@ hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_
                               hipStream_t s);
 hipError_t launch_double_quantize_ex(const float *absmax, int64_t nblocks, const nf4_format &f,
                                      uint8_t *absmax_q, float *absmax_scale,
-                                     float *absmax_offset, void *workspace, hipStream_t s);
+                                     float *absmax_offset, void *workspace, hipStream_t s,
+                                     const float *parts = nullptr, int64_t nparts = 0);
 hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format &f,
                                 const float *absmax, const uint8_t *absmax_q,
                                 const float *absmax_scale, const float *absmax_offset, void *out,

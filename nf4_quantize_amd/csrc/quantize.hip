@@ -66,6 +66,21 @@ __device__ __forceinline__ float wg_max(float v, float *s_red) {
     return r;
 }
 
+// Pairwise fp32 sum of s_v[0..255], the subtree of a pairwise sum that an
+// aligned run of 256 values forms: threads 0..255 hold one value each, lanes
+// pair up by XOR shuffles (x + y == y + x, so both lanes of a pair hold the
+// node), and the four wave sums pair last. Every thread of the workgroup
+// calls it; the result is valid in all of them.
+__device__ __forceinline__ float block256_pairwise_sum(const float *s_v, float *s_red) {
+    const int t = threadIdx.x;
+    float v = t < 256 ? s_v[t] : 0.0f;
+#pragma unroll
+    for (int k = 1; k < 64; k *= 2) v = v + __shfl_xor(v, k);
+    if ((t & 63) == 0 && t < 256) s_red[t >> 6] = v;
+    __syncthreads();
+    return (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+}
+
 // Byte offset of the table entry of a normalised value (see CodeLut).
 __device__ __forceinline__ uint32_t lut_offset(float v) {
     return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f));
@@ -190,11 +205,14 @@ __device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32
     if (t == 0) absmax_scale[g] = sc;
 }
 
-// One workgroup of TH threads per full group of 16384 weights.
+// One workgroup of TH threads per full group of 16384 weights. Without fused
+// double quantization, `partial` (if set) receives the pairwise sum of the
+// group's 256 block scales (the first levels of the mean offset's sum).
 template <typename T, bool kDQ, int TH, int F>
 __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
-    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, CodeLut lut) {
+    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
+    CodeLut lut) {
     using S = Slice<T>;
     constexpr int E = S::kElems;               // weights per lane slice
     constexpr int LPB = kBlock / E;            // lanes per block
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
         const float m = __uint_as_float(mb);
         const int blk = i * BPI + t / LPB;  // block within the group
         if ((t % LPB) == 0) {
-            if (kDQ) s_c1[blk] = m;
+            if (kDQ || partial) s_c1[blk] = m;
             if (absmax) absmax[g * kDqBlock + blk] = m;
         }
         const uint32_t packed = slice_codes<E>(f, m, s_lut);
@@ -253,6 +271,10 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     if (kDQ) {
         __syncthreads();
         group_dq<TH, F>(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
+    } else if (partial) {
+        __syncthreads();
+        const float sum = block256_pairwise_sum(s_c1, s_red);
+        if (t == 0) partial[g] = sum;
     }
 }
 
@@ -262,7 +284,7 @@ template <typename T, int F>
 __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
     const T *__restrict__ w, int64_t n, int64_t g, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale,
-    CodeLut lut) {
+    float *__restrict__ partial, CodeLut lut) {
     __shared__ float2 s_lut[kLutEntries];
     __shared__ float s_c1[kDqBlock];
     __shared__ float s_red[4];
@@ -294,6 +316,10 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
         const int64_t nblocks = (n + kBlock - 1) / kBlock;
         if (b < nblocks) absmax_q[b] = (uint8_t)dq_encode<F, false>(s_c1[t], sc);
         if (t == 0) absmax_scale[g] = sc;
+    } else if (partial) {
+        __syncthreads();
+        const float sum = block256_pairwise_sum(s_c1, s_red);  // blocks past n hold 0
+        if (t == 0) partial[g] = sum;
     }
 }
 
@@ -322,20 +348,20 @@ constexpr int kGroupThreads = 512;
 template <typename T, int F>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
                              uint8_t *absmax_q, float *absmax_scale, const CodeLut &lut,
-                             hipStream_t s) {
+                             hipStream_t s, float *partial = nullptr) {
     const int64_t full = n / kGroup;
     constexpr int TH = kGroupThreads;
     if (full > 0) {
         if (absmax_q)
             quantize_groups_kernel<T, true, TH, F><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
-                w, codes, absmax, absmax_q, absmax_scale, lut);
+                w, codes, absmax, absmax_q, absmax_scale, nullptr, lut);
         else
             quantize_groups_kernel<T, false, TH, kFmtE4M3><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
-                w, codes, absmax, nullptr, nullptr, lut);
+                w, codes, absmax, nullptr, nullptr, partial, lut);
     }
     if (n % kGroup)
         quantize_tail_kernel<T, F><<<1, kThreads, 0, s>>>(w, n, full, codes, absmax, absmax_q,
-                                                          absmax_scale, lut);
+                                                          absmax_scale, partial, lut);
     return hipGetLastError();
 }
 
@@ -460,15 +486,15 @@ __global__ __launch_bounds__(64) void quantize_blocks_tail_kernel(
 // (x + y == y + x, so both lanes of a pair hold the same node) and the four
 // wave sums pair up last. final_mean: one workgroup, writes sum / nf.
 constexpr int kSumChunk = 4096;
-__global__ __launch_bounds__(kThreads) void pairwise_sum_kernel(const float *__restrict__ x,
-                                                                int64_t n, float *__restrict__ out,
-                                                                float nf, int final_mean) {
-    __shared__ float s_w[kThreads / 64];
+// The chunk [base, base + 4096) of x (zeros past n), summed pairwise by a
+// 256-thread workgroup; every thread gets the sum.
+__device__ __forceinline__ float chunk_pairwise_sum(const float *__restrict__ x, int64_t n,
+                                                    int64_t base, float *s_w) {
     const int t = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * kSumChunk + 16 * t;
+    const int64_t b0 = base + 16 * t;
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = (base + i < n) ? x[base + i] : 0.0f;
+    for (int i = 0; i < 16; ++i) v[i] = (b0 + i < n) ? x[b0 + i] : 0.0f;
 #pragma unroll
     for (int h = 1; h < 16; h *= 2)
 #pragma unroll
@@ -478,44 +504,78 @@ __global__ __launch_bounds__(kThreads) void pairwise_sum_kernel(const float *__r
     for (int k = 1; k < 64; k *= 2) sum = sum + __shfl_xor(sum, k);
     if ((t & 63) == 0) s_w[t >> 6] = sum;
     __syncthreads();
-    if (t == 0) {
-        const float tot = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
-        out[blockIdx.x] = final_mean ? tot / nf : tot;
-    }
+    return (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void pairwise_sum_kernel(const float *__restrict__ x,
+                                                                int64_t n, float *__restrict__ out) {
+    __shared__ float s_w[kThreads / 64];
+    const float tot = chunk_pairwise_sum(x, n, (int64_t)blockIdx.x * kSumChunk, s_w);
+    if (threadIdx.x == 0) out[blockIdx.x] = tot;
 }
 
 // Double quantization with group size 2^lb2 in format F (kS: mean offset,
 // signed codes). A group of 64 or more blocks is one wave's; smaller groups
-// are aligned lane segments of a wave of 64 consecutive blocks.
+// are aligned lane segments of a wave of 64 consecutive blocks. With the
+// mean offset every workgroup first finishes the pairwise sum itself from
+// the top level's nparts <= 4096 partial sums (the same value everywhere),
+// mu = sum / nf, and workgroup 0 stores mu.
 template <int F, bool kS>
 __global__ __launch_bounds__(kThreads) void dq_generic_kernel(
-    const float *__restrict__ absmax, int64_t nblocks, int lb2, const float *__restrict__ mu_p,
-    uint8_t *__restrict__ q, float *__restrict__ scale) {
+    const float *__restrict__ absmax, int64_t nblocks, int lb2, const float *__restrict__ parts,
+    int64_t nparts, float nf, float *__restrict__ mu_out, uint8_t *__restrict__ q,
+    float *__restrict__ scale) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const float mu = kS ? *mu_p : 0.0f;
     const int b2 = 1 << lb2;
-    auto xval = [&](int64_t b) -> float {
-        const float c = absmax[b];
-        return kS ? c - mu : c;
+    // The first 256 block scales of the wave's group (or its 64 blocks) are
+    // loaded before mu is summed, so the two load chains overlap; a larger
+    // group reads the rest in its loops.
+    constexpr int kCache = 4;
+    const int64_t g = wave;
+    const int64_t b0 = b2 >= 64 ? (g << lb2) : wave * 64;
+    float c[kCache];
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+        const int j = lane + 64 * i;
+        const bool in = (b2 >= 64 ? j < b2 : i == 0) && b0 + j < nblocks;
+        c[i] = in ? absmax[b0 + j] : 0.0f;
+    }
+    float mu = 0.0f;
+    if constexpr (kS) {
+        __shared__ float s_w[kThreads / 64];
+        mu = chunk_pairwise_sum(parts, nparts, 0, s_w) / nf;
+        if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+    }
+    auto xof = [&](float cv) -> float { return kS ? cv - mu : cv; };
+    auto xval = [&](int j) -> float {  // block b0 + j (j < b2, in range)
+        return j < 64 * kCache ? xof(c[j / 64]) : xof(absmax[b0 + j]);
     };
     if (b2 >= 64) {
-        const int64_t g = wave;
         if (g >= ((nblocks + b2 - 1) >> lb2)) return;  // uniform over the wave
-        const int64_t b0 = g << lb2;
         float m = 0.0f;
-        for (int j = lane; j < b2; j += 64)
-            if (b0 + j < nblocks) m = fmaxf(m, fabsf(xval(b0 + j)));
+#pragma unroll
+        for (int i = 0; i < kCache; ++i) {
+            const int j = lane + 64 * i;
+            if (j < b2 && b0 + j < nblocks) m = fmaxf(m, fabsf(xof(c[i])));
+        }
+        for (int j = lane + 64 * kCache; j < b2; j += 64)
+            if (b0 + j < nblocks) m = fmaxf(m, fabsf(xof(absmax[b0 + j])));
         float sc = wave_max_nonneg(m);
         if (F == kFmtLin8) sc = sc / lin_levels<kS>();
         if (lane == 0) scale[g] = sc;
-        for (int j = lane; j < b2; j += 64)
-            if (b0 + j < nblocks) q[b0 + j] = (uint8_t)dq_encode<F, kS>(xval(b0 + j), sc);
+#pragma unroll
+        for (int i = 0; i < kCache; ++i) {
+            const int j = lane + 64 * i;
+            if (j < b2 && b0 + j < nblocks) q[b0 + j] = (uint8_t)dq_encode<F, kS>(xof(c[i]), sc);
+        }
+        for (int j = lane + 64 * kCache; j < b2; j += 64)
+            if (b0 + j < nblocks) q[b0 + j] = (uint8_t)dq_encode<F, kS>(xval(j), sc);
     } else {
-        const int64_t b = wave * 64 + lane;
+        const int64_t b = b0 + lane;
         const bool live = b < nblocks;
-        const float x = live ? xval(b) : 0.0f;
+        const float x = live ? xof(c[0]) : 0.0f;
         uint32_t mb = __float_as_uint(fabsf(x));
         for (int k = 1; k < b2; k *= 2) mb = max(mb, (uint32_t)__shfl_xor((int)mb, k));
         float sc = __uint_as_float(mb);
@@ -574,11 +634,11 @@ int ilog2(int64_t v) {
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 template <int F, bool kS>
-void launch_dq_generic(const float *absmax, int64_t nb, int lb2, const float *mu, uint8_t *q,
-                       float *scale, hipStream_t s) {
+void launch_dq_generic(const float *absmax, int64_t nb, int lb2, const float *parts,
+                       int64_t nparts, float *mu, uint8_t *q, float *scale, hipStream_t s) {
     const int64_t waves = lb2 >= 6 ? ((nb + (int64_t(1) << lb2) - 1) >> lb2) : (nb + 63) / 64;
     dq_generic_kernel<F, kS><<<dim3((unsigned)((waves + 3) / 4)), dim3(kThreads), 0, s>>>(
-        absmax, nb, lb2, mu, q, scale);
+        absmax, nb, lb2, parts, nparts, (float)nb, mu, q, scale);
 }
 
 // ---- merging the adapter into the quantized base ----
@@ -811,42 +871,48 @@ size_t double_quantize_ex_workspace(int64_t nblocks, const nf4_format &f) {
     return round256(4 * (size_t)l1) + round256(4 * (size_t)l2);
 }
 
+// Two-pass layout: fp32 block scales, then (mean offset, B1 = 64) the
+// pairwise sums of the 256-block groups, then the partial-sum levels.
 size_t quantize_ex_workspace(int64_t n, const nf4_format &f) {
     const int64_t nb = (n + f.blocksize - 1) / f.blocksize;
     const bool fused = f.blocksize == kBlock && f.dq_blocksize == kDqBlock && !f.dq_mean_offset;
-    return (fused ? 0 : round256(4 * (size_t)nb)) + double_quantize_ex_workspace(nb, f);
+    if (fused) return 0;
+    const size_t groups = f.dq_mean_offset ? round256(4 * (size_t)((nb + kDqBlock - 1) / kDqBlock)) : 0;
+    return round256(4 * (size_t)nb) + groups + double_quantize_ex_workspace(nb, f);
 }
 
+// parts / nparts: partial sums that already cover aligned power-of-two runs
+// of the block scales (the group sums of the quantize kernel), or nullptr to
+// start from the block scales themselves.
 hipError_t launch_double_quantize_ex(const float *absmax, int64_t nb, const nf4_format &f,
                                      uint8_t *absmax_q, float *absmax_scale,
-                                     float *absmax_offset, void *workspace, hipStream_t s) {
+                                     float *absmax_offset, void *workspace, hipStream_t s,
+                                     const float *parts, int64_t nparts) {
     const int lb2 = ilog2(f.dq_blocksize);
     if (f.dq_mean_offset) {
         // mu: the pairwise sum level by level (ping-pong between two partial
-        // buffers), the last level divides by the block count
+        // buffers) down to one chunk, which the DQ kernel finishes itself
         const int64_t l1 = std::max<int64_t>(1, (nb + kSumChunk - 1) / kSumChunk);
         float *buf[2] = {static_cast<float *>(workspace),
                          static_cast<float *>(workspace) + round256(4 * (size_t)l1) / 4};
-        const float *src = absmax;
-        int64_t len = nb;
+        const float *src = parts ? parts : absmax;
+        int64_t len = parts ? nparts : nb;
         for (int lvl = 0; len > kSumChunk; ++lvl) {
             const int64_t outlen = (len + kSumChunk - 1) / kSumChunk;
-            pairwise_sum_kernel<<<dim3((unsigned)outlen), dim3(kThreads), 0, s>>>(
-                src, len, buf[lvl & 1], 0.0f, 0);
+            pairwise_sum_kernel<<<dim3((unsigned)outlen), dim3(kThreads), 0, s>>>(src, len, buf[lvl & 1]);
             src = buf[lvl & 1];
             len = outlen;
         }
-        pairwise_sum_kernel<<<1, kThreads, 0, s>>>(src, len, absmax_offset, (float)nb, 1);
         switch (f.dq_format) {
-            case kFmtE5M2: launch_dq_generic<kFmtE5M2, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s); break;
-            case kFmtLin8: launch_dq_generic<kFmtLin8, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s); break;
-            default: launch_dq_generic<kFmtE4M3, true>(absmax, nb, lb2, absmax_offset, absmax_q, absmax_scale, s);
+            case kFmtE5M2: launch_dq_generic<kFmtE5M2, true>(absmax, nb, lb2, src, len, absmax_offset, absmax_q, absmax_scale, s); break;
+            case kFmtLin8: launch_dq_generic<kFmtLin8, true>(absmax, nb, lb2, src, len, absmax_offset, absmax_q, absmax_scale, s); break;
+            default: launch_dq_generic<kFmtE4M3, true>(absmax, nb, lb2, src, len, absmax_offset, absmax_q, absmax_scale, s);
         }
     } else {
         switch (f.dq_format) {
-            case kFmtE5M2: launch_dq_generic<kFmtE5M2, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s); break;
-            case kFmtLin8: launch_dq_generic<kFmtLin8, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s); break;
-            default: launch_dq_generic<kFmtE4M3, false>(absmax, nb, lb2, nullptr, absmax_q, absmax_scale, s);
+            case kFmtE5M2: launch_dq_generic<kFmtE5M2, false>(absmax, nb, lb2, nullptr, 0, nullptr, absmax_q, absmax_scale, s); break;
+            case kFmtLin8: launch_dq_generic<kFmtLin8, false>(absmax, nb, lb2, nullptr, 0, nullptr, absmax_q, absmax_scale, s); break;
+            default: launch_dq_generic<kFmtE4M3, false>(absmax, nb, lb2, nullptr, 0, nullptr, absmax_q, absmax_scale, s);
         }
     }
     return hipGetLastError();
@@ -871,17 +937,32 @@ hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_
     // two passes: codes and fp32 absmax, then double quantization
     const int64_t nb = (n + f.blocksize - 1) / f.blocksize;
     float *am = absmax;
-    void *rest = workspace;
+    char *rest = static_cast<char *>(workspace);
+    float *gsum = nullptr;  // group sums of the mean offset (B1 = 64)
+    int64_t ngroups = 0;
     if (dq) {
         if (!am) am = static_cast<float *>(workspace);
-        rest = static_cast<char *>(workspace) + round256(4 * (size_t)nb);
+        rest += round256(4 * (size_t)nb);
+        if (f.dq_mean_offset) {
+            ngroups = (nb + kDqBlock - 1) / kDqBlock;
+            if (f.blocksize == kBlock) gsum = reinterpret_cast<float *>(rest);
+            rest += round256(4 * (size_t)ngroups);
+        }
     }
-    hipError_t e = bf ? launch_blocks_bs<uint16_t>(static_cast<const uint16_t *>(w), n,
-                                                   f.blocksize, codes, am, lut, s)
-                      : launch_blocks_bs<float>(static_cast<const float *>(w), n, f.blocksize,
-                                                codes, am, lut, s);
+    hipError_t e;
+    if (gsum)
+        e = bf ? launch_quantize_t<uint16_t, kFmtE4M3>(static_cast<const uint16_t *>(w), n, codes, am,
+                                                       nullptr, nullptr, lut, s, gsum)
+               : launch_quantize_t<float, kFmtE4M3>(static_cast<const float *>(w), n, codes, am,
+                                                    nullptr, nullptr, lut, s, gsum);
+    else
+        e = bf ? launch_blocks_bs<uint16_t>(static_cast<const uint16_t *>(w), n, f.blocksize, codes,
+                                            am, lut, s)
+               : launch_blocks_bs<float>(static_cast<const float *>(w), n, f.blocksize, codes, am,
+                                         lut, s);
     if (e != hipSuccess || !dq) return e;
-    return launch_double_quantize_ex(am, nb, f, absmax_q, absmax_scale, absmax_offset, rest, s);
+    return launch_double_quantize_ex(am, nb, f, absmax_q, absmax_scale, absmax_offset, rest, s,
+                                     gsum, ngroups);
 }
 
 

@@ -233,7 +233,8 @@ def test_format_variant_validation(L):
     assert L.nf4_quantize_ex_workspace_size(1024, _fmt(f=2)) == 0
     assert L.nf4_quantize_ex_workspace_size(1024, _fmt(bs=48)) == ctypes.c_size_t(-1).value
     # the mean offset: block scales, then two partial-sum buffers
-    assert L.nf4_quantize_ex_workspace_size(1 << 20, _fmt(off=1)) == 4 * (1 << 14) + 256 + 256
+    # (plus the 256-block group sums when B1 = 64)
+    assert L.nf4_quantize_ex_workspace_size(1 << 20, _fmt(off=1)) == 4 * (1 << 14) + 256 + 256 + 256
     assert L.nf4_double_quantize_ex_workspace_size(5000, _fmt(off=1)) == 256 + 256
     assert L.nf4_double_quantize_ex_workspace_size(5000, _fmt(f=1)) == 0
 
