@@ -156,7 +156,10 @@ const CodeLut *code_lut_for(int cb) {
     static bool ok[3] = {false, false, false};
     static std::once_flag once[3];
     if (cb < 0 || cb > 2) return nullptr;
-    std::call_once(once[cb], [cb] { ok[cb] = build_lut(&lut[cb], levels_for(cb)); });
+    std::call_once(once[cb], [cb] {
+        ok[cb] = build_lut(&lut[cb], levels_for(cb));
+        lut[cb].refine = cb != NF4_CODEBOOK_NF4;
+    });
     return ok[cb] ? &lut[cb] : nullptr;
 }
 

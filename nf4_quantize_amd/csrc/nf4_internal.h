@@ -43,6 +43,11 @@ struct LutEntry {
 };
 struct CodeLut {
     LutEntry e[kLutEntries];
+    // 1 for codebooks whose switch points are ratios of small integers (FP4,
+    // Int4): bf16 quotients land on or next to them often, so the bf16 path
+    // refines the quotient to fl32(w / c1) instead of falling back to the
+    // division near a switch point.
+    int32_t refine;
 };
 __host__ __device__ __forceinline__ uint32_t lut_offset_bits(float fma_result) {
     return __builtin_bit_cast(uint32_t, fma_result) & 0x1F8u;

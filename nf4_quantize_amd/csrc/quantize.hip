@@ -175,6 +175,55 @@ __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, c
     return packed;
 }
 
+// Codes of a bf16 slice for the codebooks with `refine` set (see CodeLut).
+// One residual step makes the quotient exact: with rcp within 1 ulp of 1/c1,
+// x = fl(w rcp) and r = fma(-c1, x, w), the value x + r rcp is within
+// 2^-22 ulp of w / c1, while the quotient of two bf16 values (8-bit
+// significands) is never a rounding midpoint and lies at least 2^-9 ulp from
+// one. So xr = fma(r, rcp, x) = fl32(w / c1), and the switch point test
+// xr < thr is exact. Quotients below 2^-120 (subnormal results round on a
+// coarser grid) and a c1 outside [2^-118, 2^125] take the division.
+__device__ __forceinline__ uint32_t slice_codes_refined(const float (&f)[8], float c1,
+                                                        const float2 *s_lut) {
+    const bool in_range = (c1 >= 0x1p-118f) & (c1 <= 0x1p125f);
+    const bool outside = (c1 > 0.0f) & !in_range;
+    const float rcp = in_range ? __builtin_amdgcn_rcpf(c1) : 0.0f;
+    uint32_t top = 0;
+    bool tiny = false;
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = f[e] * rcp;
+        const float r = fmaf(-c1, x, f[e]);
+        const float xr = fmaf(r, rcp, x);
+        const float2 ent = lut_at(s_lut + e * kLutEntries,
+                                  lut_offset_bits(fmaf(xr, 128.0f, 128.0f + 0x1p23f)));
+        d[e] = xr - ent.x;  // negative exactly when xr < thr
+        top |= __float_as_uint(ent.y);
+        tiny |= ((__float_as_uint(xr) & 0x7FFFFFFFu) - 1u) < 0x037FFFFFu;  // 0 < |xr| < 2^-120
+    }
+    uint32_t packed = top - sign_nibbles<8>(d);
+    if (outside | tiny) {  // rare: redo with the correctly rounded division
+        packed = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f) << (4 * e);
+    }
+    return packed;
+}
+
+// Codes of a slice, refined for the codebooks that need it (bf16 only; an
+// fp32 quotient can sit next to a midpoint, so fp32 slices keep the
+// division fallback).
+template <int E>
+__device__ __forceinline__ uint32_t slice_codes_any(const float (&f)[E], float c1,
+                                                    const float2 *s_lut, int32_t refine) {
+    if constexpr (E == 8) {
+        if (refine) return slice_codes_refined(f, c1, s_lut);
+    }
+    return slice_codes<E>(f, c1, s_lut);
+}
+
 // Entry i of the table copies (copy i / kLutEntries, see slice_codes).
 __device__ __forceinline__ float2 lut_copy_entry(const LutEntry &le, int i) {
     return make_float2(le.thr, __int_as_float(le.hi << (4 * (i / kLutEntries))));
@@ -261,7 +310,7 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
             if (kDQ || partial) s_c1[blk] = m;
             if (absmax) absmax[g * kDqBlock + blk] = m;
         }
-        const uint32_t packed = slice_codes<E>(f, m, s_lut);
+        const uint32_t packed = slice_codes_any<E>(f, m, s_lut, lut.refine);
         const int64_t slice = (int64_t)g * SLICES + i * TH + t;
         if (E == 8)
             reinterpret_cast<uint32_t *>(codes)[slice] = packed;
@@ -440,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
         }
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const uint32_t packed = slice_codes<E>(f[i], m, s_lut);
+            const uint32_t packed = slice_codes_any<E>(f[i], m, s_lut, lut.refine);
             const int64_t slice = unit * (U / E) + i * 64 + lane;
             if (E == 8)
                 reinterpret_cast<uint32_t *>(codes)[slice] = packed;
