@@ -82,6 +82,8 @@ def lib():
         L.nf4ref_quantize_cb.argtypes = [_p, ctypes.c_int, _i64, _i32, ctypes.c_int, _p, _p]
         L.nf4ref_dequantize_range_cb.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, ctypes.c_int,
                                                  ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int]
+        L.nf4ref_storage_bytes_ex.argtypes = [_i64, _i32, _i32, ctypes.c_int, ctypes.c_int]
+        L.nf4ref_storage_bytes_ex.restype = _i64
         L.nf4ref_lora_grads.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _i32, ctypes.c_double,
                                         _p, _i64, _p, _p, _i64, _p]
         _lib = L
@@ -378,6 +380,11 @@ def dequantize_cb(codes, n, blocksize=BLOCK, dq_blocksize=DQ_BLOCK, dq_format="e
                                             _ptr(absmax), _ptr(q), _ptr(scale), _ptr(off),
                                             _ptr(out), out_dtype), "dequantize_range_cb")
     return out
+
+
+def storage_bytes_ex(n, blocksize=BLOCK, dq_blocksize=DQ_BLOCK, dq=True, mean_offset=False):
+    return int(lib().nf4ref_storage_bytes_ex(int(n), int(blocksize), int(dq_blocksize),
+                                             1 if dq else 0, 1 if mean_offset else 0))
 
 
 def storage_bytes(n, dq):

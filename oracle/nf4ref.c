@@ -778,3 +778,14 @@ int nf4ref_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t 
     free(acc);
     return rc;
 }
+
+int64_t nf4ref_storage_bytes_ex(int64_t n, int32_t blocksize, int32_t dq_blocksize, int dq,
+                                int mean_offset) {
+    if (n < 0 || !pow2_in(blocksize, 16, 4096) || !pow2_in(dq_blocksize, 1, 4096)) return -1;
+    int64_t nblocks = (n + blocksize - 1) / blocksize;
+    int64_t code_bytes = (n + 1) / 2;
+    if (!dq) return code_bytes + 4 * nblocks;
+    int64_t ngroups = (nblocks + dq_blocksize - 1) / dq_blocksize;
+    return code_bytes + nblocks + 4 * ngroups + (mean_offset ? 4 : 0);
+}
+

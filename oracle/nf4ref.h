@@ -234,6 +234,14 @@ int nf4ref_dequantize_range_cb(const uint8_t *codes, int64_t n, int64_t start, i
                                const float *absmax, const uint8_t *q, const float *scale,
                                const float *offset, void *out, int out_dtype);
 
+/* Storage bytes of an n-element tensor in a variant format: ceil(n/2) code
+ * bytes, then either fp32 absmax (dq == 0: 4 per block of B1) or one 8-bit
+ * code per block, one fp32 per group of B2 blocks and, with the mean offset,
+ * one fp32 for the tensor ([MF] "Double Quantization (DQ)", the footprint
+ * with B1 and B2 as parameters). Returns -1 for invalid arguments. */
+int64_t nf4ref_storage_bytes_ex(int64_t n, int32_t blocksize, int32_t dq_blocksize, int dq,
+                                int mean_offset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -292,3 +292,17 @@ def test_variant_argument_checks(oracle_mod):
         oracle_mod.quantize_bs(np.ones(10, np.float32), 8)
     with pytest.raises(ValueError):
         oracle_mod.quantize_bs(np.ones(10, np.float32), 96)
+
+
+def test_variant_footprint_closed_forms(oracle_mod):
+    """[MF] "Double Quantization (DQ)": 8 / B1 + 32 / (B1 B2) bits per parameter
+    of scale data, with B1 and B2 as parameters; 32 / B1 without DQ."""
+    n = 1 << 24
+    for b1, b2 in ((64, 256), (128, 256), (32, 64), (256, 1024)):
+        dq = oracle_mod.storage_bytes_ex(n, b1, b2, True)
+        assert (dq - n // 2) * 8 / n == 8 / b1 + 32 / (b1 * b2)
+        assert (oracle_mod.storage_bytes_ex(n, b1, b2, False) - n // 2) * 8 / n == 32 / b1
+        assert oracle_mod.storage_bytes_ex(n, b1, b2, True, True) == dq + 4
+    # the printed default: 0.127 bits of overhead (0.126953125 exactly)
+    assert oracle_mod.storage_bytes_ex(n) == oracle_mod.storage_bytes(n, True)
+    assert oracle_mod.storage_bytes_ex(10, 48) == -1
