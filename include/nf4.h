@@ -256,6 +256,12 @@ typedef struct {
 /* The 16 levels of a codebook (static host array), NULL for an unknown id. */
 const float *nf4_codebook_levels(int32_t codebook);
 
+/* Bytes of the packed storage of an n-element tensor in format f: codes plus
+ * either fp32 absmax (double_quant == 0) or the 8-bit codes, the fp32 group
+ * values and, with the mean offset, one fp32 offset. Returns -1 for invalid
+ * arguments. */
+int64_t nf4_storage_bytes_ex(int64_t n, const nf4_format *f, int32_t double_quant);
+
 /* Device workspace bytes of nf4_quantize_ex for an n-element tensor: fp32
  * block scales when the call runs in two passes (B1 != 64, B2 != 256 or the
  * mean offset, with double quantization) plus, with the mean offset, the

@@ -54,6 +54,7 @@ EXPORTS = (
     "nf4_dequantize_ex",
     "nf4_merge_lora_workspace_size",
     "nf4_merge_lora",
+    "nf4_storage_bytes_ex",
 )
 
 # nf4_dq_format: the 8-bit code of double quantization.
@@ -145,6 +146,8 @@ def lib():
     L.nf4_double_quantize_ex.restype = ctypes.c_int
     L.nf4_dequantize_ex.argtypes = [p, i64, fmt_p, p, p, p, p, p, ctypes.c_int, p]
     L.nf4_dequantize_ex.restype = ctypes.c_int
+    L.nf4_storage_bytes_ex.argtypes = [i64, fmt_p, i32]
+    L.nf4_storage_bytes_ex.restype = i64
     L.nf4_merge_lora_workspace_size.argtypes = [i64, i64]
     L.nf4_merge_lora_workspace_size.restype = ctypes.c_size_t
     L.nf4_merge_lora.argtypes = [ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p, p, p, p,
@@ -271,6 +274,10 @@ def _ws_size(fn, n, fmt):
     if size == ctypes.c_size_t(-1).value:
         raise NF4Error(3, fn.__name__)
     return int(size)
+
+
+def nf4_storage_bytes_ex(n, fmt: NF4Format, double_quant=True):
+    return int(lib().nf4_storage_bytes_ex(n, ctypes.byref(fmt.struct()), 1 if double_quant else 0))
 
 
 def nf4_quantize_ex_workspace_size(n, fmt: NF4Format):

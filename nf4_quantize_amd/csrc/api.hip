@@ -382,6 +382,14 @@ nf4_status check_workspace(size_t need, const void *ws, size_t ws_bytes) {
 
 }  // namespace
 
+NF4_API int64_t nf4_storage_bytes_ex(int64_t n, const nf4_format *f, int32_t double_quant) {
+    if (check_format(f) != NF4_OK || n < 0) return -1;
+    const int64_t nb = cdiv(n, f->blocksize);
+    const int64_t codes = cdiv(n, 2);
+    if (!double_quant) return codes + 4 * nb;
+    return codes + nb + 4 * cdiv(nb, f->dq_blocksize) + (f->dq_mean_offset ? 4 : 0);
+}
+
 NF4_API size_t nf4_quantize_ex_workspace_size(int64_t n, const nf4_format *f) {
     if (check_format(f) != NF4_OK || n < 0 || n > kMaxElems) return (size_t)-1;
     return nf4::quantize_ex_workspace(n, *f);

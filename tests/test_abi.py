@@ -302,3 +302,13 @@ def test_codebook_levels(L, oracle_mod):
         got = np.array(nq.nf4_codebook_levels(name), np.float32)
         assert np.array_equal(got.view(np.uint32), oracle_mod.codebook_levels(name).view(np.uint32))
     assert not L.nf4_codebook_levels(3)
+
+
+def test_storage_bytes_ex_matches_oracle(L, oracle_mod):
+    for n in (0, 1, 1000, 1 << 20, 11008 * 4096):
+        for bs, dqb, off in ((64, 256, 0), (128, 64, 1), (16, 1, 0), (4096, 4096, 1)):
+            for dq in (0, 1):
+                got = L.nf4_storage_bytes_ex(n, _fmt(bs, dqb, 0, off), dq)
+                assert got == oracle_mod.storage_bytes_ex(n, bs, dqb, bool(dq), bool(off))
+    assert L.nf4_storage_bytes_ex(64, _fmt(bs=48), 1) == -1
+    assert L.nf4_storage_bytes_ex(-1, _fmt(), 1) == -1
