@@ -190,3 +190,22 @@ def test_variant_mlp_shape(dev):
     outputs compared in full."""
     w = workloads.weight_mlp_outliers_bf16()
     check_variant(dev, w.ravel(), nq.NF4Format(128, 256, "e5m2", True), label="mlp")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dqb", [1, 8, 64, 256, 4096])
+def test_double_quantize_ex_standalone(dev, fmt, dqb):
+    """nf4_double_quantize_ex on existing fp32 block scales (no mean offset),
+    including a ragged last group and zero scales."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(dqb + len(fmt)))
+    nb = 3 * max(dqb, 64) + 37
+    amax = np.abs(rng.standard_normal(nb, dtype=np.float32)) * np.float32(0.05)
+    amax[:5] = 0.0
+    f = nq.NF4Format(64, dqb, fmt, False)
+    q, sc = nq.double_quantize(to_dev(amax, dev), fmt=f)
+    torch.cuda.synchronize()
+    rq, rsc, _ = oracle.double_quantize_ex(amax, dqb, fmt, False)
+    assert np.array_equal(to_host(q), rq)
+    assert np.array_equal(to_host(sc).view(np.uint32), rsc.view(np.uint32))
