@@ -490,9 +490,13 @@ def variant_benches(dev, iters, warmup):
     return out
 
 
-def stack_bench(dev):
+def stack_bench(dev, reps=3):
     """Workload 3: quantize all 224 matrices of a 32-layer 8B-shaped stack,
-    then stream-dequantize every matrix to bf16."""
+    then stream-dequantize every matrix to bf16: one call per matrix, and the
+    batched calls (all 224 matrices in one quantize call; dequantize a layer
+    at a time into one reused buffer, or all matrices into their own
+    buffers). Median of `reps` passes, each timed by events around it."""
+    import numpy as np
     import torch
     import nf4_quantize_amd as nq
     import workloads
@@ -503,31 +507,59 @@ def stack_bench(dev):
             mats.append(workloads.stack_matrix_bf16(layer, mi, dev).view(-1))
     packed = [nq.empty_nf4(tuple(m.shape), dev) for m in mats]
     outbuf = torch.empty(max(m.numel() for m in mats), dtype=torch.bfloat16, device=dev)
+    nmat = len(workloads.STACK_MATRICES)
+    layer_n = [m.numel() for m in mats[:nmat]]
+    layer_buf = torch.empty(sum(layer_n), dtype=torch.bfloat16, device=dev)
+    layer_outs = list(torch.split(layer_buf, layer_n))
+    outs_all = [torch.empty_like(m) for m in mats]
     total = sum(m.numel() for m in mats)
 
     def qall():
         for m, p in zip(mats, packed):
             nq.nf4_quantize(m, p.codes, None, p.absmax_q, p.absmax_scale)
 
+    # the batched calls' entry arrays are marshalled once, outside the timing
+    qplan = nq.NF4Batch(mats, packed)
+    layer_plans = [nq.NF4Batch(layer_outs, packed[layer * nmat:(layer + 1) * nmat])
+                   for layer in range(workloads.STACK_LAYERS)]
+    all_plan = nq.NF4Batch(outs_all, packed)
+
+    def qbatch():
+        qplan.quantize()
+
     def dall():
         for m, p in zip(mats, packed):
             nq.nf4_dequantize(p.codes, m.numel(), outbuf[:m.numel()], absmax_q=p.absmax_q,
                               absmax_scale=p.absmax_scale)
 
-    qall(); dall()
+    def dbatch_layers():
+        for plan in layer_plans:
+            plan.dequantize()
+
+    def dbatch_all():
+        all_plan.dequantize()
+
+    for fn in (qall, qbatch, dall, dbatch_layers, dbatch_all):
+        fn()
     torch.cuda.synchronize()
     res = {}
     for name, fn, byts in (("quantize", qall, bytes_quantize(total, 2)),
-                           ("dequantize", dall, bytes_dequantize(total, 2))):
-        ev = Events(2)
-        ev[0].record()
-        fn()
-        ev[1].record()
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1])
+                           ("quantize_batched", qbatch, bytes_quantize(total, 2)),
+                           ("dequantize", dall, bytes_dequantize(total, 2)),
+                           ("dequantize_batched_per_layer", dbatch_layers, bytes_dequantize(total, 2)),
+                           ("dequantize_batched", dbatch_all, bytes_dequantize(total, 2))):
+        times = []
+        for _ in range(reps):
+            ev = Events(2)
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(times))
         res[f"stack_{name}_224_matrices"] = {"ms": ms, "GB/s": byts / ms / 1e6, "params": total}
         log(f"stack {name}: {res[f'stack_{name}_224_matrices']}")
-    del mats, packed, outbuf
+    del mats, packed, outbuf, layer_buf, layer_outs, outs_all, qplan, layer_plans, all_plan
     torch.cuda.empty_cache()
     return res
 

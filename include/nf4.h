@@ -109,6 +109,48 @@ nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t blocksize, co
                           const uint8_t *absmax_q, const float *absmax_scale,
                           int32_t dq_blocksize, void *out, nf4_dtype out_dtype, void *stream);
 
+/* One tensor of a batched call: the buffers that nf4_quantize and
+ * nf4_dequantize take for an n-element tensor (block size 64, DQ block 256),
+ * with the same layout, alignment and NULL rules.
+ *   w             device, n elements of the call's dtype: the input of
+ *                 nf4_quantize_batched, the output of nf4_dequantize_batched
+ *                 (16-byte aligned)
+ *   n             elements, >= 0 (an entry with n == 0 is skipped)
+ *   codes         device, ceil(n/2) bytes (16-byte aligned)
+ *   absmax        device or NULL, ceil(n/64) floats
+ *   absmax_q      device or NULL, ceil(n/64) bytes
+ *   absmax_scale  device or NULL, ceil(n/16384) floats
+ * absmax_q and absmax_scale are both set (double quantization) or both NULL
+ * (then absmax is required), per entry. */
+typedef struct {
+    void *w;
+    int64_t n;
+    uint8_t *codes;
+    float *absmax;
+    uint8_t *absmax_q;
+    float *absmax_scale;
+} nf4_batch_entry;
+
+/* nf4_quantize of each of `count` tensors, e.g. every weight of a model
+ * ([MF] "Block-Wise Quantization Mechanics" and "Double Quantization (DQ)",
+ * applied per tensor). Each entry's outputs are exactly those of
+ * nf4_quantize(e.w, w_dtype, e.n, 64, e.codes, e.absmax, 256, e.absmax_q,
+ * e.absmax_scale, stream). The full 16384-weight groups of up to 32 entries
+ * share one launch, and the partial last groups of up to 32 entries another,
+ * so small tensors do not each pay a launch's ramp-up and drain.
+ *   entries  host array of count entries, read during the call only
+ *   count    >= 0
+ * Every entry is validated before anything is launched; the first invalid
+ * entry decides the status. Outputs of different entries must not overlap. */
+nf4_status nf4_quantize_batched(const nf4_batch_entry *entries, int32_t count, nf4_dtype w_dtype,
+                                void *stream);
+
+/* nf4_dequantize of each of `count` tensors, batched the same way: entry e's
+ * w receives nf4_dequantize(e.codes, e.n, 64, e.absmax, e.absmax_q,
+ * e.absmax_scale, 256, e.w, out_dtype, stream). */
+nf4_status nf4_dequantize_batched(const nf4_batch_entry *entries, int32_t count,
+                                  nf4_dtype out_dtype, void *stream);
+
 /* A frozen NF4 weight W stored [n_out x k_in] row-major (d_out x d_in, the
  * transpose of [MF]'s W in R^{d_in x d_out}), quantized with nf4_quantize over
  * its flattening. Either absmax_q + absmax_scale (double quantization) or

@@ -55,6 +55,8 @@ EXPORTS = (
     "nf4_merge_lora_workspace_size",
     "nf4_merge_lora",
     "nf4_storage_bytes_ex",
+    "nf4_quantize_batched",
+    "nf4_dequantize_batched",
 )
 
 # nf4_dq_format: the 8-bit code of double quantization.
@@ -93,6 +95,17 @@ class nf4_format(ctypes.Structure):
         ("dq_format", ctypes.c_int32),
         ("dq_mean_offset", ctypes.c_int32),
         ("codebook", ctypes.c_int32),
+    ]
+
+
+class nf4_batch_entry(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("absmax_scale", ctypes.c_void_p),
     ]
 
 
@@ -147,6 +160,9 @@ def lib():
     L.nf4_dequantize_ex.argtypes = [p, i64, fmt_p, p, p, p, p, p, ctypes.c_int, p]
     L.nf4_dequantize_ex.restype = ctypes.c_int
     L.nf4_storage_bytes_ex.argtypes = [i64, fmt_p, i32]
+    for fn in (L.nf4_quantize_batched, L.nf4_dequantize_batched):
+        fn.argtypes = [ctypes.POINTER(nf4_batch_entry), i32, ctypes.c_int, p]
+        fn.restype = ctypes.c_int
     L.nf4_storage_bytes_ex.restype = i64
     L.nf4_merge_lora_workspace_size.argtypes = [i64, i64]
     L.nf4_merge_lora_workspace_size.restype = ctypes.c_size_t
@@ -236,6 +252,67 @@ def nf4_dequantize(codes, n, out, absmax=None, absmax_q=None, absmax_scale=None,
 
 def nf4_linear_workspace_size(m, r):
     return int(lib().nf4_linear_workspace_size(m, r))
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _batch(ws, ts, what):
+    """nf4_batch_entry array of (dense tensor, NF4Tensor) pairs, and their
+    common dense dtype code."""
+    if len(ws) != len(ts):
+        raise ValueError(f"{what}: {len(ws)} dense tensors for {len(ts)} NF4 tensors")
+    dts = {w.dtype for w in ws}
+    if len(dts) > 1:
+        raise ValueError(f"{what}: one dtype per call, got {sorted(map(str, dts))}")
+    arr = (nf4_batch_entry * max(1, len(ws)))()
+    for i, (w, t) in enumerate(zip(ws, ts)):
+        _need_cuda(w, t.codes, t.absmax, t.absmax_q, t.absmax_scale)
+        if not t.fmt.is_default:
+            raise ValueError(f"{what}: batched calls take the default storage format")
+        if w.numel() != t.numel:
+            raise ValueError(f"{what}: entry {i} has {w.numel()} elements, its NF4 tensor {t.numel}")
+        arr[i] = nf4_batch_entry(_addr(w), w.numel(), _addr(t.codes), _addr(t.absmax),
+                                 _addr(t.absmax_q), _addr(t.absmax_scale))
+    return arr, (_dtype_code(ws[0].dtype) if ws else NF4_BF16)
+
+
+class NF4Batch:
+    """A batched call prepared once: the nf4_batch_entry array pairing dense
+    tensors ws[i] with NF4 tensors ts[i] is built here (the per-entry checks
+    and marshalling cost microseconds per entry of host time) and reused by
+    every quantize() / dequantize(). Holds references to all tensors."""
+
+    def __init__(self, ws, ts):
+        self._keep = (list(ws), list(ts))
+        self.arr, self.dtype = _batch(self._keep[0], self._keep[1], "NF4Batch")
+        self.count = len(self._keep[0])
+        self.device = self._keep[1][0].codes.device if self.count else None
+
+    def quantize(self):
+        """nf4_quantize_batched: ws[i] -> ts[i]."""
+        if self.count:
+            _check(lib().nf4_quantize_batched(self.arr, self.count, self.dtype,
+                                              _stream(self.device)), "nf4_quantize_batched")
+
+    def dequantize(self):
+        """nf4_dequantize_batched: ts[i] -> ws[i]."""
+        if self.count:
+            _check(lib().nf4_dequantize_batched(self.arr, self.count, self.dtype,
+                                                _stream(self.device)), "nf4_dequantize_batched")
+
+
+def nf4_quantize_batched(ws, outs):
+    """nf4_quantize of ws[i] into outs[i] (NF4Tensor, default format) for
+    every i, in few launches. All ws share one dtype and one device."""
+    NF4Batch(ws, outs).quantize()
+
+
+def nf4_dequantize_batched(ts, outs):
+    """nf4_dequantize of ts[i] (NF4Tensor, default format) into outs[i] for
+    every i, in few launches. All outs share one dtype and one device."""
+    NF4Batch(outs, ts).dequantize()
 
 
 @dataclass(frozen=True)
@@ -444,6 +521,24 @@ def quantize(w, double_quant=True, keep_absmax=False, out: Optional[NF4Tensor] =
         nf4_quantize_ex(w.contiguous(), fmt, t.codes, t.absmax, t.absmax_q, t.absmax_scale,
                         t.absmax_offset)
     return t
+
+
+def quantize_batched(ws, double_quant=True, keep_absmax=False):
+    """quantize() of every tensor of the list ws (one dtype, one device), in
+    few launches; returns the list of NF4Tensor."""
+    outs = [empty_nf4(tuple(w.shape), w.device, double_quant, keep_absmax) for w in ws]
+    nf4_quantize_batched([w.contiguous() for w in ws], outs)
+    return outs
+
+
+def dequantize_batched(ts, out_dtype=None):
+    """dequantize() of every NF4Tensor of the list ts, in few launches."""
+    import torch
+
+    out_dtype = out_dtype or torch.bfloat16
+    outs = [torch.empty(t.shape, dtype=out_dtype, device=t.codes.device) for t in ts]
+    nf4_dequantize_batched(ts, outs)
+    return outs
 
 
 def double_quantize(absmax, fmt: NF4Format = None):

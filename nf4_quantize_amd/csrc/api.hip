@@ -262,6 +262,55 @@ NF4_API nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t block
                                            static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// One entry of a batched call: the checks of nf4_quantize / nf4_dequantize.
+nf4_status check_batch_entry(const nf4_batch_entry &e) {
+    if (e.n < 0 || e.n > kMaxElems) return NF4_ERR_SIZE;
+    if (e.n == 0) return NF4_OK;
+    const bool dq = e.absmax_q != nullptr || e.absmax_scale != nullptr;
+    if (!e.w || !e.codes) return NF4_ERR_NULL;
+    if (dq && (!e.absmax_q || !e.absmax_scale)) return NF4_ERR_NULL;
+    if (!dq && !e.absmax) return NF4_ERR_NULL;
+    if (!aligned(e.w, 16) || !aligned(e.codes, 16)) return NF4_ERR_ALIGN;
+    if ((e.absmax && !aligned(e.absmax, 4)) || (e.absmax_q && !aligned(e.absmax_q, 4)) ||
+        (e.absmax_scale && !aligned(e.absmax_scale, 4)))
+        return NF4_ERR_ALIGN;
+    return NF4_OK;
+}
+
+nf4_status check_batch(const nf4_batch_entry *entries, int32_t count, nf4_dtype dt) {
+    if (count < 0) return NF4_ERR_SIZE;
+    if (dt != NF4_F32 && dt != NF4_BF16) return NF4_ERR_UNSUPPORTED;
+    if (count > 0 && !entries) return NF4_ERR_NULL;
+    for (int32_t i = 0; i < count; ++i) {
+        const nf4_status st = check_batch_entry(entries[i]);
+        if (st != NF4_OK) return st;
+    }
+    return NF4_OK;
+}
+
+}  // namespace
+
+NF4_API nf4_status nf4_quantize_batched(const nf4_batch_entry *entries, int32_t count,
+                                        nf4_dtype w_dtype, void *stream) {
+    const nf4_status st = check_batch(entries, count, w_dtype);
+    if (st != NF4_OK) return st;
+    if (!code_lut()) return NF4_ERR_UNSUPPORTED;  // codebook table failed its checks
+    if (count == 0) return NF4_OK;
+    return launch_status(
+        launch_quantize_batched(entries, count, w_dtype, static_cast<hipStream_t>(stream)));
+}
+
+NF4_API nf4_status nf4_dequantize_batched(const nf4_batch_entry *entries, int32_t count,
+                                          nf4_dtype out_dtype, void *stream) {
+    const nf4_status st = check_batch(entries, count, out_dtype);
+    if (st != NF4_OK) return st;
+    if (count == 0) return NF4_OK;
+    return launch_status(
+        launch_dequantize_batched(entries, count, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 NF4_API size_t nf4_linear_workspace_size(int64_t m, int32_t r) {
     if (m <= 0 || r <= 0) return 0;
     return nf4::lora_workspace_bytes(m, ((int64_t)r + 63) / 64 * 64);

@@ -74,18 +74,19 @@ template <> struct Out<float> {
     __device__ static void store1(float *dst, float v) { *dst = v; }
 };
 
+// The chunks of workgroup wg of a tensor with nchunks full chunks.
 template <typename O, bool kDQ, int kCPW>
-__global__ __launch_bounds__(kThreads) void dequantize_chunks_kernel(
+__device__ __forceinline__ void dequantize_chunks(
     const uint8_t *__restrict__ codes, int64_t nchunks, const float *__restrict__ absmax,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
-    O *__restrict__ out, Levels lv) {
+    O *__restrict__ out, Levels lv, const int64_t wg) {
     __shared__ float2 s_pair[256];
     __shared__ float s_lv[16];
     const int lane = threadIdx.x & 63;
     // wave index in scalar registers: the chunk's scale data is then fetched
     // with scalar loads (32 E4M3 codes and one c2 per chunk: a chunk of 32
     // blocks never straddles a group of 256)
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+    const int64_t wave = wg * (kThreads / 64) +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     // all code loads of the wave's chunks first (a chunk past the end reloads
     // the last one and stores nothing)
@@ -133,6 +134,27 @@ __global__ __launch_bounds__(kThreads) void dequantize_chunks_kernel(
     }
 }
 
+template <typename O, bool kDQ, int kCPW>
+__global__ __launch_bounds__(kThreads) void dequantize_chunks_kernel(
+    const uint8_t *__restrict__ codes, int64_t nchunks, const float *__restrict__ absmax,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ absmax_scale,
+    O *__restrict__ out, Levels lv) {
+    dequantize_chunks<O, kDQ, kCPW>(codes, nchunks, absmax, absmax_q, absmax_scale, out, lv,
+                                    (int64_t)blockIdx.x);
+}
+
+// Weight i of a tensor, one weight per thread (s_pair built).
+template <typename O>
+__device__ __forceinline__ void dequantize_one(const uint8_t *__restrict__ codes, int64_t i,
+                                               const float *__restrict__ absmax,
+                                               const uint8_t *__restrict__ absmax_q,
+                                               const float *__restrict__ absmax_scale,
+                                               O *__restrict__ out, const float2 *s_pair) {
+    const uint32_t code = (codes[i >> 1] >> (4 * (i & 1))) & 15u;
+    const float c1 = block_scale(i / kBlock, absmax, absmax_q, absmax_scale);
+    Out<O>::store1(out + i, s_pair[code].x * c1);
+}
+
 // Remaining weights after the last full chunk: one weight per thread.
 template <typename O>
 __global__ __launch_bounds__(kThreads) void dequantize_tail_kernel(
@@ -144,9 +166,123 @@ __global__ __launch_bounds__(kThreads) void dequantize_tail_kernel(
     build_pair_table(lv, s_lv, s_pair);
     const int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
-    const uint32_t code = (codes[i >> 1] >> (4 * (i & 1))) & 15u;
-    const float c1 = block_scale(i / kBlock, absmax, absmax_q, absmax_scale);
-    Out<O>::store1(out + i, s_pair[code].x * c1);
+    dequantize_one<O>(codes, i, absmax, absmax_q, absmax_scale, out, s_pair);
+}
+
+// ---- batched dequantization: the tensors of a model in few launches ----
+
+// Entries per launch: their pointers travel in the kernel-argument block.
+constexpr int kBatch = 32;
+constexpr int kGroupWgs = kGroup / (kChunk * 2 * (kThreads / 64));  // workgroups per group
+static_assert(kGroupWgs == 1, "a chunk workgroup covers one DQ group");
+
+// Up to kBatch tensors of one launch. In the chunk launch, workgroup i works
+// on entry k, the last with first[k] <= i, at local index i - first[k];
+// entries past the batch hold first = UINT32_MAX. In the tail launch,
+// workgroup k takes the weights of entry k from index n / 16384 * 16384 on.
+struct DequantBatch {
+    const uint8_t *codes[kBatch];
+    const float *absmax[kBatch];
+    const uint8_t *q[kBatch];
+    const float *sc[kBatch];
+    void *out[kBatch];
+    int64_t n[kBatch];
+    uint32_t first[kBatch];
+};
+
+template <typename O, bool kDQ>
+__global__ __launch_bounds__(kThreads) void dequantize_batch_kernel(DequantBatch b, Levels lv) {
+    const uint32_t wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int j = 1; j < kBatch; ++j) k = (wg >= b.first[j]) ? j : k;
+    // every chunk of a full group exists, so nchunks only bounds the loads
+    dequantize_chunks<O, kDQ, 2>(b.codes[k], (b.n[k] / kGroup) * (kGroup / kChunk), b.absmax[k],
+                                 b.q[k], b.sc[k], static_cast<O *>(b.out[k]), lv,
+                                 (int64_t)(wg - b.first[k]));
+}
+
+template <typename O>
+__global__ __launch_bounds__(kThreads) void dequantize_batch_tail_kernel(DequantBatch b, Levels lv) {
+    __shared__ float2 s_pair[256];
+    __shared__ float s_lv[16];
+    build_pair_table(lv, s_lv, s_pair);
+    const int k = blockIdx.x;
+    const int64_t n = b.n[k];
+    O *out = static_cast<O *>(b.out[k]);
+    for (int64_t i = n / kGroup * kGroup + threadIdx.x; i < n; i += kThreads)
+        dequantize_one<O>(b.codes[k], i, b.absmax[k], b.q[k], b.sc[k], out, s_pair);
+}
+
+template <typename O>
+struct DequantBatchLauncher {
+    DequantBatch b;
+    int count = 0;
+    uint32_t wgs = 0;
+    bool tail, dq;
+    const Levels &lv;
+    hipStream_t s;
+    hipError_t err = hipSuccess;
+
+    DequantBatchLauncher(bool tail_, bool dq_, const Levels &l, hipStream_t st)
+        : tail(tail_), dq(dq_), lv(l), s(st) {}
+
+    void flush() {
+        if (count == 0) return;
+        for (int j = count; j < kBatch; ++j) {
+            b.codes[j] = nullptr;
+            b.absmax[j] = nullptr;
+            b.q[j] = nullptr;
+            b.sc[j] = nullptr;
+            b.out[j] = nullptr;
+            b.n[j] = 0;
+            b.first[j] = UINT32_MAX;
+        }
+        if (tail)
+            dequantize_batch_tail_kernel<O><<<dim3((unsigned)count), dim3(kThreads), 0, s>>>(b, lv);
+        else if (dq)
+            dequantize_batch_kernel<O, true><<<dim3(wgs), dim3(kThreads), 0, s>>>(b, lv);
+        else
+            dequantize_batch_kernel<O, false><<<dim3(wgs), dim3(kThreads), 0, s>>>(b, lv);
+        const hipError_t e = hipGetLastError();
+        if (err == hipSuccess) err = e;
+        count = 0;
+        wgs = 0;
+    }
+
+    void add(const nf4_batch_entry &e, int64_t units) {
+        constexpr int64_t kMaxWgs = (int64_t(1) << 31) / kThreads;  // below 2^31 threads
+        if (count == kBatch || (!tail && (int64_t)wgs + units > kMaxWgs)) flush();
+        b.codes[count] = e.codes;
+        b.absmax[count] = dq ? nullptr : e.absmax;
+        b.q[count] = dq ? e.absmax_q : nullptr;
+        b.sc[count] = dq ? e.absmax_scale : nullptr;
+        b.out[count] = e.w;
+        b.n[count] = e.n;
+        b.first[count] = tail ? 0u : wgs;
+        wgs += tail ? 1u : (uint32_t)units;
+        ++count;
+    }
+};
+
+template <typename O>
+hipError_t launch_dequantize_batched_t(const nf4_batch_entry *e, int32_t count, hipStream_t s) {
+    Levels lv;
+    for (int i = 0; i < 16; ++i) lv.q[i] = kLevels[i];
+    hipError_t err = hipSuccess;
+    for (int dq = 1; dq >= 0; --dq) {
+        DequantBatchLauncher<O> full(false, dq != 0, lv, s), tail(true, dq != 0, lv, s);
+        for (int32_t i = 0; i < count; ++i) {
+            if ((e[i].absmax_q != nullptr) != (dq != 0) || e[i].n <= 0) continue;
+            const int64_t groups = e[i].n / kGroup;
+            if (groups > 0) full.add(e[i], groups * kGroupWgs);
+            if (e[i].n % kGroup) tail.add(e[i], 1);
+        }
+        full.flush();
+        tail.flush();
+        if (err == hipSuccess) err = full.err != hipSuccess ? full.err : tail.err;
+    }
+    return err;
 }
 
 template <typename O>
@@ -320,6 +456,11 @@ hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absma
                            kLevels, s);
 }
 
+hipError_t launch_dequantize_batched(const nf4_batch_entry *e, int32_t count, nf4_dtype dt,
+                                     hipStream_t s) {
+    if (dt == NF4_BF16) return launch_dequantize_batched_t<uint16_t>(e, count, s);
+    return launch_dequantize_batched_t<float>(e, count, s);
+}
 
 hipError_t launch_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format &f,
                                 const float *absmax, const uint8_t *absmax_q,

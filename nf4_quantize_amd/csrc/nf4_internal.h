@@ -76,6 +76,12 @@ hipError_t launch_dequantize(const uint8_t *codes, int64_t n, const float *absma
                              nf4_dtype dt, hipStream_t s);
 // Storage-format variants: block size B1, DQ block B2, the 8-bit code format
 // of double quantization and the tensor-wide mean offset (nf4_format).
+// Batched storage path (B1 = 64, B2 = 256, E4M3): the entries' full groups
+// in launches of up to 32 entries, their partial groups in one more.
+hipError_t launch_quantize_batched(const nf4_batch_entry *e, int32_t count, nf4_dtype dt,
+                                   hipStream_t s);
+hipError_t launch_dequantize_batched(const nf4_batch_entry *e, int32_t count, nf4_dtype dt,
+                                     hipStream_t s);
 hipError_t launch_quantize_ex(const void *w, nf4_dtype dt, int64_t n, const nf4_format &f,
                               uint8_t *codes, float *absmax, uint8_t *absmax_q,
                               float *absmax_scale, float *absmax_offset, void *workspace,

@@ -254,14 +254,14 @@ __device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32
     if (t == 0) absmax_scale[g] = sc;
 }
 
-// One workgroup of TH threads per full group of 16384 weights. Without fused
+// Full group g of a tensor, by a workgroup of TH threads. Without fused
 // double quantization, `partial` (if set) receives the pairwise sum of the
 // group's 256 block scales (the first levels of the mean offset's sum).
 template <typename T, bool kDQ, int TH, int F>
-__global__ __launch_bounds__(TH) void quantize_groups_kernel(
+__device__ __forceinline__ void quantize_group(
     const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
     uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
-    CodeLut lut) {
+    const CodeLut &lut, const int64_t g) {
     using S = Slice<T>;
     constexpr int E = S::kElems;               // weights per lane slice
     constexpr int LPB = kBlock / E;            // lanes per block
@@ -277,7 +277,6 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     __shared__ uint32_t s_q8[kDqBlock / 4];
 
     const int t = threadIdx.x;
-    const int64_t g = blockIdx.x;
     const typename S::Vec *src = reinterpret_cast<const typename S::Vec *>(w + g * kGroup);
 
     // The table comes from the argument block through a vector load: issued
@@ -327,13 +326,23 @@ __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     }
 }
 
-// The final partial group: thread t owns block t of the group and works
-// element by element with guarded accesses.
+// One workgroup per full group of 16384 weights.
+template <typename T, bool kDQ, int TH, int F>
+__global__ __launch_bounds__(TH) void quantize_groups_kernel(
+    const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
+    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
+    CodeLut lut) {
+    quantize_group<T, kDQ, TH, F>(w, codes, absmax, absmax_q, absmax_scale, partial, lut,
+                                  (int64_t)blockIdx.x);
+}
+
+// The final partial group g of an n-element tensor: thread t owns block t of
+// the group and works element by element with guarded accesses.
 template <typename T, int F>
-__global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
+__device__ __forceinline__ void quantize_tail(
     const T *__restrict__ w, int64_t n, int64_t g, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale,
-    float *__restrict__ partial, CodeLut lut) {
+    float *__restrict__ partial, const CodeLut &lut) {
     __shared__ float2 s_lut[kLutEntries];
     __shared__ float s_c1[kDqBlock];
     __shared__ float s_red[4];
@@ -370,6 +379,14 @@ __global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
         const float sum = block256_pairwise_sum(s_c1, s_red);  // blocks past n hold 0
         if (t == 0) partial[g] = sum;
     }
+}
+
+template <typename T, int F>
+__global__ __launch_bounds__(kThreads) void quantize_tail_kernel(
+    const T *__restrict__ w, int64_t n, int64_t g, uint8_t *__restrict__ codes,
+    float *__restrict__ absmax, uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale,
+    float *__restrict__ partial, CodeLut lut) {
+    quantize_tail<T, F>(w, n, g, codes, absmax, absmax_q, absmax_scale, partial, lut);
 }
 
 // Standalone double quantization: one workgroup per group of 256 c1 values.
@@ -423,6 +440,125 @@ hipError_t launch_quantize_fmt(const T *w, int64_t n, uint8_t *codes, float *abs
     if (fmt == kFmtLin8)
         return launch_quantize_t<T, kFmtLin8>(w, n, codes, absmax, absmax_q, absmax_scale, lut, s);
     return launch_quantize_t<T, kFmtE4M3>(w, n, codes, absmax, absmax_q, absmax_scale, lut, s);
+}
+
+// ---- batched quantization: the tensors of a model in few launches ----
+
+// Entries per launch: their pointers travel in the kernel-argument block.
+constexpr int kBatch = 32;
+
+// Up to kBatch tensors of one launch. Workgroup i works on entry k, the last
+// with first[k] <= i, at local index i - first[k]; entries past the batch
+// hold first = UINT32_MAX. For the tail launch, entry k is workgroup k and
+// first[k] is the index of the entry's partial group.
+struct QuantBatch {
+    const void *w[kBatch];
+    uint8_t *codes[kBatch];
+    float *absmax[kBatch];
+    uint8_t *q[kBatch];
+    float *sc[kBatch];
+    int64_t n[kBatch];
+    uint32_t first[kBatch];
+};
+
+__device__ __forceinline__ int batch_entry(const QuantBatch &b, uint32_t wg) {
+    int k = 0;
+#pragma unroll
+    for (int j = 1; j < kBatch; ++j) k = (wg >= b.first[j]) ? j : k;
+    return k;
+}
+
+// Full groups of every entry: one workgroup per group, as the group kernel.
+template <typename T, bool kDQ>
+__global__ __launch_bounds__(kGroupThreads) void quantize_batch_kernel(QuantBatch b, CodeLut lut) {
+    const uint32_t wg = blockIdx.x;
+    const int k = batch_entry(b, wg);
+    quantize_group<T, kDQ, kGroupThreads, kFmtE4M3>(static_cast<const T *>(b.w[k]), b.codes[k],
+                                                    b.absmax[k], b.q[k], b.sc[k], nullptr, lut,
+                                                    (int64_t)(wg - b.first[k]));
+}
+
+// The partial last group of each entry: workgroup k takes entry k's.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_batch_tail_kernel(QuantBatch b, CodeLut lut) {
+    const int k = blockIdx.x;
+    quantize_tail<T, kFmtE4M3>(static_cast<const T *>(b.w[k]), b.n[k], (int64_t)b.first[k],
+                               b.codes[k], b.absmax[k], b.q[k], b.sc[k], nullptr, lut);
+}
+
+// Collects entries into QuantBatch blocks and launches each when full.
+// `tail` selects what a launch covers: the full groups of its entries, or
+// their partial last groups.
+template <typename T>
+struct BatchLauncher {
+    QuantBatch b;
+    int count = 0;
+    uint32_t wgs = 0;
+    bool tail, dq;
+    const CodeLut &lut;
+    hipStream_t s;
+    hipError_t err = hipSuccess;
+
+    BatchLauncher(bool tail_, bool dq_, const CodeLut &l, hipStream_t st)
+        : tail(tail_), dq(dq_), lut(l), s(st) {}
+
+    void flush() {
+        if (count == 0) return;
+        for (int j = count; j < kBatch; ++j) {
+            b.w[j] = nullptr;
+            b.codes[j] = nullptr;
+            b.absmax[j] = nullptr;
+            b.q[j] = nullptr;
+            b.sc[j] = nullptr;
+            b.n[j] = 0;
+            b.first[j] = UINT32_MAX;
+        }
+        if (tail)
+            quantize_batch_tail_kernel<T><<<dim3((unsigned)count), dim3(kThreads), 0, s>>>(b, lut);
+        else if (dq)
+            quantize_batch_kernel<T, true><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
+        else
+            quantize_batch_kernel<T, false><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
+        const hipError_t e = hipGetLastError();
+        if (err == hipSuccess) err = e;
+        count = 0;
+        wgs = 0;
+    }
+
+    // Adds entry e: `units` workgroups (full groups), or its partial group.
+    void add(const nf4_batch_entry &e, int64_t units) {
+        // a full-group launch stays below 2^31 threads
+        constexpr int64_t kMaxWgs = (int64_t(1) << 31) / kGroupThreads;
+        if (count == kBatch || (!tail && (int64_t)wgs + units > kMaxWgs)) flush();
+        b.w[count] = e.w;
+        b.codes[count] = e.codes;
+        b.absmax[count] = e.absmax;
+        b.q[count] = dq ? e.absmax_q : nullptr;
+        b.sc[count] = dq ? e.absmax_scale : nullptr;
+        b.n[count] = e.n;
+        b.first[count] = tail ? (uint32_t)(e.n / kGroup) : wgs;
+        wgs += tail ? 1u : (uint32_t)units;
+        ++count;
+    }
+};
+
+template <typename T>
+hipError_t launch_quantize_batched_t(const nf4_batch_entry *e, int32_t count, const CodeLut &lut,
+                                     hipStream_t s) {
+    hipError_t err = hipSuccess;
+    for (int dq = 1; dq >= 0; --dq) {
+        BatchLauncher<T> full(false, dq != 0, lut, s), tail(true, dq != 0, lut, s);
+        for (int32_t i = 0; i < count; ++i) {
+            if ((e[i].absmax_q != nullptr) != (dq != 0) || e[i].n <= 0) continue;
+            const int64_t groups = e[i].n / kGroup;
+            if (groups > 0) full.add(e[i], groups);
+            if (e[i].n % kGroup) tail.add(e[i], 1);
+        }
+        full.flush();
+        tail.flush();
+        if (err == hipSuccess) err = full.err != hipSuccess ? full.err : tail.err;
+    }
+    return err;
 }
 
 // ---- storage-format variants: block sizes other than 64, the mean offset ----
@@ -902,6 +1038,12 @@ hipError_t launch_quantize(const void *w, nf4_dtype dt, int64_t n, uint8_t *code
                                                      absmax, absmax_q, absmax_scale, *code_lut(), s);
     return launch_quantize_t<float, kFmtE4M3>(static_cast<const float *>(w), n, codes, absmax,
                                               absmax_q, absmax_scale, *code_lut(), s);
+}
+
+hipError_t launch_quantize_batched(const nf4_batch_entry *e, int32_t count, nf4_dtype dt,
+                                   hipStream_t s) {
+    if (dt == NF4_BF16) return launch_quantize_batched_t<uint16_t>(e, count, *code_lut(), s);
+    return launch_quantize_batched_t<float>(e, count, *code_lut(), s);
 }
 
 hipError_t launch_double_quantize(const float *absmax, int64_t nblocks, uint8_t *absmax_q,

@@ -312,3 +312,48 @@ def test_storage_bytes_ex_matches_oracle(L, oracle_mod):
                 assert got == oracle_mod.storage_bytes_ex(n, bs, dqb, bool(dq), bool(off))
     assert L.nf4_storage_bytes_ex(64, _fmt(bs=48), 1) == -1
     assert L.nf4_storage_bytes_ex(-1, _fmt(), 1) == -1
+
+
+def _entry(w=FAKE, n=16384, codes=FAKE, am=None, aq=FAKE, asc=FAKE):
+    return nq.nf4_batch_entry(w, n, codes, am, aq, asc)
+
+
+def test_batched_validation(L):
+    """Every entry is checked before anything is launched: a valid call is
+    never made here (it would launch), so each case holds one bad entry, or
+    launches nothing at all."""
+    def call(fn, entries, count=None, dt=1):
+        arr = (nq.nf4_batch_entry * max(1, len(entries)))(*entries)
+        return fn(arr, len(entries) if count is None else count, dt, None)
+
+    for fn in (L.nf4_quantize_batched, L.nf4_dequantize_batched):
+        good = _entry()
+        assert fn(None, 0, 1, None) == 0                         # nothing to do
+        assert call(fn, [_entry(n=0, w=None, codes=None)]) == 0  # only empty entries
+        assert call(fn, [_entry(n=0)] * 3) == 0
+        assert fn(None, 2, 1, None) == 1                         # NULL array, count > 0
+        assert call(fn, [good], count=-1) == 2
+        assert call(fn, [good], dt=7) == 3
+        # the bad entry is last: the good ones before it launch nothing either
+        assert call(fn, [good, good, _entry(n=-1)]) == 2
+        assert call(fn, [good, _entry(n=(1 << 37) + 1)]) == 2
+        assert call(fn, [good, _entry(w=None)]) == 1
+        assert call(fn, [good, _entry(codes=None)]) == 1
+        assert call(fn, [good, _entry(aq=None)]) == 1            # one of the pair
+        assert call(fn, [good, _entry(asc=None)]) == 1
+        assert call(fn, [good, _entry(aq=None, asc=None)]) == 1  # no DQ and no absmax
+        assert call(fn, [good, _entry(w=FAKE + 8)]) == 4
+        assert call(fn, [good, _entry(codes=FAKE + 4)]) == 4
+        assert call(fn, [good, _entry(aq=FAKE + 2)]) == 4
+        assert call(fn, [good, _entry(asc=FAKE + 1)]) == 4
+        assert call(fn, [good, _entry(aq=None, asc=None, am=FAKE + 2)]) == 4
+
+
+def test_batched_binding_checks():
+    """The Python side refuses mismatched lists before calling the library."""
+    import torch
+
+    with pytest.raises(ValueError):
+        nq._batch([torch.zeros(4)], [], "x")
+    with pytest.raises(ValueError):
+        nq._batch([torch.zeros(4), torch.zeros(4, dtype=torch.bfloat16)], [None, None], "x")
