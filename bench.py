@@ -600,6 +600,8 @@ def main():
     kernels = {}
     if not args.no_kernels:
         kernels = kernel_benches(dev, iters=20, warmup=5, with_stack=args.stack)
+    elif args.stack:
+        kernels = stack_bench(dev)
 
     q_bytes = main_res["quantize_bytes"]
     q_ms = main_res["quantize_ms"]
