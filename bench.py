@@ -107,6 +107,36 @@ def prep_dequantize(p, n, out):
                     _stream())
 
 
+def stream_ceilings(dev, groups, iters):
+    """The measured HBM ceiling of the storage path: bench_stream.so's plain
+    streaming kernels with quantize's traffic (reads 32 KiB, writes 8 KiB per
+    16384-weight group) and dequantize's (the reverse), over 4 rotating sets,
+    timed like the kernels they bound."""
+    import ctypes
+    import torch
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bench_stream.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build()")
+    so = ctypes.CDLL(path)
+    so.bench_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_void_p]
+    so.bench_stream.restype = ctypes.c_int
+    big, small = groups * 32768, groups * 8192
+    res = {}
+    for kind, name, rb, wb in ((0, "read4_write1", big, small), (1, "read1_write4", small, big)):
+        srcs = [torch.full((rb,), 1 + i, dtype=torch.uint8, device=dev) for i in range(4)]
+        dsts = [torch.empty(wb, dtype=torch.uint8, device=dev) for _ in range(4)]
+        calls = [Prepared(so.bench_stream, kind, _p(a), _p(b), groups, _stream())
+                 for a, b in zip(srcs, dsts)]
+        ms, pc = time_op(lambda i: calls[i % 4](), iters, 2)
+        res[name] = {"ms": ms, "p10_p50_p90_ms": pc, "bytes": rb + wb,
+                     "GB/s": (rb + wb) / ms / 1e6}
+        del srcs, dsts, calls
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_ahead():
     """Queues a GPU spin so the host can enqueue a whole timed batch before
     the GPU reaches it (used for per-kernel timings outside the step loop)."""
@@ -225,6 +255,9 @@ def main_step_bench(args, dev):
     # each kernel of the step alone, timed the same way as every kernel bench
     q_avg, q_pct = time_op(lambda i: qcalls[i % 4](), args.steps, 2)
     d_avg, d_pct = time_op(lambda i: dcalls[i % 4](), args.steps, 2)
+    del sets, qcalls, dcalls
+    torch.cuda.empty_cache()
+    ceil = stream_ceilings(dev, n // 16384, args.steps)
     qb = bytes_quantize(n, 2)
     db = bytes_dequantize(n, 2)
     step_bytes = qb + db
@@ -243,9 +276,8 @@ def main_step_bench(args, dev):
         "dequantize_bytes": db,
         "quantize_p10_p50_p90_ms": q_pct,
         "dequantize_p10_p50_p90_ms": d_pct,
+        "stream_ceiling": ceil,
     }
-    del sets
-    torch.cuda.empty_cache()
     return res, w_bits
 
 
@@ -618,6 +650,13 @@ def main():
         "avg_launch_ms": round(q_ms, 5),
         "timing": "mean of K back-to-back launches over 4 rotating inputs between two HIP "
                   "events on the launch stream",
+        # the practical ceiling: a plain streaming kernel with the same traffic
+        # (bench_stream.so stream_r4w1), timed the same way in this run
+        "measured_ceiling": {
+            "kernel": "stream_r4w1 (reads 32 KiB, writes 8 KiB per 16384-weight group)",
+            "GB/s": round(main_res["stream_ceiling"]["read4_write1"]["GB/s"], 1),
+            "frac": round(achieved / main_res["stream_ceiling"]["read4_write1"]["GB/s"], 4),
+        },
     }
     cpu = None if args.no_cpu_baseline else cpu_baseline(w_bits)
 
@@ -652,7 +691,12 @@ def main():
                            "GB/s": round(main_res["dequantize_gbs"], 1),
                            "hbm_frac": round(main_res["dequantize_gbs"] / HBM_PEAK_GBS, 4),
                            "p10_p50_p90_ms": main_res["dequantize_p10_p50_p90_ms"],
-                           "traffic": counter_traffic("dequantize_chunks_kernel<bf16,DQ> 11008x4096")},
+                           "traffic": counter_traffic("dequantize_chunks_kernel<bf16,DQ> 11008x4096"),
+                           "ceiling_frac": round(main_res["dequantize_gbs"] /
+                                                 main_res["stream_ceiling"]["read1_write4"]["GB/s"], 4)},
+            "stream_ceiling": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["GB/s"], 1),
+                                   "bytes": v["bytes"], "p10_p50_p90_ms": v["p10_p50_p90_ms"]}
+                               for k, v in main_res["stream_ceiling"].items()},
         },
         "kernels": kernels,
     }

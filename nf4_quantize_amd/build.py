@@ -67,5 +67,17 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_single(src: str, out: str, verbose: bool = False) -> str:
+    """One HIP source to its own shared library, with the library's flags."""
+    obj = _compile(src, verbose)
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
