@@ -107,13 +107,8 @@ def prep_dequantize(p, n, out):
                     _stream())
 
 
-def stream_ceilings(dev, groups, iters):
-    """The measured HBM ceiling of the storage path: bench_stream.so's plain
-    streaming kernels with quantize's traffic (reads 32 KiB, writes 8 KiB per
-    16384-weight group) and dequantize's (the reverse), over 4 rotating sets,
-    timed like the kernels they bound."""
+def _stream_lib():
     import ctypes
-    import torch
 
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bench_stream.so")
     if not os.path.exists(path):
@@ -122,11 +117,25 @@ def stream_ceilings(dev, groups, iters):
     so.bench_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                 ctypes.c_void_p]
     so.bench_stream.restype = ctypes.c_int
+    return so
+
+
+def stream_ceilings(dev, groups, iters, kinds=("read4_write1", "read1_write4")):
+    """Measured HBM ceilings: bench_stream.so's plain streaming kernels over
+    `groups` 16384-weight groups, 4 rotating sets, timed like the kernels they
+    bound. read4_write1 has quantize's traffic (reads 32 KiB, writes 8 KiB per
+    group), read1_write4 dequantize's, read_only reads 32 KiB per group."""
+    import torch
+
+    so = _stream_lib()
     big, small = groups * 32768, groups * 8192
+    spec = {"read4_write1": (0, big, small), "read1_write4": (1, small, big),
+            "read_only": (2, big, 0)}
     res = {}
-    for kind, name, rb, wb in ((0, "read4_write1", big, small), (1, "read1_write4", small, big)):
+    for name in kinds:
+        kind, rb, wb = spec[name]
         srcs = [torch.full((rb,), 1 + i, dtype=torch.uint8, device=dev) for i in range(4)]
-        dsts = [torch.empty(wb, dtype=torch.uint8, device=dev) for _ in range(4)]
+        dsts = [torch.empty(max(wb, groups * 16), dtype=torch.uint8, device=dev) for _ in range(4)]
         calls = [Prepared(so.bench_stream, kind, _p(a), _p(b), groups, _stream())
                  for a, b in zip(srcs, dsts)]
         ms, pc = time_op(lambda i: calls[i % 4](), iters, 2)
@@ -380,6 +389,13 @@ def kernel_benches(dev, iters, warmup, with_stack):
         log(f"gemv M={m}: {out[f'gemv_M{m}_28672x8192']}")
     del wts, x
     torch.cuda.empty_cache()
+    # the practical ceiling: a plain read-only stream of the weight's bytes
+    rd = stream_ceilings(dev, (wbytes + 32767) // 32768, iters, ("read_only",))["read_only"]
+    out["stream_read_only_28672x8192_weight"] = rd
+    for m in workloads.GEMV_MS:
+        e = out[f"gemv_M{m}_28672x8192"]
+        e["ceiling_frac"] = e["GB/s"] / rd["GB/s"]
+    log(f"read-only stream of the GEMV weight bytes: {rd}")
 
     # workload 5: QLoRA linear 4096 x 8192 x 8192, r = 64
     M, N, K, r, s = (workloads.LIN_M, workloads.LIN_N, workloads.LIN_K, workloads.LIN_R,

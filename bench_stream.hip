@@ -13,6 +13,10 @@
 //     256 threads; thread t reads two 16-byte vectors (t, t+256) and writes
 //     four 16-byte vectors per read (v, v^1, v^2, v^3), every wave
 //     instruction one contiguous 1 KiB run, stores non-temporal.
+//   stream_r1w0 (the decode GEMV's weight stream): reads 32 KiB per group as
+//     stream_r4w1 does and writes nothing unless the XOR of a thread's four
+//     vectors equals `key` (the caller passes a key the data never forms, so
+//     the loads stay and no store happens).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,10 +51,24 @@ __global__ __launch_bounds__(256) void stream_r1w4(const u32x4 *__restrict__ src
     }
 }
 
+__global__ __launch_bounds__(512) void stream_r1w0(const u32x4 *__restrict__ src,
+                                                   u32x4 *__restrict__ dst, uint32_t key) {
+    const int t = threadIdx.x;
+    const u32x4 *s = src + (int64_t)blockIdx.x * 2048;
+    const u32x4 a = __builtin_nontemporal_load(s + t);
+    const u32x4 b = __builtin_nontemporal_load(s + 512 + t);
+    const u32x4 c = __builtin_nontemporal_load(s + 1024 + t);
+    const u32x4 d = __builtin_nontemporal_load(s + 1536 + t);
+    const u32x4 x = a ^ b ^ c ^ d;
+    if ((x.x | x.y | x.z | x.w) == key) dst[blockIdx.x] = x;
+}
+
 }  // namespace
 
 // kind 0: stream_r4w1, src >= groups * 32 KiB, dst >= groups * 8 KiB.
 // kind 1: stream_r1w4, src >= groups * 8 KiB, dst >= groups * 32 KiB.
+// kind 2: stream_r1w0, src >= groups * 32 KiB, dst >= groups * 16 B (key
+//         0xFFFFFFFF: the caller fills src so that no thread's XOR has all bits set).
 // Device buffers, 16-byte aligned; 0 < groups < 2^22. Returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int bench_stream(int kind, const void *src,
                                                                    void *dst, int64_t groups,
@@ -65,6 +83,9 @@ extern "C" __attribute__((visibility("default"))) int bench_stream(int kind, con
     else if (kind == 1)
         stream_r1w4<<<dim3((unsigned)groups), dim3(256), 0, s>>>(
             static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst));
+    else if (kind == 2)
+        stream_r1w0<<<dim3((unsigned)groups), dim3(512), 0, s>>>(
+            static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), 0xFFFFFFFFu);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
