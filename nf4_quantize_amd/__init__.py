@@ -120,6 +120,12 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise NF4LibraryMissing(
             f"{LIB_PATH} is not built; run `python -m nf4_quantize_amd.build` (hipcc, gfx950)")
+    # torch ships its own HIP runtime under the same soname as ROCm's. Loading
+    # torch first makes libnf4.so bind to that copy; loaded the other way
+    # round, a process would hold two HIP runtimes, and torch's device
+    # pointers would be foreign to the library's launches.
+    import torch  # noqa: F401
+
     L = ctypes.CDLL(LIB_PATH)
     p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     L.nf4_status_string.argtypes = [ctypes.c_int]

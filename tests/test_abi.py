@@ -357,3 +357,18 @@ def test_batched_binding_checks():
         nq._batch([torch.zeros(4)], [], "x")
     with pytest.raises(ValueError):
         nq._batch([torch.zeros(4), torch.zeros(4, dtype=torch.bfloat16)], [None, None], "x")
+
+
+def test_one_hip_runtime_after_lib():
+    """nq.lib() loads torch first, so libnf4.so binds to torch's HIP runtime and
+    a process holds one copy (checked in a fresh interpreter, on the CPU)."""
+    import subprocess
+    import sys
+
+    code = ("import os, nf4_quantize_amd as nq; nq.lib(); import torch; "
+            "m = open(f'/proc/{os.getpid()}/maps').read(); "
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
