@@ -462,6 +462,11 @@ def kernel_benches(dev, iters, warmup, with_stack):
     ms, pc = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))
     out["hipblaslt_bf16_4096x8192x8192_reference"] = {"ms": ms, "p10_p50_p90_ms": pc,
                                                       "TFLOP/s": 2 * M * N * K / ms / 1e9}
+    # the fused kernels' rate as a fraction of the vendor GEMM's (the measured
+    # MFMA ceiling on this shape; each counts its own flops)
+    for name in ("linear_fwd_4096x8192x8192_r64", "linear_dgrad_4096x8192x8192_r64"):
+        out[name]["hipblaslt_frac"] = (out[name]["TFLOP/s"] /
+                                       out["hipblaslt_bf16_4096x8192x8192_reference"]["TFLOP/s"])
     del X, dY, A, B, Y, dX, ws, Wd, wt
     torch.cuda.empty_cache()
 
