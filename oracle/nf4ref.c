@@ -525,13 +525,15 @@ int nf4ref_codebook_levels(int codebook, float q[16]) {
     if (codebook == NF4REF_CB_NF4) {
         for (int i = 0; i < 16; ++i) q[i] = NF4_Q[i];
     } else if (codebook == NF4REF_CB_FP4) {
-        static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-        for (int i = 1; i < 8; ++i) {
-            q[7 + i] = mag[i] / 6.0f;     /* 1/12 .. 1 */
-            q[7 - i] = -(mag[i] / 6.0f);  /* -1/12 .. -1 */
+        /* OCP E2M1 encoding: bit 3 is the sign, bits 2..1 the exponent (bias
+         * 1), bit 0 the mantissa; exponent 0 is subnormal (0 or 0.5). The
+         * code's value divided by 6 puts the largest magnitude at 1. */
+        for (int c = 0; c < 16; ++c) {
+            const int e = (c >> 1) & 3, m = c & 1;
+            const float mag = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+            const float v = mag / 6.0f;
+            q[c] = (c & 8) ? -v : v;  /* code 8 is -0 */
         }
-        q[7] = 0.0f;
-        q[15] = -0.0f;                    /* the second zero of the format */
     } else if (codebook == NF4REF_CB_INT4) {
         for (int k = 0; k < 16; ++k) q[k] = (float)(2 * k - 15) / 15.0f;
     } else {

@@ -211,11 +211,12 @@ int nf4ref_merged_weight(const uint8_t *codes, const float *absmax, const uint8_
  * naive uniform 4-bit quantizer). The same blockwise scheme with
  * another set of 16 levels in [-1, 1]:
  *   NF4REF_CB_NF4   the printed NF4 list
- *   NF4REF_CB_FP4   the OCP FP4 (E2M1) values {0, .5, 1, 1.5, 2, 3, 4, 6} with
- *                   both signs, divided by 6 (fl32(v / 6)): the 15 distinct
- *                   values ascending at indices 0..14 (0 at 7), and -0 at 15
- *                   (equal to level 7, so the tie rule never picks it).
- *                   PARITY UNPINNED: the pages name FP4 without defining it.
+ *   NF4REF_CB_FP4   OCP FP4 (E2M1) in its own encoding, each value divided by
+ *                   6 (fl32(v / 6)): code = 8 * sign + the index of the
+ *                   magnitude in {0, .5, 1, 1.5, 2, 3, 4, 6}, so +0 is code 0
+ *                   and -0 code 8 (equal to code 0, so the tie rule never
+ *                   picks it). The pages name FP4 without defining it; the
+ *                   OCP Microscaling Formats specification fixes the encoding.
  *   NF4REF_CB_INT4  16 evenly spaced levels fl32((2k - 15) / 15), k = 0..15:
  *                   the dequantized values (k' + 1/2) / 7.5, k' = -8..7, of the
  *                   uniform toy

@@ -8,13 +8,16 @@ Pins: the Int4 codebook reproduces the uniform quantizer of that comparison
 (one block = its per-tensor absmax), exhaustive nearest-level search in
 numpy for every codebook, and the pages' claim itself on Gaussian weights:
 NF4's mean squared error is below FP4's and Int4's.
-The FP4 level set (OCP E2M1 / 6) is a reading: the pages name FP4 without
-defining it (parity unpinned for the format, the ordering claim still
-applies).
+The FP4 codebook is OCP E2M1 in its own encoding with every value divided
+by 6 (the pages name FP4 without defining it): pinned code by code to the
+E2M1 table of the OCP Microscaling Formats specification
+(tests/golden/fp4_e2m1.txt), and its nearest-code function to the
+sign-magnitude form that encoding implies.
 """
 import numpy as np
 import pytest
 
+from conftest import read_golden_column
 from workloads import to_bf16_bits
 
 
@@ -46,12 +49,12 @@ def test_int4_is_the_uniform_quantizer_of_the_comparison(oracle_mod):
 def test_codebook_brute_force(oracle_mod, cb):
     rng = np.random.Generator(np.random.PCG64(len(cb)))
     lv = oracle_mod.codebook_levels(cb)
-    used = lv[:15] if cb == "fp4" else lv  # FP4's index 15 is its -0, equal to level 7
-    assert np.all(np.diff(used) > 0) and used[0] == -1 and used[-1] == 1
     if cb == "fp4":
-        assert lv[15] == 0 and np.signbit(lv[15]) and lv[7] == 0 and not np.signbit(lv[7])
-        assert np.array_equal(np.sort(np.abs(lv[:15] * 6).astype(np.float64))[::2],
-                              [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+        # OCP order: +0 .. +1 at codes 0..7, -0 .. -1 at codes 8..15
+        assert np.all(np.diff(lv[:8]) > 0) and np.all(np.diff(lv[8:]) < 0)
+        assert lv[7] == 1 and lv[15] == -1
+    else:
+        assert np.all(np.diff(lv) > 0) and lv[0] == -1 and lv[-1] == 1
     n = 64 * 40 + 9
     w = rng.standard_normal(n, dtype=np.float32)
     w[:64] = 0.0
@@ -89,3 +92,42 @@ def test_nf4_beats_fp4_and_int4_on_gaussian_weights(oracle_mod, bs):
         deq = oracle_mod.dequantize_cb(codes, w.size, blocksize=bs, codebook=cb, absmax=amax)
         mse[cb] = float(np.mean((deq.astype(np.float64) - w) ** 2))
     assert mse["nf4"] < mse["fp4"] and mse["nf4"] < mse["int4"], mse
+
+
+def test_fp4_is_the_ocp_e2m1_encoding(oracle_mod):
+    """Code c of the FP4 codebook is the E2M1 value of bit pattern c, divided
+    by 6 (rounded once to fp32), sign of zero included."""
+    rows = read_golden_column("fp4_e2m1.txt", col=None)
+    assert len(rows) == 16
+    lv = oracle_mod.codebook_levels("fp4")
+    for code, sign, exp, man, val in rows:
+        c, sgn, e, m = int(code), int(sign), int(exp), int(man)
+        v = float(val)
+        assert c == 8 * sgn + 2 * e + m  # the table's own bit fields
+        mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m)
+        assert abs(v) == mag and bool(np.signbit(v)) == bool(sgn)
+        assert lv[c] == np.float32(np.float32(v) / np.float32(6.0))
+        assert bool(np.signbit(lv[c])) == bool(sgn)
+
+
+def test_fp4_nearest_code_is_sign_magnitude(oracle_mod):
+    """With the E2M1 encoding, the lowest-index nearest code of n is
+    8 * sign(n) + the nearest magnitude index of |n|, except that every n
+    nearest to zero gets +0 (code 0, the lower index of the +0 / -0 tie);
+    -0 (code 8) is never chosen."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    n = 64 * 200
+    w = rng.standard_normal(n, dtype=np.float32)
+    w[::97] = 0.0
+    w[1::89] = -0.0
+    w[2::83] *= np.float32(1e-3)                   # near the zero switch
+    w[::64] = np.float32(4.0)                      # c1 = 4 in every block
+    codes, amax = oracle_mod.quantize_cb(w, 64, "fp4")
+    got = unpack(codes, n)
+    assert not np.any(got == 8)
+    pos, _ = oracle_mod.quantize_cb(np.abs(w), 64, "fp4")
+    mag = unpack(pos, n)
+    assert np.all(mag < 8)
+    want = np.where((w < 0) & (mag > 0), mag + 8, mag)
+    assert np.array_equal(got, want)
+    assert np.all(got[w == 0] == 0)
