@@ -230,7 +230,7 @@ uint8_t nf4ref_e4m3_encode(float r) {
     uint8_t sign = 0;
     double v = (double)r;
     if (isnan(r)) return 0x7F;
-    if (v < 0) {
+    if (signbit(r)) { /* negative values and -0 keep the sign bit */
         sign = 0x80;
         v = -v;
     }
@@ -341,7 +341,7 @@ uint8_t nf4ref_e5m2_encode(float r) {
     uint8_t sign = 0;
     double v = (double)r;
     if (isnan(r)) return 0x7F;
-    if (v < 0) {
+    if (signbit(r)) { /* negative values and -0 keep the sign bit */
         sign = 0x80;
         v = -v;
     }
@@ -425,8 +425,12 @@ int nf4ref_double_quantize_ex(const float *absmax, int64_t nblocks, int32_t dq_b
         return 0;
     }
     if (!absmax || !q || !scale) return -1;
-    for (int64_t b = 0; b < nblocks; ++b)
+    for (int64_t b = 0; b < nblocks; ++b) {
         if (!isfinite(absmax[b])) return -2;
+        /* the unsigned linear code holds 0..255 steps of a non-negative c1
+         * (a block absmax); it has no code for a negative scale */
+        if (dq_format == NF4REF_DQ_LINEAR8 && !mean_offset && absmax[b] < 0.0f) return -1;
+    }
     float mu = 0.0f;
     if (mean_offset) {
         mu = nf4ref_pairwise_sum(absmax, nblocks) / (float)nblocks;

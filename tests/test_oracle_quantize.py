@@ -184,6 +184,41 @@ def test_double_quantize_against_definition(oracle_mod):
     assert q.max() <= 0x38  # ratios are in [0, 1]
 
 
+def test_fp8_encoders_on_signed_values(oracle_mod):
+    """Negative ratios and -0 against torch's CPU float8_e4m3fn and
+    float8_e5m2 casts (round to nearest even, sign of zero kept): the sign
+    bit on the magnitude's code."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    r = -np.abs(rng.standard_normal(200000).astype(np.float32))
+    r[::3] *= np.float32(1e-3)
+    r[::7] *= np.float32(1e-6)                 # rounds to -0
+    r[:4] = [-0.0, -1.0, -2.0 ** -10, -2.0 ** -17]
+    r = np.concatenate([r, -r]).astype(np.float32)
+    for enc, dt in ((oracle_mod.e4m3_encode, torch.float8_e4m3fn),
+                    (oracle_mod.e5m2_encode, torch.float8_e5m2)):
+        lib = torch.from_numpy(r).to(dt).view(torch.uint8).numpy()
+        assert np.array_equal(enc(r), lib), dt
+    assert oracle_mod.e4m3_encode(np.float32([-0.0]))[0] == 0x80
+
+
+def test_double_quantize_signed_scales(oracle_mod):
+    """c2 = max |c1| of the group; a negative c1 is the signed E4M3 code of
+    fl32(c1 / c2) (torch's cast); the unsigned linear code rejects it."""
+    rng = np.random.Generator(np.random.PCG64(18))
+    a = (rng.standard_normal(700) * 0.05).astype(np.float32)
+    a[::4] = -0.0
+    q, scale = oracle_mod.double_quantize(a)
+    for g in range(scale.size):
+        grp = a[g * 256:(g + 1) * 256]
+        assert scale[g] == np.max(np.abs(grp))
+        lib = torch.from_numpy((grp / scale[g]).astype(np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(q[g * 256:(g + 1) * 256], lib)
+    with pytest.raises(Exception):
+        oracle_mod.double_quantize_ex(a, 256, "linear8", False)
+    oracle_mod.double_quantize_ex(np.abs(a), 256, "linear8", False)
+
+
 def test_double_quantize_zero_group(oracle_mod):
     absmax = np.zeros(300, np.float32)
     absmax[260] = 0.5
