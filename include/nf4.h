@@ -91,8 +91,12 @@ nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int32_t blo
                         float *absmax_scale, void *stream);
 
 /* Double quantization of existing fp32 block scales ([MF] "Double
- * Quantization (DQ)"): c2 = max over each group of 256 absmax values, and
- * absmax_q[b] = E4M3FN(fl32(absmax[b] / c2)) with round to nearest even.
+ * Quantization (DQ)"): c2 = max over each group of 256 of |absmax|, and
+ * absmax_q[b] = E4M3FN(fl32(absmax[b] / c2)) with round to nearest even
+ * (0 when c2 == 0). Block absmax values are >= 0; a negative value is
+ * encoded with the E4M3 sign bit (bit 7 on the magnitude's code), as the
+ * format defines. Every absmax value must be finite: NaN or infinity is
+ * outside the contract (the result is unspecified; nothing faults).
  *   absmax        device, nblocks floats;  absmax_q device out, nblocks bytes;
  *   absmax_scale  device out, ceil(nblocks/256) floats. */
 nf4_status nf4_double_quantize(const float *absmax, int64_t nblocks, int32_t dq_blocksize,
@@ -278,10 +282,12 @@ typedef enum { NF4_DQ_E4M3 = 0, NF4_DQ_E5M2 = 1, NF4_DQ_LINEAR8 = 2 } nf4_dq_for
  * Architectural Guidelines" compares NF4 with FP4 and Int4; [QP] "1. 4-bit
  * NormalFloat (NF4)" compares it with a naive uniform 4-bit quantizer):
  *   NF4_CODEBOOK_NF4   the printed NF4 list (nf4_codebook())
- *   NF4_CODEBOOK_FP4   the OCP FP4 (E2M1) values 0, 0.5, 1, 1.5, 2, 3, 4, 6
- *                      with both signs, each fl32(v / 6): the 15 distinct
- *                      values ascending at codes 0..14 (0 at 7), and -0 at
- *                      code 15 (equal to level 7, so never chosen)
+ *   NF4_CODEBOOK_FP4   OCP FP4 (E2M1) in its own encoding, each value
+ *                      fl32(v / 6): code = 8 * sign + the index of the
+ *                      magnitude in 0, 0.5, 1, 1.5, 2, 3, 4, 6 (OCP
+ *                      Microscaling Formats specification, the E2M1 table);
+ *                      +0 is code 0 and -0 code 8 (equal to code 0, so never
+ *                      chosen)
  *   NF4_CODEBOOK_INT4  fl32((2k - 15) / 15), k = 0..15: evenly spaced, no zero
  * A code is the index of the nearest level (lower index on a tie), and a
  * block with c1 == 0 gets the code of the level nearest 0. */
@@ -331,7 +337,10 @@ size_t nf4_double_quantize_ex_workspace_size(int64_t nblocks, const nf4_format *
 
 /* Double quantization of nblocks existing fp32 block scales in f's format
  * (f->blocksize is not used). absmax_offset: device out, one float, required
- * iff f->dq_mean_offset. */
+ * iff f->dq_mean_offset. As in nf4_double_quantize, the values must be
+ * finite, and the FP8 formats encode a negative value with the sign bit;
+ * the unsigned linear code (NF4_DQ_LINEAR8 without the mean offset) takes
+ * non-negative values only (a negative one is outside the contract). */
 nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, const nf4_format *f,
                                   uint8_t *absmax_q, float *absmax_scale, float *absmax_offset,
                                   void *workspace, size_t workspace_bytes, void *stream);

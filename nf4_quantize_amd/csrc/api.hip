@@ -40,20 +40,18 @@ const float kLevels[16] = {
 
 namespace {
 
-// The other codebooks (nf4.h, nf4_codebook_id): OCP FP4 E2M1 values / 6
-// (the 15 distinct ones ascending, then -0) and evenly spaced Int4 levels,
-// each rounded once to fp32.
+// The other codebooks (nf4.h, nf4_codebook_id), each level rounded once to
+// fp32: FP4 in the OCP E2M1 encoding (code = 8 * sign + magnitude index of
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6}) divided by 6, and evenly spaced Int4 levels.
 struct OtherLevels {
     float fp4[16];
     float int4[16];
     OtherLevels() {
-        const float e2m1[7] = {0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-        fp4[7] = 0.0f;
-        for (int i = 0; i < 7; ++i) {
-            fp4[8 + i] = e2m1[i] / 6.0f;
-            fp4[6 - i] = -(e2m1[i] / 6.0f);
+        const float e2m1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+        for (int i = 0; i < 8; ++i) {
+            fp4[i] = e2m1[i] / 6.0f;
+            fp4[8 + i] = -(e2m1[i] / 6.0f);
         }
-        fp4[15] = -0.0f;
         for (int k = 0; k < 16; ++k) int4[k] = (float)(2 * k - 15) / 15.0f;
     }
 };
@@ -94,8 +92,16 @@ float ord2f(int64_t o) {
 // Bucket of v, with the same fp32 formula as the kernels (see CodeLut).
 uint32_t bucket_of(float v) { return lut_offset_bits(fmaf(v, 128.0f, 128.0f + 0x1p23f)) >> 3; }
 
-bool build_lut(CodeLut *lut, const float *lv) {
+// The code function the table encodes: the nearest level of v, or, for a
+// sign-magnitude codebook (looked up with |v|), the nearest level of v >= 0
+// and a constant 0 below zero (those buckets are never read).
+int table_code(const float *lv, bool signmag, float v) {
+    return (signmag && v < 0.0f) ? 0 : nearest_by_search(lv, v);
+}
+
+bool build_lut(CodeLut *lut, const float *lv, bool signmag) {
     const float vmin = -1.0f - 0x1p-20f, vmax = 1.0f + 0x1p-20f;
+    auto code = [&](float v) { return table_code(lv, signmag, v); };
     // bucket_of is non-decreasing in v, so each bucket is an interval of floats.
     int64_t start = f2ord(vmin);
     const int64_t end = f2ord(vmax);
@@ -113,8 +119,8 @@ bool build_lut(CodeLut *lut, const float *lv) {
         }
         const float lo = ord2f(start), hi = ord2f(a);
         if (bucket_of(lo) != (uint32_t)k || bucket_of(hi) != (uint32_t)k) return false;
-        const int c_lo = nearest_by_search(lv, lo);
-        const int c_hi = nearest_by_search(lv, hi);
+        const int c_lo = code(lo);
+        const int c_hi = code(hi);
         lut->e[k].hi = c_hi;
         lut->e[k].thr = -2.0f;
         if (c_hi != c_lo) {
@@ -122,7 +128,7 @@ bool build_lut(CodeLut *lut, const float *lv) {
             int64_t u = f2ord(lo), v = f2ord(hi);  // code(u) == c_lo, code(v) == c_lo + 1
             while (v - u > 1) {
                 const int64_t mid = u + (v - u) / 2;
-                if (nearest_by_search(lv, ord2f(mid)) > c_lo) v = mid; else u = mid;
+                if (code(ord2f(mid)) > c_lo) v = mid; else u = mid;
             }
             const float thr = ord2f(v);
             // A switch point must sit inside its bucket by more than the
@@ -136,8 +142,19 @@ bool build_lut(CodeLut *lut, const float *lv) {
     for (int k = kLutUsed; k < kLutEntries; ++k) lut->e[k] = LutEntry{-2.0f, nearest_by_search(lv, 1.0f)};
     // the code of 0 (a block with c1 == 0) must come out of the table
     const LutEntry &z = lut->e[bucket_of(0.0f)];
-    return lut->e[kLutUsed - 1].hi == nearest_by_search(lv, 1.0f) &&
-           z.hi - (0.0f < z.thr ? 1 : 0) == nearest_by_search(lv, 0.0f);
+    if (!(lut->e[kLutUsed - 1].hi == nearest_by_search(lv, 1.0f) &&
+          z.hi - (0.0f < z.thr ? 1 : 0) == nearest_by_search(lv, 0.0f)))
+        return false;
+    if (signmag) {
+        // code 8 + m is the mirror of magnitude code m, +0 is code 0 and -0
+        // code 8, and every magnitude code in the table is below 8
+        for (int m = 0; m < 8; ++m)
+            if (!(lv[8 + m] == -lv[m])) return false;
+        if (!(lv[0] == 0.0f && !signbit(lv[0]) && signbit(lv[8]))) return false;
+        for (int k = 0; k < kLutEntries; ++k)
+            if (lut->e[k].hi >= 8) return false;
+    }
+    return true;
 }
 
 }  // namespace
@@ -157,7 +174,8 @@ const CodeLut *code_lut_for(int cb) {
     static std::once_flag once[3];
     if (cb < 0 || cb > 2) return nullptr;
     std::call_once(once[cb], [cb] {
-        ok[cb] = build_lut(&lut[cb], levels_for(cb));
+        lut[cb].signmag = cb == NF4_CODEBOOK_FP4;
+        ok[cb] = build_lut(&lut[cb], levels_for(cb), lut[cb].signmag != 0);
         lut[cb].refine = cb != NF4_CODEBOOK_NF4;
     });
     return ok[cb] ? &lut[cb] : nullptr;

@@ -48,6 +48,12 @@ struct CodeLut {
     // refines the quotient to fl32(w / c1) instead of falling back to the
     // division near a switch point.
     int32_t refine;
+    // 1 for a sign-magnitude codebook (FP4 in the OCP E2M1 encoding: code
+    // 8 + m is the negative of magnitude code m, 0 and 8 are +0 and -0). The
+    // table then encodes the code of |v|, which is monotone; a negative v
+    // with a non-zero magnitude code m gets 8 + m, and every v nearest zero
+    // gets +0, the lower index of the +0 / -0 tie.
+    int32_t signmag;
 };
 __host__ __device__ __forceinline__ uint32_t lut_offset_bits(float fma_result) {
     return __builtin_bit_cast(uint32_t, fma_result) & 0x1F8u;
@@ -176,9 +182,11 @@ __device__ __forceinline__ uint32_t dq_encode(float x, float sc) {
         const float t = fminf(fmaxf(__builtin_rintf(x / sc), -l), l);
         return (uint32_t)(int)t & 0xFFu;
     } else {
+        // the FP8 formats carry a sign: a negative ratio (a signed scale, or
+        // c1 - mu with the mean offset) is its magnitude's code plus bit 7
         const float r = (sc == 0.0f) ? 0.0f : x / sc;
-        const uint32_t sign = (kS && r < 0.0f) ? 0x80u : 0u;
-        const float a = kS ? fabsf(r) : r;
+        const uint32_t sign = signbit(r) ? 0x80u : 0u;
+        const float a = fabsf(r);
         return sign | (F == kFmtE5M2 ? e5m2_encode_unit(a) : e4m3_encode_unit(a));
     }
 }

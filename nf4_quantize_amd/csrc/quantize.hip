@@ -88,10 +88,14 @@ __device__ __forceinline__ uint32_t lut_offset(float v) {
 __device__ __forceinline__ float2 lut_at(const float2 *s_lut, uint32_t off) {
     return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(s_lut) + off);
 }
-// Code of an exactly normalised value (the definition's fl32(w / c1)).
-__device__ __forceinline__ uint32_t exact_code(const float2 *s_lut, float nrm) {
-    const float2 ent = lut_at(s_lut, lut_offset(nrm));
-    return (uint32_t)__float_as_int(ent.y) - (nrm < ent.x ? 1u : 0u);
+// Code of an exactly normalised value (the definition's fl32(w / c1)); with
+// a sign-magnitude table (CodeLut::signmag), the code of |nrm| plus 8 for a
+// negative value with a non-zero magnitude code.
+__device__ __forceinline__ uint32_t exact_code(const float2 *s_lut, float nrm, bool signmag = false) {
+    const float v = signmag ? fabsf(nrm) : nrm;
+    const float2 ent = lut_at(s_lut, lut_offset(v));
+    const uint32_t c = (uint32_t)__float_as_int(ent.y) - (v < ent.x ? 1u : 0u);
+    return (signmag && c != 0u && signbit(nrm)) ? c + 8u : c;
 }
 
 // Input traits: one 16-byte slice per lane.
@@ -133,11 +137,21 @@ __device__ __forceinline__ uint32_t sign_nibbles(const float (&d)[E]) {
     }
 }
 
+// Packed sign-magnitude codes: packed holds the magnitude codes (each below
+// 8), and the code of a negative weight with a non-zero magnitude code gets
+// bit 3 of its nibble (see CodeLut::signmag). Adding 7 to a nibble below 8
+// sets its bit 3 exactly when it is non-zero, with no carry between nibbles.
+template <int E>
+__device__ __forceinline__ uint32_t apply_signs(uint32_t packed, const float (&f)[E]) {
+    const uint32_t nonzero = (packed + 0x77777777u) & 0x88888888u;
+    return packed | (nonzero & (sign_nibbles<E>(f) << 3));
+}
+
 // Codes of one lane's slice. c1 is the block absmax (all lanes of the block
 // hold the same value). s_lut holds E copies of the table, copy e with the
 // top code shifted to nibble e. Returns the packed nibbles, element e at
-// bits 4e.
-template <int E>
+// bits 4e. SM: a sign-magnitude table, looked up with |w|.
+template <int E, bool SM = false>
 __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, const float2 *s_lut) {
     // rcp ~ 1/c1 from v_rcp_f32 (within 1 ulp for a normal result). With
     // x = w * rcp as a real number, |x - fl(w/c1)| < 1.5e-7 for |w| <= c1.
@@ -157,20 +171,22 @@ __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, c
     float d[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
+        const float fe = SM ? fabsf(f[e]) : f[e];
         const float2 ent = lut_at(s_lut + e * kLutEntries,
-                                  lut_offset_bits(fmaf(f[e], rcp128, 128.0f + 0x1p23f)));
-        d[e] = fmaf(f[e], rcp, -ent.x);
+                                  lut_offset_bits(fmaf(fe, rcp128, 128.0f + 0x1p23f)));
+        d[e] = fmaf(fe, rcp, -ent.x);
         top |= __float_as_uint(ent.y);
     }
     float dmin = fabsf(d[0]);
 #pragma unroll
     for (int e = 1; e < E; ++e) dmin = fminf(dmin, fabsf(d[e]));
     uint32_t packed = top - sign_nibbles<E>(d);
+    if (SM) packed = apply_signs<E>(packed, f);
     if (outside | !(dmin >= kNearTol)) {  // rare: redo with the correctly rounded division
         packed = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f) << (4 * e);
+            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f, SM) << (4 * e);
     }
     return packed;
 }
@@ -183,6 +199,7 @@ __device__ __forceinline__ uint32_t slice_codes(const float (&f)[E], float c1, c
 // one. So xr = fma(r, rcp, x) = fl32(w / c1), and the switch point test
 // xr < thr is exact. Quotients below 2^-120 (subnormal results round on a
 // coarser grid) and a c1 outside [2^-118, 2^125] take the division.
+template <bool SM>
 __device__ __forceinline__ uint32_t slice_codes_refined(const float (&f)[8], float c1,
                                                         const float2 *s_lut) {
     const bool in_range = (c1 >= 0x1p-118f) & (c1 <= 0x1p125f);
@@ -196,18 +213,20 @@ __device__ __forceinline__ uint32_t slice_codes_refined(const float (&f)[8], flo
         const float x = f[e] * rcp;
         const float r = fmaf(-c1, x, f[e]);
         const float xr = fmaf(r, rcp, x);
+        const float xe = SM ? fabsf(xr) : xr;
         const float2 ent = lut_at(s_lut + e * kLutEntries,
-                                  lut_offset_bits(fmaf(xr, 128.0f, 128.0f + 0x1p23f)));
-        d[e] = xr - ent.x;  // negative exactly when xr < thr
+                                  lut_offset_bits(fmaf(xe, 128.0f, 128.0f + 0x1p23f)));
+        d[e] = xe - ent.x;  // negative exactly when xe < thr
         top |= __float_as_uint(ent.y);
         tiny |= ((__float_as_uint(xr) & 0x7FFFFFFFu) - 1u) < 0x037FFFFFu;  // 0 < |xr| < 2^-120
     }
     uint32_t packed = top - sign_nibbles<8>(d);
+    if (SM) packed = apply_signs<8>(packed, f);
     if (outside | tiny) {  // rare: redo with the correctly rounded division
         packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f) << (4 * e);
+            packed |= exact_code(s_lut, c1 > 0.0f ? f[e] / c1 : 0.0f, SM) << (4 * e);
     }
     return packed;
 }
@@ -217,11 +236,13 @@ __device__ __forceinline__ uint32_t slice_codes_refined(const float (&f)[8], flo
 // division fallback).
 template <int E>
 __device__ __forceinline__ uint32_t slice_codes_any(const float (&f)[E], float c1,
-                                                    const float2 *s_lut, int32_t refine) {
+                                                    const float2 *s_lut, const CodeLut &lut) {
     if constexpr (E == 8) {
-        if (refine) return slice_codes_refined(f, c1, s_lut);
+        if (lut.refine)
+            return lut.signmag ? slice_codes_refined<true>(f, c1, s_lut)
+                               : slice_codes_refined<false>(f, c1, s_lut);
     }
-    return slice_codes<E>(f, c1, s_lut);
+    return lut.signmag ? slice_codes<E, true>(f, c1, s_lut) : slice_codes<E, false>(f, c1, s_lut);
 }
 
 // Entry i of the table copies (copy i / kLutEntries, see slice_codes).
@@ -309,7 +330,7 @@ __device__ __forceinline__ void quantize_group(
             if (kDQ || partial) s_c1[blk] = m;
             if (absmax) absmax[g * kDqBlock + blk] = m;
         }
-        const uint32_t packed = slice_codes_any<E>(f, m, s_lut, lut.refine);
+        const uint32_t packed = slice_codes_any<E>(f, m, s_lut, lut);
         const int64_t slice = (int64_t)g * SLICES + i * TH + t;
         if (E == 8)
             reinterpret_cast<uint32_t *>(codes)[slice] = packed;
@@ -363,7 +384,7 @@ __device__ __forceinline__ void quantize_tail(
     for (int64_t i = lo; i < hi; i += 2) {
         uint32_t byte = 0;
         for (int j = 0; j < 2 && i + j < hi; ++j) {
-            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f);
+            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f, lut.signmag != 0);
             byte |= code << (4 * j);
         }
         codes[i / 2] = (uint8_t)byte;
@@ -399,10 +420,7 @@ __global__ __launch_bounds__(kThreads) void double_quantize_kernel(
     const int64_t b = g * kDqBlock + t;
     const float c1 = (b < nblocks) ? absmax[b] : 0.0f;
     const float c2 = wg_max(fabsf(c1), s_red);
-    if (b < nblocks) {
-        const float ratio = (c2 > 0.0f) ? c1 / c2 : 0.0f;
-        absmax_q[b] = (uint8_t)e4m3_encode_unit(ratio);
-    }
+    if (b < nblocks) absmax_q[b] = (uint8_t)dq_encode<kFmtE4M3, true>(c1, c2);
     if (t == 0) absmax_scale[g] = c2;
 }
 
@@ -625,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
         }
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const uint32_t packed = slice_codes_any<E>(f[i], m, s_lut, lut.refine);
+            const uint32_t packed = slice_codes_any<E>(f[i], m, s_lut, lut);
             const int64_t slice = unit * (U / E) + i * 64 + lane;
             if (E == 8)
                 reinterpret_cast<uint32_t *>(codes)[slice] = packed;
@@ -658,7 +676,7 @@ __global__ __launch_bounds__(64) void quantize_blocks_tail_kernel(
     for (int64_t i = lo; i < hi; i += 2) {
         uint32_t byte = 0;
         for (int j = 0; j < 2 && i + j < hi; ++j) {
-            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f);
+            const uint32_t code = exact_code(s_lut, (c1 > 0.0f) ? elem(i + j) / c1 : 0.0f, lut.signmag != 0);
             byte |= code << (4 * j);
         }
         codes[i / 2] = (uint8_t)byte;

@@ -118,6 +118,49 @@ def test_fused_equals_two_step(dev):
         assert np.array_equal(to_host(q8), oq) and np.array_equal(to_host(sc), osc), nb
 
 
+def test_double_quantize_signed_and_zero_groups(dev):
+    """nf4_double_quantize on block scales of either sign: c2 is the group's
+    max |absmax| and a negative ratio gets the E4M3 sign bit, as in the
+    oracle. Groups: all zero, all negative, mixed signs with -0, a ragged
+    last group."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(31))
+    nb = 5 * 256 + 77
+    a = (rng.standard_normal(nb) * 0.05).astype(np.float32)
+    a[:256] = 0.0                                 # group 0: all zero
+    a[256:512] = -np.abs(a[256:512])              # group 1: all negative
+    a[512:768:3] = -0.0                           # group 2: mixed, with -0
+    a[768:1024] *= np.float32(1e-4)               # tiny ratios round to (signed) zero
+    a[800] = np.float32(0.5)
+    q8, sc = nq.double_quantize(to_dev(a, dev))
+    torch.cuda.synchronize()
+    oq, osc = oracle.double_quantize(a)
+    assert np.array_equal(to_host(q8), oq)
+    assert np.array_equal(to_host(sc).view(np.uint32), osc.view(np.uint32))
+    assert np.any(oq & 0x80) and np.all(oq[:256] == 0)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_double_quantize_ex_signed(dev, fmt):
+    """nf4_double_quantize_ex (FP8 formats, no mean offset) on signed block
+    scales, against the oracle."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(32 + len(fmt)))
+    for dqb in (1, 64, 256, 4096):
+        nb = 2 * max(dqb, 64) + 19
+        a = (rng.standard_normal(nb) * 0.05).astype(np.float32)
+        a[::5] = -np.abs(a[::5])
+        a[1::11] = -0.0
+        f = nq.NF4Format(64, dqb, fmt, False)
+        q, sc = nq.double_quantize(to_dev(a, dev), fmt=f)
+        torch.cuda.synchronize()
+        rq, rsc, _ = oracle.double_quantize_ex(a, dqb, fmt, False)
+        assert np.array_equal(to_host(q), rq), dqb
+        assert np.array_equal(to_host(sc).view(np.uint32), rsc.view(np.uint32)), dqb
+
+
 def test_code_function_exhaustive_fp32(dev, code_thresholds):
     """Every binary32 n in [-1, 1]: blocks [1.0, n_1 .. n_63] have c1 = 1 and
     normalised values n_j exactly, so the kernel's code must equal the number
@@ -150,6 +193,43 @@ def test_code_function_exhaustive_fp32(dev, code_thresholds):
             total += nb * 63
             del bits, vals, w, t, codes, got, want
     log(f"exhaustive fp32 code function: {total} values, {bad} mismatches")
+    assert bad == 0
+
+
+def test_fp32_reciprocal_near_switch_points(dev, code_thresholds):
+    """fp32 input where the reciprocal shortcut can matter: every binary32 c1
+    in [1, 2) (2^23 values) with w = fl32(thr_i * c1) and its +-3-ulp
+    neighbours for the 15 oracle switch points thr_i, about 8.8e8 (w, c1)
+    pairs. Each c1 heads two blocks [c1, w..]. The expected code of w is
+    i + (fl32(w / c1) >= thr_i), with the quotient from the host's IEEE
+    division (numpy float32): w / c1 lies a few ulps from thr_i and far
+    from every other switch point."""
+    import torch
+
+    thr = code_thresholds
+    offs = np.arange(-3, 4, dtype=np.int32)
+    idx = np.repeat(np.arange(15), offs.size)  # switch point of each of the 105 values
+    slots = np.r_[1:64, 65:107]                # their places in a c1's two blocks
+    per = 1 << 19
+    bad = total = 0
+    for lo in range(0, 1 << 23, per):
+        c1 = (np.uint32(0x3F800000) + np.arange(lo, lo + per, dtype=np.uint32)).view(np.float32)
+        base = (c1[:, None] * thr[None, :]).astype(np.float32)
+        vals = (base.view(np.int32)[:, :, None] + offs).reshape(per, -1).view(np.float32)
+        quot = vals / c1[:, None]
+        assert quot.dtype == np.float32 and np.all(np.abs(vals) <= c1[:, None])
+        want = (idx + (quot >= thr[idx])).astype(np.uint8)
+        w = np.zeros((per, 128), np.float32)
+        w[:, 0] = c1
+        w[:, 64] = c1
+        w[:, slots] = vals
+        t = nq.quantize(to_dev(w.ravel(), dev), double_quant=False)
+        codes = t.codes.view(per, 64)
+        got = torch.stack([codes & 15, codes >> 4], dim=2).view(per, 128)[:, slots]
+        bad += int((got != to_dev(want, dev)).sum().item())
+        total += want.size
+        del t, codes, got
+    log(f"fp32 reciprocal sweep: {total} (w, c1) pairs, {bad} mismatches")
     assert bad == 0
 
 
