@@ -8,16 +8,26 @@ once). Inputs are resident in HBM; four input/output sets rotate so that the
 256 MB last-level cache never holds a step's input from the previous use.
 
 Printed: one JSON line with the contract fields, plus
-  roofline      the dominant kernel (quantize), bytes / HIP-event duration
-  cpu_baseline  the CPU oracle on the same workload (single thread)
+  roofline      the dominant kernel (quantize), bytes / HIP-event duration,
+                against the 8 TB/s peak and the measured streaming ceilings
+  cpu_baseline  the CPU oracle on the same workload (all usable host threads
+                and one thread), with the host's core count and CPU model, and
+                the oracle's matmuls on a 64-row sample of the QLoRA linear
+  stack_8b      the 224-matrix 8B-shaped stack (6.98e9 bf16 weights):
+                quantize all and dequantize all, batched and one call per
+                matrix, end to end and per matrix kind
   kernels       every kernel of the path measured alone: quantize and
                 dequantize on the 1024x1024 fp32 and 11008x4096 bf16 weights,
                 the decode GEMV (M = 1, 4, 16 on 28672 x 8192), the QLoRA
-                linear forward / input gradient (4096 x 8192 x 8192, r = 64)
-                and the adapter gradients at that shape.
+                linear forward / input gradient (4096 x 8192 x 8192, r = 64),
+                the adapter gradients at that shape, the merge, the storage
+                format variants and codebooks
+  context       the pages' own figures, quoted as context only (footprints,
+                card sizes, the per-step slowdown), beside the footprints this
+                library's storage gives for the same parameter counts
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-kernels]
-                       [--no-cpu-baseline] [--stack]
+                       [--no-cpu-baseline] [--no-stack]
 """
 import argparse
 import json
@@ -118,6 +128,9 @@ def _stream_lib():
     so.bench_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                 ctypes.c_void_p]
     so.bench_stream.restype = ctypes.c_int
+    so.bench_stream_grid.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    so.bench_stream_grid.restype = ctypes.c_int
     return so
 
 
@@ -125,12 +138,16 @@ def stream_ceilings(dev, groups, iters, kinds=("read4_write1", "read1_write4")):
     """Measured HBM ceilings: bench_stream.so's plain streaming kernels over
     `groups` 16384-weight groups, 4 rotating sets, timed like the kernels they
     bound. read4_write1 has quantize's traffic (reads 32 KiB, writes 8 KiB per
-    group), read1_write4 dequantize's, read_only reads 32 KiB per group."""
+    group), read1_write4 dequantize's, read_only reads 32 KiB per group.
+    Each is measured twice: on the storage kernels' own grid (one workgroup
+    per group), and as the best of a sweep of persistent grids (`best`, with
+    its grid size), the best-effort ceiling for the same bytes."""
     import torch
 
     so = _stream_lib()
     if so is None:
         return None
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     big, small = groups * 32768, groups * 8192
     spec = {"read4_write1": (0, big, small), "read1_write4": (1, small, big),
             "read_only": (2, big, 0)}
@@ -144,6 +161,20 @@ def stream_ceilings(dev, groups, iters, kinds=("read4_write1", "read1_write4")):
         ms, pc = time_op(lambda i: calls[i % 4](), iters, 2)
         res[name] = {"ms": ms, "p10_p50_p90_ms": pc, "bytes": rb + wb,
                      "GB/s": (rb + wb) / ms / 1e6}
+        # best effort: the fastest of the one-workgroup-per-group grid and the
+        # persistent grids
+        best = {"ms": ms, "p10_p50_p90_ms": pc, "grid": groups, "kernel": "one workgroup per group",
+                "GB/s": (rb + wb) / ms / 1e6}
+        for per_cu in (1, 2, 4, 8):
+            grid = min(cus * per_cu, groups)
+            pcalls = [Prepared(so.bench_stream_grid, kind + 3, _p(a), _p(b), groups, grid, _stream())
+                      for a, b in zip(srcs, dsts)]
+            pms, ppc = time_op(lambda i: pcalls[i % 4](), iters, 2)
+            if pms < best["ms"]:
+                best = {"ms": pms, "p10_p50_p90_ms": ppc, "grid": grid,
+                        "kernel": "persistent, grid-stride over groups",
+                        "GB/s": (rb + wb) / pms / 1e6}
+        res[name]["best"] = best
         del srcs, dsts, calls
     torch.cuda.empty_cache()
     return res
@@ -304,11 +335,75 @@ def _oracle_pass(flat, lo, hi):
     oracle.dequantize(codes, part.size, q=q8, scale=scale, out_dtype=oracle.BF16)
 
 
+# Host threads for the CPU baseline: a node's host cores are shared by its
+# GPUs, and one GPU's share is 16 of them, so the oracle runs on at most 16.
+CPU_THREAD_CAP = 16
+
+
+def host_cpu():
+    """The host's CPU model, logical core count and the cores this process
+    may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"model": model, "nproc": os.cpu_count(), "usable": usable}
+
+
+def cpu_threads():
+    return max(1, min(host_cpu()["usable"], CPU_THREAD_CAP))
+
+
+def cpu_matmul_baseline(cores, rows=64):
+    """The oracle's linear forward and input gradient (double precision, plain
+    loops) on a `rows`-row sample of the 4096 x 8192 x 8192, r = 64 QLoRA
+    linear with seeded inputs of the same shapes and distributions, rows split
+    over `cores` threads. Reported as GFLOP/s of the sample and, extrapolated
+    from it, the time of the whole 4096-row call."""
+    import numpy as np
+    import oracle
+    import workloads
+    from concurrent.futures import ThreadPoolExecutor
+
+    M, N, K, r, s = (workloads.LIN_M, workloads.LIN_N, workloads.LIN_K, workloads.LIN_R,
+                     workloads.LIN_SCALE)
+    d = workloads.linear_inputs(m=rows)
+    codes, absmax = oracle.quantize(d["w"].ravel())
+    q8, sc = oracle.double_quantize(absmax)
+    wd = oracle.dequantize(codes, N * K, q=q8, scale=sc).reshape(N, K)
+    flops_row = 2 * N * K + 2 * K * r + 2 * r * N
+    parts = [p for p in np.array_split(np.arange(rows), cores) if p.size]
+    res = {}
+    with ThreadPoolExecutor(len(parts)) as ex:
+        for name, fn, act in (("forward", oracle.linear_forward, d["x"]),
+                              ("input_grad", oracle.linear_backward_input, d["dy"])):
+            t0 = time.perf_counter()
+            list(ex.map(lambda idx: fn(act, wd, d["a"], d["b"], s, rows=idx), parts))
+            dt = time.perf_counter() - t0
+            gflops = rows * flops_row / dt / 1e9
+            res[name] = {"GFLOP/s": round(gflops, 3), "sample_s": round(dt, 3),
+                         "extrapolated_full_ms": round(M * flops_row / gflops / 1e6, 1)}
+    res["sample"] = (f"{rows} of {M} rows x all {N} outputs (forward) or {K} (input gradient), "
+                     f"K = {K}, r = {r}, double accumulation, over {len(parts)} host threads; "
+                     "the full-call time is extrapolated from the sample")
+    return res
+
+
 def cpu_baseline(w_bits, target_s=6.0):
     """The CPU oracle, as it stands, on the same weight: quantize, double
     quantize, dequantize to bf16, repeated for about target_s seconds; first on
-    one host thread, then on every host core the process may use, each thread
-    taking whole DQ groups (the library call releases the interpreter lock)."""
+    one host thread, then on up to CPU_THREAD_CAP threads, each taking whole DQ
+    groups (the library call releases the interpreter lock). Then the oracle's
+    matmuls on a row sample of the QLoRA linear."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
 
@@ -325,11 +420,7 @@ def cpu_baseline(w_bits, target_s=6.0):
                 return reps, (time.perf_counter() - t0) / reps
 
     reps1, dt1 = timed(lambda: _oracle_pass(flat, 0, n))
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores = cpu_threads()
     grp = 64 * 256
     ngroups = (n + grp - 1) // grp
     bounds = [min(n, (ngroups * i // cores) * grp) for i in range(cores + 1)]
@@ -346,6 +437,10 @@ def cpu_baseline(w_bits, target_s=6.0):
         "sample": f"whole 11008x4096 bf16 weight, quantize+DQ+dequantize: {repsn} passes "
                   f"({dtn:.3f} s each) split by DQ group over {cores} host threads; "
                   f"single_core_value: {reps1} passes ({dt1:.2f} s each) on one thread",
+        "host": dict(host_cpu(), thread_cap=CPU_THREAD_CAP,
+                     thread_cap_reason="a node's host cores are shared by its GPUs; one GPU's "
+                                       "share is 16"),
+        "matmul": cpu_matmul_baseline(cores),
     }
 
 
@@ -601,6 +696,30 @@ def stack_bench(dev, reps=3):
         fn()
     torch.cuda.synchronize()
     res = {}
+    # one call per matrix, by matrix kind: the 32 matrices of a kind between
+    # two events, as a per-matrix time
+    kinds = {}
+    for mi, (kname, shape) in enumerate(workloads.STACK_MATRICES):
+        idx = range(mi, len(mats), nmat)
+        kn = shape[0] * shape[1]
+        for label, fn, byts in (
+                ("quantize", lambda i: nq.nf4_quantize(mats[i], packed[i].codes, None,
+                                                       packed[i].absmax_q, packed[i].absmax_scale),
+                 bytes_quantize(kn, 2)),
+                ("dequantize", lambda i: nq.nf4_dequantize(
+                    packed[i].codes, kn, outs_all[i], absmax_q=packed[i].absmax_q,
+                    absmax_scale=packed[i].absmax_scale), bytes_dequantize(kn, 2))):
+            ev = Events(2)
+            ev[0].record()
+            for i in idx:
+                fn(i)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / len(idx)
+            kinds.setdefault(kname, {"shape": list(shape)})[f"{label}_ms"] = round(ms, 5)
+            kinds[kname][f"{label}_GB/s"] = round(byts / ms / 1e6, 1)
+    res["stack_per_matrix_kind"] = kinds
+    log(f"stack per matrix kind: {kinds}")
     for name, fn, byts in (("quantize", qall, bytes_quantize(total, 2)),
                            ("quantize_batched", qbatch, bytes_quantize(total, 2)),
                            ("dequantize", dall, bytes_dequantize(total, 2)),
@@ -622,6 +741,30 @@ def stack_bench(dev, reps=3):
     return res
 
 
+def pages_context():
+    """The pages' own figures, quoted as context (none measures these kernels;
+    none is on this GPU), beside what this library's storage gives for the same
+    parameter counts (nf4_storage_bytes, NF4 + double quantization)."""
+    import nf4_quantize_amd as nq
+
+    return {
+        "note": "figures from the source pages, context only, not targets",
+        "70b_weights": {"pages": "more than 140 GB in 16-bit, about 36 GB after NF4 "
+                                 "(\"QLoRA: quantising the part you are not training\", "
+                                 "The idea in one line)",
+                        "this_storage_GB": round(nq.nf4_storage_bytes(70_000_000_000) / 1e9, 2)},
+        "8b_weights": {"pages": "16 GB in 16-bit to about 4.1 GB (same section)",
+                       "this_storage_GB": round(nq.nf4_storage_bytes(8_030_000_000) / 1e9, 2)},
+        "fine_tuning_card": "70B QLoRA fine-tuning on one 48 GB card (same section)",
+        "consumer_card": "training and serving on an RTX 4090 with 24 GB (\"QLoRA in Production\", "
+                         "opening section)",
+        "step_slowdown": "25-40% slower per training step than 16-bit LoRA, no hardware stated "
+                         "(\"QLoRA: quantising the part you are not training\", What it costs, "
+                         "item 1); 20-30% in \"QLoRA: Mathematical Foundations ...\", Empirical "
+                         "Performance and Architectural Guidelines",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -629,7 +772,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stack", action="store_true", help="also time the 224-matrix 8B stack")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 224-matrix 8B stack")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (reference for "
                          "HBM byte counters under a profiler)")
@@ -657,9 +800,8 @@ def main():
 
     kernels = {}
     if not args.no_kernels:
-        kernels = kernel_benches(dev, iters=20, warmup=5, with_stack=args.stack)
-    elif args.stack:
-        kernels = stack_bench(dev)
+        kernels = kernel_benches(dev, iters=20, warmup=5, with_stack=False)
+    stack = None if args.no_stack else stack_bench(dev)
 
     q_bytes = main_res["quantize_bytes"]
     q_ms = main_res["quantize_ms"]
@@ -679,12 +821,19 @@ def main():
     }
     ceil = main_res["stream_ceiling"]
     if ceil is not None:
-        # the practical ceiling: a plain streaming kernel with the same traffic
-        # (bench_stream.so stream_r4w1), timed the same way in this run
+        # the practical ceilings: plain streaming kernels with the same traffic
+        # (bench_stream.so), timed the same way in this run: on quantize's own
+        # grid, and the best of a sweep of persistent grids
+        best = ceil["read4_write1"]["best"]
         roofline["measured_ceiling"] = {
-            "kernel": "stream_r4w1 (reads 32 KiB, writes 8 KiB per 16384-weight group)",
+            "kernel": "stream_r4w1 (reads 32 KiB, writes 8 KiB per 16384-weight group, "
+                      "one workgroup per group)",
             "GB/s": round(ceil["read4_write1"]["GB/s"], 1),
             "frac": round(achieved / ceil["read4_write1"]["GB/s"], 4),
+            "best_effort": {"kernel": "fastest of stream_r4w1 and stream_persistent<8,2> on "
+                                      "grids of 1, 2, 4, 8 workgroups per CU: " + best["kernel"],
+                            "grid": best["grid"], "GB/s": round(best["GB/s"], 1),
+                            "frac": round(achieved / best["GB/s"], 4)},
         }
     cpu = None if args.no_cpu_baseline else cpu_baseline(w_bits)
 
@@ -722,12 +871,22 @@ def main():
                            "traffic": counter_traffic("dequantize_chunks_kernel<bf16,DQ> 11008x4096"),
                            "ceiling_frac": (round(main_res["dequantize_gbs"] /
                                                   ceil["read1_write4"]["GB/s"], 4)
-                                            if ceil is not None else None)},
+                                            if ceil is not None else None),
+                           "best_effort_ceiling_frac": (
+                               round(main_res["dequantize_gbs"] /
+                                     ceil["read1_write4"]["best"]["GB/s"], 4)
+                               if ceil is not None else None)},
             "stream_ceiling": ({k: {"ms": round(v["ms"], 5), "GB/s": round(v["GB/s"], 1),
-                                    "bytes": v["bytes"], "p10_p50_p90_ms": v["p10_p50_p90_ms"]}
+                                    "bytes": v["bytes"], "p10_p50_p90_ms": v["p10_p50_p90_ms"],
+                                    "best_effort": {"ms": round(v["best"]["ms"], 5),
+                                                    "GB/s": round(v["best"]["GB/s"], 1),
+                                                    "grid": v["best"]["grid"],
+                                                    "kernel": v["best"]["kernel"]}}
                                 for k, v in ceil.items()} if ceil is not None else None),
         },
+        "stack_8b": stack,
         "kernels": kernels,
+        "context": pages_context(),
     }
     print(json.dumps(line), flush=True)
 

@@ -17,6 +17,13 @@
 //     stream_r4w1 does and writes nothing unless the XOR of a thread's four
 //     vectors equals `key` (the caller passes a key the data never forms, so
 //     the loads stay and no store happens).
+// Best-effort forms of the same three traffic patterns, free of the
+// one-workgroup-per-group grid: stream_persistent<R, W> runs a grid of the
+// caller's size (a few workgroups per CU) whose 256-thread workgroups walk
+// the groups with a grid stride. Each thread handles R 16-byte reads and W
+// 16-byte writes per group, and the loads of its next group are issued
+// before the stores of the current one, so every thread keeps two groups'
+// loads in flight. The caller sweeps the grid size and keeps the fastest.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,20 +70,74 @@ __global__ __launch_bounds__(512) void stream_r1w0(const u32x4 *__restrict__ src
     if ((x.x | x.y | x.z | x.w) == key) dst[blockIdx.x] = x;
 }
 
+// R reads and W writes of 16 bytes per thread and group (256 threads): a
+// group is 256 * R read vectors and 256 * W written vectors, each wave
+// instruction one contiguous 1 KiB run. W == 0: the loads are kept by a
+// store that never happens (key as in stream_r1w0).
+template <int R, int W>
+__global__ __launch_bounds__(256) void stream_persistent(const u32x4 *__restrict__ src,
+                                                         u32x4 *__restrict__ dst, int64_t groups,
+                                                         uint32_t key) {
+    const int t = threadIdx.x;
+    int64_t g = blockIdx.x;
+    if (g >= groups) return;
+    u32x4 v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) v[i] = __builtin_nontemporal_load(src + g * (256 * R) + i * 256 + t);
+    for (; g < groups; g += gridDim.x) {
+        const int64_t gn = g + gridDim.x;
+        u32x4 nv[R];
+        if (gn < groups) {
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                nv[i] = __builtin_nontemporal_load(src + gn * (256 * R) + i * 256 + t);
+        }
+        u32x4 x = v[0];
+#pragma unroll
+        for (int i = 1; i < R; ++i) x ^= v[i];
+        if constexpr (W == 0) {
+            if ((x.x | x.y | x.z | x.w) == key) dst[g] = x;
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j)
+                __builtin_nontemporal_store(x ^ (uint32_t)j, dst + g * (256 * W) + j * 256 + t);
+        }
+        if (gn < groups) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) v[i] = nv[i];
+        }
+    }
+}
+
 }  // namespace
 
 // kind 0: stream_r4w1, src >= groups * 32 KiB, dst >= groups * 8 KiB.
 // kind 1: stream_r1w4, src >= groups * 8 KiB, dst >= groups * 32 KiB.
 // kind 2: stream_r1w0, src >= groups * 32 KiB, dst >= groups * 16 B (key
 //         0xFFFFFFFF: the caller fills src so that no thread's XOR has all bits set).
+// kind 3, 4, 5: the traffic of kinds 0, 1, 2 by stream_persistent on a grid
+//         of `grid` workgroups (1 <= grid <= 65536; kinds 0..2 ignore it).
 // Device buffers, 16-byte aligned; 0 < groups < 2^22. Returns a hipError_t.
-extern "C" __attribute__((visibility("default"))) int bench_stream(int kind, const void *src,
-                                                                   void *dst, int64_t groups,
-                                                                   void *stream) {
+extern "C" __attribute__((visibility("default"))) int bench_stream_grid(int kind, const void *src,
+                                                                        void *dst, int64_t groups,
+                                                                        int grid, void *stream) {
     if (groups <= 0 || groups >= (int64_t(1) << 22) || !src || !dst ||
         (reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15))
         return (int)hipErrorInvalidValue;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kind >= 3 && kind <= 5) {
+        if (grid < 1 || grid > 65536) return (int)hipErrorInvalidValue;
+        const u32x4 *a = static_cast<const u32x4 *>(src);
+        u32x4 *b = static_cast<u32x4 *>(dst);
+        if (kind == 3)
+            stream_persistent<8, 2><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, b, groups, 0u);
+        else if (kind == 4)
+            stream_persistent<2, 8><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, b, groups, 0u);
+        else
+            stream_persistent<8, 0><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a, b, groups,
+                                                                               0xFFFFFFFFu);
+        return (int)hipGetLastError();
+    }
     if (kind == 0)
         stream_r4w1<<<dim3((unsigned)groups), dim3(512), 0, s>>>(
             static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst));
@@ -89,4 +150,11 @@ extern "C" __attribute__((visibility("default"))) int bench_stream(int kind, con
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("default"))) int bench_stream(int kind, const void *src,
+                                                                   void *dst, int64_t groups,
+                                                                   void *stream) {
+    return kind <= 2 ? bench_stream_grid(kind, src, dst, groups, 1, stream)
+                     : (int)hipErrorInvalidValue;
 }

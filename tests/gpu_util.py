@@ -40,3 +40,14 @@ def rel_err_metric(y, ref):
     rms = np.sqrt(np.mean(ref * ref))
     den = np.maximum(np.abs(ref), rms)
     return float(np.max(np.abs(y - ref) / den)), float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
+
+
+def plain_rel_err(y, ref):
+    """max_i |y_i - r_i| / |r_i| over the outputs with r_i != 0, and its
+    99.9th percentile: reported beside the gated metric (an output that
+    cancels to near zero makes the plain maximum large for any rounding)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nz = ref != 0
+    e = np.abs(y[nz] - ref[nz]) / np.abs(ref[nz])
+    return float(np.max(e)), float(np.quantile(e, 0.999))
