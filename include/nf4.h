@@ -191,6 +191,32 @@ nf4_status nf4_linear_forward(const void *x, int64_t m, const nf4_weight *w, con
                               const void *lora_b, int32_t r, float lora_scale, void *y,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the device scratch array that nf4_linear_forward_noalloc uses in
+ * place of a workspace (32 MiB; held on each GPU the library runs on until the
+ * process ends). */
+#define NF4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* nf4_linear_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. It computes exactly what nf4_linear_forward computes (the same
+ * kernels, in the same order, so the same bits), with the same arguments less
+ * the workspace, which comes from a static device array of
+ * NF4_NOALLOC_SCRATCH_BYTES per GPU instead. The call allocates nothing and
+ * calls no allocating routine. The caller still owns x, the adapter and y.
+ *   Limit: nf4_linear_workspace_size(m, r) <= NF4_NOALLOC_SCRATCH_BYTES, else
+ *          NF4_ERR_SIZE, nothing launched (about m * r <= 986,000 after r is
+ *          rounded up to 64: m = 4096 takes r up to 192).
+ *   The scratch of a GPU is shared by every call on it and keeps the last
+ *   call's contents; nothing in it has to start at zero (each call writes
+ *   every byte it reads). Calls that overlap on one GPU (different streams,
+ *   or host threads) race on it: order them on one stream.
+ *   The stream must belong to the current device. The first call on a device
+ *   looks up that device's copy of the array (hipGetSymbolAddress); if that
+ *   fails the call returns NF4_ERR_LAUNCH. */
+nf4_status nf4_linear_forward_noalloc(const void *x, int64_t m, const nf4_weight *w,
+                                      const void *lora_a, const void *lora_b, int32_t r,
+                                      float lora_scale, void *y, void *stream);
+
 /* Input gradient of the same linear ([MF] "Gradient Computation", the
  * activation-gradient equation):
  *   dX = dY . dequantize(W) + lora_scale * (dY . B^T) . A^T

@@ -44,6 +44,7 @@ EXPORTS = (
     "nf4_dequantize",
     "nf4_linear_workspace_size",
     "nf4_linear_forward",
+    "nf4_linear_forward_noalloc",
     "nf4_linear_backward_input",
     "nf4_lora_backward_workspace_size",
     "nf4_lora_backward",
@@ -149,6 +150,9 @@ def lib():
         fn.argtypes = [p, i64, ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p,
                        ctypes.c_size_t, p]
         fn.restype = ctypes.c_int
+    L.nf4_linear_forward_noalloc.argtypes = [p, i64, ctypes.POINTER(nf4_weight), p, p, i32, f32,
+                                             p, p]
+    L.nf4_linear_forward_noalloc.restype = ctypes.c_int
     L.nf4_lora_backward_workspace_size.argtypes = [i64, i64, i64, i32]
     L.nf4_lora_backward_workspace_size.restype = ctypes.c_size_t
     L.nf4_lora_backward.argtypes = [p, p, i64, i64, i64, p, p, i32, f32, p, p, ctypes.c_int, p,
@@ -612,6 +616,31 @@ def nf4_linear_forward(x, w: NF4Tensor, lora_a=None, lora_b=None, lora_scale=1.0
     """Y = X . dequantize(W)^T + lora_scale * (X . A) . B; x bf16 [m x K], W [N x K]."""
     return _linear("nf4_linear_forward", x, w, lora_a, lora_b, lora_scale, w.shape[0], out,
                    workspace)
+
+
+NF4_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/nf4.h
+
+
+def nf4_linear_forward_noalloc(x, w: NF4Tensor, lora_a=None, lora_b=None, lora_scale=1.0,
+                               out=None):
+    """nf4_linear_forward without a workspace: the library's static device
+    scratch stands in for it (nothing is allocated by the call when `out` is
+    given). Calls that overlap on one GPU race on that scratch."""
+    import torch
+
+    _need_cuda(x, lora_a, lora_b, out)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("activations are bfloat16")
+    m = x.shape[0]
+    r = 0 if lora_a is None else lora_a.shape[1]
+    if out is None:
+        out = torch.empty((m, w.shape[0]), dtype=torch.bfloat16, device=x.device)
+    ws = w.weight_struct()
+    st = lib().nf4_linear_forward_noalloc(_ptr(x), m, ctypes.byref(ws), _ptr(lora_a),
+                                          _ptr(lora_b), r, float(lora_scale), _ptr(out),
+                                          _stream(x.device))
+    _check(st, "nf4_linear_forward_noalloc")
+    return out
 
 
 def nf4_linear_backward_input(dy, w: NF4Tensor, lora_a=None, lora_b=None, lora_scale=1.0,

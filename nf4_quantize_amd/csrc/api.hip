@@ -336,9 +336,9 @@ NF4_API size_t nf4_linear_workspace_size(int64_t m, int32_t r) {
 
 namespace {
 
-nf4_status check_linear(const void *act, int64_t m, const nf4_weight *w, const void *a,
-                        const void *b, int32_t r, const void *out, const void *ws,
-                        size_t ws_bytes) {
+// Everything of a linear call but its workspace.
+nf4_status check_linear_args(const void *act, int64_t m, const nf4_weight *w, const void *a,
+                             const void *b, int32_t r, const void *out) {
     if (!w) return NF4_ERR_NULL;
     if (m < 0 || w->n_out <= 0 || w->k_in <= 0 || (w->k_in % kBlock) != 0) return NF4_ERR_SIZE;
     if (w->n_out * w->k_in > kMaxElems || m > (int64_t(1) << 31)) return NF4_ERR_SIZE;
@@ -356,8 +356,16 @@ nf4_status check_linear(const void *act, int64_t m, const nf4_weight *w, const v
     if ((w->absmax && !aligned(w->absmax, 4)) || (w->absmax_q && !aligned(w->absmax_q, 4)) ||
         (w->absmax_scale && !aligned(w->absmax_scale, 4)))
         return NF4_ERR_ALIGN;
+    if (r > 0 && (!aligned(a, 16) || !aligned(b, 16))) return NF4_ERR_ALIGN;
+    return NF4_OK;
+}
+
+nf4_status check_linear(const void *act, int64_t m, const nf4_weight *w, const void *a,
+                        const void *b, int32_t r, const void *out, const void *ws,
+                        size_t ws_bytes) {
+    const nf4_status st = check_linear_args(act, m, w, a, b, r, out);
+    if (st != NF4_OK || m == 0) return st;
     if (r > 0) {
-        if (!aligned(a, 16) || !aligned(b, 16)) return NF4_ERR_ALIGN;
         if (!ws || ws_bytes < nf4_linear_workspace_size(m, r)) return NF4_ERR_WORKSPACE;
         if (!aligned(ws, 16)) return NF4_ERR_ALIGN;
     }
@@ -382,6 +390,57 @@ NF4_API nf4_status nf4_linear_forward(const void *x, int64_t m, const nf4_weight
         static_cast<const uint16_t *>(x), m, normalised(w), static_cast<const uint16_t *>(lora_a),
         static_cast<const uint16_t *>(lora_b), r, lora_scale, static_cast<uint16_t *>(y),
         workspace, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// The scratch of nf4_linear_forward_noalloc: the adapter product and its
+// split-K partial sums, the same bytes nf4_linear_forward takes as its
+// workspace, in a device array that every call on a GPU shares. In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[NF4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess && !slot.ptr) slot.err = hipErrorInvalidSymbol;
+    });
+    if (slot.err != hipSuccess) return slot.err;
+    *out = slot.ptr;
+    return hipSuccess;
+}
+
+}  // namespace
+
+NF4_API nf4_status nf4_linear_forward_noalloc(const void *x, int64_t m, const nf4_weight *w,
+                                              const void *lora_a, const void *lora_b, int32_t r,
+                                              float lora_scale, void *y, void *stream) {
+    const nf4_status st = check_linear_args(x, m, w, lora_a, lora_b, r, y);
+    if (st != NF4_OK || m == 0) return st;
+    const size_t need = nf4_linear_workspace_size(m, r);
+    if (need > (size_t)NF4_NOALLOC_SCRATCH_BYTES) return NF4_ERR_SIZE;
+    void *ws = nullptr;
+    if (need > 0 && scratch_address(&ws) != hipSuccess) return NF4_ERR_LAUNCH;
+    return launch_status(launch_linear_forward(
+        static_cast<const uint16_t *>(x), m, normalised(w), static_cast<const uint16_t *>(lora_a),
+        static_cast<const uint16_t *>(lora_b), r, lora_scale, static_cast<uint16_t *>(y), ws,
+        static_cast<hipStream_t>(stream)));
 }
 
 NF4_API nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf4_weight *w,

@@ -139,6 +139,31 @@ def test_linear_validation(L, fn):
     assert call(wsb=ws - 1) == 5
 
 
+def test_linear_forward_noalloc_validation(L):
+    """The allocation-free forward validates like nf4_linear_forward and
+    rejects a shape whose workspace exceeds its scratch, before any HIP call."""
+    f = L.nf4_linear_forward_noalloc
+
+    def call(act=FAKE, m=64, w=None, a=FAKE, b=FAKE, r=16, out=FAKE):
+        w = w if w is not None else _w()
+        return f(act, m, ctypes.byref(w), a, b, r, 2.0, out, None)
+
+    assert f(FAKE, 64, None, FAKE, FAKE, 16, 2.0, FAKE, None) == 1
+    assert call(m=0) == 0
+    assert call(m=-1) == 2
+    assert call(r=300) == 2
+    assert call(w=_w(bs=32)) == 3
+    assert call(act=None) == 1
+    assert call(a=None) == 1
+    assert call(act=FAKE + 2) == 4
+    text = open(os.path.join(ROOT, "include", "nf4.h")).read()
+    mac = re.search(r"#define NF4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert mac and int(mac.group(1)) << int(mac.group(2)) == nq.NF4_NOALLOC_SCRATCH_BYTES
+    big = nq.nf4_linear_workspace_size(4096, 256)
+    assert big > nq.NF4_NOALLOC_SCRATCH_BYTES >= nq.nf4_linear_workspace_size(4096, 192)
+    assert call(m=4096, r=256) == 2  # scratch too small: NF4_ERR_SIZE, nothing launched
+
+
 def test_workspace_size(L):
     # bf16 product [m x rp] padded to 256 bytes, then 8 fp32 partials [8 x m x rp]
     assert nq.nf4_linear_workspace_size(4096, 64) == 4096 * 64 * 2 + 8 * 4096 * 64 * 4
