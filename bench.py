@@ -444,14 +444,37 @@ def cpu_baseline(w_bits, target_s=6.0):
     }
 
 
-def kernel_benches(dev, iters, warmup, with_stack):
+KERNEL_GROUPS = ("small", "gemv", "linear", "variants")
+
+
+def kernel_benches(dev, iters, warmup, groups=KERNEL_GROUPS):
+    """The kernels of the path measured alone, by group: `small` (the
+    1024x1024 fp32 weight), `gemv` (decode GEMV), `linear` (the QLoRA
+    linear, adapter gradients, merge, vendor GEMM reference), `variants`
+    (storage formats and codebooks)."""
     import torch
-    import numpy as np
     import nf4_quantize_amd as nq
     import workloads
 
     out = {}
+    g = torch.Generator(device=dev)
+    if "small" in groups:
+        out.update(small_benches(dev, iters, warmup))
+    if "gemv" in groups:
+        out.update(gemv_benches(dev, iters, warmup, g))
+    if "linear" in groups:
+        out.update(linear_benches(dev, iters, warmup, g))
+    if "variants" in groups:
+        out.update(variant_benches(dev, iters, warmup))
+    return out
 
+
+def small_benches(dev, iters, warmup):
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    out = {}
     # workload 1: 1024 x 1024 fp32 (launch-bound size)
     w1 = torch.from_numpy(workloads.weight_1024_f32()).to(dev)
     n1 = w1.numel()
@@ -464,10 +487,17 @@ def kernel_benches(dev, iters, warmup, with_stack):
     out["dequantize_1024x1024_f32"] = {"ms": ms, "GB/s": bytes_dequantize(n1, 4) / ms / 1e6,
                                        "p10_p50_p90_ms": pc}
     log(f"1024x1024: {out['quantize_1024x1024_f32']} {out['dequantize_1024x1024_f32']}")
+    return out
 
+
+def gemv_benches(dev, iters, warmup, g):
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    out = {}
     # workload 4: decode GEMV on a 28672 x 8192 NF4 weight, 4 rotating copies
     N, K = workloads.GEMV_N, workloads.GEMV_K
-    g = torch.Generator(device=dev)
     g.manual_seed(4)
     wts = []
     for c in range(4):
@@ -496,7 +526,15 @@ def kernel_benches(dev, iters, warmup, with_stack):
             e = out[f"gemv_M{m}_28672x8192"]
             e["ceiling_frac"] = e["GB/s"] / rd["GB/s"]
         log(f"read-only stream of the GEMV weight bytes: {rd}")
+    return out
 
+
+def linear_benches(dev, iters, warmup, g):
+    import torch
+    import nf4_quantize_amd as nq
+    import workloads
+
+    out = {}
     # workload 5: QLoRA linear 4096 x 8192 x 8192, r = 64
     M, N, K, r, s = (workloads.LIN_M, workloads.LIN_N, workloads.LIN_K, workloads.LIN_R,
                      workloads.LIN_SCALE)
@@ -564,10 +602,6 @@ def kernel_benches(dev, iters, warmup, with_stack):
                                        out["hipblaslt_bf16_4096x8192x8192_reference"]["TFLOP/s"])
     del X, dY, A, B, Y, dX, ws, Wd, wt
     torch.cuda.empty_cache()
-
-    out.update(variant_benches(dev, iters, warmup))
-    if with_stack:
-        out.update(stack_bench(dev))
     return out
 
 
@@ -771,6 +805,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-kernels", action="store_true")
+    ap.add_argument("--kernels", default=",".join(KERNEL_GROUPS),
+                    help="comma-separated kernel groups to time alone: " + ",".join(KERNEL_GROUPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 224-matrix 8B stack")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -800,7 +836,11 @@ def main():
 
     kernels = {}
     if not args.no_kernels:
-        kernels = kernel_benches(dev, iters=20, warmup=5, with_stack=False)
+        groups = tuple(k for k in args.kernels.split(",") if k)
+        bad = [k for k in groups if k not in KERNEL_GROUPS]
+        if bad:
+            ap.error(f"unknown kernel groups {bad}")
+        kernels = kernel_benches(dev, iters=20, warmup=5, groups=groups)
     stack = None if args.no_stack else stack_bench(dev)
 
     q_bytes = main_res["quantize_bytes"]

@@ -59,6 +59,9 @@ typedef enum {
     NF4_ERR_LAUNCH = 6       /* the HIP runtime reported an error at launch */
 } nf4_status;
 
+/* Element types. Entry points take them as int32_t (an nf4_dtype value), so
+ * that any value a caller passes is representable and an unknown one is
+ * rejected with NF4_ERR_UNSUPPORTED. */
 typedef enum { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
 
 /* Human-readable name of a status code (static string). */
@@ -86,7 +89,7 @@ int64_t nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t dq_blocksize, in
  * (then absmax is required). For each element the code is the index of the
  * nearest level to fl32(w / c1), lower index on an exact tie; a block with
  * c1 == 0 gets code 7 (the zero level); a group with c2 == 0 gets code8 0. */
-nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int32_t blocksize,
+nf4_status nf4_quantize(const void *w, int32_t w_dtype, int64_t n, int32_t blocksize,
                         uint8_t *codes, float *absmax, int32_t dq_blocksize, uint8_t *absmax_q,
                         float *absmax_scale, void *stream);
 
@@ -111,7 +114,7 @@ nf4_status nf4_double_quantize(const float *absmax, int64_t nblocks, int32_t dq_
  *   codes device ceil(n/2) bytes; out device n elements (16-byte aligned). */
 nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t blocksize, const float *absmax,
                           const uint8_t *absmax_q, const float *absmax_scale,
-                          int32_t dq_blocksize, void *out, nf4_dtype out_dtype, void *stream);
+                          int32_t dq_blocksize, void *out, int32_t out_dtype, void *stream);
 
 /* One tensor of a batched call: the buffers that nf4_quantize and
  * nf4_dequantize take for an n-element tensor (block size 64, DQ block 256),
@@ -146,14 +149,14 @@ typedef struct {
  *   count    >= 0
  * Every entry is validated before anything is launched; the first invalid
  * entry decides the status. Outputs of different entries must not overlap. */
-nf4_status nf4_quantize_batched(const nf4_batch_entry *entries, int32_t count, nf4_dtype w_dtype,
+nf4_status nf4_quantize_batched(const nf4_batch_entry *entries, int32_t count, int32_t w_dtype,
                                 void *stream);
 
 /* nf4_dequantize of each of `count` tensors, batched the same way: entry e's
  * w receives nf4_dequantize(e.codes, e.n, 64, e.absmax, e.absmax_q,
  * e.absmax_scale, 256, e.w, out_dtype, stream). */
 nf4_status nf4_dequantize_batched(const nf4_batch_entry *entries, int32_t count,
-                                  nf4_dtype out_dtype, void *stream);
+                                  int32_t out_dtype, void *stream);
 
 /* A frozen NF4 weight W stored [n_out x k_in] row-major (d_out x d_in, the
  * transpose of [MF]'s W in R^{d_in x d_out}), quantized with nf4_quantize over
@@ -248,7 +251,7 @@ size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, 
  * aligned, >= nf4_lora_backward_workspace_size(m, k_in, n_out, r) bytes. */
 nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k_in, int64_t n_out,
                              const void *lora_a, const void *lora_b, int32_t r, float lora_scale,
-                             void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
+                             void *grad_a, void *grad_b, int32_t grad_dtype, void *workspace,
                              size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace nf4_merge_lora needs: the fp32 block scales of the
@@ -352,7 +355,7 @@ size_t nf4_quantize_ex_workspace_size(int64_t n, const nf4_format *f);
  * The 4-bit codes index f->codebook's levels.
  * f = {64, 256, NF4_DQ_E4M3, 0, NF4_CODEBOOK_NF4} computes exactly what
  * nf4_quantize does. */
-nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, const nf4_format *f,
+nf4_status nf4_quantize_ex(const void *w, int32_t w_dtype, int64_t n, const nf4_format *f,
                            uint8_t *codes, float *absmax, uint8_t *absmax_q, float *absmax_scale,
                            float *absmax_offset, void *workspace, size_t workspace_bytes,
                            void *stream);
@@ -378,7 +381,7 @@ nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, const nf
 nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format *f,
                              const float *absmax, const uint8_t *absmax_q,
                              const float *absmax_scale, const float *absmax_offset, void *out,
-                             nf4_dtype out_dtype, void *stream);
+                             int32_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -225,7 +225,7 @@ NF4_API int64_t nf4_storage_bytes(int64_t n, int32_t blocksize, int32_t dq_block
     return codes + nb + 4 * cdiv(nb, kDqBlock);
 }
 
-NF4_API nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int32_t blocksize,
+NF4_API nf4_status nf4_quantize(const void *w, int32_t w_dtype, int64_t n, int32_t blocksize,
                                 uint8_t *codes, float *absmax, int32_t dq_blocksize,
                                 uint8_t *absmax_q, float *absmax_scale, void *stream) {
     if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
@@ -242,7 +242,7 @@ NF4_API nf4_status nf4_quantize(const void *w, nf4_dtype w_dtype, int64_t n, int
     if ((absmax && !aligned(absmax, 4)) || (absmax_q && !aligned(absmax_q, 4)) ||
         (absmax_scale && !aligned(absmax_scale, 4)))
         return NF4_ERR_ALIGN;
-    return launch_status(launch_quantize(w, w_dtype, n, codes, absmax, absmax_q, absmax_scale,
+    return launch_status(launch_quantize(w, static_cast<nf4_dtype>(w_dtype), n, codes, absmax, absmax_q, absmax_scale,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -261,7 +261,7 @@ NF4_API nf4_status nf4_double_quantize(const float *absmax, int64_t nblocks, int
 NF4_API nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t blocksize,
                                   const float *absmax, const uint8_t *absmax_q,
                                   const float *absmax_scale, int32_t dq_blocksize, void *out,
-                                  nf4_dtype out_dtype, void *stream) {
+                                  int32_t out_dtype, void *stream) {
     if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
     if (blocksize != kBlock) return NF4_ERR_UNSUPPORTED;
     if (out_dtype != NF4_F32 && out_dtype != NF4_BF16) return NF4_ERR_UNSUPPORTED;
@@ -276,7 +276,7 @@ NF4_API nf4_status nf4_dequantize(const uint8_t *codes, int64_t n, int32_t block
         (absmax_scale && !aligned(absmax_scale, 4)))
         return NF4_ERR_ALIGN;
     return launch_status(launch_dequantize(codes, n, dq ? nullptr : absmax, dq ? absmax_q : nullptr,
-                                           dq ? absmax_scale : nullptr, out, out_dtype,
+                                           dq ? absmax_scale : nullptr, out, static_cast<nf4_dtype>(out_dtype),
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -297,7 +297,7 @@ nf4_status check_batch_entry(const nf4_batch_entry &e) {
     return NF4_OK;
 }
 
-nf4_status check_batch(const nf4_batch_entry *entries, int32_t count, nf4_dtype dt) {
+nf4_status check_batch(const nf4_batch_entry *entries, int32_t count, int32_t dt) {
     if (count < 0) return NF4_ERR_SIZE;
     if (dt != NF4_F32 && dt != NF4_BF16) return NF4_ERR_UNSUPPORTED;
     if (count > 0 && !entries) return NF4_ERR_NULL;
@@ -311,22 +311,22 @@ nf4_status check_batch(const nf4_batch_entry *entries, int32_t count, nf4_dtype 
 }  // namespace
 
 NF4_API nf4_status nf4_quantize_batched(const nf4_batch_entry *entries, int32_t count,
-                                        nf4_dtype w_dtype, void *stream) {
+                                        int32_t w_dtype, void *stream) {
     const nf4_status st = check_batch(entries, count, w_dtype);
     if (st != NF4_OK) return st;
     if (!code_lut()) return NF4_ERR_UNSUPPORTED;  // codebook table failed its checks
     if (count == 0) return NF4_OK;
     return launch_status(
-        launch_quantize_batched(entries, count, w_dtype, static_cast<hipStream_t>(stream)));
+        launch_quantize_batched(entries, count, static_cast<nf4_dtype>(w_dtype), static_cast<hipStream_t>(stream)));
 }
 
 NF4_API nf4_status nf4_dequantize_batched(const nf4_batch_entry *entries, int32_t count,
-                                          nf4_dtype out_dtype, void *stream) {
+                                          int32_t out_dtype, void *stream) {
     const nf4_status st = check_batch(entries, count, out_dtype);
     if (st != NF4_OK) return st;
     if (count == 0) return NF4_OK;
     return launch_status(
-        launch_dequantize_batched(entries, count, out_dtype, static_cast<hipStream_t>(stream)));
+        launch_dequantize_batched(entries, count, static_cast<nf4_dtype>(out_dtype), static_cast<hipStream_t>(stream)));
 }
 
 NF4_API size_t nf4_linear_workspace_size(int64_t m, int32_t r) {
@@ -462,7 +462,7 @@ NF4_API size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t
 
 NF4_API nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k_in, int64_t n_out,
                                      const void *lora_a, const void *lora_b, int32_t r, float lora_scale,
-                                     void *grad_a, void *grad_b, nf4_dtype grad_dtype, void *workspace,
+                                     void *grad_a, void *grad_b, int32_t grad_dtype, void *workspace,
                                      size_t workspace_bytes, void *stream) {
     if (m < 0 || k_in <= 0 || n_out <= 0 || (k_in % 64) != 0 || (n_out % 64) != 0) return NF4_ERR_SIZE;
     if (r <= 0 || r > 256 || (r % 8) != 0) return NF4_ERR_SIZE;
@@ -526,7 +526,7 @@ NF4_API size_t nf4_double_quantize_ex_workspace_size(int64_t nblocks, const nf4_
     return nf4::double_quantize_ex_workspace(nblocks, *f);
 }
 
-NF4_API nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, const nf4_format *f,
+NF4_API nf4_status nf4_quantize_ex(const void *w, int32_t w_dtype, int64_t n, const nf4_format *f,
                                    uint8_t *codes, float *absmax, uint8_t *absmax_q,
                                    float *absmax_scale, float *absmax_offset, void *workspace,
                                    size_t workspace_bytes, void *stream) {
@@ -548,7 +548,7 @@ NF4_API nf4_status nf4_quantize_ex(const void *w, nf4_dtype w_dtype, int64_t n, 
     if (dq && (st = check_workspace(nf4::quantize_ex_workspace(n, *f), workspace,
                                     workspace_bytes)) != NF4_OK)
         return st;
-    return launch_status(nf4::launch_quantize_ex(w, w_dtype, n, *f, codes, absmax,
+    return launch_status(nf4::launch_quantize_ex(w, static_cast<nf4_dtype>(w_dtype), n, *f, codes, absmax,
                                                  dq ? absmax_q : nullptr,
                                                  dq ? absmax_scale : nullptr, absmax_offset,
                                                  workspace, static_cast<hipStream_t>(stream)));
@@ -578,7 +578,7 @@ NF4_API nf4_status nf4_double_quantize_ex(const float *absmax, int64_t nblocks, 
 NF4_API nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_format *f,
                                      const float *absmax, const uint8_t *absmax_q,
                                      const float *absmax_scale, const float *absmax_offset,
-                                     void *out, nf4_dtype out_dtype, void *stream) {
+                                     void *out, int32_t out_dtype, void *stream) {
     nf4_status st = check_format(f);
     if (st != NF4_OK) return st;
     if (n < 0 || n > kMaxElems) return NF4_ERR_SIZE;
@@ -595,7 +595,7 @@ NF4_API nf4_status nf4_dequantize_ex(const uint8_t *codes, int64_t n, const nf4_
         return NF4_ERR_ALIGN;
     return launch_status(nf4::launch_dequantize_ex(
         codes, n, *f, dq ? nullptr : absmax, dq ? absmax_q : nullptr, dq ? absmax_scale : nullptr,
-        (dq && f->dq_mean_offset) ? absmax_offset : nullptr, out, out_dtype,
+        (dq && f->dq_mean_offset) ? absmax_offset : nullptr, out, static_cast<nf4_dtype>(out_dtype),
         static_cast<hipStream_t>(stream)));
 }
 
