@@ -89,5 +89,22 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// LDS layout of a tile of 128-byte rows (64 bf16 of K) fed by direct-to-LDS
+// loads and read as MFMA fragments. Row r sits in 128-byte segment
+// tile_seg(r): rows 0-7 of each 16-row block at its even segments, rows 8-15
+// at the odd ones; its 16-byte chunk c at position c ^ (r & 7).
+//  - A fragment read (lanes 16k .. 16k+15 read one chunk of 16 consecutive
+//    rows) then puts lanes 0-7 of each group on one half of the 64 LDS banks
+//    and lanes 8-15 on the other, each on 8 distinct 16-byte positions: the
+//    ds_read_b128 rate of a contiguous read, measured on gfx950. A chunk
+//    swizzle by row with both halves inside each 8-lane octet runs at 0.7 of
+//    it (bank conflicts).
+//  - A direct-to-LDS load writes 16 bytes per lane, lane-linearly: lanes 8j
+//    .. 8j+7 fill one segment, so they read one row's 128 bytes.
+__host__ __device__ constexpr int tile_seg(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+// the row held by segment s (the inverse of tile_seg)
+__host__ __device__ constexpr int seg_row(int s) { return (s & ~15) | ((s >> 1) & 7) | ((s & 1) << 3); }
+static_assert(seg_row(tile_seg(13)) == 13 && tile_seg(seg_row(7)) == 7, "tile_seg and seg_row are inverse");
+
 }  // namespace gemm
 }  // namespace nf4

@@ -15,7 +15,7 @@
 // moves 224 KiB instead of 256 KiB.
 //
 //  - dY goes global -> LDS directly (buffer_load ... lds), double buffered,
-//    like X in the forward kernel.
+//    like X in the forward kernel (the tile_seg layout of gemm_common.h).
 //  - The MFMA operand needs 8 consecutive contraction indices of one dX
 //    column, i.e. 8 rows of W: each thread loads an 8 x 8 patch of codes
 //    (8 rows of 8 columns), dequantizes it as bf16(q[code] * c1'),
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     uint32_t a_off[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const int row = 64 * w + 8 * q + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        const int row = seg_row(64 * w + 8 * q + (lane >> 3));
+        const int chunk = (lane & 7) ^ (row & 7);
         a_off[q] = (uint32_t)(row * N * 2 + chunk * 16);
     }
 
@@ -169,9 +169,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     auto scale = [&](const Patch &pt, int i) {
         return kDQ ? __builtin_amdgcn_cvt_f32_fp8((int)pt.q[i], 0) * pt.s[i] : pt.s[i];
     };
-    // W tile layout: row c (0..255) of 64 contraction values, 128 B, 16-byte
-    // chunks XOR-swizzled by (c >> 1) & 7; the patch's column e goes to row
-    // 8 cp + e, chunk jp.
+    // W tile layout: row c (0..255) of 64 contraction values, 128 B, in the
+    // tile_seg layout (gemm_common.h); the patch's column e goes to row
+    // 8 cp + e, chunk jp. The 8 lanes of an octet write one row's segment,
+    // and octets 2k, 2k+1 (rows c, c + 8) opposite halves of the banks.
     auto write_patch = [&](const uint32_t (&rows)[8][4], int buf) {
         u32x4 cols[8];
         transpose8x8(rows, cols);
@@ -179,19 +180,19 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = 8 * cp + e;
-            *reinterpret_cast<u32x4 *>(dst + c * 128 + 16 * (jp ^ ((c >> 1) & 7))) = cols[e];
+            *reinterpret_cast<u32x4 *>(dst + tile_seg(c) * 128 + 16 * (jp ^ (c & 7))) = cols[e];
         }
     };
 
     // ---- MFMA operands: dY tile row 128 wr + 16 i + lr and W tile row
-    // 128 wc + 16 jt + lr, logical chunk 2g + ks (the swizzle of such a row is
-    // (lr >> 1) & 7)
+    // 128 wc + 16 jt + lr, logical chunk 2g + ks (tile_seg layout: such a row
+    // is in segment 16 * (its block) + tile_seg(lr), chunks swizzled by lr & 7)
     const int wr = w >> 1, wc = w & 1;
     uint32_t frag_off[2], bfrag_off[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        frag_off[ks] = (128 * wr + lr) * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
-        bfrag_off[ks] = (128 * wc + lr) * 128 + 16 * ((2 * g + ks) ^ ((lr >> 1) & 7));
+        frag_off[ks] = (128 * wr + tile_seg(lr)) * 128 + 16 * ((2 * g + ks) ^ (lr & 7));
+        bfrag_off[ks] = (128 * wc + tile_seg(lr)) * 128 + 16 * ((2 * g + ks) ^ (lr & 7));
     }
     auto afrag = [&](const char *a_t, int idx) {
         return *reinterpret_cast<const u32x4 *>(a_t + frag_off[idx / kTM] + (idx % kTM) * 2048);
@@ -336,8 +337,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         uint32_t u_off[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int row = 64 * w + 8 * q + (lane >> 3);
-            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            const int row = seg_row(64 * w + 8 * q + (lane >> 3));
+            const int chunk = (lane & 7) ^ (row & 7);
             u_off[q] = (uint32_t)(row * p.rp * 2 + chunk * 16);
         }
         for (int64_t sa = 0; sa < p.rp / kBK; ++sa) {
