@@ -131,7 +131,33 @@ def _stream_lib():
     so.bench_stream_grid.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     so.bench_stream_grid.restype = ctypes.c_int
+    so.bench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p]
+    so.bench_mfma.restype = ctypes.c_int
     return so
+
+
+def mfma_ceiling(dev, grid=512, iters=300):
+    """TFLOP/s of bench_stream.so's MFMA-only kernel: 64 back-to-back
+    v_mfma_f32_32x32x16_bf16 per wave and iteration on random bf16 operands
+    (the operand bits change with every instruction, as in a GEMM on data),
+    one workgroup of 4 waves per CU twice over. The practical ceiling of the
+    matrix cores on this part, beside the 2.5 PFLOP/s published peak."""
+    import torch
+
+    so = _stream_lib()
+    if so is None:
+        return None
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    src = torch.randn(grid * 4 * 16 * 64 * 8, generator=g, device=dev).to(torch.bfloat16)
+    dst = torch.empty(grid * 4 * 4096, dtype=torch.float32, device=dev)
+    call = Prepared(so.bench_mfma, _p(src), _p(dst), grid, iters, _stream())
+    ms, pc = time_op(lambda i: call(), 5, 2)
+    flops = grid * 4 * iters * 64 * 32 * 32 * 16 * 2
+    del src, dst
+    return {"ms": ms, "p10_p50_p90_ms": pc, "TFLOP/s": flops / ms / 1e9,
+            "peak_frac": flops / ms / 1e9 / BF16_PEAK_TFLOPS}
 
 
 def stream_ceilings(dev, groups, iters, kinds=("read4_write1", "read1_write4")):
@@ -590,6 +616,14 @@ def linear_benches(dev, iters, warmup, g):
                                        "TFLOP/s": 2 * N * K * r / ms / 1e9}
     log(f"merge: {out['merge_lora_8192x8192_r64']}")
     del bases[1:], merged, mws
+    # practical ceiling of the matrix cores on data: bench_stream.so's
+    # back-to-back 32x32x16 bf16 MFMAs on random bf16 operands
+    mc = mfma_ceiling(dev)
+    if mc is not None:
+        out["mfma_ceiling_bf16_32x32x16"] = mc
+        for name in ("linear_fwd_4096x8192x8192_r64", "linear_dgrad_4096x8192x8192_r64"):
+            out[name]["mfma_ceiling_frac"] = out[name]["TFLOP/s"] / mc["TFLOP/s"]
+        log(f"MFMA ceiling: {mc}")
     # practical ceiling: the vendor bf16 GEMM on a pre-dequantized weight
     Wd = nq.dequantize(wt, torch.bfloat16)
     ms, pc = time_op(lambda i: torch.matmul(X, Wd.t(), out=Y), lin_iters, max(1, warmup // 2))

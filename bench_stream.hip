@@ -109,7 +109,57 @@ __global__ __launch_bounds__(256) void stream_persistent(const u32x4 *__restrict
     }
 }
 
+// The matrix cores' practical ceiling on data (the bf16 MFMA of the fused
+// GEMM, v_mfma_f32_32x32x16_bf16): each wave loads 8 A and 8 B operands
+// (16 bytes per lane each, bf16 values from src) and issues 64 MFMAs per
+// iteration, every one on a different (A, B) pair, into 4 accumulator tiles,
+// so the operand bits change with every instruction as they do in a GEMM on
+// real data (the matrix cores' power, and so the clock they hold, depends on
+// it). No other instruction sits between the MFMAs. Each workgroup (4
+// waves) writes its 4 waves' accumulators, 64 x 64 floats per wave.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256) void mfma_ceiling(const u32x4 *__restrict__ src, int iters,
+                                                    float *__restrict__ dst) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const u32x4 *s = src + (int64_t)(blockIdx.x * 4 + wv) * 16 * 64;
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = s[i * 64 + lane];
+        b[i] = s[(8 + i) * 64 + lane];
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 64; ++m)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[m % 4]) : "v"(a[m % 8]), "v"(b[(m / 8 + m) % 8]));
+    }
+    // wait states before the accumulators are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    float *o = dst + (int64_t)(blockIdx.x * 4 + wv) * 4096;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[(t * 16 + v) * 64 + lane] = acc[t][v];
+}
+
 }  // namespace
+
+// Runs mfma_ceiling on `grid` workgroups: src >= grid * 4 * 16 KiB of bf16,
+// dst >= grid * 4 * 4096 floats, 16-byte aligned; 1 <= grid <= 65536,
+// 1 <= iters <= 2^20. Returns a hipError_t.
+extern "C" __attribute__((visibility("default"))) int bench_mfma(const void *src, void *dst, int grid,
+                                                                 int iters, void *stream) {
+    if (!src || !dst || grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 20) ||
+        (reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15))
+        return (int)hipErrorInvalidValue;
+    mfma_ceiling<<<dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4 *>(src), iters, static_cast<float *>(dst));
+    return (int)hipGetLastError();
+}
 
 // kind 0: stream_r4w1, src >= groups * 32 KiB, dst >= groups * 8 KiB.
 // kind 1: stream_r1w4, src >= groups * 8 KiB, dst >= groups * 32 KiB.

@@ -104,3 +104,43 @@ def test_rejects_bad_arguments(so):
     assert so.bench_stream(0, 8, 16, GROUPS, None) != 0
     assert so.bench_stream_grid(3, 16, 16, GROUPS, 0, None) != 0
     assert so.bench_stream_grid(4, 16, 16, GROUPS, 65537, None) != 0
+
+
+def test_mfma_ceiling_computes_its_products(so):
+    """bench_mfma issues the MFMAs it is timed for: one workgroup, two
+    iterations, against the same products in float64 on the host."""
+    import torch
+
+    so.bench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p]
+    so.bench_mfma.restype = ctypes.c_int
+    rng = np.random.Generator(np.random.PCG64(3))
+    vals = rng.standard_normal(4 * 16 * 64 * 8).astype(np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)  # bf16 by truncation: exact operands
+    src = to_dev(bits, torch.device("cuda:0"))
+    dst = torch.zeros(4 * 4096, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert so.bench_mfma(src.data_ptr(), dst.data_ptr(), 1, 2, stream) == 0
+    torch.cuda.synchronize()
+    got = to_host(dst).reshape(4, 4, 16, 64)  # wave, tile, register, lane
+    op = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(4, 16, 64, 8)
+    lane = np.arange(64)
+    for wv in range(4):
+        # operand set i as a 32 x 16 matrix: lane l holds row l % 32, k = 8 (l / 32) + e
+        def mat(i):
+            m = np.zeros((32, 16))
+            for l in range(64):
+                m[l % 32, 8 * (l // 32): 8 * (l // 32) + 8] = op[wv, i, l]
+            return m
+        A = [mat(i) for i in range(8)]
+        B = [mat(8 + i) for i in range(8)]
+        want = np.zeros((4, 32, 32))
+        for _ in range(2):
+            for m in range(64):
+                want[m % 4] += A[m % 8] @ B[(m // 8 + m) % 8].T
+        for t in range(4):
+            for v in range(16):
+                rows = 8 * (v // 4) + 4 * (lane // 32) + v % 4
+                np.testing.assert_allclose(got[wv, t, v], want[t, rows, lane % 32], rtol=2e-5,
+                                           atol=2e-4)
+    assert so.bench_mfma(src.data_ptr(), dst.data_ptr(), 0, 1, stream) != 0
