@@ -21,6 +21,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <type_traits>
 
 #include "nf4_internal.h"
 
@@ -245,6 +246,37 @@ __device__ __forceinline__ uint32_t slice_codes_any(const float (&f)[E], float c
     return lut.signmag ? slice_codes<E, true>(f, c1, s_lut) : slice_codes<E, false>(f, c1, s_lut);
 }
 
+// Codebook kinds, fixed at compile time in the group kernels so that each
+// kernel holds one slice path: bit 0 a sign-magnitude table (CodeLut::signmag),
+// bit 1 the refined bf16 quotient (CodeLut::refine; fp32 slices keep the
+// division fallback, so the bit is dropped for them).
+template <typename T>
+int cb_kind(const CodeLut &lut) {
+    return (lut.signmag ? 1 : 0) | ((sizeof(T) == 2 && lut.refine) ? 2 : 0);
+}
+
+// slice_codes_any with the codebook kind CB fixed.
+template <int E, int CB>
+__device__ __forceinline__ uint32_t slice_codes_cb(const float (&f)[E], float c1, const float2 *s_lut) {
+    constexpr bool SM = (CB & 1) != 0;
+    if constexpr (E == 8 && (CB & 2) != 0)
+        return slice_codes_refined<SM>(f, c1, s_lut);
+    else
+        return slice_codes<E, SM>(f, c1, s_lut);
+}
+
+// Calls fn(std::integral_constant<int, CB>()) for the codebook kind of lut.
+template <typename T, typename Fn>
+hipError_t with_cb(const CodeLut &lut, Fn &&fn) {
+    const int k = cb_kind<T>(lut);
+    if (k == 1) return fn(std::integral_constant<int, 1>());
+    if constexpr (sizeof(T) == 2) {
+        if (k == 2) return fn(std::integral_constant<int, 2>());
+        if (k == 3) return fn(std::integral_constant<int, 3>());
+    }
+    return fn(std::integral_constant<int, 0>());
+}
+
 // Entry i of the table copies (copy i / kLutEntries, see slice_codes).
 __device__ __forceinline__ float2 lut_copy_entry(const LutEntry &le, int i) {
     return make_float2(le.thr, __int_as_float(le.hi << (4 * (i / kLutEntries))));
@@ -260,58 +292,59 @@ __device__ __forceinline__ float group_value(float c2) {
     return F == kFmtLin8 ? c2 / lin_levels<false>() : c2;
 }
 
-// Double quantization of the group's 256 c1 values held in s_c1 (threads
-// 0..255 each own one block; a larger workgroup's other threads only join
-// the barriers), 8-bit codes in format F.
+// Double quantization of a group's 256 block scales: s_c1 holds them and
+// s_red the maxima of the workgroup's waves (so c2 is their max); threads
+// 0..63 each encode 4 consecutive blocks as one 32-bit store of 8-bit codes
+// in format F.
 template <int T, int F>
-__device__ __forceinline__ void group_dq(const float *s_c1, float *s_red, uint32_t *s_q8,
-                                         uint8_t *absmax_q, float *absmax_scale, int64_t g) {
+__device__ __forceinline__ void group_dq(const float *s_c1, const float *s_red, uint8_t *absmax_q,
+                                         float *absmax_scale, int64_t g) {
     const int t = threadIdx.x;
-    const float c1 = (t < kDqBlock) ? s_c1[t] : 0.0f;
-    const float sc = group_value<F>(wg_max<T>(c1, s_red));
-    if (t < kDqBlock) reinterpret_cast<uint8_t *>(s_q8)[t] = (uint8_t)dq_encode<F, false>(c1, sc);
-    __syncthreads();
-    if (t < kDqBlock / 4) reinterpret_cast<uint32_t *>(absmax_q + g * kDqBlock)[t] = s_q8[t];
+    if (t >= kDqBlock / 4) return;
+    float c2 = s_red[0];
+#pragma unroll
+    for (int i = 1; i < T / 64; ++i) c2 = fmaxf(c2, s_red[i]);
+    const float sc = group_value<F>(c2);
+    const float4 c = reinterpret_cast<const float4 *>(s_c1)[t];
+    const uint32_t q = dq_encode<F, false>(c.x, sc) | (dq_encode<F, false>(c.y, sc) << 8) |
+                       (dq_encode<F, false>(c.z, sc) << 16) | (dq_encode<F, false>(c.w, sc) << 24);
+    reinterpret_cast<uint32_t *>(absmax_q + g * kDqBlock)[t] = q;
     if (t == 0) absmax_scale[g] = sc;
 }
 
-// Full group g of a tensor, by a workgroup of TH threads. Without fused
-// double quantization, `partial` (if set) receives the pairwise sum of the
-// group's 256 block scales (the first levels of the mean offset's sum).
-template <typename T, bool kDQ, int TH, int F>
-__device__ __forceinline__ void quantize_group(
-    const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
-    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
-    const CodeLut &lut, const int64_t g) {
+// LDS of one group in flight: its codes, gathered for 16-byte stores, its
+// 256 block scales and the maxima of the workgroup's waves.
+template <int TH>
+struct GroupLds {
+    u32x4 codes[kGroup / 32];
+    float c1[kDqBlock];
+    float red[TH / 64];
+};
+
+// The table copies of slice_codes in LDS, from the argument block: entry
+// t % kTab for thread t (threads past the table store a duplicate).
+template <int E, int TH>
+__device__ __forceinline__ void store_lut(const LutEntry &le, float2 *s_lut) {
+    constexpr int kTab = E * kLutEntries;
+    static_assert(kTab <= TH, "one table entry per thread");
+    s_lut[threadIdx.x % kTab] = lut_copy_entry(le, threadIdx.x % kTab);
+}
+
+// Codes and block scales of group g, whose weights thread t holds in v
+// (slices t, t + TH, ...). Writes the codes and the block scales to L, the
+// wave maxima too with double quantization, and the block scales to absmax
+// if set. The caller's barrier then publishes L to group_finish.
+template <typename T, bool kDQ, int TH, int CB>
+__device__ __forceinline__ void group_codes(const typename Slice<T>::Vec (&v)[kGroup / Slice<T>::kElems / TH],
+                                            GroupLds<TH> &L, float *__restrict__ absmax,
+                                            const float2 *s_lut, bool keep_c1, const int64_t g) {
     using S = Slice<T>;
     constexpr int E = S::kElems;               // weights per lane slice
     constexpr int LPB = kBlock / E;            // lanes per block
-    constexpr int SLICES = kGroup / E;         // slices per group
-    constexpr int ITERS = SLICES / TH;         // slices per thread
+    constexpr int ITERS = kGroup / E / TH;     // slices per thread
     constexpr int BPI = TH / LPB;              // blocks per iteration
-
-    constexpr int kTab = E * kLutEntries;       // entries of the E table copies
-    static_assert(kTab <= TH, "one table entry per thread");
-    __shared__ float2 s_lut[kTab];
-    __shared__ float s_c1[kDqBlock];
-    __shared__ float s_red[TH / 64];
-    __shared__ uint32_t s_q8[kDqBlock / 4];
-
     const int t = threadIdx.x;
-    const typename S::Vec *src = reinterpret_cast<const typename S::Vec *>(w + g * kGroup);
-
-    // The table comes from the argument block through a vector load: issued
-    // first and stored to LDS after the weight loads are on their way, so its
-    // wait does not cover them.
-    const LutEntry le = lut.e[t % kLutEntries];
-    __builtin_amdgcn_sched_barrier(0);
-    typename S::Vec v[ITERS];
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * TH + t]);
-    // (threads past the table store a duplicate of an entry, unconditionally)
-    s_lut[t % kTab] = lut_copy_entry(le, t % kTab);
-    __syncthreads();
-
+    float mmax = 0.0f;  // max of this thread's block scales
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
         float f[E];
@@ -325,35 +358,78 @@ __device__ __forceinline__ void quantize_group(
         mb = dpp_umax<0x141>(mb);  // row_half_mirror: lanes i <-> 7-i
         if (LPB == 16) mb = dpp_umax<0x140>(mb);  // row_mirror: lanes i <-> 15-i
         const float m = __uint_as_float(mb);
+        mmax = fmaxf(mmax, m);
         const int blk = i * BPI + t / LPB;  // block within the group
         if ((t % LPB) == 0) {
-            if (kDQ || partial) s_c1[blk] = m;
+            if (kDQ || keep_c1) L.c1[blk] = m;
             if (absmax) absmax[g * kDqBlock + blk] = m;
         }
-        const uint32_t packed = slice_codes_any<E>(f, m, s_lut, lut);
-        const int64_t slice = (int64_t)g * SLICES + i * TH + t;
+        const uint32_t packed = slice_codes_cb<E, CB>(f, m, s_lut);
         if (E == 8)
-            reinterpret_cast<uint32_t *>(codes)[slice] = packed;
+            reinterpret_cast<uint32_t *>(L.codes)[i * TH + t] = packed;
         else
-            reinterpret_cast<uint16_t *>(codes)[slice] = (uint16_t)packed;
+            reinterpret_cast<uint16_t *>(L.codes)[i * TH + t] = (uint16_t)packed;
     }
     if (kDQ) {
-        __syncthreads();
-        group_dq<TH, F>(s_c1, s_red, s_q8, absmax_q, absmax_scale, g);
-    } else if (partial) {
-        __syncthreads();
-        const float sum = block256_pairwise_sum(s_c1, s_red);
+        const float wm = wave_max_nonneg(mmax);
+        if ((t & 63) == 0) L.red[t >> 6] = wm;
+    }
+}
+
+// After the barrier that follows group_codes: the group's codes, 16 bytes
+// per thread (each wave one contiguous 1 KiB run), and its double
+// quantization.
+template <bool kDQ, int TH, int F>
+__device__ __forceinline__ void group_finish(const GroupLds<TH> &L, uint8_t *__restrict__ codes,
+                                             uint8_t *__restrict__ absmax_q,
+                                             float *__restrict__ absmax_scale, const int64_t g) {
+    static_assert(kGroup / 32 == TH, "one 16-byte piece of the group's codes per thread");
+    __builtin_nontemporal_store(L.codes[threadIdx.x],
+                                reinterpret_cast<u32x4 *>(codes + g * (kGroup / 2)) + threadIdx.x);
+    if (kDQ) group_dq<TH, F>(L.c1, L.red, absmax_q, absmax_scale, g);
+}
+
+// Full group g of a tensor, by a workgroup of TH threads. Without fused
+// double quantization, `partial` (if set) receives the pairwise sum of the
+// group's 256 block scales (the first levels of the mean offset's sum).
+template <typename T, bool kDQ, int TH, int F, int CB>
+__device__ __forceinline__ void quantize_group(
+    const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
+    uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
+    const CodeLut &lut, const int64_t g) {
+    using S = Slice<T>;
+    constexpr int ITERS = kGroup / S::kElems / TH;
+    __shared__ float2 s_lut[S::kElems * kLutEntries];
+    __shared__ __align__(16) GroupLds<TH> L;
+
+    const int t = threadIdx.x;
+    const typename S::Vec *src = reinterpret_cast<const typename S::Vec *>(w + g * kGroup);
+    // The table comes from the argument block through a vector load: issued
+    // first and stored to LDS after the weight loads are on their way, so its
+    // wait does not cover them.
+    const LutEntry le = lut.e[t % kLutEntries];
+    __builtin_amdgcn_sched_barrier(0);
+    typename S::Vec v[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) v[i] = __builtin_nontemporal_load(&src[i * TH + t]);
+    store_lut<S::kElems, TH>(le, s_lut);
+    __syncthreads();
+    group_codes<T, kDQ, TH, CB>(v, L, absmax, s_lut, partial != nullptr, g);
+    __syncthreads();
+    group_finish<kDQ, TH, F>(L, codes, absmax_q, absmax_scale, g);
+    if (!kDQ && partial) {
+        const float sum = block256_pairwise_sum(L.c1, L.red);
         if (t == 0) partial[g] = sum;
     }
 }
 
 // One workgroup per full group of 16384 weights.
-template <typename T, bool kDQ, int TH, int F>
+template <typename T, bool kDQ, int TH, int F, int CB>
 __global__ __launch_bounds__(TH) void quantize_groups_kernel(
     const T *__restrict__ w, uint8_t *__restrict__ codes, float *__restrict__ absmax,
     uint8_t *__restrict__ absmax_q, float *__restrict__ absmax_scale, float *__restrict__ partial,
     CodeLut lut) {
-    quantize_group<T, kDQ, TH, F>(w, codes, absmax, absmax_q, absmax_scale, partial, lut,
+    quantize_group<T, kDQ, TH, F, CB>(w, codes, absmax, absmax_q, absmax_scale, partial, lut,
                                   (int64_t)blockIdx.x);
 }
 
@@ -428,7 +504,8 @@ __global__ __launch_bounds__(kThreads) void double_quantize_kernel(
 constexpr int kGroupThreads = 512;
 
 // B1 = 64 (and, with double quantization, B2 = 256 without the mean
-// offset): the fused group kernel, 8-bit codes in format F.
+// offset): the fused group kernel, 8-bit codes in format F, one kernel per
+// codebook kind.
 template <typename T, int F>
 hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absmax,
                              uint8_t *absmax_q, float *absmax_scale, const CodeLut &lut,
@@ -436,12 +513,16 @@ hipError_t launch_quantize_t(const T *w, int64_t n, uint8_t *codes, float *absma
     const int64_t full = n / kGroup;
     constexpr int TH = kGroupThreads;
     if (full > 0) {
-        if (absmax_q)
-            quantize_groups_kernel<T, true, TH, F><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
-                w, codes, absmax, absmax_q, absmax_scale, nullptr, lut);
-        else
-            quantize_groups_kernel<T, false, TH, kFmtE4M3><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
-                w, codes, absmax, nullptr, nullptr, partial, lut);
+        with_cb<T>(lut, [&](auto cbc) {
+            constexpr int CB = decltype(cbc)::value;
+            if (absmax_q)
+                quantize_groups_kernel<T, true, TH, F, CB><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
+                    w, codes, absmax, absmax_q, absmax_scale, nullptr, lut);
+            else
+                quantize_groups_kernel<T, false, TH, kFmtE4M3, CB><<<dim3((unsigned)full), dim3(TH), 0, s>>>(
+                    w, codes, absmax, nullptr, nullptr, partial, lut);
+            return hipSuccess;
+        });
     }
     if (n % kGroup)
         quantize_tail_kernel<T, F><<<1, kThreads, 0, s>>>(w, n, full, codes, absmax, absmax_q,
@@ -487,11 +568,11 @@ __device__ __forceinline__ int batch_entry(const QuantBatch &b, uint32_t wg) {
 }
 
 // Full groups of every entry: one workgroup per group, as the group kernel.
-template <typename T, bool kDQ>
+template <typename T, bool kDQ, int CB>
 __global__ __launch_bounds__(kGroupThreads) void quantize_batch_kernel(QuantBatch b, CodeLut lut) {
     const uint32_t wg = blockIdx.x;
     const int k = batch_entry(b, wg);
-    quantize_group<T, kDQ, kGroupThreads, kFmtE4M3>(static_cast<const T *>(b.w[k]), b.codes[k],
+    quantize_group<T, kDQ, kGroupThreads, kFmtE4M3, CB>(static_cast<const T *>(b.w[k]), b.codes[k],
                                                     b.absmax[k], b.q[k], b.sc[k], nullptr, lut,
                                                     (int64_t)(wg - b.first[k]));
 }
@@ -533,10 +614,15 @@ struct BatchLauncher {
         }
         if (tail)
             quantize_batch_tail_kernel<T><<<dim3((unsigned)count), dim3(kThreads), 0, s>>>(b, lut);
-        else if (dq)
-            quantize_batch_kernel<T, true><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
         else
-            quantize_batch_kernel<T, false><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
+            with_cb<T>(lut, [&](auto cbc) {
+                constexpr int CB = decltype(cbc)::value;
+                if (dq)
+                    quantize_batch_kernel<T, true, CB><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
+                else
+                    quantize_batch_kernel<T, false, CB><<<dim3(wgs), dim3(kGroupThreads), 0, s>>>(b, lut);
+                return hipSuccess;
+            });
         const hipError_t e = hipGetLastError();
         if (err == hipSuccess) err = e;
         count = 0;
