@@ -42,6 +42,8 @@ __device__ __forceinline__ void mfma_drain() {
 // outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
 // lgkmcnt left at their no-wait maximum).
 constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// The same with every LDS operation of the wave complete (lgkmcnt 0).
+constexpr int vmcnt_at_most_lds_done(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 
 // Wait states between VALU writes of MFMA operands and the first MFMA.
 __device__ __forceinline__ void valu_to_mfma() {

@@ -644,6 +644,206 @@ void launch_mi(int nt, dim3 grid, const uint16_t *x, int m, const WView &w, uint
     }
 }
 
+// ---- 2 <= m <= 16 with K = 2048 QS (QS = 1, 2, 4): long code runs through LDS
+//
+// The kernel above reads, per load instruction, 64 bytes from each of 16
+// weight rows, which streams HBM well below the rate of long contiguous
+// runs. Here every code load is one row's contiguous 1 KiB, copied straight
+// into LDS (direct-to-LDS), and the 16-row MFMA operands are read from there.
+//
+// A workgroup of 8 waves owns NT tiles of 16 weight rows and walks them in
+// stages: stage s holds tile s / QS, k-range (s % QS) 2048 + [0, 2048) of
+// its 16 rows (16 KiB of codes); wave w loads two of the rows and computes
+// blocks 4w .. 4w + 3 of every stage for all 16 rows, so each wave's k-ranges
+// are fixed and their x stays in registers for the whole kernel. Four stage
+// buffers rotate: a stage's loads are issued three stages before it is
+// computed, and one barrier per stage both publishes its codes and frees the
+// buffer of the stage before. In LDS, 16-byte piece p of stage row r sits at
+// slot p ^ r (each lane of a row load fetches piece lane ^ r), so that the
+// 16 rows' reads of one block hit distinct banks. The block scales travel in
+// a register ring beside the stages. At the end of a tile each wave writes
+// its partial 16 x 16 tile to LDS (two buffers, alternating by tile), and
+// after the next barrier 256 threads add the 8 waves' partials and store y.
+constexpr int kSW = 8;              // waves per workgroup
+constexpr int kSR = 4;              // stage buffers
+constexpr int kStage = 16 * 1024;   // bytes of codes per stage: 16 rows x 1 KiB
+
+template <bool kDQ> struct StageScales;
+template <> struct StageScales<true> {
+    uint32_t q8;  // E4M3 codes of the lane's row, its wave's 4 blocks
+    float c2;
+};
+template <> struct StageScales<false> {
+    f32x4 am;
+};
+
+template <int QS, bool kDQ>
+__global__ __launch_bounds__(64 * kSW) void gemv_staged_kernel(const uint16_t *__restrict__ x, int m, WView w,
+                                                                uint16_t *__restrict__ y, Levels lv, int nt) {
+    constexpr int kOps = 2 + (kDQ ? 2 : 1);  // vector-memory instructions per stage and wave
+    static_assert(kSR % QS == 0, "a ring turn holds whole tiles");
+    __shared__ uint32_t s_tab[256 * 64];                 // lane-private code -> bf16 pair table
+    // the stage buffers as separate arrays, so that the compiler's wait
+    // before an LDS read covers only the direct-to-LDS loads into that buffer
+    __shared__ __align__(16) char s_stage0[kStage];
+    __shared__ __align__(16) char s_stage1[kStage];
+    __shared__ __align__(16) char s_stage2[kStage];
+    __shared__ __align__(16) char s_stage3[kStage];
+    static_assert(kSR == 4, "four stage arrays");
+    __shared__ __align__(16) f32x4_t s_part[2][kSW * 64];
+    auto stage_buf = [&](auto SLOT) -> char * {
+        constexpr int slot = decltype(SLOT)::value;
+        if constexpr (slot == 0) return s_stage0;
+        else if constexpr (slot == 1) return s_stage1;
+        else if constexpr (slot == 2) return s_stage2;
+        else return s_stage3;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t K = w.k, nblk = K / kBlock;
+    const uint32_t half_k = (uint32_t)(K / 2);
+    const int64_t n_base = (int64_t)blockIdx.x * 16 * nt;
+    const int64_t rows = std::min<int64_t>(w.n - n_base, 16 * (int64_t)nt);
+    const int stages = nt * QS;
+
+    const Rsrc none = rsrc(w.codes, 0);
+    const Rsrc cr = rsrc(w.codes + n_base * (K / 2), rows * (K / 2));
+    const Rsrc xr = rsrc(x, (int64_t)m * K * 2);
+    Rsrc qr, sr;
+    if constexpr (kDQ) {
+        qr = rsrc(w.q + n_base * nblk, rows * nblk);
+        sr = rsrc(w.scale, ((w.n * nblk + 255) / 256) * 4);
+    } else {
+        qr = rsrc(w.absmax + n_base * nblk, rows * nblk * 4);
+        sr = none;
+    }
+
+    // x of the wave's blocks: stage position q, block j -> k = 2048 q + 64 (4 wave + j) + 16 g + [0, 16)
+    u32x4 xa[QS][4], xb[QS][4];
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t vo = 2u * (uint32_t)(r * K + 2048 * q + 64 * (4 * wave + j) + 16 * g);
+            xa[q][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo, 0, 0));
+            xb[q][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo + 16u, 0, 0));
+        }
+
+    // Stage s's loads: this wave's two rows of codes into buffer s % kSR, and
+    // the block scales of the lane's row into ring slot s % kSR. Stages past
+    // the last go through the empty descriptor (zeros, no memory traffic), so
+    // every stage issues the same instructions.
+    StageScales<kDQ> ring[kSR];
+    const uint32_t piece = 16u * (uint32_t)lane;
+    auto issue = [&](int s, auto SLOT) {
+        constexpr int slot = decltype(SLOT)::value;
+        const bool live = s < stages;
+        const int t = s / QS, q = s % QS;
+        char *buf = stage_buf(SLOT);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rho = 2 * wave + h;
+            const uint32_t vo = (uint32_t)(16 * t + rho) * half_k + (piece ^ (16u * (uint32_t)rho));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? cr : none, (gemm::lds_void *)(buf + rho * 1024), 16, vo,
+                                                     1024 * q, 0, 0);
+        }
+        const uint32_t blk = (uint32_t)(16 * t + r) * (uint32_t)nblk + 32u * q + 4u * wave;
+        if constexpr (kDQ) {
+            ring[slot].q8 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(live ? qr : none, blk, 0, 0);
+            const uint32_t grp = (uint32_t)((n_base * nblk + blk) >> 8);
+            ring[slot].c2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(live ? sr : none, 4u * grp, 0, 0));
+        } else {
+            ring[slot].am = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? qr : none, 4u * blk, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<kSR - 1>([&](auto JC) { issue(decltype(JC)::value, JC); });
+
+    // The table: word i = e * 64 + lane holds (level[e & 15], level[e >> 4])
+    // as bf16; thread tid writes i = tid + 512 j, entry e = wave + 8 j.
+    {
+        const float lo0 = lv.q[wave], lo1 = lv.q[wave + 8];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) s_tab[tid + 512 * j] = pack_bf16x2((j & 1) ? lo1 : lo0, lv.q[j >> 1]);
+    }
+
+    // fragment offsets of the wave's 4 blocks inside a stage (the same in every stage)
+    uint32_t foff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        foff[j] = (uint32_t)(r * 1024 + 8 * (g & 1)) + 16u * ((uint32_t)(2 * (4 * wave + j) + (g >> 1)) ^ (uint32_t)r);
+    const char *tab = reinterpret_cast<const char *>(s_tab);
+    const uint32_t lane4 = 4u * lane;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc = z;
+
+    // 256 threads: the sum of the 8 waves' partials of tile t (from buffer t % 2)
+    auto reduce = [&](int t) {
+        if (tid < 256) {
+            const int i = tid >> 6, l = tid & 63;
+            const int row = 4 * (l >> 4) + i;
+            const int64_t n = n_base + 16 * t + (l & 15);
+            const float *pp = reinterpret_cast<const float *>(s_part[t & 1]);
+            float v = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kSW; ++u) v += pp[(u * 64 + l) * 4 + i];
+            if (row < m && n < w.n) y[(int64_t)row * w.n + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+        }
+    };
+
+    // (a do-while: stages >= 1, and no branch ahead of the loop that would
+    // let the compiler sink the x loads below the prologue's stage loads)
+    int s0 = 0;
+    do {
+        static_for<kSR>([&](auto PC) {
+            constexpr int p = decltype(PC)::value;
+            constexpr int q = p % QS;
+            const int s = s0 + p;
+            // this wave's loads of stage s have landed once at most the two
+            // stages issued after it are outstanding; the barrier then makes
+            // every wave's rows visible and frees the buffer of stage s - 1.
+            // A plain s_barrier: the fence of __syncthreads would also wait
+            // for the loads of the stages still in flight.
+            __builtin_amdgcn_s_waitcnt(gemm::vmcnt_at_most_lds_done(2 * kOps));
+            __builtin_amdgcn_s_barrier();
+            if (q == 0 && s > 0 && s < stages) reduce(s / QS - 1);
+            issue(s + kSR - 1, std::integral_constant<int, (p + kSR - 1) % kSR>{});
+            if (s < stages) {
+                const char *buf = stage_buf(PC);
+                const StageScales<kDQ> &sc = ring[p];
+                static_for<4>([&](auto JC) {
+                    constexpr int j = decltype(JC)::value;
+                    const gemm::u32x2 d = *reinterpret_cast<const gemm::u32x2 *>(buf + foff[j]);
+                    const u32x4 lo = lookup4(tab, d.x, lane4);
+                    const u32x4 hi = lookup4(tab, d.y, lane4);
+                    f32x4_t pr = mfma(xa[q][j], lo, z);
+                    pr = mfma(xb[q][j], hi, pr);
+                    float scj;
+                    if constexpr (kDQ) scj = __builtin_amdgcn_cvt_f32_fp8((int)sc.q8, j) * sc.c2;
+                    else scj = sc.am[j];
+                    acc += pr * scj;
+                });
+                if (q == QS - 1) {
+                    s_part[(s / QS) & 1][wave * 64 + lane] = acc;
+                    acc = z;
+                }
+            }
+        });
+        s0 += kSR;
+    } while (s0 < stages);
+    __builtin_amdgcn_s_waitcnt(gemm::vmcnt_at_most(0));
+    __syncthreads();
+    reduce(nt - 1);
+}
+
+template <int QS, bool kDQ>
+void launch_staged(dim3 grid, const uint16_t *x, int m, const WView &w, uint16_t *y, int nt, hipStream_t s) {
+    gemv_staged_kernel<QS, kDQ><<<grid, dim3(64 * kSW), 0, s>>>(x, m, w, y, levels(), nt);
+}
+
 }  // namespace
 
 // K at most kMaxK: the staged scale data of a workgroup's rows fits LDS.
@@ -672,6 +872,16 @@ hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint1
         return hipGetLastError();
     }
     const int64_t tiles = (w.n + 15) / 16;
+    if (m >= 2 && (w.k == 2048 || w.k == 4096 || w.k == 8192)) {
+        // stage walk: about one workgroup per CU, each with ceil(tiles / CUs) tiles
+        const int nt = (int)std::max<int64_t>((tiles + cus - 1) / cus, 1);
+        const dim3 grid((unsigned)((tiles + nt - 1) / nt));
+        const int xm = (int)m;
+        if (w.k == 8192) w.q ? launch_staged<4, true>(grid, x, xm, w, y, nt, s) : launch_staged<4, false>(grid, x, xm, w, y, nt, s);
+        else if (w.k == 4096) w.q ? launch_staged<2, true>(grid, x, xm, w, y, nt, s) : launch_staged<2, false>(grid, x, xm, w, y, nt, s);
+        else w.q ? launch_staged<1, true>(grid, x, xm, w, y, nt, s) : launch_staged<1, false>(grid, x, xm, w, y, nt, s);
+        return hipGetLastError();
+    }
     const int nt = (int)std::min<int64_t>(std::max<int64_t>((tiles + cus - 1) / cus, 1), kMaxNT);
     const dim3 grid((unsigned)((tiles + nt - 1) / nt));
     if (m == 1)

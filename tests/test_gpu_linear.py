@@ -100,6 +100,16 @@ CASES = [
     (1, 77, 8192, 0),
     (1, 5000, 8192, 0),
     (1, 640, 6144, 0),
+    # 2 <= m <= 16 with K = 2048, 4096 or 8192 (the LDS-staged decode
+    # kernel): 1, 2 and 4 stages per tile, ragged last tiles, a last
+    # workgroup whose second tile lies past N, and stage walks that end
+    # part-way through the four-stage ring
+    (2, 100, 2048, 0),
+    (5, 16 * 37 + 3, 4096, 0),
+    (16, 16 * 300 + 9, 8192, 0),
+    (3, 16 * 1100, 2048, 0),
+    (7, 16 * 257, 4096, 0),
+    (16, 16 * 700 + 1, 8192, 0),
 ]
 
 
