@@ -230,6 +230,24 @@ nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf4_weight
                                      float lora_scale, void *dx, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* The kernel family that nf4_linear_forward (backward == 0) or
+ * nf4_linear_backward_input (backward != 0) runs for m activation rows, a
+ * weight [n_out x k_in] and adapter rank r. A host-only query; it launches
+ * nothing and needs no device.
+ *   NF4_LINEAR_DECODE    forward only, r == 0, 1 <= m <= 16, k_in % 256 == 0
+ *                        and k_in <= 32768: the decode kernels, which stream
+ *                        the weight once
+ *   NF4_LINEAR_MFMA      n_out % 64 == 0 and r % 8 == 0: the bf16 matrix-core
+ *                        GEMM, its adapter product on the matrix cores too
+ *   NF4_LINEAR_PORTABLE  every other shape: a tiled fp32 kernel without the
+ *                        matrix cores, one to two orders of magnitude slower
+ *                        than the MFMA path at the same size (the same
+ *                        results within the same tolerance)
+ * Returns -1 for a shape the calls reject with NF4_ERR_SIZE (m < 0,
+ * n_out < 1, k_in < 1 or not a multiple of 64, r outside 0..256). */
+typedef enum { NF4_LINEAR_DECODE = 1, NF4_LINEAR_MFMA = 2, NF4_LINEAR_PORTABLE = 3 } nf4_linear_path;
+int32_t nf4_linear_kernel_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r, int32_t backward);
+
 /* Bytes of device workspace that nf4_lora_backward needs: with rp = r rounded
  * up to 64, the bf16 products X.A and dY.B^T ([m x rp] each, rounded up to 256
  * bytes) followed by 8 fp32 partial sums of the largest of [m x rp], [k_in x r]

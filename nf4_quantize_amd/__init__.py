@@ -46,6 +46,7 @@ EXPORTS = (
     "nf4_linear_forward",
     "nf4_linear_forward_noalloc",
     "nf4_linear_backward_input",
+    "nf4_linear_kernel_path",
     "nf4_lora_backward_workspace_size",
     "nf4_lora_backward",
     "nf4_quantize_ex_workspace_size",
@@ -145,6 +146,8 @@ def lib():
     L.nf4_dequantize.restype = ctypes.c_int
     L.nf4_linear_workspace_size.argtypes = [i64, i32]
     L.nf4_linear_workspace_size.restype = ctypes.c_size_t
+    L.nf4_linear_kernel_path.argtypes = [i64, i64, i64, i32, i32]
+    L.nf4_linear_kernel_path.restype = i32
     for name in ("nf4_linear_forward", "nf4_linear_backward_input"):
         fn = getattr(L, name)
         fn.argtypes = [p, i64, ctypes.POINTER(nf4_weight), p, p, i32, f32, p, p,
@@ -262,6 +265,16 @@ def nf4_dequantize(codes, n, out, absmax=None, absmax_q=None, absmax_scale=None,
 
 def nf4_linear_workspace_size(m, r):
     return int(lib().nf4_linear_workspace_size(m, r))
+
+
+LINEAR_PATHS = {1: "decode", 2: "mfma", 3: "portable"}
+
+
+def linear_kernel_path(m, n_out, k_in, r=0, backward=False):
+    """Kernel family of a linear call of this shape (nf4_linear_kernel_path):
+    "decode", "mfma", or "portable" (the fp32 fallback without matrix
+    cores); None for a shape the calls reject."""
+    return LINEAR_PATHS.get(int(lib().nf4_linear_kernel_path(m, n_out, k_in, r, 1 if backward else 0)))
 
 
 def _addr(t):

@@ -455,6 +455,11 @@ NF4_API nf4_status nf4_linear_backward_input(const void *dy, int64_t m, const nf
         workspace, static_cast<hipStream_t>(stream)));
 }
 
+NF4_API int32_t nf4_linear_kernel_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r, int32_t backward) {
+    if (m < 0 || n_out < 1 || k_in < 1 || k_in % kBlock != 0 || r < 0 || r > 256) return -1;
+    return (int32_t)linear_path(m, n_out, k_in, r, backward != 0);
+}
+
 NF4_API size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, int32_t r) {
     if (m < 0 || k_in <= 0 || n_out <= 0 || r <= 0 || r > 256) return 0;
     return nf4::lora_grads_workspace_bytes(m, k_in, n_out, ((int64_t)r + 63) / 64 * 64, r);

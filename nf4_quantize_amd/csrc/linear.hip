@@ -116,11 +116,18 @@ __global__ __launch_bounds__(kThreads) void linear_tiled_kernel(
 
 }  // namespace
 
+nf4_linear_path linear_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r, bool backward) {
+    if (!backward && r == 0 && gemv_supported(m, k_in)) return NF4_LINEAR_DECODE;
+    if (gemm_supported(n_out, r)) return NF4_LINEAR_MFMA;
+    return NF4_LINEAR_PORTABLE;
+}
+
 hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s) {
-    if (r == 0 && gemv_supported(m, w.k_in)) return launch_gemv(x, m, w, y, s);
-    if (gemm_supported(w.n_out, r))
+    const nf4_linear_path path = linear_path(m, w.n_out, w.k_in, r, false);
+    if (path == NF4_LINEAR_DECODE) return launch_gemv(x, m, w, y, s);
+    if (path == NF4_LINEAR_MFMA)
         return launch_gemm_forward(x, m, w, a, b, r, s_lora, y, static_cast<uint16_t *>(workspace), s);
     uint16_t *t = static_cast<uint16_t *>(workspace);
     if (r > 0)
@@ -135,7 +142,7 @@ hipError_t launch_linear_backward_input(const uint16_t *dy, int64_t m, const nf4
                                         const uint16_t *a, const uint16_t *b, int32_t r,
                                         float s_lora, uint16_t *dx, void *workspace,
                                         hipStream_t s) {
-    if (gemm_supported(w.n_out, r))
+    if (linear_path(m, w.n_out, w.k_in, r, true) == NF4_LINEAR_MFMA)
         return launch_gemm_dgrad(dy, m, w, a, b, r, s_lora, dx, static_cast<uint16_t *>(workspace), s);
     uint16_t *u = static_cast<uint16_t *>(workspace);
     if (r > 0)

@@ -109,6 +109,9 @@ size_t merge_workspace(int64_t n_out, int64_t k_in);
 hipError_t launch_merge(const nf4_weight &w, const uint16_t *a, const uint16_t *b, int32_t r,
                         float s_lora, uint8_t *codes_out, float *absmax_out, uint8_t *absmax_q_out,
                         float *absmax_scale_out, void *workspace, hipStream_t s);
+// The kernel family (nf4_linear_path) a linear call of this shape runs;
+// the launchers below dispatch by it.
+nf4_linear_path linear_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r, bool backward);
 hipError_t launch_linear_forward(const uint16_t *x, int64_t m, const nf4_weight &w,
                                  const uint16_t *a, const uint16_t *b, int32_t r, float s_lora,
                                  uint16_t *y, void *workspace, hipStream_t s);

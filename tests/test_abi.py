@@ -172,6 +172,29 @@ def test_workspace_size(L):
     assert nq.nf4_linear_workspace_size(100, 0) == 0
 
 
+def test_linear_kernel_path(L):
+    """Which kernel family a linear shape runs, without a device: the decode
+    kernels only forward with r = 0, 1 <= m <= 16 and K % 256 == 0 up to
+    32768; the MFMA GEMM for N % 64 == 0 and r % 8 == 0; the portable fp32
+    kernel otherwise; -1 for rejected sizes."""
+    p = nq.linear_kernel_path
+    assert p(4, 28672, 8192) == "decode"
+    assert p(16, 28672, 8192) == "decode"
+    assert p(1, 100, 256) == "decode"                 # any N on the decode path
+    assert p(17, 28672, 8192) == "mfma"               # more rows than the decode kernels take
+    assert p(4, 28672, 8192, backward=True) == "mfma"  # the input gradient has no decode path
+    assert p(4, 28672, 8192, r=64) == "mfma"          # an adapter leaves the decode path
+    assert p(16, 4096, 32768 + 256) == "mfma"         # longer rows than the decode kernels take
+    assert p(4096, 8192, 8192, r=64) == "mfma"
+    assert p(37, 100, 192, r=5) == "portable"         # N % 64 != 0
+    assert p(64, 512, 256, r=12) == "portable"        # r % 8 != 0
+    assert p(64, 512, 256, r=12, backward=True) == "portable"
+    assert p(4, 100, 192) == "portable"               # decode-shaped but K % 256 != 0
+    for bad in ((-1, 64, 64, 0), (4, 0, 64, 0), (4, 64, 96, 0), (4, 64, 64, 257), (4, 64, 64, -1)):
+        assert L.nf4_linear_kernel_path(*bad, 0) == -1
+    assert p(4, 64, 96) is None
+
+
 def test_config_surface():
     nq.NF4Config().validate()
     for bad in (dict(quant_type="fp4"), dict(compute_dtype="float32"), dict(blocksize=96),
