@@ -673,7 +673,7 @@ hipError_t launch_quantize_batched_t(const nf4_batch_entry *e, int32_t count, co
 // holds S = U / (64 E) slices of a unit, slice i at i * 64 + lane, so every
 // wave load is one contiguous 1 KiB run as in the group kernel. A block's
 // absmax is a DPP max over its B1 / E lanes, or a whole-wave max.
-template <typename T, int B1>
+template <typename T, int B1, int CB>
 __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
     const T *__restrict__ w, int64_t nunits, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, CodeLut lut) {
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
         }
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const uint32_t packed = slice_codes_any<E>(f[i], m, s_lut, lut);
+            const uint32_t packed = slice_codes_cb<E, CB>(f[i], m, s_lut);
             const int64_t slice = unit * (U / E) + i * 64 + lane;
             if (E == 8)
                 reinterpret_cast<uint32_t *>(codes)[slice] = packed;
@@ -887,8 +887,11 @@ hipError_t launch_blocks(const T *w, int64_t n, uint8_t *codes, float *absmax, c
     if (nunits > 0) {
         const int64_t waves = (nunits + UPW - 1) / UPW;
         const int64_t wgs = (waves + 3) / 4;
-        quantize_blocks_kernel<T, B1><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
-            w, nunits, codes, absmax, lut);
+        with_cb<T>(lut, [&](auto cbc) {
+            quantize_blocks_kernel<T, B1, decltype(cbc)::value><<<dim3((unsigned)wgs), dim3(kThreads), 0, s>>>(
+                w, nunits, codes, absmax, lut);
+            return hipSuccess;
+        });
     }
     const int64_t nb = (n + B1 - 1) / B1;
     const int64_t b0 = nunits * (U / B1);
