@@ -634,7 +634,23 @@ def linear_benches(dev, iters, warmup, g):
     for name in ("linear_fwd_4096x8192x8192_r64", "linear_dgrad_4096x8192x8192_r64"):
         out[name]["hipblaslt_frac"] = (out[name]["TFLOP/s"] /
                                        out["hipblaslt_bf16_4096x8192x8192_reference"]["TFLOP/s"])
-    del X, dY, A, B, Y, dX, ws, Wd, wt
+    # the vendor GEMM on the adapter gradients' four thin products (T = X.A,
+    # U = dY.B^T, X^T.U, T^T.dY; bf16, fp32 accumulation) beside the fused call
+    Bt = B.t().contiguous()
+    Tr, Ur = X @ A, dY @ Bt
+
+    def vendor_lora(i):
+        torch.matmul(X, A, out=Tr)
+        torch.matmul(dY, Bt, out=Ur)
+        X.t() @ Ur
+        Tr.t() @ dY
+
+    ms, pc = time_op(vendor_lora, lin_iters, max(1, warmup // 2))
+    out["hipblaslt_lora_backward_4096x8192x8192_r64_reference"] = {"ms": ms, "p10_p50_p90_ms": pc}
+    out["lora_backward_4096x8192x8192_r64"]["hipblaslt_speedup"] = (
+        ms / out["lora_backward_4096x8192x8192_r64"]["ms"])
+    log(f"hipBLASLt adapter-gradient products: {ms * 1e3:.1f} us")
+    del X, dY, A, B, Y, dX, ws, Wd, wt, Bt, Tr, Ur
     torch.cuda.empty_cache()
     return out
 
