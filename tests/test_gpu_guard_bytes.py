@@ -145,6 +145,8 @@ LINEAR_SHAPES = [
     # m, N, K, r: decode GEMV, the fused GEMM kernels, the portable path
     (1, 320, 512, 0),
     (16, 192, 2048, 0),
+    (3, 16 * 5 + 7, 4096, 0),   # the LDS-staged decode kernel, ragged last tile
+    (2, 50, 8192, 0),
     (37, 320, 512, 8),
     (300, 256, 256, 16),
     (17, 64, 64, 0),
