@@ -763,3 +763,88 @@ def quantization_mse(w, fmt: NF4Format = None, double_quant=True):
     d = dequantize(t, out_dtype=torch.float32)
     return float(((d.double() - w.double()) ** 2).mean())
 
+
+
+# ------------------------------------------------------------ serialization
+
+# The packed storage is its own file format: every part of an NF4Tensor is a
+# tensor of the file, and the shape and storage format go into its metadata.
+# Bytes are written and read back unchanged, so a loaded weight dequantizes to
+# exactly what the saved one did ("QLoRA in Production: 4-bit NormalFloat &
+# Double Quantization Deep Dive", "Step 4: Merging and Inference", keeps the
+# quantized base on disk between training and serving).
+_PARTS = ("codes", "absmax", "absmax_q", "absmax_scale", "absmax_offset")
+_FILE_TAG = "nf4-packed-v1"
+
+
+def _expected_parts(shape, fmt: NF4Format, parts):
+    n = 1
+    for d in shape:
+        n *= d
+    sizes = {"codes": (n + 1) // 2, "absmax": fmt.nblocks(n), "absmax_q": fmt.nblocks(n),
+             "absmax_scale": fmt.ngroups(n), "absmax_offset": 1}
+    dtypes = {"codes": "uint8", "absmax": "float32", "absmax_q": "uint8",
+              "absmax_scale": "float32", "absmax_offset": "float32"}
+    return {p: (sizes[p], dtypes[p]) for p in parts}
+
+
+def save_nf4(path, tensors):
+    """Write the dict {name: NF4Tensor} to the safetensors file `path`.
+    Each present part is copied to host memory as it is; nothing is
+    re-quantized."""
+    import json
+    from safetensors.torch import save_file
+
+    if not tensors:
+        raise ValueError("nothing to save")
+    flat, meta = {}, {}
+    for name, t in tensors.items():
+        if "." in name:
+            raise ValueError(f"tensor name {name!r}: '.' separates a name from its parts")
+        parts = [p for p in _PARTS if getattr(t, p) is not None]
+        for p in parts:
+            flat[f"{name}.{p}"] = getattr(t, p).detach().contiguous().cpu()
+        f = t.fmt
+        meta[name] = {"shape": list(t.shape), "blocksize": f.blocksize,
+                      "dq_blocksize": f.dq_blocksize, "dq_format": f.dq_format,
+                      "mean_offset": bool(f.mean_offset), "codebook": f.codebook,
+                      "parts": parts}
+    save_file(flat, path, metadata={"format": _FILE_TAG, "nf4": json.dumps(meta)})
+
+
+def load_nf4(path, device="cpu"):
+    """Read a file written by save_nf4 into {name: NF4Tensor} on `device`.
+    Raises ValueError when a part is missing or has the wrong size or type
+    for the recorded shape and format."""
+    import json
+    from safetensors import safe_open
+
+    out = {}
+    with safe_open(path, framework="pt", device="cpu") as fh:
+        md = fh.metadata() or {}
+        if md.get("format") != _FILE_TAG:
+            raise ValueError(f"{path}: not an NF4 packed file")
+        meta = json.loads(md["nf4"])
+        keys = set(fh.keys())
+        for name, m in meta.items():
+            fmt = NF4Format(m["blocksize"], m["dq_blocksize"], m["dq_format"],
+                            bool(m["mean_offset"]), m["codebook"])
+            fmt.struct()
+            shape = tuple(int(d) for d in m["shape"])
+            parts = {}
+            for p, (size, dt) in _expected_parts(shape, fmt, m["parts"]).items():
+                key = f"{name}.{p}"
+                if key not in keys:
+                    raise ValueError(f"{path}: {key} is missing")
+                t = fh.get_tensor(key)
+                if t.dim() != 1 or t.numel() != size or str(t.dtype) != f"torch.{dt}":
+                    raise ValueError(f"{path}: {key} is {tuple(t.shape)} {t.dtype}, "
+                                     f"expected ({size},) {dt}")
+                parts[p] = t.to(device)
+            if "codes" not in parts or (("absmax_q" in parts) != ("absmax_scale" in parts)) \
+                    or ("absmax" not in parts and "absmax_q" not in parts):
+                raise ValueError(f"{path}: {name} lacks the parts its scales need")
+            out[name] = NF4Tensor(parts["codes"], parts.get("absmax"), parts.get("absmax_q"),
+                                  parts.get("absmax_scale"), shape, fmt,
+                                  parts.get("absmax_offset"))
+    return out
