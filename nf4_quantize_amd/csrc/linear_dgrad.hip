@@ -68,11 +68,12 @@ struct DgradParams {
     Levels lv;
 };
 
-// A thread's 8 x 8 patch of W for one step: rows 8 jp + i, columns 8 cp .. 8 cp + 7.
+// A thread's 8 x 8 patch of W for one step: rows 8 jp + i, columns 8 cp .. 8 cp + 7,
+// and the scale data of one row of the step (lane l: row l, in the wave's block).
 struct Patch {
     uint32_t c[8];  // code dword of row i (8 columns)
-    uint32_t q[8];  // E4M3 code of c1/c2 of row i's block
-    float s[8];     // c2 (double quantization) or c1
+    uint32_t q;     // E4M3 code of c1/c2 of row `lane`
+    float s;        // c2 (double quantization) or c1 of row `lane`
 };
 
 // 8x8 bf16 transpose within a thread: in[i] holds row i (8 values as 4
@@ -132,7 +133,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     }
 
     // ---- W patches: thread (jp, cp) = (t % 8, t / 8); columns beyond K read
-    // as zero (the descriptors stop at the end of the arrays).
+    // as zero (the descriptors stop at the end of the arrays). The 64 columns
+    // of wave w's patches are block w of the tile, so the wave needs one
+    // scale per row of the step: lane l loads that of row l and the patch
+    // rows take theirs with ds_bpermute (two loads per step, not sixteen).
     // (descriptors are per tile, so uniform; the patch column is in the
     // per-lane offset, pushed out of range for columns beyond K)
     const int jp = t & 7, cp = t >> 3;
@@ -142,32 +146,40 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                           : rsrc(p.absmax + c0 / kBlock, (N * kb_row - c0 / kBlock) * 4);
     const Rsrc s_rs = rsrc(p.c2, p.n_groups * 4);
     const bool col_ok = col < K;
-    uint32_t c_off[8], q_off[8], b_abs[8];
+    uint32_t c_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t jr = 8 * jp + i;  // row within the step
         c_off[i] = col_ok ? (uint32_t)(jr * (K / 2) + 4 * cp) : 0xFFFFFFF0u;
-        q_off[i] = col_ok ? (uint32_t)((jr * kb_row + (cp >> 3)) * (kDQ ? 1 : 4)) : 0xFFFFFFF0u;
-        b_abs[i] = (uint32_t)(jr * kb_row + col / kBlock);
     }
+    // the scale of row `lane` of the step, block w of the tile (out of range,
+    // so zero, for a block beyond K: its patches' weights are then zero)
+    const bool blk_ok = c0 + kBlock * w < K;
+    const uint32_t q_off = blk_ok ? (uint32_t)((lane * kb_row + w) * (kDQ ? 1 : 4)) : 0xFFFFFFF0u;
+    const uint32_t b_abs = (uint32_t)(lane * kb_row + c0 / kBlock + w);
+    auto load_scale = [&](int64_t j0, Patch &pt) {
+        if (kDQ) {
+            pt.q = __builtin_amdgcn_raw_buffer_load_b8(q_rs, q_off, (int)(j0 * kb_row), 0);
+            pt.s = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(s_rs, ((b_abs + (uint32_t)(j0 * kb_row)) >> 8) * 4u, 0, 0));
+        } else {
+            pt.s = __builtin_bit_cast(float,
+                                      __builtin_amdgcn_raw_buffer_load_b32(q_rs, q_off, (int)(j0 * kb_row * 4), 0));
+        }
+    };
     auto load_patch = [&](int64_t s, Patch &pt) {
         const int64_t j0 = s * kBK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; ++i)
             pt.c[i] = __builtin_amdgcn_raw_buffer_load_b32(c_rs, c_off[i], (int)(j0 * (K / 2)), 0);
-            if (kDQ) {
-                pt.q[i] = __builtin_amdgcn_raw_buffer_load_b8(q_rs, q_off[i], (int)(j0 * kb_row), 0);
-                pt.s[i] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               s_rs, ((b_abs[i] + (uint32_t)(j0 * kb_row)) >> 8) * 4u, 0, 0));
-            } else {
-                pt.s[i] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(q_rs, q_off[i], (int)(j0 * kb_row * 4), 0));
-            }
-        }
+        load_scale(j0, pt);
     };
-    auto scale = [&](const Patch &pt, int i) {
-        return kDQ ? __builtin_amdgcn_cvt_f32_fp8((int)pt.q[i], 0) * pt.s[i] : pt.s[i];
+    // c1' of row `lane`; the scale of patch row i comes from lane 8 jp + i
+    auto own_scale = [&](const Patch &pt) {
+        return kDQ ? __builtin_amdgcn_cvt_f32_fp8((int)pt.q, 0) * pt.s : pt.s;
+    };
+    auto row_scale = [&](float own, int i) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (8 * jp + i), __builtin_bit_cast(int, own)));
     };
     // W tile layout: row c (0..255) of 64 contraction values, 128 B, in the
     // tile_seg layout (gemm_common.h); the patch's column e goes to row
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         const char *b_n = wbuf + nxt * kBTile;
         uint32_t rows[8][4];
         uint32_t lq[kLookRing];
-        float sc[8];
+        float sc[8], own = 0.0f;
 #pragma clang loop unroll(full)
         for (int m = 0; m < 128; ++m) {
             const int grp = m / kTN, sub = m % kTN, ks = grp / kTM, i = grp % kTM;
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                 // dY tile s+1 has landed (only this step's patch loads may be
                 // in flight), W tile s+1 is written, and every read of the
                 // buffers step s+1 overwrites is done
-                __builtin_amdgcn_s_waitcnt(vmcnt_at_most(8 * (kDQ ? 3 : 2)));
+                __builtin_amdgcn_s_waitcnt(vmcnt_at_most(8 + (kDQ ? 2 : 1)));
                 __syncthreads();
             }
             // loads spread over the step (the four waves run this schedule in
@@ -247,19 +259,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                                                          (int)(min(s + 1, steps - 1) * (kBK * 2)), 0, 0);
             }
             if (m >= 32 && (m - 32) % 10 == 0 && (m - 32) / 10 < 8) {
-                // patch loads of step s+2, one row per slot
+                // patch loads of step s+2, one row per slot, and with the
+                // first row the scale data
                 const int r8 = (m - 32) / 10;
                 const int64_t j0 = min(s + 2, steps - 1) * kBK;
                 pl.c[r8] = __builtin_amdgcn_raw_buffer_load_b32(c_rs, c_off[r8], (int)(j0 * (K / 2)), 0);
-                if (kDQ) {
-                    pl.q[r8] = __builtin_amdgcn_raw_buffer_load_b8(q_rs, q_off[r8], (int)(j0 * kb_row), 0);
-                    pl.s[r8] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(
-                                   s_rs, ((b_abs[r8] + (uint32_t)(j0 * kb_row)) >> 8) * 4u, 0, 0));
-                } else {
-                    pl.s[r8] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(q_rs, q_off[r8], (int)(j0 * kb_row * 4), 0));
-                }
+                if (r8 == 0) load_scale(j0, pl);
             }
             if (m >= 16 && m < 16 + kTN) bq1[m - 16] = bfrag(b_t, m - 16, 1);
             if (m > kBarrierSlot && m <= kBarrierSlot + kTN) bq0[m - kBarrierSlot - 1] = bfrag(b_n, m - kBarrierSlot - 1, 0);
@@ -279,9 +284,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                 const int u = (m - kLookAhead) / 2, r8 = u / 4, h = u % 4;
                 rows[r8][h] = scale_pair(lq[u % kLookRing], sc[r8]);
             }
+            if (m == 0) own = own_scale(pc);
             if (m % 2 == 0 && m / 2 < 32) {
                 const int u = m / 2, r8 = u / 4, h = u % 4;
-                if (h == 0) sc[r8] = scale(pc, r8);
+                if (h == 0) sc[r8] = row_scale(own, r8);
                 lq[u % kLookRing] = level(pc.c[r8], h);
             }
             if (m == 96) write_patch(rows, nxt);
@@ -304,9 +310,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     __syncthreads();  // table
     {
         uint32_t rows[8][4];
+        const float own = own_scale(pa);
 #pragma unroll
         for (int r8 = 0; r8 < 8; ++r8) {
-            const float s8 = scale(pa, r8);
+            const float s8 = row_scale(own, r8);
 #pragma unroll
             for (int h = 0; h < 4; ++h) rows[r8][h] = scale_pair(level(pa.c[r8], h), s8);
         }

@@ -412,30 +412,34 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
 // ---- one activation row (m == 1): VALU dot products over row-linear loads
 //
 // With a single activation row the MFMA's 16-row A operand is 1/16 used and
-// the 16-row tile makes every load touch 16 weight rows. Here each wave owns
-// a contiguous range of weight rows - a contiguous range of codes - and
-// streams it linearly, 1 KiB per load instruction: in piece p of a row, lane
-// l holds the 16 code bytes of weights k = 2048 p + 32 l + [0, 32), one half
-// of block 32 p + l/2. Code bytes become bf16 level pairs through the same
-// lane-private table, v_dot2c_f32_bf16 multiplies them with the lane's x
-// pairs (16 registers per piece, loaded once), and the half-block sum is
-// scaled by its c1' (one FMA). At the end of a row a wave reduction adds the
-// 64 lanes and lane 0 stores y. Requires K = P * 2048 with P <= 4 (the x
-// registers). With double quantization the workgroup's E4M3 codes and c2
-// values are copied to LDS once, at the start, by direct-to-LDS loads: two
-// small loads per 1 KiB piece had cost 1.5 us of the 25.5 us at
-// 28672 x 8192.
+// the 16-row tile makes every load touch 16 weight rows. Here one wave
+// handles one weight row at a time and streams its codes linearly, 1 KiB per
+// load instruction: in piece p of a row, lane l holds the 16 code bytes of
+// weights k = 2048 p + 32 l + [0, 32), one half of block 32 p + l/2. Wave g
+// of the W waves of the grid takes rows g, g + W, g + 2W, ..., so at any
+// moment the whole chip reads one window of consecutive rows: HBM streams
+// such a sweep faster than the same bytes read as one contiguous region per
+// wave. Code bytes become bf16 level pairs through the lane-private table,
+// v_dot2c_f32_bf16 multiplies them with the lane's x pairs (16 registers per
+// piece, loaded once), and the half-block sum is scaled by its c1' (one
+// FMA). At the end of a row a wave reduction adds the 64 lanes and lane 0
+// stores y. Requires K = P * 2048 with P <= 4 (the x registers). With double
+// quantization a row's E4M3 codes (32 P bytes) arrive with its first piece,
+// one dword per lane, and each piece takes its lanes' codes from there with
+// one ds_bpermute; the row's c2 is one value, as K is a divisor of 256 x 64
+// weights.
 constexpr int kWaves1 = 8;
 constexpr int kRing1 = 4;      // pieces in flight per wave
 constexpr int kPiece = 2048;   // weights per piece: one 1 KiB load instruction
 constexpr int kMaxP1 = 4;      // pieces per row (x registers: 16 per piece)
-constexpr int kQ8Stage1 = 12288;  // staged E4M3 code bytes per workgroup (the grid is sized for it)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool kDQ> struct Piece;
 template <> struct Piece<true> {
     u32x4 c;
+    uint32_t q8w;  // first piece of a row: E4M3 codes of blocks 4 (lane % 8P) .. + 3
+    float c2;      // first piece of a row: the row's c2
 };
 template <> struct Piece<false> {
     u32x4 c;
@@ -460,11 +464,6 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     static_assert(kRing1 % P == 0, "ring must hold whole rows' pieces in phase");
     __shared__ uint32_t s_lds[256 * 64];
     __shared__ float s_lv[16];
-    // with double quantization: the E4M3 codes of the workgroup's rows
-    // (contiguous in memory) and the c2 values of its groups
-    // (whole 64-dword loads: a direct-to-LDS load writes every lane's dword)
-    __shared__ uint32_t s_q8[kDQ ? round64w(kQ8Stage1 / 4) : 1];
-    __shared__ float s_c2[kDQ ? round64w(kQ8Stage1 / 256 + 2) : 1];
     const char *lds = reinterpret_cast<const char *>(s_lds);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -472,29 +471,9 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     const uint32_t lane4 = 4u * lane;
     const int64_t K = w.k, nblk = K / kBlock;
     const int64_t W = (int64_t)gridDim.x * kWaves1, gw = (int64_t)blockIdx.x * kWaves1 + wave;
-    const int64_t r0 = gw * w.n / W, r1 = (gw + 1) * w.n / W;  // this wave's rows
-    const int nrows = (int)(r1 - r0), npieces = nrows * P;
-    // the workgroup's rows (its waves' ranges are consecutive)
-    const int64_t wg0 = (int64_t)blockIdx.x * kWaves1;
-    const int64_t R0 = wg0 * w.n / W, R1 = (wg0 + kWaves1) * w.n / W;
-
-    // Stage the workgroup's scale data first (before any other vector-memory
-    // load, so the wait before the main loop counts only the pieces after it).
-    int64_t g0 = 0;
-    if constexpr (kDQ) {
-        g0 = R0 * nblk / 256;
-        const int64_t g1 = R1 > R0 ? (R1 * nblk - 1) / 256 : g0;
-        const uint32_t qdw = (uint32_t)((R1 - R0) * nblk / 4);  // nblk % 4 == 0 (K % 256 == 0)
-        const Rsrc qsrc = rsrc(w.q + R0 * nblk, (R1 - R0) * nblk);
-        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < qdw; p0 += 64u * kWaves1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qsrc, (gemm::lds_void *)(s_q8 + p0), 4, (p0 + lane) * 4u, 0, 0,
-                                                     0);
-        const uint32_t ng = (uint32_t)(g1 - g0 + 1);
-        const Rsrc csrc = rsrc(w.scale + g0, (int64_t)ng * 4);
-        for (uint32_t p0 = (uint32_t)wave * 64u; p0 < ng; p0 += 64u * kWaves1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(csrc, (gemm::lds_void *)(s_c2 + p0), 4, (p0 + lane) * 4u, 0, 0,
-                                                     0);
-    }
+    // this wave's rows: gw, gw + W, gw + 2W, ...
+    const int nrows = gw < w.n ? (int)((w.n - 1 - gw) / W + 1) : 0;
+    const int npieces = nrows * P;
 
     // x pairs of every piece: x[2048 p + 32 lane + 2 m], m = 0..15
     u32x4 xv[P][4];
@@ -508,17 +487,11 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(2 * (kPiece * pp + 32 * lane) + 16 * i), 0, 0));
     }
 
-    // descriptors over this wave's rows; loads of pieces past the end go
-    // through an empty descriptor (the wait counts then match on every path)
+    // one descriptor per row (no offset grows with the matrix); loads of
+    // pieces past the end go through an empty descriptor (the wait counts
+    // then match on every path)
     const Rsrc none = rsrc(w.codes, 0);
-    const Rsrc cr = rsrc(w.codes + r0 * (K / 2), (int64_t)nrows * (K / 2));
-    Rsrc qr = none;
-    if constexpr (!kDQ) qr = rsrc(w.absmax + r0 * nblk, (int64_t)nrows * nblk * 4);
     const uint32_t half_blk = (uint32_t)(lane >> 1);  // lane's block within a piece
-    // block index of this wave's first row, block 0: within the staged codes
-    // and counted from the first staged group
-    const uint32_t q8_0 = (uint32_t)((r0 - R0) * nblk);
-    const uint32_t flat0 = (uint32_t)(r0 * nblk - g0 * 256);
 
     Piece<kDQ> ring[kRing1];
     auto issue = [&](int j0, auto JC) {
@@ -526,13 +499,20 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
         constexpr int pp = J % P;
         const int j = j0 + J;
         const bool live = j < npieces;
-        const uint32_t row = (uint32_t)(j / P);
+        const int64_t row = gw + (int64_t)(j0 / P + J / P) * W;
         Piece<kDQ> &pc = ring[J % kRing1];
-        pc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(live ? cr : none, 16u * lane,
-                                                                               (int)(1024u * (uint32_t)j), 0));
-        if constexpr (!kDQ) {
-            const uint32_t blk = row * (uint32_t)nblk + 32u * pp + half_blk;  // block, from the wave's first row
-            pc.am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(live ? qr : none, 4u * blk, 0, 0));
+        const Rsrc cr = live ? rsrc(w.codes + row * (K / 2), K / 2) : none;
+        pc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, 16u * lane, 1024 * pp, 0));
+        if constexpr (kDQ) {
+            if constexpr (pp == 0) {
+                const Rsrc qr = live ? rsrc(w.q + row * nblk, nblk) : none;
+                pc.q8w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(qr, 4u * (uint32_t)(lane & (8 * P - 1)), 0, 0);
+                const Rsrc sr = live ? rsrc(w.scale + ((row * nblk) >> 8), 4) : none;
+                pc.c2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 0u, 0, 0));
+            }
+        } else {
+            const Rsrc ar = live ? rsrc(w.absmax + row * nblk, nblk * 4) : none;
+            pc.am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, 4u * (32u * pp + half_blk), 0, 0));
         }
     };
 
@@ -555,13 +535,11 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
         const int e = i >> 6;
         s_lds[i] = pack_bf16x2(s_lv[e & 15], s_lv[e >> 4]);
     }
-    // this wave's scale copies have landed once at most the prologue's piece
-    // loads (issued after them) are outstanding; the barrier publishes every
-    // wave's copies
-    if constexpr (kDQ) __builtin_amdgcn_s_waitcnt(gemm::vmcnt_at_most(kRing1 - 1));
     __syncthreads();
 
     float acc = 0.0f;
+    uint32_t row_q8w = 0;  // the current row's scale data, kept past its ring slot
+    float row_c2 = 0.0f;
     for (int j0 = 0; j0 < npieces; j0 += kRing1) {
         static_for<kRing1>([&](auto JC) {
             constexpr int J = decltype(JC)::value;
@@ -573,14 +551,20 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
             }
             if (j0 + J < npieces) {
                 const Piece<kDQ> &pc = ring[J % kRing1];
-                // all LDS reads of the piece first (the 16 level-pair lookups
-                // and the scale data), then the dot products on two chains
-                uint32_t q8 = 0;
-                float c2 = 0.0f;
+                // the level-pair lookups and the scale first, then the dot
+                // products on two chains
+                float sc;
                 if constexpr (kDQ) {
-                    const uint32_t blk = (uint32_t)((j0 + J) / P) * (uint32_t)nblk + 32u * pp + half_blk;
-                    q8 = reinterpret_cast<const uint8_t *>(s_q8)[q8_0 + blk];
-                    c2 = s_c2[(flat0 + blk) >> 8];
+                    if constexpr (pp == 0) {
+                        row_q8w = pc.q8w;
+                        row_c2 = pc.c2;
+                    }
+                    // block 32 pp + lane/2 sits in byte (lane/2) % 4 of lane 8 pp + lane/8's dword
+                    const uint32_t dw = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                        (int)(4u * (8u * pp + (uint32_t)(lane >> 3))), (int)row_q8w);
+                    sc = __builtin_amdgcn_cvt_f32_fp8((int)(dw >> (8u * (half_blk & 3u))), 0) * row_c2;
+                } else {
+                    sc = pc.am;
                 }
                 u32x4 lv4[4];
 #pragma unroll
@@ -599,13 +583,11 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
                                                                       false);
                     }
                 }
-                float sc;
-                if constexpr (kDQ) sc = __builtin_amdgcn_cvt_f32_fp8((int)q8, 0) * c2;
-                else sc = pc.am;
                 acc = fmaf(part[0] + part[1], sc, acc);
                 if constexpr (pp == P - 1) {
                     const float sum = wave_sum(acc);
-                    if (lane == 0) y[r0 + (j0 + J) / P] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
+                    const int64_t row = gw + (int64_t)(j0 / P + J / P) * W;
+                    if (lane == 0) y[row] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xFFFFu);
                     acc = 0.0f;
                 }
             }
@@ -856,14 +838,10 @@ hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint1
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     if (m == 1 && w.k % kPiece == 0 && w.k / kPiece <= kMaxP1 && w.k / kPiece != 3) {
-        // rows split over the waves of two workgroups per CU
-        // two workgroups per CU, or more when a workgroup's E4M3 codes would
-        // not fit its staging area (the rows split evenly over all waves)
+        // two workgroups per CU (fewer for a short matrix), the rows dealt
+        // round-robin over their waves
         const int p = (int)(w.k / kPiece);
-        const int64_t nblk = w.k / kBlock;
-        const int64_t per_row_wg = (kQ8Stage1 / nblk - 2) / kWaves1 * kWaves1;  // rows per workgroup that fit
-        int64_t g1n = std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1);
-        if (w.q) g1n = std::max<int64_t>(g1n, (w.n + per_row_wg - 1) / per_row_wg);
+        const int64_t g1n = std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1);
         const dim3 grid1((unsigned)std::max<int64_t>(1, g1n));
         if (w.q)
             launch_gemv1<true>(p, grid1, x, w, y, s);

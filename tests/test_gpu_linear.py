@@ -100,6 +100,10 @@ CASES = [
     (1, 77, 8192, 0),
     (1, 5000, 8192, 0),
     (1, 640, 6144, 0),
+    # rows dealt round-robin over the grid's waves: some waves take one row
+    # more than others
+    (1, 16 * 300 + 5, 2048, 0),
+    (1, 9000, 4096, 0),
     # 2 <= m <= 16 with K = 2048, 4096 or 8192 (the LDS-staged decode
     # kernel): 1, 2 and 4 stages per tile, ragged last tiles, a last
     # workgroup whose second tile lies past N, and stage walks that end
