@@ -250,8 +250,9 @@ int32_t nf4_linear_kernel_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r
 
 /* Bytes of device workspace that nf4_lora_backward needs: with rp = r rounded
  * up to 64, the bf16 products X.A and dY.B^T ([m x rp] each, rounded up to 256
- * bytes) followed by 8 fp32 partial sums of the largest of [m x rp], [k_in x r]
- * and [r x n_out]. Returns 0 for invalid sizes. */
+ * bytes), then 8 fp32 partial sums of the larger of 2 x [m x rp] and
+ * [k_in x r] + [r x n_out] (both products, or both gradients, are split at
+ * once). No initialization is needed. Returns 0 for invalid sizes. */
 size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, int32_t r);
 
 /* Gradients of the low-rank adapter of the same linear ([MF] "Gradient
@@ -266,7 +267,8 @@ size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, 
  * bf16 operands; X.A and dY.B^T are rounded to bf16, the sums over the m
  * tokens accumulate in fp32. k_in % 64 == 0, n_out % 64 == 0, r % 8 == 0,
  * 8 <= r <= 256. m == 0 gives zero gradients. workspace: device, 256-byte
- * aligned, >= nf4_lora_backward_workspace_size(m, k_in, n_out, r) bytes. */
+ * aligned, >= nf4_lora_backward_workspace_size(m, k_in, n_out, r) bytes; calls
+ * that overlap in time must not share one. */
 nf4_status nf4_lora_backward(const void *x, const void *dy, int64_t m, int64_t k_in, int64_t n_out,
                              const void *lora_a, const void *lora_b, int32_t r, float lora_scale,
                              void *grad_a, void *grad_b, int32_t grad_dtype, void *workspace,

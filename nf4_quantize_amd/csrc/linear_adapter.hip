@@ -60,8 +60,11 @@ struct AdapterParams {
     float scale;
 };
 
-template <bool kNN>
-__global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p) {
+// kMode 0: Bop is B (input gradient), 1: Bop is A^T (forward), 2: both in one
+// launch, products p0 (forward form) for blockIdx.z < p0.rp / 64 and p1
+// (input-gradient form) above.
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0, AdapterParams p1) {
     // One static object per ring slot, so that the compiler's waits for a
     // direct-to-LDS load cover only reads of its own slot.
     __shared__ __align__(16) char s_x0[kTile], s_x1[kTile], s_x2[kTile], s_x3[kTile];
@@ -85,180 +88,193 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p)
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
 
-    const int t = threadIdx.x, lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int lr = lane & 15, g = lane >> 4;
-    const int64_t m0 = (int64_t)blockIdx.x * kBM;
-    const int cg = blockIdx.z;  // 64-column group of C
-    const int64_t steps = p.klen / kBK;
-    const int64_t per = (steps + p.splits - 1) / p.splits;
-    const int64_t s_lo = min(steps, (int64_t)blockIdx.y * per);
-    const int n = (int)(min(steps, s_lo + per) - s_lo);
-    const int64_t m_rows = min((int64_t)kBM, p.m - m0);
-    const Rsrc none = rsrc(p.a, 0);
+    auto body = [&](const AdapterParams &p, auto NNC, const int cg) {  // cg: 64-column group of C
+        constexpr bool kNN = decltype(NNC)::value;
+        if ((int)blockIdx.y >= p.splits) return;  // (a paired launch sizes y for the larger split)
+        const int t = threadIdx.x, lane = t & 63;
+        const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+        const int lr = lane & 15, g = lane >> 4;
+        const int64_t m0 = (int64_t)blockIdx.x * kBM;
+        const int64_t steps = p.klen / kBK;
+        const int64_t per = (steps + p.splits - 1) / p.splits;
+        const int64_t s_lo = min(steps, (int64_t)blockIdx.y * per);
+        const int n = (int)(min(steps, s_lo + per) - s_lo);
+        const int64_t m_rows = min((int64_t)kBM, p.m - m0);
+        const Rsrc none = rsrc(p.a, 0);
 
-    // Aop tile: wave w moves rows 16w .. 16w+15, 8 rows per load; lane l of
-    // load q fills row 16w + 8q + l/8, physical chunk l % 8, which holds
-    // logical chunk (l % 8) ^ ((row >> 1) & 7). Rows past m read as zeros
-    // (the row is in the range-checked lane offset, K in the scalar offset).
-    const Rsrc x_rs = rsrc(p.a + m0 * p.lda, m_rows * p.lda * 2);
-    uint32_t x_off[2];
+        // Aop tile: wave w moves rows 16w .. 16w+15, 8 rows per load; lane l of
+        // load q fills row 16w + 8q + l/8, physical chunk l % 8, which holds
+        // logical chunk (l % 8) ^ ((row >> 1) & 7). Rows past m read as zeros
+        // (the row is in the range-checked lane offset, K in the scalar offset).
+        const Rsrc x_rs = rsrc(p.a + m0 * p.lda, m_rows * p.lda * 2);
+        uint32_t x_off[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = 16 * w + 8 * q + (lane >> 3);
-        x_off[q] = (uint32_t)(row * p.lda * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
-    }
+        for (int q = 0; q < 2; ++q) {
+            const int row = 16 * w + 8 * q + (lane >> 3);
+            x_off[q] = (uint32_t)(row * p.lda * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        }
 
-    // Bop tile, input gradient: rows c of B, moved like the Aop tile.
-    const int64_t c_rows = max((int64_t)0, min((int64_t)kBC, (int64_t)p.r - (int64_t)cg * kBC));
-    const Rsrc bt_rs = rsrc(p.mat + (int64_t)cg * kBC * p.ldm, kNN ? 0 : c_rows * p.ldm * 2);
-    uint32_t bt_off[2];
+        // Bop tile, input gradient: rows c of B, moved like the Aop tile.
+        const int64_t c_rows = max((int64_t)0, min((int64_t)kBC, (int64_t)p.r - (int64_t)cg * kBC));
+        const Rsrc bt_rs = rsrc(p.mat + (int64_t)cg * kBC * p.ldm, kNN ? 0 : c_rows * p.ldm * 2);
+        uint32_t bt_off[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = 16 * w + 8 * q + (lane >> 3);
-        bt_off[q] = (uint32_t)(row * p.ldm * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
-    }
+        for (int q = 0; q < 2; ++q) {
+            const int row = 16 * w + 8 * q + (lane >> 3);
+            bt_off[q] = (uint32_t)(row * p.ldm * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        }
 
-    // Bop tile, forward: thread (kp = 8w + lane / 8, cc = lane % 8) loads A
-    // rows 2kp and 2kp + 1 of the step, columns 64 cg + 8cc .. + 7 (all
-    // valid or all past r, as r % 8 == 0); each octet of lanes reads one
-    // row's 128 contiguous bytes. A column chunk past r takes the lane offset
-    // num_records, out of range with or without the scalar offset (the
-    // descriptor stays wave-uniform).
-    const int kp = 8 * w + (lane >> 3), cc = lane & 7;
-    const bool cc_live = (int64_t)cg * kBC + 8 * cc < p.r;
-    const int64_t bn_bytes = kNN ? p.klen * p.ldm * 2 : 0;
-    const Rsrc bn_rs = rsrc(p.mat, bn_bytes);
-    const uint32_t bn_off = cc_live ? (uint32_t)((2 * kp * p.ldm + (int64_t)cg * kBC + 8 * cc) * 2)
-                                    : (uint32_t)bn_bytes;
-    const uint32_t bn_off1 = cc_live ? bn_off + (uint32_t)(p.ldm * 2) : bn_off;
-    u32x4 braw[kStages][2];
+        // Bop tile, forward: thread (kp = 8w + lane / 8, cc = lane % 8) loads A
+        // rows 2kp and 2kp + 1 of the step, columns 64 cg + 8cc .. + 7 (all
+        // valid or all past r, as r % 8 == 0); each octet of lanes reads one
+        // row's 128 contiguous bytes. A column chunk past r takes the lane offset
+        // num_records, out of range with or without the scalar offset (the
+        // descriptor stays wave-uniform).
+        const int kp = 8 * w + (lane >> 3), cc = lane & 7;
+        const bool cc_live = (int64_t)cg * kBC + 8 * cc < p.r;
+        const int64_t bn_bytes = kNN ? p.klen * p.ldm * 2 : 0;
+        const Rsrc bn_rs = rsrc(p.mat, bn_bytes);
+        const uint32_t bn_off = cc_live ? (uint32_t)((2 * kp * p.ldm + (int64_t)cg * kBC + 8 * cc) * 2)
+                                        : (uint32_t)bn_bytes;
+        const uint32_t bn_off1 = cc_live ? bn_off + (uint32_t)(p.ldm * 2) : bn_off;
+        u32x4 braw[kStages][2];
 
-    // Loads of this workgroup's step i into ring slot SC (i % kStages): always
-    // issued, through the empty descriptor for steps past the slice.
-    auto issue = [&](int i, auto SC) {
-        const bool live = i < n;
-        const int64_t k0 = (s_lo + (live ? i : 0)) * kBK;
-        // (scalar offsets: uniform by construction, said so for the compiler)
-        const int so_k = __builtin_amdgcn_readfirstlane((int)(k0 * 2));
-        const Rsrc xr = live ? x_rs : none;
-        char *xd = xs(SC) + 16 * w * 128;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(xd + q * 1024), 16, x_off[q], so_k, 0,
-                                                     0);
-        if constexpr (!kNN) {
-            const Rsrc br = live ? bt_rs : none;
-            char *bd = bs(SC) + 16 * w * 128;
+        // Loads of this workgroup's step i into ring slot SC (i % kStages): always
+        // issued, through the empty descriptor for steps past the slice.
+        auto issue = [&](int i, auto SC) {
+            const bool live = i < n;
+            const int64_t k0 = (s_lo + (live ? i : 0)) * kBK;
+            // (scalar offsets: uniform by construction, said so for the compiler)
+            const int so_k = __builtin_amdgcn_readfirstlane((int)(k0 * 2));
+            const Rsrc xr = live ? x_rs : none;
+            char *xd = xs(SC) + 16 * w * 128;
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(bd + q * 1024), 16, bt_off[q], so_k,
-                                                         0, 0);
-        } else {
-            constexpr int s = decltype(SC)::value;
-            const Rsrc br = live ? bn_rs : none;
-            const int so = __builtin_amdgcn_readfirstlane((int)(k0 * p.ldm * 2));
-            braw[s][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off, so, 0));
-            braw[s][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off1, so, 0));
-        }
-    };
-    // Forward: the column pairs of the step in slot SC to its Bop tile.
-    auto write_bn = [&](auto SC) {
-        if constexpr (kNN) {
-            constexpr int s = decltype(SC)::value;
-            char *bd = bs(SC);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(xd + q * 1024), 16, x_off[q], so_k, 0,
+                                                         0);
+            if constexpr (!kNN) {
+                const Rsrc br = live ? bt_rs : none;
+                char *bd = bs(SC) + 16 * w * 128;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = braw[s][0][j >> 1], hi = braw[s][1][j >> 1];
-                const uint32_t d = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-                *reinterpret_cast<uint32_t *>(bd + swz(8 * cc + j, kp >> 2) + 4 * (kp & 3)) = d;
+                for (int q = 0; q < 2; ++q)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(bd + q * 1024), 16, bt_off[q], so_k,
+                                                             0, 0);
+            } else {
+                constexpr int s = decltype(SC)::value;
+                const Rsrc br = live ? bn_rs : none;
+                const int so = __builtin_amdgcn_readfirstlane((int)(k0 * p.ldm * 2));
+                braw[s][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off, so, 0));
+                braw[s][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off1, so, 0));
             }
-        }
-    };
+        };
+        // Forward: the column pairs of the step in slot SC to its Bop tile.
+        auto write_bn = [&](auto SC) {
+            if constexpr (kNN) {
+                constexpr int s = decltype(SC)::value;
+                char *bd = bs(SC);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = braw[s][0][j >> 1], hi = braw[s][1][j >> 1];
+                    const uint32_t d = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                                               : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    *reinterpret_cast<uint32_t *>(bd + swz(8 * cc + j, kp >> 2) + 4 * (kp & 3)) = d;
+                }
+            }
+        };
 
-    // MFMA fragments: wave (wr, wc) owns rows 32 wr .. +31, columns 32 wc .. +31;
-    // tile row 16i + lr, logical chunk 2g + ks.
-    const int wr = w >> 1, wc = w & 1;
-    uint32_t fa[2][2], fb[2][2];
+        // MFMA fragments: wave (wr, wc) owns rows 32 wr .. +31, columns 32 wc .. +31;
+        // tile row 16i + lr, logical chunk 2g + ks.
+        const int wr = w >> 1, wc = w & 1;
+        uint32_t fa[2][2], fb[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
-            fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
-        }
-    f32x4_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // Step i from slot SC; the loads of step i + kStages - 1 go to slot SI.
-    auto step = [&](int i, auto SC, auto SN, auto SI) {
-        // This wave's loads of step i have landed once at most the loads of
-        // the two later steps are outstanding; LDS writes are done too. The
-        // barrier then makes every wave's part of the tiles visible, and all
-        // waves have finished step i - 1, so its slot can be refilled.
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kStages - 2) * kLoads) & ~(0xF << 8));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue(i + kStages - 1, SI);
-        write_bn(SN);  // forward: Bop tile of step i + 1
-        if (i < n) {
-            const char *xa = xs(SC), *xb = bs(SC);
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                u32x4 a[2], b[2];
+                fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
+                fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
+            }
+        f32x4_t acc[2][2];
 #pragma unroll
-                for (int i2 = 0; i2 < 2; ++i2) {
-                    a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
-                    b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // Step i from slot SC; the loads of step i + kStages - 1 go to slot SI.
+        auto step = [&](int i, auto SC, auto SN, auto SI) {
+            // This wave's loads of step i have landed once at most the loads of
+            // the two later steps are outstanding; LDS writes are done too. The
+            // barrier then makes every wave's part of the tiles visible, and all
+            // waves have finished step i - 1, so its slot can be refilled.
+            __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kStages - 2) * kLoads) & ~(0xF << 8));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue(i + kStages - 1, SI);
+            write_bn(SN);  // forward: Bop tile of step i + 1
+            if (i < n) {
+                const char *xa = xs(SC), *xb = bs(SC);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    u32x4 a[2], b[2];
+#pragma unroll
+                    for (int i2 = 0; i2 < 2; ++i2) {
+                        a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
+                        b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+                    }
+#pragma unroll
+                    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[i2]), __builtin_bit_cast(bf16x8_t, b[j]),
+                                acc[i2][j], 0, 0, 0);
                 }
-#pragma unroll
-                for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, a[i2]), __builtin_bit_cast(bf16x8_t, b[j]),
-                            acc[i2][j], 0, 0, 0);
             }
+        };
+
+        issue(0, S0{});
+        issue(1, S1{});
+        issue(2, S2{});
+        write_bn(S0{});
+        for (int i = 0; i < n; i += kStages) {
+            step(i, S0{}, S1{}, S3{});
+            step(i + 1, S1{}, S2{}, S0{});
+            step(i + 2, S2{}, S3{}, S1{});
+            step(i + 3, S3{}, S0{}, S2{});
         }
+        // no direct-to-LDS load may still be in flight when the workgroup ends
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+
+        // D row 4g + q, column lr of each 16 x 16 tile; columns from r to rp are
+        // written as zeros whatever the padding rows of the tiles held.
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t col = (int64_t)cg * kBC + 32 * wc + 16 * j + lr;
+                const bool col_live = col < p.r;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t row = m0 + 32 * wr + 16 * i + 4 * g + q;
+                    if (row >= p.m) continue;
+                    const float v = col_live ? acc[i][j][q] : 0.0f;
+                    if (p.partial)
+                        p.partial[((int64_t)blockIdx.y * p.m + row) * p.rp + col] = v;
+                    else
+                        p.c[row * p.rp + col] = (uint16_t)(pack_bf16x2(v * p.scale, 0.0f) & 0xFFFFu);
+                }
+            }
+
     };
-
-    issue(0, S0{});
-    issue(1, S1{});
-    issue(2, S2{});
-    write_bn(S0{});
-    for (int i = 0; i < n; i += kStages) {
-        step(i, S0{}, S1{}, S3{});
-        step(i + 1, S1{}, S2{}, S0{});
-        step(i + 2, S2{}, S3{}, S1{});
-        step(i + 3, S3{}, S0{}, S2{});
+    if constexpr (kMode == 2) {
+        const int z_nn = (int)(p0.rp / kBC);
+        if ((int)blockIdx.z < z_nn)
+            body(p0, std::true_type{}, (int)blockIdx.z);
+        else
+            body(p1, std::false_type{}, (int)blockIdx.z - z_nn);
+    } else {
+        body(p0, std::integral_constant<bool, kMode == 1>{}, (int)blockIdx.z);
     }
-    // no direct-to-LDS load may still be in flight when the workgroup ends
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-
-    // D row 4g + q, column lr of each 16 x 16 tile; columns from r to rp are
-    // written as zeros whatever the padding rows of the tiles held.
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = (int64_t)cg * kBC + 32 * wc + 16 * j + lr;
-            const bool col_live = col < p.r;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t row = m0 + 32 * wr + 16 * i + 4 * g + q;
-                if (row >= p.m) continue;
-                const float v = col_live ? acc[i][j][q] : 0.0f;
-                if (p.partial)
-                    p.partial[((int64_t)blockIdx.y * p.m + row) * p.rp + col] = v;
-                else
-                    p.c[row * p.rp + col] = (uint16_t)(pack_bf16x2(v * p.scale, 0.0f) & 0xFFFFu);
-            }
-        }
 }
 
 // ---- token sums of the adapter gradients ([MF] "Gradient Computation"):
@@ -282,7 +298,9 @@ struct TokenSumParams {
     float scale;
 };
 
-__global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p) {
+// Workgroups with blockIdx.x < x1 run the sums of p0, the others those of p1
+// (blockIdx.x - x1); one launch then covers both adapter gradients.
+__global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, TokenSumParams p1, int x1) {
     __shared__ __align__(16) char s_p0[kTile], s_p1[kTile], s_q0[kTile], s_q1[kTile];
     auto ps = [&](auto SC) -> char * {
         if constexpr (decltype(SC)::value == 0) return s_p0;
@@ -297,10 +315,14 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p) {
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
 
+    const bool second = (int)blockIdx.x >= x1;
+    const TokenSumParams &p = second ? p1 : p0;
+    const int bx = second ? (int)blockIdx.x - x1 : (int)blockIdx.x;
+    if ((int)blockIdx.y >= p.splits) return;  // (sized for the larger split of the two)
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lr = lane & 15, g = lane >> 4;
-    const int64_t o0 = (int64_t)blockIdx.x * kBM;
+    const int64_t o0 = (int64_t)bx * kBM;
     const int cg = blockIdx.z;
     const int64_t steps = (p.m + kBK - 1) / kBK;
     const int64_t per = (steps + p.splits - 1) / p.splits;
@@ -436,6 +458,7 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p) {
                 }
             }
         }
+
 }
 
 }  // namespace
@@ -445,9 +468,9 @@ bool token_sum_supported(int64_t m, int64_t O, int64_t rp) {
     return O % kBM == 0 && 64 * O * 2 < ((int64_t)1 << 31) && 64 * rp * 2 < ((int64_t)1 << 31) && m >= 0;
 }
 
-hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
-                            int splits, float *partial, void *out, bool f32, bool transposed, float scale,
-                            hipStream_t s) {
+namespace {
+TokenSumParams token_params(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
+                            int splits, float *partial, void *out, bool f32, bool transposed, float scale) {
     TokenSumParams p{};
     p.p = pm;
     p.q = qm;
@@ -461,8 +484,28 @@ hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, i
     p.f32 = f32;
     p.transposed = transposed;
     p.scale = scale;
+    return p;
+}
+}  // namespace
+
+hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
+                            int splits, float *partial, void *out, bool f32, bool transposed, float scale,
+                            hipStream_t s) {
+    const TokenSumParams p = token_params(pm, qm, m, O, rp, r, splits, partial, out, f32, transposed, scale);
     const dim3 grid((unsigned)(O / kBM), (unsigned)p.splits, (unsigned)(rp / kBC));
-    token_sum_kernel<<<grid, kThreads, 0, s>>>(p);
+    token_sum_kernel<<<grid, kThreads, 0, s>>>(p, p, (int)grid.x);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_sum_pair(const TokenSumJob &a, const TokenSumJob &b, int64_t m, int64_t rp, int32_t r,
+                                 bool f32, float scale, hipStream_t s) {
+    const TokenSumParams pa = token_params(a.pm, a.qm, m, a.O, rp, r, a.splits, a.partial, a.out, f32,
+                                           a.transposed, scale);
+    const TokenSumParams pb = token_params(b.pm, b.qm, m, b.O, rp, r, b.splits, b.partial, b.out, f32,
+                                           b.transposed, scale);
+    const int xa = (int)(a.O / kBM);
+    const dim3 grid((unsigned)(xa + b.O / kBM), (unsigned)max(pa.splits, pb.splits), (unsigned)(rp / kBC));
+    token_sum_kernel<<<grid, kThreads, 0, s>>>(pa, pb, xa);
     return hipGetLastError();
 }
 
@@ -473,9 +516,9 @@ bool adapter_down_supported(bool nn, int64_t lda, int64_t klen, int64_t ldm, int
     return ldm <= ((int64_t)1 << 23) && (int64_t)r * ldm * 2 < ((int64_t)1 << 31);
 }
 
-hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_t m, int64_t klen,
-                               const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
-                               float *partial, uint16_t *c, float scale, hipStream_t s) {
+namespace {
+AdapterParams down_params(const uint16_t *aop, int64_t lda, int64_t m, int64_t klen, const uint16_t *mat,
+                          int64_t ldm, int32_t r, int64_t rp, int splits, float *partial, uint16_t *c, float scale) {
     AdapterParams p{};
     p.a = aop;
     p.lda = lda;
@@ -489,11 +532,30 @@ hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_
     p.partial = partial;
     p.c = c;
     p.scale = scale;
+    return p;
+}
+}  // namespace
+
+hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_t m, int64_t klen,
+                               const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
+                               float *partial, uint16_t *c, float scale, hipStream_t s) {
+    const AdapterParams p = down_params(aop, lda, m, klen, mat, ldm, r, rp, splits, partial, c, scale);
     const dim3 grid((unsigned)((m + kBM - 1) / kBM), (unsigned)p.splits, (unsigned)(rp / kBC));
     if (nn)
-        adapter_down_kernel<true><<<grid, kThreads, 0, s>>>(p);
+        adapter_down_kernel<1><<<grid, kThreads, 0, s>>>(p, p);
     else
-        adapter_down_kernel<false><<<grid, kThreads, 0, s>>>(p);
+        adapter_down_kernel<0><<<grid, kThreads, 0, s>>>(p, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_adapter_down_pair(const DownJob &fwd, const DownJob &bwd, int64_t m, int32_t r, int64_t rp,
+                                    float scale, hipStream_t s) {
+    const AdapterParams pa = down_params(fwd.aop, fwd.lda, m, fwd.klen, fwd.mat, fwd.ldm, r, rp, fwd.splits,
+                                         fwd.partial, fwd.c, scale);
+    const AdapterParams pb = down_params(bwd.aop, bwd.lda, m, bwd.klen, bwd.mat, bwd.ldm, r, rp, bwd.splits,
+                                         bwd.partial, bwd.c, scale);
+    const dim3 grid((unsigned)((m + kBM - 1) / kBM), (unsigned)max(pa.splits, pb.splits), (unsigned)(2 * rp / kBC));
+    adapter_down_kernel<2><<<grid, kThreads, 0, s>>>(pa, pb);
     return hipGetLastError();
 }
 

@@ -57,6 +57,20 @@ bool adapter_down_supported(bool nn, int64_t lda, int64_t klen, int64_t ldm, int
 hipError_t launch_adapter_down(bool nn, const uint16_t *aop, int64_t lda, int64_t m, int64_t klen,
                                const uint16_t *mat, int64_t ldm, int32_t r, int64_t rp, int splits,
                                float *partial, uint16_t *c, float scale, hipStream_t s);
+// Both down-projections of the adapter gradients in one launch: T = X.A
+// (fwd, the forward form) and U = dY.B^T (bwd), each with its own split count
+// and partial area (nullptr when not split).
+struct DownJob {
+    const uint16_t *aop;
+    int64_t lda, klen;
+    const uint16_t *mat;
+    int64_t ldm;
+    int splits;
+    float *partial;
+    uint16_t *c;
+};
+hipError_t launch_adapter_down_pair(const DownJob &fwd, const DownJob &bwd, int64_t m, int32_t r, int64_t rp,
+                                    float scale, hipStream_t s);
 
 // Token sums of the adapter gradients (linear_adapter.hip): C[o][j] =
 // sum over the m tokens of P[t][o] * Q[t][j], P [m x O] (O % 64 == 0),
@@ -68,6 +82,18 @@ bool token_sum_supported(int64_t m, int64_t O, int64_t rp);
 hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
                             int splits, float *partial, void *out, bool f32, bool transposed, float scale,
                             hipStream_t s);
+// Two token sums in one launch (dA and dB), each with its own split count and
+// partial area (nullptr when not split: then scale * C goes to out).
+struct TokenSumJob {
+    const uint16_t *pm, *qm;
+    int64_t O;
+    bool transposed;
+    int splits;
+    float *partial;
+    void *out;
+};
+hipError_t launch_token_sum_pair(const TokenSumJob &a, const TokenSumJob &b, int64_t m, int64_t rp, int32_t r,
+                                 bool f32, float scale, hipStream_t s);
 
 // Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
 bool gemm_supported(int64_t n, int32_t r);
@@ -81,8 +107,10 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w,
 // Adapter gradients dA = s X^T (dY B^T) [K x r] and dB = s (X A)^T dY [r x N]
 // (linear_gemm.hip); da or db may be nullptr. Needs K % 64 == 0, N % 64 == 0,
 // r % 8 == 0, r <= 256, and a workspace of lora_grads_workspace_bytes.
+// Layout: T and U (bf16, lora_product_bytes each), then the fp32 partial sums
+// of both down-projections, later of both token sums.
 inline size_t lora_grads_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t rp, int64_t r) {
-    const int64_t most = std::max(m * rp, std::max(k * r, r * n));
+    const int64_t most = std::max(2 * m * rp, k * r + r * n);
     return 2 * lora_product_bytes(m, rp) + (size_t)kSplitMax * (size_t)most * 4u;
 }
 hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,

@@ -6,9 +6,13 @@
 // contraction runs over N, the rows of W.
 //
 // Tile: a workgroup of 4 waves owns 256 rows x 256 columns of dX; wave
-// w = 2 wr + wc owns rows 128 wr .. +127 and columns 128 wc .. +127 as 8 x 8
-// tiles of v_mfma_f32_16x16x32_bf16 (accumulators in AGPRs). A step contracts
-// 64 rows of W (one NF4 block width of dX columns per row). W' is dequantized
+// w = 2 wr + wc owns rows 128 wr .. +127 and columns 128 wc .. +127 as 4 x 4
+// tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs). A step contracts
+// 64 rows of W (one NF4 block width of dX columns per row), in 4 substeps of
+// 16. The 32 x 32 form issues half the MFMAs of the 16 x 16 one for the same
+// work, each hiding about three times the other instructions (see the
+// forward kernel), and the dequantization, transposition and LDS traffic of
+// the W' tile then fit in its shadow. W' is dequantized
 // once per workgroup into an LDS tile, so the 2 x 2 split of the waves costs
 // no extra dequantization; it halves the dY operand reads (each wave reads
 // 128 rows, not 256) for twice the W' operand reads: per step the CU's LDS
@@ -21,6 +25,9 @@
 //    (8 rows of 8 columns), dequantizes it as bf16(q[code] * c1'),
 //    transposes it in registers and writes 8 columns into a double-buffered
 //    LDS tile [column][row]; waves read their operands from there.
+//  - K order: within a step, lane half h covers contraction indices
+//    32 h .. 32 h + 31 (substep ks: 32 h + 8 ks .. + 7) of both operands, so
+//    an operand fragment is one 16-byte chunk of a tile row.
 //  - One barrier per step, at MFMA slot kBarrierSlot: by then this step's
 //    operand reads of both buffers it will overwrite are done, the next dY
 //    tile has landed and the next W tile is written; the slots after it
@@ -32,25 +39,28 @@ namespace {
 
 using namespace gemm;
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 constexpr int kThreads = 256;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kTM = 128 / 16;             // 8 row tiles per wave
-constexpr int kTN = 128 / 16;             // 8 column tiles per wave
+constexpr int kTM = 128 / 32;             // 4 row tiles per wave
+constexpr int kTN = 128 / 32;             // 4 column tiles per wave
+constexpr int kSlots = 4 * kTM * kTN;      // 64 MFMA slots per step (4 substeps)
 constexpr int kATile = kBM * kBK * 2;      // 32 KiB of bf16 dY per step
 constexpr int kBTile = kBN * kBK * 2;      // 32 KiB of bf16 W' per step
 constexpr int kTable = 256 * 32 * 4;       // level-pair table, one copy per half-wave lane
 constexpr int kLds = kTable + 2 * kATile + 2 * kBTile;  // 160 KiB
-constexpr int kFragAhead = 3;              // dY fragments read this many row groups ahead
-constexpr int kLookAhead = 16;             // MFMA slots between a level read and its use
+constexpr int kFragAhead = 8;              // operand reads this many slots before their first use
+constexpr int kLookAhead = 8;              // slots between a level read and its arithmetic
 constexpr int kLookRing = 8;
-// the first slot that reads the next step's dY tile (a row group is kTN slots)
-constexpr int kBarrierSlot = kTN * (2 * kTM - kFragAhead);
-static_assert(2 * kLookRing >= kLookAhead, "level reads in flight exceed the ring");
-static_assert(62 + kLookAhead < 96, "the patch must be finished before it is written");
-static_assert((2 * kTM) % (kFragAhead + 1) == 0, "fragment ring must divide a step");
-static_assert(kTM * kTN * 2 == 128, "128 MFMA slots per step");
-static_assert(32 + 10 * 7 < kBarrierSlot && 96 < kBarrierSlot, "all loads and the W' write of a step before its barrier");
-static_assert(kBarrierSlot + kTN < 128, "next step's first W' operands read within the step");
+constexpr int kPatchWrite = 40;            // first slot of the W' patch transposition and write
+// the first slot that reads the next step's tiles
+constexpr int kBarrierSlot = kSlots - kFragAhead;
+static_assert(kLookRing >= kLookAhead, "level reads in flight exceed the ring");
+static_assert(31 + kLookAhead < kPatchWrite, "the patch must be finished before it is written");
+static_assert(kPatchWrite + 8 <= kBarrierSlot, "the W' write of a step before its barrier");
+static_assert(2 * 7 + 1 < kBarrierSlot && 17 + 3 * 7 < kBarrierSlot, "all loads of a step before its barrier");
+static_assert(kFragAhead == 8, "operand reads: slots 16 ks + {0..4, 8, 12} - 8");
 
 struct DgradParams {
     const uint16_t *dy;     // dY [M x N]
@@ -76,6 +86,10 @@ struct Patch {
     float s;        // c2 (double quantization) or c1 of row `lane`
 };
 
+__device__ __forceinline__ void mfma32(f32x16_t &c, const u32x4 &a, const u32x4 &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // 8x8 bf16 transpose within a thread: in[i] holds row i (8 values as 4
 // dwords, element e in half e & 1 of dword e >> 1), out[e] holds column e.
 __device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], u32x4 (&out)[8]) {
@@ -96,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     extern __shared__ __align__(16) char smem[];
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int lr = lane & 15, g = lane >> 4;
+    const int lr = lane & 31, h = lane >> 5;
 
     // level-pair table at LDS address 0 (no static LDS in this kernel): the
     // fp16 pair of code byte b for copy p at byte 128 b + 4 p. Lane l reads
@@ -196,37 +210,45 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         }
     };
 
-    // ---- MFMA operands: dY tile row 128 wr + 16 i + lr and W tile row
-    // 128 wc + 16 jt + lr, logical chunk 2g + ks (tile_seg layout: such a row
-    // is in segment 16 * (its block) + tile_seg(lr), chunks swizzled by lr & 7)
+    // ---- MFMA operands: lane (lr, h) reads dY tile row 128 wr + 32 i + lr and
+    // W' tile row 128 wc + 32 jt + lr, logical chunk 4 h + ks (tile_seg layout:
+    // such a row is in segment (its 32-row base) + tile_seg(lr), chunks
+    // swizzled by lr & 7)
     const int wr = w >> 1, wc = w & 1;
-    uint32_t frag_off[2], bfrag_off[2];
+    uint32_t afrag_off[4], bfrag_off[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        frag_off[ks] = (128 * wr + tile_seg(lr)) * 128 + 16 * ((2 * g + ks) ^ (lr & 7));
-        bfrag_off[ks] = (128 * wc + tile_seg(lr)) * 128 + 16 * ((2 * g + ks) ^ (lr & 7));
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t in_row = 16u * (uint32_t)((4 * h + ks) ^ (lr & 7));
+        afrag_off[ks] = (uint32_t)(128 * wr + tile_seg(lr)) * 128u + in_row;
+        bfrag_off[ks] = (uint32_t)(128 * wc + tile_seg(lr)) * 128u + in_row;
     }
-    auto afrag = [&](const char *a_t, int idx) {
-        return *reinterpret_cast<const u32x4 *>(a_t + frag_off[idx / kTM] + (idx % kTM) * 2048);
+    auto afrag = [&](const char *a_t, int ks, int i) {
+        return *reinterpret_cast<const u32x4 *>(a_t + afrag_off[ks] + i * 4096);
     };
-    auto bfrag = [&](const char *b_t, int jt, int ks) {
-        return *reinterpret_cast<const u32x4 *>(b_t + bfrag_off[ks] + jt * 2048);
+    auto bfrag = [&](const char *b_t, int ks, int jt) {
+        return *reinterpret_cast<const u32x4 *>(b_t + bfrag_off[ks] + jt * 4096);
     };
 
-    f32x4_t acc[kTM][kTN];
+    f32x16_t acc[kTM][kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16_t{};
 
-    u32x4 af[kFragAhead + 1];
-    u32x4 bq0[kTN], bq1[kTN];  // B operands of halves 0 and 1
+    // operands of substeps with even (index 0) and odd (index 1) ks
+    u32x4 fa[2][kTM], fb[2][kTN];
 
-    // One step s: 128 MFMA slots (row group grp = m / 8 of dY operands, W'
-    // column tile m % 8) with, around them,
-    // the dY tile s+1 DMA, the patch loads of step s+2, the dequantization,
-    // transpose and LDS write of step s+1's patch (from pc), the barrier, and
-    // the first operands of step s+1.
+    // One step s: 64 MFMA slots; slot m issues MFMA (row tile i, column tile
+    // jt) of substep ks = m / 16, i = (m % 16) / 4, jt = m % 4, and around it:
+    //  - the operand reads kFragAhead slots before their first use (slot
+    //    16 ks + jt for B, 16 ks + 4 i for A; the next step's first ones, from
+    //    the other buffers, after the barrier);
+    //  - the dY tile s+1 DMA (part q at slot 2q + 1) and the patch loads of
+    //    step s+2 (row r at slot 17 + 3r, the scale with row 0);
+    //  - the dequantization of step s+1's patch (unit u = 4 r + byte: level
+    //    read at slot u, arithmetic kLookAhead slots later), its transposition
+    //    and LDS write from slot kPatchWrite;
+    //  - the barrier at kBarrierSlot.
     auto step = [&](int64_t s, const Patch &pc, Patch &pl) {
         const int cur = (int)(s & 1), nxt = cur ^ 1;
         const char *a_t = ybuf + cur * kATile;
@@ -236,9 +258,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         uint32_t rows[8][4];
         uint32_t lq[kLookRing];
         float sc[8], own = 0.0f;
+        u32x4 cols[8];
 #pragma clang loop unroll(full)
-        for (int m = 0; m < 128; ++m) {
-            const int grp = m / kTN, sub = m % kTN, ks = grp / kTM, i = grp % kTM;
+        for (int m = 0; m < kSlots; ++m) {
+            const int ks = m / 16, sm = m % 16, i = sm / 4, jt = sm % 4;
             if (m == kBarrierSlot) {
                 // dY tile s+1 has landed (only this step's patch loads may be
                 // in flight), W tile s+1 is written, and every read of the
@@ -246,52 +269,45 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_at_most(8 + (kDQ ? 2 : 1)));
                 __syncthreads();
             }
-            // loads spread over the step (the four waves run this schedule in
-            // step, so bunched loads would meet at the memory pipeline
-            // together): part q of dY tile s+1 at slot 4q + 1, then the patch
-            // row r8 of step s+2 at slot 32 + 10 r8, all before the barrier.
-            // The W' operands of half 1 are read at slots 16 .. 23 (used from
-            // slot 64), those of the next step's half 0 right after the barrier.
-            if (m % 4 == 1 && m / 4 < 8) {
-                const int q = m / 4;
+            // operand reads for slot m + kFragAhead
+            {
+                const int tm = m + kFragAhead, tks = (tm / 16) % 4, tsm = tm % 16;
+                const char *at = tm < kSlots ? a_t : a_n;
+                const char *bt = tm < kSlots ? b_t : b_n;
+                if (tsm < 4) fb[tks & 1][tsm] = bfrag(bt, tks, tsm);
+                if (tsm % 4 == 0) fa[tks & 1][tsm / 4] = afrag(at, tks, tsm / 4);
+            }
+            if (m % 2 == 1 && m / 2 < 8) {
+                const int q = m / 2;
                 char *dst = ybuf + nxt * kATile + (64 * w) * 128;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(y_rs, (lds_void *)(dst + q * 1024), 16, a_off[q],
                                                          (int)(min(s + 1, steps - 1) * (kBK * 2)), 0, 0);
             }
-            if (m >= 32 && (m - 32) % 10 == 0 && (m - 32) / 10 < 8) {
+            if (m >= 17 && (m - 17) % 3 == 0 && (m - 17) / 3 < 8) {
                 // patch loads of step s+2, one row per slot, and with the
                 // first row the scale data
-                const int r8 = (m - 32) / 10;
+                const int r8 = (m - 17) / 3;
                 const int64_t j0 = min(s + 2, steps - 1) * kBK;
                 pl.c[r8] = __builtin_amdgcn_raw_buffer_load_b32(c_rs, c_off[r8], (int)(j0 * (K / 2)), 0);
                 if (r8 == 0) load_scale(j0, pl);
             }
-            if (m >= 16 && m < 16 + kTN) bq1[m - 16] = bfrag(b_t, m - 16, 1);
-            if (m > kBarrierSlot && m <= kBarrierSlot + kTN) bq0[m - kBarrierSlot - 1] = bfrag(b_n, m - kBarrierSlot - 1, 0);
-            // dY fragments: this step's before the barrier, the next step's
-            // first ones after it
-            if (sub == 0) {
-                u32x4 &dst = af[(grp + kFragAhead) % (kFragAhead + 1)];
-                if (grp + kFragAhead < 2 * kTM)
-                    dst = afrag(a_t, grp + kFragAhead);
-                else
-                    dst = afrag(a_n, grp + kFragAhead - 2 * kTM);
-            }
-            // patch of step s+1: unit u = 4 r + h is code byte h of row r; its
-            // level read at slot 2u, its arithmetic kLookAhead slots later
-            // (before the read that reuses its ring entry)
-            if (m >= kLookAhead && (m - kLookAhead) % 2 == 0 && (m - kLookAhead) / 2 < 32) {
-                const int u = (m - kLookAhead) / 2, r8 = u / 4, h = u % 4;
-                rows[r8][h] = scale_pair(lq[u % kLookRing], sc[r8]);
+            // patch of step s+1
+            if (m >= kLookAhead && m - kLookAhead < 32) {
+                const int u = m - kLookAhead, r8 = u / 4, hb = u % 4;
+                rows[r8][hb] = scale_pair(lq[u % kLookRing], sc[r8]);
             }
             if (m == 0) own = own_scale(pc);
-            if (m % 2 == 0 && m / 2 < 32) {
-                const int u = m / 2, r8 = u / 4, h = u % 4;
-                if (h == 0) sc[r8] = row_scale(own, r8);
-                lq[u % kLookRing] = level(pc.c[r8], h);
+            if (m < 32) {
+                const int u = m, r8 = u / 4, hb = u % 4;
+                if (hb == 0) sc[r8] = row_scale(own, r8);
+                lq[u % kLookRing] = level(pc.c[r8], hb);
             }
-            if (m == 96) write_patch(rows, nxt);
-            mfma(acc[i][sub], af[grp % (kFragAhead + 1)], ks ? bq1[sub] : bq0[sub]);
+            if (m == kPatchWrite) transpose8x8(rows, cols);
+            if (m >= kPatchWrite && m < kPatchWrite + 8) {
+                const int e = m - kPatchWrite, c = 8 * cp + e;
+                *reinterpret_cast<u32x4 *>(wbuf + nxt * kBTile + tile_seg(c) * 128 + 16 * (jp ^ (c & 7))) = cols[e];
+            }
+            mfma32(acc[i][jt], fa[ks & 1][i], fb[ks & 1][jt]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -315,15 +331,16 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
         for (int r8 = 0; r8 < 8; ++r8) {
             const float s8 = row_scale(own, r8);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) rows[r8][h] = scale_pair(level(pa.c[r8], h), s8);
+            for (int hb = 0; hb < 4; ++hb) rows[r8][hb] = scale_pair(level(pa.c[r8], hb), s8);
         }
         write_patch(rows, 0);
     }
     __syncthreads();  // W tile 0
+    // the operands of step 0's first kFragAhead slots (slot m < 8: ks 0)
 #pragma unroll
-    for (int f = 0; f < kFragAhead; ++f) af[f] = afrag(ybuf, f);
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) bq0[j] = bfrag(wbuf, j, 0);
+    for (int jt = 0; jt < kTN; ++jt) fb[0][jt] = bfrag(wbuf, 0, jt);
+    fa[0][0] = afrag(ybuf, 0, 0);
+    fa[0][1] = afrag(ybuf, 0, 1);
     valu_to_mfma();
 
     // ---- main loop: step s consumes the patch of s+1 and loads that of s+2
@@ -337,8 +354,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     __syncthreads();
 
     // ---- adapter segment: + U' . A^T over rp / 64 steps (not pipelined).
-    // B operand of lane (lr, g), tile jt, half ks: A[c][k] for 8 consecutive
-    // k = 64 sa + 16 g + 8 ks + e (rows of A are contiguous in k).
+    // B operand of lane (lr, h), tile jt, substep ks: A[c][k] for the 8
+    // consecutive k = 64 sa + 32 h + 8 ks + e (rows of A are contiguous in k).
     if (p.u != nullptr) {
         const Rsrc u_rs = rsrc(p.u + m0 * p.rp, m_rows * p.rp * 2);
         uint32_t u_off[8];
@@ -354,28 +371,30 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
             for (int q = 0; q < 8; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(u_rs, (lds_void *)(dst + q * 1024), 16, u_off[q],
                                                          (int)(sa * (kBK * 2)), 0, 0);
+            u32x4 ba[4][kTN];
 #pragma unroll
             for (int jt = 0; jt < kTN; ++jt) {
-                const int64_t c = c0 + 128 * wc + 16 * jt + lr;
+                const int64_t c = c0 + 128 * wc + 32 * jt + lr;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int64_t k = 64 * sa + 16 * g + 8 * ks;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int64_t k = 64 * sa + 32 * h + 8 * ks;
                     u32x4 v = u32x4{0, 0, 0, 0};
                     if (c < K && k < p.r) v = *reinterpret_cast<const u32x4 *>(p.a + c * p.r + k);
-                    (ks ? bq1[jt] : bq0[jt]) = v;
+                    ba[ks][jt] = v;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             valu_to_mfma();
 #pragma unroll
-            for (int idx = 0; idx < 2 * kTM; ++idx) {
-                const int ks = idx / kTM, i = idx % kTM;
-                const u32x4 a = afrag(ybuf, idx);
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int jt = 0; jt < kTN; ++jt) mfma(acc[i][jt], a, ks ? bq1[jt] : bq0[jt]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                for (int i = 0; i < kTM; ++i) {
+                    const u32x4 av = afrag(ybuf, ks, i);
+#pragma unroll
+                    for (int jt = 0; jt < kTN; ++jt) mfma32(acc[i][jt], av, ba[ks][jt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             mfma_drain();
             __syncthreads();
         }
@@ -385,23 +404,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dgrad_kernel(DgradParams p) {
     mfma_drain();
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
-        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
-                     "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
     __syncthreads();
     {
         // the wave's 128 x 128 bf16 block through LDS: row stride 256 B,
-        // 16-byte chunks XOR-swizzled by row, then 16-byte stores along rows
+        // 16-byte chunks XOR-swizzled by row, then 16-byte stores along rows.
+        // Accumulator v of tile (i, jt): row 32 i + 8 (v / 4) + 4 h + v % 4,
+        // column 32 jt + lr.
         char *const ep = smem + w * 32768;
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int row = 16 * i + 4 * g + q, cc = 16 * j + lr;
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3), cc = 32 * j + lr;
                     const int chunk = (cc >> 3) ^ ((row >> 2) & 15);
                     *reinterpret_cast<uint16_t *>(ep + row * 256 + chunk * 16 + (cc & 7) * 2) =
-                        (uint16_t)(pack_bf16x2(acc[i][j][q], 0.0f) & 0xFFFFu);
+                        (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu);
                 }
         __syncthreads();
         const int64_t rw = m0 + 128 * wr, colw = c0 + 128 * wc;

@@ -483,10 +483,9 @@ int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 
 // out[i] = scale * sum over z of part[z * count + i], rounded to bf16 or kept
 // fp32, 4 elements per thread (count is a multiple of 4).
-template <bool kF32 = false>
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ part, int splits,
-                                                              int64_t count, float scale, void *__restrict__ out) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+template <bool kF32>
+__device__ __forceinline__ void reduce_partials_at(const float *__restrict__ part, int splits, int64_t count,
+                                                   float scale, void *__restrict__ out, int64_t i) {
     if (i >= count) return;
     f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
     for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4 *>(part + z * count + i);
@@ -498,6 +497,37 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
         o.y = pack_bf16x2(scale * acc[2], scale * acc[3]);
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + i) = o;
     }
+}
+
+template <bool kF32 = false>
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ part, int splits,
+                                                              int64_t count, float scale, void *__restrict__ out) {
+    reduce_partials_at<kF32>(part, splits, count, scale, out, ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4);
+}
+
+// Two such passes in one launch: workgroups below b1 take job a, the others job b.
+struct ReduceJob {
+    const float *part;
+    int splits;
+    int64_t count;  // 0: nothing to add
+    void *out;
+};
+template <bool kF32>
+__global__ __launch_bounds__(256) void reduce_partials_pair_kernel(ReduceJob a, ReduceJob b, int64_t b1,
+                                                                   float scale) {
+    const bool second = (int64_t)blockIdx.x >= b1;
+    const ReduceJob &j = second ? b : a;
+    const int64_t blk = second ? (int64_t)blockIdx.x - b1 : (int64_t)blockIdx.x;
+    reduce_partials_at<kF32>(j.part, j.splits, j.count, scale, j.out, (blk * 256 + threadIdx.x) * 4);
+}
+hipError_t reduce_pair(bool f32, const ReduceJob &a, const ReduceJob &b, float scale, hipStream_t s) {
+    const int64_t ba = (a.count / 4 + 255) / 256, bb = (b.count / 4 + 255) / 256;
+    if (ba + bb == 0) return hipSuccess;
+    if (f32)
+        reduce_partials_pair_kernel<true><<<dim3((unsigned)(ba + bb)), 256, 0, s>>>(a, b, ba, scale);
+    else
+        reduce_partials_pair_kernel<false><<<dim3((unsigned)(ba + bb)), 256, 0, s>>>(a, b, ba, scale);
+    return hipGetLastError();
 }
 
 // Adapter down-projection C[m x rp] = s * Aop . Bop^T (bf16) into the start of
@@ -626,6 +656,34 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
     float *const part = reinterpret_cast<float *>(base + 2 * lora_product_bytes(m, rp));
     const Levels lv = levels();
     hipError_t e = hipSuccess;
+    const int64_t msteps = round64(m) / kBK;
+    auto split_count = [](int64_t tiles, int64_t steps, int64_t target) {
+        const int sp = (int)min((int64_t)kSplitMax, max((int64_t)1, (target + tiles - 1) / tiles));
+        return (int)min((int64_t)sp, max((int64_t)1, steps));
+    };
+    if (m > 0 && da && db && adapter_down_supported(true, K, K, r, r) && adapter_down_supported(false, N, N, N, r) &&
+        token_sum_supported(m, K, rp) && token_sum_supported(m, N, rp)) {
+        // Four launches: both down-projections (T = X.A, U = dY.B^T), their
+        // split sums, both token sums (dA, dB), their split sums.
+        const int64_t mt = (m + 63) / 64, ct = rp / 64;
+        const int sT = split_count(mt * ct, K / kBK, 512), sU = split_count(mt * ct, N / kBK, 512);
+        float *const part_u = part + (int64_t)sT * m * rp;
+        const DownJob jt{x, K, K, a, r, sT, sT > 1 ? part : nullptr, T};
+        const DownJob ju{dy, N, N, b, N, sU, sU > 1 ? part_u : nullptr, U};
+        e = launch_adapter_down_pair(jt, ju, m, r, rp, 1.0f, s);
+        if (e != hipSuccess) return e;
+        e = reduce_pair(false, ReduceJob{part, sT, sT > 1 ? m * rp : 0, T},
+                        ReduceJob{part_u, sU, sU > 1 ? m * rp : 0, U}, 1.0f, s);
+        if (e != hipSuccess) return e;
+        const int sA = split_count((K / 64) * ct, msteps, 1024), sB = split_count((N / 64) * ct, msteps, 1024);
+        float *const part_b = part + (int64_t)sA * K * r;
+        const TokenSumJob ja{x, U, K, false, sA, sA > 1 ? part : nullptr, da};
+        const TokenSumJob jb{dy, T, N, true, sB, sB > 1 ? part_b : nullptr, db};
+        e = launch_token_sum_pair(ja, jb, m, rp, r, f32_out, s_lora, s);
+        if (e != hipSuccess) return e;
+        return reduce_pair(f32_out, ReduceJob{part, sA, sA > 1 ? K * r : 0, da},
+                           ReduceJob{part_b, sB, sB > 1 ? (int64_t)r * N : 0, db}, s_lora, s);
+    }
     if (m > 0) {
         if (db) {
             e = lora_down<BF16_NN>(bf16_segment(x, K, K, a, r, K, r), m, rp, 1.0f, T, lv, s, part);

@@ -113,3 +113,33 @@ def test_lora_grads_qlora_shape_sampled(dev):
     eb, _ = rel_err_metric(host_f32(gb)[:, cols], rb)
     log(f"  dA err {ea:.3e}, dB err {eb:.3e}")
     assert ea <= TOL and eb <= TOL
+
+
+@pytest.mark.parametrize("m,k,n,r", [(1000, 128, 640, 24), (300, 1024, 512, 40), (1, 64, 64, 8)])
+def test_lora_grads_reused_dirty_workspace(dev, m, k, n, r):
+    """The workspace holds the products X.A, dY.B^T and the split partial
+    sums of both products, then of both gradients, at once: a workspace full
+    of non-zero bytes, used by two calls in a row, gives the same gradients
+    both times, equal to those of a fresh workspace and within the tolerance
+    of the oracle."""
+    import torch
+
+    log(f"lora grads, reused dirty workspace m={m} K={k} N={n} r={r}")
+    x, dy, a, b = case(40 + m, m, k, n, r)
+    args = (to_dev(x, dev), to_dev(dy, dev), to_dev(a, dev), to_dev(b, dev), 2.0)
+    size = nq.nf4_lora_backward_workspace_size(m, k, n, r)
+    ws = torch.full((size,), 0x7F, dtype=torch.uint8, device=dev)
+    out = []
+    for _ in range(2):
+        ga = torch.empty((k, r), dtype=torch.float32, device=dev)
+        gb = torch.empty((r, n), dtype=torch.float32, device=dev)
+        nq.lora_backward(*args, grad_a=ga, grad_b=gb, workspace=ws)
+        out.append((ga, gb))
+    fa, fb = nq.lora_backward(*args)
+    torch.cuda.synchronize()
+    for ga, gb in out:
+        assert torch.equal(ga.view(torch.int32), fa.view(torch.int32))
+        assert torch.equal(gb.view(torch.int32), fb.view(torch.int32))
+    ra, rb = oracle.lora_grads(x, dy, a, b, 2.0)
+    assert rel_err_metric(host_f32(fa), ra)[0] <= TOL
+    assert rel_err_metric(host_f32(fb), rb)[0] <= TOL
