@@ -848,3 +848,91 @@ def load_nf4(path, device="cpu"):
                                   parts.get("absmax_scale"), shape, fmt,
                                   parts.get("absmax_offset"))
     return out
+
+
+# ------------------------------------------------------- autograd integration
+
+# The QLoRA linear as a torch autograd function ("QLoRA: Mathematical
+# Foundations of 4-Bit NormalFloat Quantization, Double Quantization, and
+# Paged Optimizers", "Forward Pass Computation" and "Gradient Computation"):
+# forward Y = X W'^T + s (X A) B with W' the dequantized frozen base, backward
+# dX from nf4_linear_backward_input and dA, dB from nf4_lora_backward. The base
+# gets no gradient. Every product runs in the library's kernels; this layer
+# only reshapes and routes tensors.
+def _autograd_function():
+    import torch
+
+    class NF4LoRALinearFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, lora_a, lora_b, weight, lora_scale):
+            lead = x.shape[:-1]
+            x2 = x.reshape(-1, x.shape[-1]).contiguous()
+            y = nf4_linear_forward(x2, weight, lora_a, lora_b, lora_scale)
+            ctx.save_for_backward(x2, lora_a, lora_b)
+            ctx.weight, ctx.lora_scale, ctx.lead = weight, lora_scale, lead
+            return y.reshape(*lead, y.shape[-1])
+
+        @staticmethod
+        def backward(ctx, dy):
+            x2, lora_a, lora_b = ctx.saved_tensors
+            dy2 = dy.reshape(-1, dy.shape[-1]).to(torch.bfloat16).contiguous()
+            dx = da = db = None
+            if ctx.needs_input_grad[0]:
+                dx = nf4_linear_backward_input(dy2, ctx.weight, lora_a, lora_b, ctx.lora_scale)
+                dx = dx.reshape(*ctx.lead, dx.shape[-1])
+            want_a, want_b = ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+            if want_a or want_b:
+                da, db = nf4_lora_backward(x2, dy2, lora_a, lora_b, ctx.lora_scale, grad_dtype=lora_a.dtype,
+                                           grad_a=want_a, grad_b=want_b)
+            return dx, da, db, None, None
+
+    return NF4LoRALinearFunction
+
+
+_FN = None
+
+
+def nf4_lora_linear(x, weight: NF4Tensor, lora_a, lora_b, lora_scale=1.0):
+    """Differentiable QLoRA linear: x bf16 [..., K], weight NF4 [N x K] (frozen),
+    lora_a bf16 [K x r], lora_b bf16 [r x N]; returns bf16 [..., N]. Gradients
+    flow to x, lora_a and lora_b."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    return _FN.apply(x, lora_a, lora_b, weight, float(lora_scale))
+
+
+def make_lora_linear_module():
+    """torch.nn.Module class of a QLoRA linear layer (created on first use so
+    that importing this package does not import torch)."""
+    import math
+
+    import torch
+
+    class NF4LoRALinear(torch.nn.Module):
+        """A linear layer whose weight is stored in NF4 (+ double quantization)
+        and frozen, with a trainable low-rank adapter: y = x W'^T + (alpha / r)
+        (x A) B. A starts random (Kaiming-uniform bound), B at zero, so the
+        layer starts as the quantized base alone."""
+
+        def __init__(self, weight, r=64, alpha=16.0, generator=None):
+            super().__init__()
+            if not isinstance(weight, NF4Tensor):
+                weight = quantize(weight.to(torch.bfloat16).contiguous())
+            n_out, k_in = weight.shape
+            dev = weight.codes.device
+            self.weight = weight
+            self.r, self.scale = r, float(alpha) / r
+            bound = 1.0 / math.sqrt(k_in)
+            a = (torch.rand((k_in, r), generator=generator, device=dev) * 2 - 1) * bound
+            self.lora_a = torch.nn.Parameter(a.to(torch.bfloat16))
+            self.lora_b = torch.nn.Parameter(torch.zeros((r, n_out), dtype=torch.bfloat16, device=dev))
+
+        def forward(self, x):
+            return nf4_lora_linear(x, self.weight, self.lora_a, self.lora_b, self.scale)
+
+        def merged(self):
+            """The adapter merged into the base and re-quantized (nf4_merge_lora)."""
+            return merge_lora(self.weight, self.lora_a.detach(), self.lora_b.detach(), self.scale)
+
+    return NF4LoRALinear
