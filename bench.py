@@ -650,7 +650,32 @@ def linear_benches(dev, iters, warmup, g):
     out["lora_backward_4096x8192x8192_r64"]["hipblaslt_speedup"] = (
         ms / out["lora_backward_4096x8192x8192_r64"]["ms"])
     log(f"hipBLASLt adapter-gradient products: {ms * 1e3:.1f} us")
-    del X, dY, A, B, Y, dX, ws, Wd, wt, Bt, Tr, Ur
+    # one QLoRA training step of the linear (forward, input gradient, adapter
+    # gradients) against the same step of a 16-bit LoRA linear on the vendor
+    # GEMM (bf16 weight already in memory): the per-step cost of the 4-bit base
+    # that the pages put at 20-40% (context only)
+    At = A.t().contiguous()
+
+    def lora16_step(i):
+        torch.matmul(X, Wd.t(), out=Y)
+        torch.matmul(X, A, out=Tr)
+        Y.addmm_(Tr, B, alpha=s)
+        torch.matmul(dY, Wd, out=dX)
+        torch.matmul(dY, Bt, out=Ur)
+        dX.addmm_(Ur, At, alpha=s)
+        X.t() @ Ur
+        Tr.t() @ dY
+
+    ms16, pc16 = time_op(lora16_step, lin_iters, max(1, warmup // 2))
+    q_ms = sum(out[k]["ms"] for k in ("linear_fwd_4096x8192x8192_r64", "linear_dgrad_4096x8192x8192_r64",
+                                      "lora_backward_4096x8192x8192_r64"))
+    out["qlora_training_step_4096x8192x8192_r64"] = {
+        "ms": q_ms, "parts": "linear forward + input gradient + adapter gradients (each timed above)",
+        "lora16_vendor_ms": ms16, "lora16_p10_p50_p90_ms": pc16,
+        "lora16": "bf16 weight: hipBLASLt X.W^T, dY.W and the adapter products (torch.matmul / addmm)",
+        "qlora_over_lora16": q_ms / ms16}
+    log(f"QLoRA step {q_ms * 1e3:.0f} us against a 16-bit LoRA step {ms16 * 1e3:.0f} us")
+    del X, dY, A, B, Y, dX, ws, Wd, wt, Bt, Tr, Ur, At
     torch.cuda.empty_cache()
     return out
 
