@@ -948,9 +948,11 @@ void launch_dq_generic(const float *absmax, int64_t nb, int lb2, const float *pa
 //     load); the lane dequantizes them, adds s * d, the block max is the max
 //     of the lane pair, and the merged values get their codes from the same
 //     nearest-level search as the quantize kernels.
-// The next tile's A fragments, codes and scales are loaded while the current
-// tile is computed; waves never wait for each other inside the loop. The new
-// fp32 block scales go to absmax (or the workspace) for double quantization.
+// The next tile's codes and scales are loaded while the current tile is
+// computed; the A fragments are loaded at their use (L2 hits: A is shared by
+// every workgroup), which keeps the kernel within 168 VGPRs, three waves per
+// SIMD. Waves never wait for each other inside the loop. The new fp32 block
+// scales go to absmax (or the workspace) for double quantization.
 typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf32x4_t __attribute__((ext_vector_type(4)));
 
@@ -978,12 +980,14 @@ struct MergeParams {
 // Global data of one tile for one lane: A fragments of the first two rank
 // steps, and for each 32-row pass the lane's 16 code bytes and block scale.
 struct MergeTile {
-    u32x4 bo[2][4];
     u32x4 code[2];
     float c1o[2];
 };
 
-__global__ __launch_bounds__(kThreads) void merge_requantize_kernel(MergeParams p, CodeLut lut) {
+// (three waves per SIMD: the register budget fits 168 VGPRs, so three workgroups
+// share a CU when their LDS does)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void merge_requantize_kernel(
+    MergeParams p, CodeLut lut) {
     constexpr int kTab = 8 * kLutEntries;
     extern __shared__ __attribute__((aligned(16))) uint16_t s_bt[];  // [64][rp + 8]
     __shared__ __attribute__((aligned(16))) float s_c[4][32 * kCStride];
@@ -1004,15 +1008,6 @@ __global__ __launch_bounds__(kThreads) void merge_requantize_kernel(MergeParams 
         const int64_t kb = (int64_t)ct * kMergeCols + 64 * w;
         const bool live = kb < p.k_cols;  // uniform over the wave
         const int64_t kl = live ? kb : 0;
-#pragma unroll
-        for (int js = 0; js < 2; ++js)
-#pragma unroll
-            for (int tk = 0; tk < 4; ++tk) {
-                const int j0 = 32 * js + 8 * g;
-                d.bo[js][tk] = (live && j0 < p.r)
-                                   ? *reinterpret_cast<const u32x4 *>(p.a + (kl + 16 * tk + lr) * p.r + j0)
-                                   : u32x4{0u, 0u, 0u, 0u};
-            }
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
             const int64_t n = n0 + 32 * ps + (lane >> 1);
@@ -1064,9 +1059,6 @@ __global__ __launch_bounds__(kThreads) void merge_requantize_kernel(MergeParams 
             u32x4 bq[4], ao[4];
 #pragma unroll
             for (int tk = 0; tk < 4; ++tk) {
-                if (js < 2)
-                    bq[tk] = cur.bo[js & 1][tk];
-                else
                     bq[tk] = j0 < p.r
                                  ? *reinterpret_cast<const u32x4 *>(p.a + (kb + 16 * tk + lr) * p.r + j0)
                                  : u32x4{0u, 0u, 0u, 0u};
@@ -1287,15 +1279,25 @@ hipError_t launch_merge(const nf4_weight &w, const uint16_t *a, const uint16_t *
     p.new_codes = codes_out;
     p.new_absmax = absmax_out ? absmax_out : static_cast<float *>(workspace);
     for (int i = 0; i < 16; ++i) p.lv[i] = kLevels[i];
-    // two workgroups per CU (the register budget's occupancy), each walking a
-    // run of column tiles
+    // as many workgroups as fit the CUs at once (three per CU by registers,
+    // fewer when the adapter's LDS tile is large), each walking a run of
+    // column tiles
+    const size_t lds = (size_t)kMergeRows * (p.rp + 8) * 2;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    hipFuncAttributes fa{};
+    size_t static_lds = 0;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(merge_requantize_kernel)) == hipSuccess)
+        static_lds = fa.sharedSizeBytes;
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(3, (int64_t)(160 * 1024) / (int64_t)(lds + static_lds)));
     const int64_t row_tiles = (w.n_out + kMergeRows - 1) / kMergeRows;
-    const int64_t target = 2 * 256;
+    const int64_t target = per_cu * cus;
     int64_t per = (row_tiles * p.col_tiles + target - 1) / target;
     per = std::max<int64_t>(1, std::min<int64_t>(per, p.col_tiles));
     p.tiles_per_wg = (int32_t)per;
     p.chunks = (int32_t)((p.col_tiles + per - 1) / per);
-    const size_t lds = (size_t)kMergeRows * (p.rp + 8) * 2;
     merge_requantize_kernel<<<dim3((unsigned)(row_tiles * p.chunks)), dim3(kThreads), lds, s>>>(
         p, *code_lut());
     if (absmax_q_out) {
