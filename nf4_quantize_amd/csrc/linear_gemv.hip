@@ -420,18 +420,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(const uint16_t *__res
 // moment the whole chip reads one window of consecutive rows: HBM streams
 // such a sweep faster than the same bytes read as one contiguous region per
 // wave. Code bytes become bf16 level pairs through the lane-private table,
-// v_dot2c_f32_bf16 multiplies them with the lane's x pairs (16 registers per
-// piece, loaded once), and the half-block sum is scaled by its c1' (one
-// FMA). At the end of a row a wave reduction adds the 64 lanes and lane 0
-// stores y. Requires K = P * 2048 with P <= 4 (the x registers). With double
-// quantization a row's E4M3 codes (32 P bytes) arrive with its first piece,
-// one dword per lane, and each piece takes its lanes' codes from there with
-// one ds_bpermute; the row's c2 is one value, as K is a divisor of 256 x 64
-// weights.
-constexpr int kWaves1 = 8;
+// v_dot2c_f32_bf16 multiplies them with the lane's x pairs, and the
+// half-block sum is scaled by its c1' (one FMA). At the end of a row a wave
+// reduction adds the 64 lanes and lane 0 stores y. Requires K = P * 2048
+// with P <= 4. With double quantization a row's E4M3 codes (32 P bytes)
+// arrive with its first piece, one dword per lane, and each piece takes its
+// lanes' codes from there with one ds_bpermute; the row's c2 is one value, as
+// K is a divisor of 256 x 64 weights.
+//
+// x sits in LDS beside the table (up to 16 KiB) and each piece reads its
+// lane's 64 bytes of it: held in registers for the whole kernel it took 64
+// VGPRs per lane and capped the CU at 16 waves. With x in LDS a wave needs
+// about 80 VGPRs, and two 12-wave workgroups (the table plus x fill the
+// 160 KiB of LDS) keep 24 waves, so 72 rather than 48 pieces in flight per
+// CU.
+constexpr int kWaves1 = 12;
 constexpr int kRing1 = 4;      // pieces in flight per wave
 constexpr int kPiece = 2048;   // weights per piece: one 1 KiB load instruction
-constexpr int kMaxP1 = 4;      // pieces per row (x registers: 16 per piece)
+constexpr int kMaxP1 = 4;      // pieces per row (x in LDS: 4 KiB per piece)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -458,12 +464,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// LDS byte offset of chunk i (x pairs 4i .. 4i+3) of lane l's part of piece
+// p: 4096 p + 64 l + 16 ((i + l / 4) % 4). The rotation puts the 16 lanes of
+// an aligned group, reading one chunk index, on 16 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ uint32_t x_slot(int p, int l, int i) {
+    return (uint32_t)(4096 * p + 64 * l + 16 * ((i + (l >> 2)) & 3));
+}
+
 template <int P, bool kDQ>
-__global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__restrict__ x, WView w,
-                                                              uint16_t *__restrict__ y, Levels lv) {
+__global__ __launch_bounds__(64 * kWaves1) __attribute__((amdgpu_waves_per_eu(6))) void gemv1_kernel(
+    const uint16_t *__restrict__ x, WView w, uint16_t *__restrict__ y, Levels lv) {
     static_assert(kRing1 % P == 0, "ring must hold whole rows' pieces in phase");
+    constexpr int kXChunks = P * 256;  // 16-byte chunks of x
+    constexpr int kXIters = (kXChunks + 64 * kWaves1 - 1) / (64 * kWaves1);
     __shared__ uint32_t s_lds[256 * 64];
-    __shared__ float s_lv[16];
+    __shared__ __align__(16) char s_x[P * 4096];
     const char *lds = reinterpret_cast<const char *>(s_lds);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -474,18 +490,6 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
     // this wave's rows: gw, gw + W, gw + 2W, ...
     const int nrows = gw < w.n ? (int)((w.n - 1 - gw) / W + 1) : 0;
     const int npieces = nrows * P;
-
-    // x pairs of every piece: x[2048 p + 32 lane + 2 m], m = 0..15
-    u32x4 xv[P][4];
-    {
-        const Rsrc xr = rsrc(x, K * 2);
-#pragma unroll
-        for (int pp = 0; pp < P; ++pp)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xv[pp][i] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(2 * (kPiece * pp + 32 * lane) + 16 * i), 0, 0));
-    }
 
     // one descriptor per row (no offset grows with the matrix); loads of
     // pieces past the end go through an empty descriptor (the wait counts
@@ -518,9 +522,23 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
 
     static_for<kRing1 - 1>([&](auto JC) { issue(0, JC); });
 
+    // x: chunk c (bytes 16 c .. 16 c + 15) is chunk c % 4 of lane (c / 4) % 64
+    // of piece c / 256
+    u32x4 xc[kXIters];
+    {
+        const Rsrc xr = rsrc(x, K * 2);
+#pragma unroll
+        for (int j = 0; j < kXIters; ++j) {
+            const int c = tid + 64 * kWaves1 * j;
+            if (c < kXChunks) xc[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, 16u * c, 0, 0));
+        }
+    }
+
+    // the 16 levels go through the x area first (the empty asm keeps each an
+    // opaque scalar, so the chain is not turned back into an indexed load of
+    // the argument block); the table is built from there, then x replaces them
+    float *const s_lv = reinterpret_cast<float *>(s_x);
     if (tid < 16) {
-        // (the empty asm keeps each level an opaque scalar, so the chain is
-        // not turned back into an indexed load of the argument block)
         float v = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -536,6 +554,16 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
         s_lds[i] = pack_bf16x2(s_lv[e & 15], s_lv[e >> 4]);
     }
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kXIters; ++j) {
+        const int c = tid + 64 * kWaves1 * j;
+        if (c < kXChunks)
+            *reinterpret_cast<u32x4 *>(s_x + x_slot(c >> 8, (c >> 2) & 63, c & 3)) = xc[j];
+    }
+    __syncthreads();
+    uint32_t xo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xo[i] = x_slot(0, lane, i);
 
     float acc = 0.0f;
     uint32_t row_q8w = 0;  // the current row's scale data, kept past its ring slot
@@ -566,7 +594,9 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
                 } else {
                     sc = pc.am;
                 }
-                u32x4 lv4[4];
+                u32x4 xv[4], lv4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4 *>(s_x + 4096 * pp + xo[i]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lv4[i] = lookup4(lds, pc.c[i], lane4);
                 __builtin_amdgcn_sched_barrier(0);
@@ -577,7 +607,7 @@ __global__ __launch_bounds__(64 * kWaves1) void gemv1_kernel(const uint16_t *__r
                     for (int b = 0; b < 4; ++b) {
                         // (vector elements are copied to scalars first: a bit cast of
                         // an element expression reads element 0 with this compiler)
-                        const uint32_t lw = lv4[i][b], xw = xv[pp][i][b];
+                        const uint32_t lw = lv4[i][b], xw = xv[i][b];
                         part[b & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lw),
                                                                       __builtin_bit_cast(bf16x2_t, xw), part[b & 1],
                                                                       false);
@@ -839,9 +869,11 @@ hipError_t launch_gemv(const uint16_t *x, int64_t m, const nf4_weight &wt, uint1
         cus = 256;
     if (m == 1 && w.k % kPiece == 0 && w.k / kPiece <= kMaxP1 && w.k / kPiece != 3) {
         // two workgroups per CU (fewer for a short matrix), the rows dealt
-        // round-robin over their waves
+        // round-robin over their waves; the grid is trimmed so that every
+        // wave takes the same number of rows, give or take the last one
         const int p = (int)(w.k / kPiece);
-        const int64_t g1n = std::min<int64_t>(2 * cus, (w.n + kWaves1 - 1) / kWaves1);
+        const int64_t rows_per_wave = (w.n + 2 * cus * kWaves1 - 1) / (2 * cus * kWaves1);
+        const int64_t g1n = std::min<int64_t>(2 * cus, ((w.n + rows_per_wave - 1) / rows_per_wave + kWaves1 - 1) / kWaves1);
         const dim3 grid1((unsigned)std::max<int64_t>(1, g1n));
         if (w.q)
             launch_gemv1<true>(p, grid1, x, w, y, s);
