@@ -666,7 +666,7 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         // Four launches: both down-projections (T = X.A, U = dY.B^T), their
         // split sums, both token sums (dA, dB), their split sums.
         const int64_t mt = (m + 63) / 64, ct = rp / 64;
-        const int sT = split_count(mt * ct, K / kBK, 512), sU = split_count(mt * ct, N / kBK, 512);
+        const int sT = split_count(mt * ct, K / kBK, 256), sU = split_count(mt * ct, N / kBK, 256);
         float *const part_u = part + (int64_t)sT * m * rp;
         const DownJob jt{x, K, K, a, r, sT, sT > 1 ? part : nullptr, T};
         const DownJob ju{dy, N, N, b, N, sU, sU > 1 ? part_u : nullptr, U};
@@ -675,7 +675,7 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         e = reduce_pair(false, ReduceJob{part, sT, sT > 1 ? m * rp : 0, T},
                         ReduceJob{part_u, sU, sU > 1 ? m * rp : 0, U}, 1.0f, s);
         if (e != hipSuccess) return e;
-        const int sA = split_count((K / 64) * ct, msteps, 1024), sB = split_count((N / 64) * ct, msteps, 1024);
+        const int sA = split_count((K / 64) * ct, msteps, 512), sB = split_count((N / 64) * ct, msteps, 512);
         float *const part_b = part + (int64_t)sA * K * r;
         const TokenSumJob ja{x, U, K, false, sA, sA > 1 ? part : nullptr, da};
         const TokenSumJob jb{dy, T, N, true, sB, sB > 1 ? part_b : nullptr, db};
