@@ -249,10 +249,12 @@ typedef enum { NF4_LINEAR_DECODE = 1, NF4_LINEAR_MFMA = 2, NF4_LINEAR_PORTABLE =
 int32_t nf4_linear_kernel_path(int64_t m, int64_t n_out, int64_t k_in, int32_t r, int32_t backward);
 
 /* Bytes of device workspace that nf4_lora_backward needs: with rp = r rounded
- * up to 64, the bf16 products X.A and dY.B^T ([m x rp] each, rounded up to 256
- * bytes), then 8 fp32 partial sums of the larger of 2 x [m x rp] and
- * [k_in x r] + [r x n_out] (both products, or both gradients, are split at
- * once). No initialization is needed. Returns 0 for invalid sizes. */
+ * up to 64 and mq = m rounded up to 64 plus 64, the bf16 products X.A and
+ * dY.B^T (room for [mq x rp] each, rounded up to 256 bytes: they are stored
+ * transposed with padded rows), then 8 fp32 partial sums of the larger of
+ * 2 x [m x rp] and [k_in x r] + [r x n_out] (both products, or both gradients,
+ * are split at once). No initialization is needed. Returns 0 for invalid
+ * sizes. */
 size_t nf4_lora_backward_workspace_size(int64_t m, int64_t k_in, int64_t n_out, int32_t r);
 
 /* Gradients of the low-rank adapter of the same linear ([MF] "Gradient

@@ -286,6 +286,13 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
 // pairs. A workgroup of 4 waves owns 64 x 64 of C and a slice of the tokens;
 // loads run 3 steps of 64 tokens ahead through a register ring, and the LDS
 // tiles of a step are written one step before use.
+// With kQT, Q arrives transposed (Q^T [rp x qs], tokens contiguous, zeros
+// past m), written so by the split-sum pass of the down-projections. Its tile
+// rows are then already [column][token] runs of 128 bytes: each thread loads
+// two 16-byte chunks (through the same register ring) and stores them as they
+// are, so only P is turned around. Every column tile of the launch reads the
+// same small Q, and this takes 8 permutes and 6 of the 16 LDS stores out of
+// each thread's step.
 struct TokenSumParams {
     const uint16_t *p;  // [m x O] row-major
     const uint16_t *q;  // [m x rp] row-major
@@ -296,10 +303,12 @@ struct TokenSumParams {
     void *out;          // final C (splits == 1): fp32 or bf16, [O x r] or [r x O]
     bool f32, transposed;
     float scale;
+    int64_t qs;         // with Q transposed: the row length of Q^T in tokens
 };
 
 // Workgroups with blockIdx.x < x1 run the sums of p0, the others those of p1
 // (blockIdx.x - x1); one launch then covers both adapter gradients.
+template <bool kQT>
 __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, TokenSumParams p1, int x1) {
     __shared__ __align__(16) char s_p0[kTile], s_p1[kTile], s_q0[kTile], s_q1[kTile];
     auto ps = [&](auto SC) -> char * {
@@ -315,9 +324,10 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
 
-    const bool second = (int)blockIdx.x >= x1;
-    const TokenSumParams &p = second ? p1 : p0;
-    const int bx = second ? (int)blockIdx.x - x1 : (int)blockIdx.x;
+    // The body runs from two uniform branches, one per job, so the compiler
+    // never selects between the two parameter blocks at run time (a select
+    // of the whole struct went through scratch memory).
+    auto body = [&](const TokenSumParams &p, const int bx) {
     if ((int)blockIdx.y >= p.splits) return;  // (sized for the larger split of the two)
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -339,7 +349,16 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
     const bool q_live = (int64_t)cg * kBC + 8 * cc < p.r;
     const uint32_t p_off = (uint32_t)((2 * kp * p.O + o0 + 8 * cc) * 2);
     const uint32_t q_off = q_live ? (uint32_t)((2 * kp * p.rp + (int64_t)cg * kBC + 8 * cc) * 2) : 0xFFFFFFF0u;
-    u32x4 raw[4][4];  // [ring slot][P row 0, P row 1, Q row 0, Q row 1]
+    u32x4 raw[4][4];  // [ring slot][P row 0, P row 1, Q row 0, Q row 1] (kQT: Q^T chunks 0, 1)
+    // kQT: thread (w, lane), chunk h: tile row 16w + 8h + lane/8, tokens
+    // 8 (lane % 8) .. +7 of the step
+    uint32_t qt_off[2], qt_lds[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 16 * w + 8 * h + (lane >> 3);
+        qt_off[h] = kQT ? (uint32_t)((((int64_t)cg * kBC + row) * p.qs + 8 * (lane & 7)) * 2) : 0u;
+        qt_lds[h] = swz(row, lane & 7);
+    }
 
     // Loads of step i (ring slot SC): descriptors start at the step's first
     // token and end at token m, so tokens past m read as zeros.
@@ -349,13 +368,24 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
         const int64_t tok0 = (s_lo + (live ? i : 0)) * kBK;
         const int64_t rows = live ? min((int64_t)kBK, p.m - tok0) : 0;
         const Rsrc pr = live ? rsrc(p.p + tok0 * p.O, rows * p.O * 2) : none;
-        const Rsrc qr = live ? rsrc(p.q + tok0 * p.rp, rows * p.rp * 2) : none;
         raw[sl][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off, 0, 0));
         raw[sl][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off + (uint32_t)(p.O * 2), 0, 0));
-        raw[sl][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_off, 0, 0));
-        raw[sl][3] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_live ? q_off + (uint32_t)(p.rp * 2) : q_off, 0, 0));
+        if constexpr (kQT) {
+            // the Q^T tile: chunk h is tokens 8 (lane % 8) .. +7 of tile row
+            // (column) 16 w + 8 h + lane / 8. The descriptor starts at the
+            // step's first token; Q^T rows hold whole steps, so every access
+            // stays inside Q^T.
+            const Rsrc qr = live ? rsrc(p.q + tok0, (p.rp * p.qs - tok0) * 2) : none;
+            raw[sl][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qt_off[0], 0, 0));
+            raw[sl][3] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qt_off[1], 0, 0));
+        } else {
+            const Rsrc qr = live ? rsrc(p.q + tok0 * p.rp, rows * p.rp * 2) : none;
+            raw[sl][2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_off, 0, 0));
+            raw[sl][3] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, q_live ? q_off + (uint32_t)(p.rp * 2) : q_off, 0, 0));
+        }
     };
+
     // The column pairs of ring slot SR to LDS slot SL ([column][token] tiles).
     auto write = [&](auto SR, auto SL) {
         constexpr int sl = decltype(SR)::value;
@@ -365,9 +395,15 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
             const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
             const uint32_t off = swz(8 * cc + j, kp >> 2) + 4 * (kp & 3);
             const uint32_t a0 = raw[sl][0][j >> 1], a1 = raw[sl][1][j >> 1];
-            const uint32_t b0 = raw[sl][2][j >> 1], b1 = raw[sl][3][j >> 1];
             *reinterpret_cast<uint32_t *>(pd + off) = __builtin_amdgcn_perm(a1, a0, sel);
-            *reinterpret_cast<uint32_t *>(qd + off) = __builtin_amdgcn_perm(b1, b0, sel);
+            if constexpr (!kQT) {
+                const uint32_t b0 = raw[sl][2][j >> 1], b1 = raw[sl][3][j >> 1];
+                *reinterpret_cast<uint32_t *>(qd + off) = __builtin_amdgcn_perm(b1, b0, sel);
+            }
+        }
+        if constexpr (kQT) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4 *>(qd + qt_lds[h]) = raw[sl][2 + h];
         }
     };
 
@@ -458,7 +494,11 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
                 }
             }
         }
-
+    };
+    if ((int)blockIdx.x >= x1)
+        body(p1, (int)blockIdx.x - x1);
+    else
+        body(p0, (int)blockIdx.x);
 }
 
 }  // namespace
@@ -470,7 +510,8 @@ bool token_sum_supported(int64_t m, int64_t O, int64_t rp) {
 
 namespace {
 TokenSumParams token_params(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
-                            int splits, float *partial, void *out, bool f32, bool transposed, float scale) {
+                            int splits, float *partial, void *out, bool f32, bool transposed, float scale,
+                            int64_t qs = 0) {
     TokenSumParams p{};
     p.p = pm;
     p.q = qm;
@@ -484,6 +525,7 @@ TokenSumParams token_params(const uint16_t *pm, const uint16_t *qm, int64_t m, i
     p.f32 = f32;
     p.transposed = transposed;
     p.scale = scale;
+    p.qs = qs;
     return p;
 }
 }  // namespace
@@ -493,19 +535,22 @@ hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, i
                             hipStream_t s) {
     const TokenSumParams p = token_params(pm, qm, m, O, rp, r, splits, partial, out, f32, transposed, scale);
     const dim3 grid((unsigned)(O / kBM), (unsigned)p.splits, (unsigned)(rp / kBC));
-    token_sum_kernel<<<grid, kThreads, 0, s>>>(p, p, (int)grid.x);
+    token_sum_kernel<false><<<grid, kThreads, 0, s>>>(p, p, (int)grid.x);
     return hipGetLastError();
 }
 
 hipError_t launch_token_sum_pair(const TokenSumJob &a, const TokenSumJob &b, int64_t m, int64_t rp, int32_t r,
-                                 bool f32, float scale, hipStream_t s) {
+                                 bool f32, float scale, int64_t qt, hipStream_t s) {
     const TokenSumParams pa = token_params(a.pm, a.qm, m, a.O, rp, r, a.splits, a.partial, a.out, f32,
-                                           a.transposed, scale);
+                                           a.transposed, scale, qt);
     const TokenSumParams pb = token_params(b.pm, b.qm, m, b.O, rp, r, b.splits, b.partial, b.out, f32,
-                                           b.transposed, scale);
+                                           b.transposed, scale, qt);
     const int xa = (int)(a.O / kBM);
     const dim3 grid((unsigned)(xa + b.O / kBM), (unsigned)max(pa.splits, pb.splits), (unsigned)(rp / kBC));
-    token_sum_kernel<<<grid, kThreads, 0, s>>>(pa, pb, xa);
+    if (qt > 0)
+        token_sum_kernel<true><<<grid, kThreads, 0, s>>>(pa, pb, xa);
+    else
+        token_sum_kernel<false><<<grid, kThreads, 0, s>>>(pa, pb, xa);
     return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ hipError_t launch_adapter_down_pair(const DownJob &fwd, const DownJob &bwd, int6
 // Q [m x rp] bf16 (columns past r unused). With partial != nullptr split z of
 // `splits` writes its fp32 sum to partial[z] ([O x r], or [r x O] when
 // transposed); otherwise scale * C goes to out (fp32 or bf16, [O x r] or
-// [r x O]).
+// [r x O]). The paired launch can take Q transposed instead: Q^T [rp x qt]
+// bf16, row j holding Q[t][j] at t (qt = lora_qt_row(m), zeros past m).
 bool token_sum_supported(int64_t m, int64_t O, int64_t rp);
 hipError_t launch_token_sum(const uint16_t *pm, const uint16_t *qm, int64_t m, int64_t O, int64_t rp, int32_t r,
                             int splits, float *partial, void *out, bool f32, bool transposed, float scale,
@@ -92,8 +93,16 @@ struct TokenSumJob {
     float *partial;
     void *out;
 };
+// qt: 0 for Q [m x rp], else the row length of Q^T [rp x qt] (both jobs).
 hipError_t launch_token_sum_pair(const TokenSumJob &a, const TokenSumJob &b, int64_t m, int64_t rp, int32_t r,
-                                 bool f32, float scale, hipStream_t s);
+                                 bool f32, float scale, int64_t qt, hipStream_t s);
+// Row length (tokens) of the transposed Q of the paired token sums: m
+// rounded up to whole 64-token steps, plus one more 128-byte line, so that
+// rows do not sit a power of two apart (every workgroup reads the same 64
+// rows per step; with a 2^k-byte row stride they shared one L2 channel).
+inline int64_t lora_qt_row(int64_t m) { return (m + 63) / 64 * 64 + 64; }
+// The transposed Q fits 32-bit buffer offsets.
+inline bool token_sum_qt_supported(int64_t m, int64_t rp) { return rp * lora_qt_row(m) * 2 < ((int64_t)1 << 31); }
 
 // Large-M MFMA path (N % 64 == 0, r % 8 == 0, r <= 256): linear_gemm.hip.
 bool gemm_supported(int64_t n, int32_t r);
@@ -107,11 +116,12 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &w,
 // Adapter gradients dA = s X^T (dY B^T) [K x r] and dB = s (X A)^T dY [r x N]
 // (linear_gemm.hip); da or db may be nullptr. Needs K % 64 == 0, N % 64 == 0,
 // r % 8 == 0, r <= 256, and a workspace of lora_grads_workspace_bytes.
-// Layout: T and U (bf16, lora_product_bytes each), then the fp32 partial sums
-// of both down-projections, later of both token sums.
+// Layout: T and U (bf16, lora_product_bytes of lora_qt_row(m) tokens each:
+// the token sums read them transposed and zero-padded), then the fp32
+// partial sums of both down-projections, later of both token sums.
 inline size_t lora_grads_workspace_bytes(int64_t m, int64_t k, int64_t n, int64_t rp, int64_t r) {
     const int64_t most = std::max(2 * m * rp, k * r + r * n);
-    return 2 * lora_product_bytes(m, rp) + (size_t)kSplitMax * (size_t)most * 4u;
+    return 2 * lora_product_bytes(lora_qt_row(m), rp) + (size_t)kSplitMax * (size_t)most * 4u;
 }
 hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
                              const uint16_t *a, const uint16_t *b, int32_t r, float s_lora, void *da, void *db,

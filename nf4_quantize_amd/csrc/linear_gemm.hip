@@ -520,6 +520,58 @@ __global__ __launch_bounds__(256) void reduce_partials_pair_kernel(ReduceJob a, 
     const int64_t blk = second ? (int64_t)blockIdx.x - b1 : (int64_t)blockIdx.x;
     reduce_partials_at<kF32>(j.part, j.splits, j.count, scale, j.out, (blk * 256 + threadIdx.x) * 4);
 }
+// The split sums of a down-projection written transposed, for the token
+// sums: out[j][t] = bf16(scale * sum_z part[z][t][j]) (the sum in the order
+// of reduce_partials_at, so the values are those of the row-major pass), with
+// zeros for tokens m <= t < ld and columns j >= r (ld: lora_qt_row(m)).
+// A workgroup owns 32 tokens x 64 columns and turns them around in LDS (row
+// stride 65 floats: both the row writes and the column reads hit distinct
+// banks).
+struct TransposeJob {
+    const float *part;  // [splits][m][rp] fp32
+    int splits;
+    int64_t m, rp, ld;
+    int32_t r;
+    uint16_t *out;      // [rp][ld] bf16
+};
+__global__ __launch_bounds__(256) void reduce_transpose_pair_kernel(TransposeJob a, TransposeJob b, int64_t b1,
+                                                                    float scale) {
+    __shared__ float s_t[32][65];
+    const bool second = (int64_t)blockIdx.x >= b1;
+    const TransposeJob &J = second ? b : a;
+    const int64_t blk = second ? (int64_t)blockIdx.x - b1 : (int64_t)blockIdx.x;
+    const int64_t tiles_t = J.ld / 32;
+    const int64_t t0 = (blk % tiles_t) * 32, j0 = (blk / tiles_t) * 64;
+    const int tid = threadIdx.x;
+    const int cc = 4 * (tid & 15);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int rr = (tid >> 4) + 16 * k;
+        const int64_t t = t0 + rr;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < J.m) {
+            const float *src = J.part + t * J.rp + j0 + cc;
+            acc = *reinterpret_cast<const f32x4 *>(src);
+            for (int z = 1; z < J.splits; ++z) acc += *reinterpret_cast<const f32x4 *>(src + z * J.m * J.rp);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_t[rr][cc + e] = (j0 + cc + e < J.r) ? scale * acc[e] : 0.0f;
+    }
+    __syncthreads();
+    // thread: column j0 + tid / 4, tokens t0 + 8 (tid % 4) .. +7 (one 16-byte store)
+    const int jj = tid >> 2, tq = 8 * (tid & 3);
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(s_t[tq + 2 * e][jj], s_t[tq + 2 * e + 1][jj]);
+    *reinterpret_cast<u32x4 *>(J.out + (j0 + jj) * J.ld + t0 + tq) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+}
+hipError_t reduce_transpose_pair(const TransposeJob &a, const TransposeJob &b, float scale, hipStream_t s) {
+    const int64_t ba = (a.ld / 32) * (a.rp / 64), bb = (b.ld / 32) * (b.rp / 64);
+    if (ba + bb == 0) return hipSuccess;
+    reduce_transpose_pair_kernel<<<dim3((unsigned)(ba + bb)), 256, 0, s>>>(a, b, ba, scale);
+    return hipGetLastError();
+}
+
 hipError_t reduce_pair(bool f32, const ReduceJob &a, const ReduceJob &b, float scale, hipStream_t s) {
     const int64_t ba = (a.count / 4 + 255) / 256, bb = (b.count / 4 + 255) / 256;
     if (ba + bb == 0) return hipSuccess;
@@ -639,21 +691,24 @@ hipError_t launch_gemm_dgrad(const uint16_t *dy, int64_t m, const nf4_weight &wt
 }
 
 // Adapter gradients ([MF] "Gradient Computation"): T = X.A and U = dY.B^T
-// (bf16, unscaled) by the down-projection, then two token sums on the generic
-// kernel with a transposed A tile:
+// (bf16, unscaled) by the down-projection, then two token sums (on the
+// streaming kernel of linear_adapter.hip, or the generic kernel with a
+// transposed A tile):
 //   dA = s X^T U   [K x r]: Aop[k][i] = X[i][k], Bop[c][i] = U[i][c]
 //   dB = s T^T dY  [r x N]: Aop[c][i] = T[i][c], Bop[n][i] = dY[i][n]
 // Each token sum is split over up to kSplitMax workgroups per tile; its fp32
 // partial sums are added, scaled by s and stored (bf16 or fp32) by one more
-// pass. Workspace: T, U (lora_product_bytes each), then the partial sums.
+// pass. Workspace: T, U (lora_product_bytes of m rounded up to 64 each), then
+// the partial sums. On the four-launch path T and U are stored transposed
+// ([rp][lora_qt_row(m)]) for the token sums.
 hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, int64_t K, int64_t N,
                              const uint16_t *a, const uint16_t *b, int32_t r, float s_lora, void *da, void *db,
                              bool f32_out, void *ws, hipStream_t s) {
-    const int64_t rp = round64(r);
+    const int64_t rp = round64(r), mq = lora_qt_row(m);
     char *const base = static_cast<char *>(ws);
     uint16_t *const T = reinterpret_cast<uint16_t *>(base);
-    uint16_t *const U = reinterpret_cast<uint16_t *>(base + lora_product_bytes(m, rp));
-    float *const part = reinterpret_cast<float *>(base + 2 * lora_product_bytes(m, rp));
+    uint16_t *const U = reinterpret_cast<uint16_t *>(base + lora_product_bytes(mq, rp));
+    float *const part = reinterpret_cast<float *>(base + 2 * lora_product_bytes(mq, rp));
     const Levels lv = levels();
     hipError_t e = hipSuccess;
     const int64_t msteps = round64(m) / kBK;
@@ -662,24 +717,26 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         return (int)min((int64_t)sp, max((int64_t)1, steps));
     };
     if (m > 0 && da && db && adapter_down_supported(true, K, K, r, r) && adapter_down_supported(false, N, N, N, r) &&
-        token_sum_supported(m, K, rp) && token_sum_supported(m, N, rp)) {
-        // Four launches: both down-projections (T = X.A, U = dY.B^T), their
-        // split sums, both token sums (dA, dB), their split sums.
+        token_sum_supported(m, K, rp) && token_sum_supported(m, N, rp) && token_sum_qt_supported(m, rp)) {
+        // Four launches: both down-projections (T = X.A, U = dY.B^T, fp32
+        // partial sums even without a split), their split sums written
+        // transposed (T^T, U^T [rp][mq]), both token sums (dA, dB), their
+        // split sums.
         const int64_t mt = (m + 63) / 64, ct = rp / 64;
         const int sT = split_count(mt * ct, K / kBK, 256), sU = split_count(mt * ct, N / kBK, 256);
         float *const part_u = part + (int64_t)sT * m * rp;
-        const DownJob jt{x, K, K, a, r, sT, sT > 1 ? part : nullptr, T};
-        const DownJob ju{dy, N, N, b, N, sU, sU > 1 ? part_u : nullptr, U};
+        const DownJob jt{x, K, K, a, r, sT, part, T};
+        const DownJob ju{dy, N, N, b, N, sU, part_u, U};
         e = launch_adapter_down_pair(jt, ju, m, r, rp, 1.0f, s);
         if (e != hipSuccess) return e;
-        e = reduce_pair(false, ReduceJob{part, sT, sT > 1 ? m * rp : 0, T},
-                        ReduceJob{part_u, sU, sU > 1 ? m * rp : 0, U}, 1.0f, s);
+        e = reduce_transpose_pair(TransposeJob{part, sT, m, rp, mq, r, T}, TransposeJob{part_u, sU, m, rp, mq, r, U},
+                                  1.0f, s);
         if (e != hipSuccess) return e;
         const int sA = split_count((K / 64) * ct, msteps, 512), sB = split_count((N / 64) * ct, msteps, 512);
         float *const part_b = part + (int64_t)sA * K * r;
         const TokenSumJob ja{x, U, K, false, sA, sA > 1 ? part : nullptr, da};
         const TokenSumJob jb{dy, T, N, true, sB, sB > 1 ? part_b : nullptr, db};
-        e = launch_token_sum_pair(ja, jb, m, rp, r, f32_out, s_lora, s);
+        e = launch_token_sum_pair(ja, jb, m, rp, r, f32_out, s_lora, mq, s);
         if (e != hipSuccess) return e;
         return reduce_pair(f32_out, ReduceJob{part, sA, sA > 1 ? K * r : 0, da},
                            ReduceJob{part_b, sB, sB > 1 ? (int64_t)r * N : 0, db}, s_lora, s);

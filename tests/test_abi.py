@@ -213,9 +213,10 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_lora_backward_validation(L):
     f = L.nf4_lora_backward
     ws = nq.nf4_lora_backward_workspace_size(64, 512, 256, 16)
-    # X.A and dY.B^T as bf16 [64 x 64], then 8 fp32 partial sums of the larger
-    # of 2 x [64 x 64] and [512 x 16] + [16 x 256]
-    assert ws == 2 * 64 * 64 * 2 + 8 * (512 * 16 + 16 * 256) * 4
+    # X.A and dY.B^T as bf16, stored transposed [64 x 128] (64 tokens rounded
+    # up to a step of 64, plus one padding step), then 8 fp32 partial sums of
+    # the larger of 2 x [64 x 64] and [512 x 16] + [16 x 256]
+    assert ws == 2 * 64 * 128 * 2 + 8 * (512 * 16 + 16 * 256) * 4
     assert nq.nf4_lora_backward_workspace_size(64, 512, 256, 0) == 0
     assert nq.nf4_lora_backward_workspace_size(-1, 512, 256, 16) == 0
 
