@@ -290,9 +290,28 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
 // past m), written so by the split-sum pass of the down-projections. Its tile
 // rows are then already [column][token] runs of 128 bytes: each thread loads
 // two 16-byte chunks (through the same register ring) and stores them as they
-// are, so only P is turned around. Every column tile of the launch reads the
-// same small Q, and this takes 8 permutes and 6 of the 16 LDS stores out of
-// each thread's step.
+// are. P is not turned around in registers either: its tile stays row-major
+// ([token][column], 16-byte stores) and the MFMA operand comes from gfx950's
+// transposing LDS read, ds_read_b64_tr_b16 (lds_read_tr16). Within each group
+// of 16 lanes that read returns to lane i the 16-bit element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12;
+// with lane j pointing at token row tau + j / 4, columns 4 (j % 4) .. +3 of
+// an operand's 16 columns, lane i receives tokens tau .. tau + 3 of column i.
+// Two such reads make the lane's 8 tokens. No permutes are left in the step.
+// The transposing LDS read of 16-bit data (see above): 4 elements, 2 dwords.
+__device__ __forceinline__ gemm::u32x2 lds_read_tr16(const char *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(gemm::u32x2, v);
+}
+// 16-byte chunk swizzle of the row-major P tile (64 rows x 128 B): chunk c of
+// row r sits at c ^ tsig(r). The 8 rows that one half-wave's transposing
+// reads touch (tau + q and tau + 16 + q, q < 4, tau % 8 in {0, 4}) then fall
+// on 8 distinct 32-byte bank windows, and each 16-byte store instruction
+// (8 consecutive rows, whole rows) fills the 64 banks 4 times over.
+__device__ __forceinline__ int tsig(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 4) & 1); }
+
 struct TokenSumParams {
     const uint16_t *p;  // [m x O] row-major
     const uint16_t *q;  // [m x rp] row-major
@@ -359,6 +378,17 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
         qt_off[h] = kQT ? (uint32_t)((((int64_t)cg * kBC + row) * p.qs + 8 * (lane & 7)) * 2) : 0u;
         qt_lds[h] = swz(row, lane & 7);
     }
+    // kQT: the P tile row-major. Thread (w, lane), load h: token row
+    // 16w + 8h + lane/8, columns o0 + 8 (lane % 8) .. +7 (each load
+    // instruction 8 rows x 128 contiguous bytes), stored at chunk
+    // (lane % 8) ^ tsig(row).
+    uint32_t pt_off[2], pt_lds[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 16 * w + 8 * h + (lane >> 3);
+        pt_off[h] = kQT ? (uint32_t)((row * p.O + o0 + 8 * (lane & 7)) * 2) : 0u;
+        pt_lds[h] = (uint32_t)(row * 128 + 16 * ((lane & 7) ^ tsig(row)));
+    }
 
     // Loads of step i (ring slot SC): descriptors start at the step's first
     // token and end at token m, so tokens past m read as zeros.
@@ -368,8 +398,10 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
         const int64_t tok0 = (s_lo + (live ? i : 0)) * kBK;
         const int64_t rows = live ? min((int64_t)kBK, p.m - tok0) : 0;
         const Rsrc pr = live ? rsrc(p.p + tok0 * p.O, rows * p.O * 2) : none;
-        raw[sl][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off, 0, 0));
-        raw[sl][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, p_off + (uint32_t)(p.O * 2), 0, 0));
+        raw[sl][0] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, kQT ? pt_off[0] : p_off, 0, 0));
+        raw[sl][1] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, kQT ? pt_off[1] : p_off + (uint32_t)(p.O * 2), 0, 0));
         if constexpr (kQT) {
             // the Q^T tile: chunk h is tokens 8 (lane % 8) .. +7 of tile row
             // (column) 16 w + 8 h + lane / 8. The descriptor starts at the
@@ -390,20 +422,22 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
     auto write = [&](auto SR, auto SL) {
         constexpr int sl = decltype(SR)::value;
         char *pd = ps(SL), *qd = qs(SL);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t off = swz(8 * cc + j, kp >> 2) + 4 * (kp & 3);
-            const uint32_t a0 = raw[sl][0][j >> 1], a1 = raw[sl][1][j >> 1];
-            *reinterpret_cast<uint32_t *>(pd + off) = __builtin_amdgcn_perm(a1, a0, sel);
-            if constexpr (!kQT) {
-                const uint32_t b0 = raw[sl][2][j >> 1], b1 = raw[sl][3][j >> 1];
-                *reinterpret_cast<uint32_t *>(qd + off) = __builtin_amdgcn_perm(b1, b0, sel);
-            }
-        }
         if constexpr (kQT) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4 *>(qd + qt_lds[h]) = raw[sl][2 + h];
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<u32x4 *>(pd + pt_lds[h]) = raw[sl][h];
+                *reinterpret_cast<u32x4 *>(qd + qt_lds[h]) = raw[sl][2 + h];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t off = swz(8 * cc + j, kp >> 2) + 4 * (kp & 3);
+                const uint32_t a0 = raw[sl][0][j >> 1], a1 = raw[sl][1][j >> 1];
+                const uint32_t b0 = raw[sl][2][j >> 1], b1 = raw[sl][3][j >> 1];
+                *reinterpret_cast<uint32_t *>(pd + off) = __builtin_amdgcn_perm(a1, a0, sel);
+                *reinterpret_cast<uint32_t *>(qd + off) = __builtin_amdgcn_perm(b1, b0, sel);
+            }
         }
     };
 
@@ -416,6 +450,22 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
             fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
             fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
         }
+    // kQT: the two transposing reads h of the P operand of row tile i and
+    // substep ks: lane (lr, g) points at token row tau = 16g + 8ks + 4h + lr/4,
+    // columns 32wr + 16i + 4 (lr % 4) .. +3 (logical chunk 4wr + 2i +
+    // (lr % 4) / 2, byte 8 (lr % 2) within it), and receives tokens
+    // 16g + 8ks + 4h .. +3 of column 32wr + 16i + lr.
+    uint32_t tr_off[2][2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tau = 16 * g + 8 * ks + 4 * h + (lr >> 2);
+                const int c = 4 * wr + 2 * i + ((lr & 3) >> 1);
+                tr_off[i][ks][h] = (uint32_t)(tau * 128 + 16 * (c ^ tsig(tau)) + 8 * (lr & 1));
+            }
     f32x4_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -439,7 +489,13 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
                 u32x4 a[2], b[2];
 #pragma unroll
                 for (int i2 = 0; i2 < 2; ++i2) {
-                    a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
+                    if constexpr (kQT) {
+                        const gemm::u32x2 lo = lds_read_tr16(xa + tr_off[i2][ks][0]);
+                        const gemm::u32x2 hi = lds_read_tr16(xa + tr_off[i2][ks][1]);
+                        a[i2] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    } else {
+                        a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
+                    }
                     b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
                 }
 #pragma unroll
