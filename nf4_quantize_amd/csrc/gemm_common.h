@@ -52,6 +52,20 @@ __device__ __forceinline__ void valu_to_mfma() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// gfx950's transposing LDS read of 16-bit data (ds_read_b64_tr_b16): every
+// lane gives the address of an 8-byte piece (4 elements); within each group
+// of 16 lanes, lane i receives element i % 4 of the pieces of lanes i / 4,
+// i / 4 + 4, i / 4 + 8 and i / 4 + 12, in that order. With lane j pointing at
+// row tau + j / 4, columns 4 (j % 4) .. +3 of a row-major tile, lane i thus
+// receives rows tau .. tau + 3 of column i: half of an MFMA operand whose
+// contraction runs down the tile's rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 // Two fp32 values as an fp16 pair (low half first).
 __device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |

@@ -298,13 +298,6 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
 // with lane j pointing at token row tau + j / 4, columns 4 (j % 4) .. +3 of
 // an operand's 16 columns, lane i receives tokens tau .. tau + 3 of column i.
 // Two such reads make the lane's 8 tokens. No permutes are left in the step.
-// The transposing LDS read of 16-bit data (see above): 4 elements, 2 dwords.
-__device__ __forceinline__ gemm::u32x2 lds_read_tr16(const char *p) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
-    return __builtin_bit_cast(gemm::u32x2, v);
-}
 // 16-byte chunk swizzle of the row-major P tile (64 rows x 128 B): chunk c of
 // row r sits at c ^ tsig(r). The 8 rows that one half-wave's transposing
 // reads touch (tau + q and tau + 16 + q, q < 4, tau % 8 in {0, 4}) then fall
@@ -490,8 +483,8 @@ __global__ __launch_bounds__(kThreads) void token_sum_kernel(TokenSumParams p0, 
 #pragma unroll
                 for (int i2 = 0; i2 < 2; ++i2) {
                     if constexpr (kQT) {
-                        const gemm::u32x2 lo = lds_read_tr16(xa + tr_off[i2][ks][0]);
-                        const gemm::u32x2 hi = lds_read_tr16(xa + tr_off[i2][ks][1]);
+                        const gemm::u32x2 lo = gemm::lds_read_tr16(xa + tr_off[i2][ks][0]);
+                        const gemm::u32x2 hi = gemm::lds_read_tr16(xa + tr_off[i2][ks][1]);
                         a[i2] = u32x4{lo.x, lo.y, hi.x, hi.y};
                     } else {
                         a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
