@@ -732,7 +732,7 @@ hipError_t launch_lora_grads(const uint16_t *x, const uint16_t *dy, int64_t m, i
         e = reduce_transpose_pair(TransposeJob{part, sT, m, rp, mq, r, T}, TransposeJob{part_u, sU, m, rp, mq, r, U},
                                   1.0f, s);
         if (e != hipSuccess) return e;
-        const int sA = split_count((K / 64) * ct, msteps, 512), sB = split_count((N / 64) * ct, msteps, 512);
+        const int sA = split_count((K / 64) * ct, msteps, 256), sB = split_count((N / 64) * ct, msteps, 256);
         float *const part_b = part + (int64_t)sA * K * r;
         const TokenSumJob ja{x, U, K, false, sA, sA > 1 ? part : nullptr, da};
         const TokenSumJob jb{dy, T, N, true, sB, sB > 1 ? part_b : nullptr, db};
