@@ -13,10 +13,11 @@
 // K advances 64 per step. Each step's Aop tile (64 rows x 128 B) goes global
 // -> LDS by direct-to-LDS loads into a ring of kStages slots, issued
 // kStages - 1 steps ahead; so does the Bop tile of the input gradient (rows
-// of B). The forward's Bop tile is a column slice of A: each thread loads two
-// 16-byte row pieces and writes their 8 column pairs (v_perm_b32) to LDS, a
-// step before use. Tiles are stored [row][64] with 16-byte chunks XOR-
-// swizzled by row. The four waves split the 64 x 64 output 2 x 2 and run
+// of B). The forward's Bop operand is a column slice of A: each thread loads
+// two 16-byte row pieces and stores them as they are into a row-major [k][c]
+// tile a step before use, and the operand comes from the transposing LDS read
+// (lds_read_tr16). The DMA-fed tiles are stored [row][64] with 16-byte chunks
+// XOR-swizzled by row. The four waves split the 64 x 64 output 2 x 2 and run
 // v_mfma_f32_16x16x32_bf16.
 #include <type_traits>
 
@@ -30,6 +31,8 @@ using gemm::lds_void;
 using gemm::Rsrc;
 using gemm::rsrc;
 using gemm::vmcnt_at_most;
+using gemm::lds_read_tr16;
+using gemm::u32x2;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -41,6 +44,14 @@ constexpr int kStages = 4;              // LDS ring slots
 constexpr int kTile = kBM * kBK * 2;    // one tile: 64 rows x 128 B
 constexpr int kLoads = 4;               // vector-memory instructions per wave per step
 static_assert(kBC == kBM, "Aop and Bop tiles share one layout");
+
+// 16-byte chunk swizzle of a row-major 64 x 128 B tile read by the
+// transposing LDS read (lds_read_tr16, gemm_common.h): chunk c of
+// row r sits at c ^ tsig(r). The 8 rows that one half-wave's transposing
+// reads touch (tau + q and tau + 16 + q, q < 4, tau % 8 in {0, 4}) then fall
+// on 8 distinct 32-byte bank windows, and each 16-byte store instruction
+// (8 consecutive rows, whole rows) fills the 64 banks 4 times over.
+__device__ __forceinline__ int tsig(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 4) & 1); }
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
@@ -134,9 +145,17 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
         const bool cc_live = (int64_t)cg * kBC + 8 * cc < p.r;
         const int64_t bn_bytes = kNN ? p.klen * p.ldm * 2 : 0;
         const Rsrc bn_rs = rsrc(p.mat, bn_bytes);
-        const uint32_t bn_off = cc_live ? (uint32_t)((2 * kp * p.ldm + (int64_t)cg * kBC + 8 * cc) * 2)
-                                        : (uint32_t)bn_bytes;
-        const uint32_t bn_off1 = cc_live ? bn_off + (uint32_t)(p.ldm * 2) : bn_off;
+        // forward: the step's 64 rows of A (columns 64 cg .. +63) go to LDS
+        // row-major, [k][c] with the tsig swizzle: thread (w, lane), load h:
+        // row 16 w + 8 h + lane / 8, columns 8 (lane % 8) .. +7 (past r the
+        // lane offset is pushed out of the descriptor's range)
+        uint32_t bn_o[2], bn_lds[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int row = 16 * w + 8 * h2 + (lane >> 3);
+            bn_o[h2] = cc_live ? (uint32_t)((row * p.ldm + (int64_t)cg * kBC + 8 * cc) * 2) : (uint32_t)bn_bytes;
+            bn_lds[h2] = (uint32_t)(row * 128 + 16 * (cc ^ tsig(row)));
+        }
         u32x4 braw[kStages][2];
 
         // Loads of this workgroup's step i into ring slot SC (i % kStages): always
@@ -163,22 +182,17 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
                 constexpr int s = decltype(SC)::value;
                 const Rsrc br = live ? bn_rs : none;
                 const int so = __builtin_amdgcn_readfirstlane((int)(k0 * p.ldm * 2));
-                braw[s][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off, so, 0));
-                braw[s][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_off1, so, 0));
+                braw[s][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_o[0], so, 0));
+                braw[s][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, bn_o[1], so, 0));
             }
         };
-        // Forward: the column pairs of the step in slot SC to its Bop tile.
+        // Forward: the rows of A of the step in slot SC, stored as loaded.
         auto write_bn = [&](auto SC) {
             if constexpr (kNN) {
                 constexpr int s = decltype(SC)::value;
                 char *bd = bs(SC);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t lo = braw[s][0][j >> 1], hi = braw[s][1][j >> 1];
-                    const uint32_t d = (j & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                                               : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-                    *reinterpret_cast<uint32_t *>(bd + swz(8 * cc + j, kp >> 2) + 4 * (kp & 3)) = d;
-                }
+                for (int h2 = 0; h2 < 2; ++h2) *reinterpret_cast<u32x4 *>(bd + bn_lds[h2]) = braw[s][h2];
             }
         };
 
@@ -193,6 +207,22 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
                 fa[i][ks] = swz(32 * wr + 16 * i + lr, 2 * g + ks);
                 fb[i][ks] = swz(32 * wc + 16 * i + lr, 2 * g + ks);
             }
+        // forward: Bop of column tile i, substep ks by two transposing reads
+        // h2 of the row-major A tile: lane (lr, g) points at row
+        // 16 g + 8 ks + 4 h2 + lr / 4, columns 32 wc + 16 i + 4 (lr % 4) .. +3,
+        // and receives rows (k) 16 g + 8 ks + 4 h2 .. +3 of column
+        // 32 wc + 16 i + lr, the k order of the Aop fragments
+        uint32_t trb[2][2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int tau = 16 * g + 8 * ks + 4 * h2 + (lr >> 2);
+                    const int c = 4 * wc + 2 * i + ((lr & 3) >> 1);
+                    trb[i][ks][h2] = (uint32_t)(tau * 128 + 16 * (c ^ tsig(tau)) + 8 * (lr & 1));
+                }
         f32x4_t acc[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -219,7 +249,13 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
 #pragma unroll
                     for (int i2 = 0; i2 < 2; ++i2) {
                         a[i2] = *reinterpret_cast<const u32x4 *>(xa + fa[i2][ks]);
-                        b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+                        if constexpr (kNN) {
+                            const u32x2 lo = lds_read_tr16(xb + trb[i2][ks][0]);
+                            const u32x2 hi = lds_read_tr16(xb + trb[i2][ks][1]);
+                            b[i2] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                        } else {
+                            b[i2] = *reinterpret_cast<const u32x4 *>(xb + fb[i2][ks]);
+                        }
                     }
 #pragma unroll
                     for (int i2 = 0; i2 < 2; ++i2)
@@ -298,12 +334,6 @@ __global__ __launch_bounds__(kThreads) void adapter_down_kernel(AdapterParams p0
 // with lane j pointing at token row tau + j / 4, columns 4 (j % 4) .. +3 of
 // an operand's 16 columns, lane i receives tokens tau .. tau + 3 of column i.
 // Two such reads make the lane's 8 tokens. No permutes are left in the step.
-// 16-byte chunk swizzle of the row-major P tile (64 rows x 128 B): chunk c of
-// row r sits at c ^ tsig(r). The 8 rows that one half-wave's transposing
-// reads touch (tau + q and tau + 16 + q, q < 4, tau % 8 in {0, 4}) then fall
-// on 8 distinct 32-byte bank windows, and each 16-byte store instruction
-// (8 consecutive rows, whole rows) fills the 64 banks 4 times over.
-__device__ __forceinline__ int tsig(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 4) & 1); }
 
 struct TokenSumParams {
     const uint16_t *p;  // [m x O] row-major
